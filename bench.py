@@ -1,0 +1,250 @@
+"""Benchmark of the scaled FP8 linear layer on one MI355X.
+
+One step = one pass of the whole hot path over the 70B-MLP workload
+(X[16384 x 8192] bf16 activations with 0.05% outliers x100, W[28672 x 8192]
+bf16 weights ~ 0.015 N(0,1), synthetic, seeded), inputs resident in HBM:
+
+  per-tensor:  amax(X), amax(W) -> biases -> E4M3 casts -> FP8 GEMM
+               Y = X W^T (bf16 out, fused output amax) -> the output amax is
+               pushed into a 16-entry delayed-scaling history and the next
+               layer's delayed bias is derived from it
+  MXFP8:       1x32-block E8M0 casts of X and W -> block-scaled GEMM
+               (bf16 out, fused output amax)
+
+Prints ONE JSON line.  `value` is the whole step's effective FP8 GEMM
+throughput (both GEMMs' 2MNK flops over the step time, quantization
+included); per-kernel GB/s and TFLOP/s are in `breakdown`; `roofline` is the
+dominant kernel (the FP8 GEMM) against the dense FP8 MFMA peak; `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (no sparsity)
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+WORKLOAD = "llama2_70b_mlp_16384x28672x8192"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(xb, wb, target_s: float):
+    """Time the oracle (as it stands) on a bounded sample of the workload and
+    scale to the metric: TFLOP/s of the full step's GEMM flops over the
+    oracle's extrapolated full-step time."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    M, K = xb.shape
+    N = wb.shape[0]
+    # element-wise part: amax, bias, E4M3 cast and MX cast of a row sample
+    rows = 256
+    t0 = time.perf_counter()
+    xs = oracle.bf16_bits_to_f64(xb[:rows])
+    ws = oracle.bf16_bits_to_f64(wb[:rows])
+    bx = oracle.compute_bias(oracle.amax(xs), oracle.E4M3)
+    bw = oracle.compute_bias(oracle.amax(ws), oracle.E4M3)
+    qx = oracle.quantize(xs, oracle.E4M3, bx)
+    qw = oracle.quantize(ws, oracle.E4M3, bw)
+    mqx, msx = oracle.mx_quantize(xs, oracle.E4M3)
+    mqw, msw = oracle.mx_quantize(ws, oracle.E4M3)
+    t_elem = (time.perf_counter() - t0) / (2 * rows * K)          # seconds per element
+    # GEMM part: float64 reference GEMMs on growing samples until ~target_s
+    m = n = 256
+    t_gemm = 0.0
+    flops = 0.0
+    t_start = time.perf_counter()
+    while time.perf_counter() - t_start < target_s:
+        t0 = time.perf_counter()
+        oracle.scaled_gemm_ref(qx[:m], oracle.E4M3, bx, qw[:n], oracle.E4M3, bw)
+        oracle.mx_gemm_ref(mqx[:m], msx[:m], oracle.E4M3, mqw[:n], msw[:n], oracle.E4M3)
+        t_gemm += time.perf_counter() - t0
+        flops += 2 * 2.0 * m * n * K
+    gemm_rate = flops / t_gemm                                      # flop/s
+    full_flops = 2 * 2.0 * M * N * K
+    full_time = t_elem * (M + N) * K * 1.0 + full_flops / gemm_rate
+    return {
+        "value": full_flops / full_time / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"oracle (NumPy float64) on rows 0..{rows - 1} of X and W for amax/bias/E4M3/MX casts "
+                   f"({t_elem * 1e9:.1f} ns/element, 1 thread) and repeated {m}x{n}x{K} per-tensor + MX "
+                   f"reference GEMMs for {t_gemm:.1f} s ({gemm_rate / 1e9:.1f} GFLOP/s, BLAS threads={threads}); "
+                   f"extrapolated to the full step: {full_time:.0f} s"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import scaled_quantize_fp8_amd as sq
+    from workloads import make
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    xb, wb = make("c5", "X"), make("c5", "W")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, w = up(xb), up(wb)
+    M, K = x.shape
+    N = w.shape[0]
+    gen_s = time.perf_counter() - t_gen
+
+    # device buffers (allocated once, outside the timed region)
+    f32 = dict(dtype=torch.float32, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    ax, aw, ay, aym = (torch.empty(1, **f32) for _ in range(4))
+    bx, bw, bnext = (torch.empty(1, **i32) for _ in range(3))
+    qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    qw = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    mqx = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    mqw = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    msx = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    msw = torch.empty((N, K // 32), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ym = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    hist = torch.empty(16, **f32)
+    state = torch.empty(2, **i32)
+    sq.fp8_history_init(hist, state)
+
+    names = ["amax_x", "amax_w", "scale", "quant_x", "quant_w", "gemm_pt", "delayed",
+             "mxq_x", "mxq_w", "gemm_mx"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        sq.fp8_amax(x, out=ax)
+        mark(1)
+        sq.fp8_amax(w, out=aw)
+        mark(2)
+        sq.fp8_compute_scale(ax, sq.E4M3, 0, bias_out=bx)
+        sq.fp8_compute_scale(aw, sq.E4M3, 0, bias_out=bw)
+        mark(3)
+        sq.fp8_quantize(x, sq.E4M3, bx, q=qx)
+        mark(4)
+        sq.fp8_quantize(w, sq.E4M3, bw, q=qw)
+        mark(5)
+        sq.fp8_scaled_gemm(qx, sq.E4M3, bx, qw, sq.E4M3, bw, out=y, amax_out=ay)
+        mark(6)
+        sq.fp8_history_push(hist, state, ay)
+        sq.fp8_compute_scale_delayed(hist, state, sq.E4M3, 0, bias_out=bnext)
+        mark(7)
+        sq.mx_quantize(x, sq.E4M3, q=mqx, scales=msx)
+        mark(8)
+        sq.mx_quantize(w, sq.E4M3, q=mqw, scales=msw)
+        mark(9)
+        sq.mx_scaled_gemm(mqx, sq.E4M3, msx, mqw, sq.E4M3, msw, out=ym, amax_out=aym)
+        mark(10)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps bracketed by events; per-kernel events inside
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(11)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    per = {nm: sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)) / args.steps
+           for i, nm in enumerate(names)}
+
+    gemm_flops = 2.0 * M * N * K
+    step_flops = 2 * gemm_flops
+    bx_b, bw_b = M * K, N * K          # elements
+    breakdown = {
+        "amax_x_GBps": 2 * bx_b / per["amax_x"] / 1e6,
+        "amax_w_GBps": 2 * bw_b / per["amax_w"] / 1e6,
+        "quant_x_GBps": 3 * bx_b / per["quant_x"] / 1e6,
+        "quant_w_GBps": 3 * bw_b / per["quant_w"] / 1e6,
+        "mxq_x_GBps": (3 + 1 / 32) * bx_b / per["mxq_x"] / 1e6,
+        "mxq_w_GBps": (3 + 1 / 32) * bw_b / per["mxq_w"] / 1e6,
+        "current_scaling_effective_GBps": 3 * (bx_b + bw_b) / (per["amax_x"] + per["amax_w"] + per["scale"]
+                                                               + per["quant_x"] + per["quant_w"]) / 1e6,
+        "gemm_pt_TFLOPs": gemm_flops / per["gemm_pt"] / 1e9,
+        "gemm_mx_TFLOPs": gemm_flops / per["gemm_mx"] / 1e9,
+        "ms": {k: round(v, 4) for k, v in per.items()},
+    }
+    dom = "gemm_pt" if per["gemm_pt"] >= per["gemm_mx"] else "gemm_mx"
+    achieved = gemm_flops / per[dom] / 1e9
+    traffic = None
+    tr_path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    if os.path.exists(tr_path):
+        try:
+            with open(tr_path) as f:
+                traffic = json.load(f).get(dom)
+        except Exception:
+            traffic = None
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(xb, wb, args.cpu_seconds)
+
+    out = {
+        "metric": "scaled FP8 GEMM TFLOP/s + amax/quantize GB/s (per-tensor, MXFP8), 1 GPU",
+        "value": round(step_flops / ms_step / 1e9, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "M": M, "N": N, "K": K, "x_dist": "N(0,1), 0.05% x100",
+                   "w_dist": "0.015 N(0,1)", "out": "bf16", "history_window": 16,
+                   "step": "amax+bias+E4M3 cast (X,W), per-tensor GEMM+out amax, delayed-history push, "
+                           "MX cast (X,W), MX GEMM+out amax"},
+        "breakdown": {k: (round(v, 1) if isinstance(v, float) else v) for k, v in breakdown.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "input_generation_s": round(gen_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

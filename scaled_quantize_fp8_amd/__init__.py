@@ -1,0 +1,349 @@
+"""scaled_quantize_fp8_amd — scaled FP8 linear-layer kernels for MI355X (gfx950).
+
+A thin ctypes binding over ``libscaled_fp8.so`` (C ABI declared in
+``include/scaled_fp8.h``).  Each function here has the name of the C entry
+point it marshals arguments for; every step of the computation runs in the
+library's HIP kernels on the tensors' device and on the current HIP stream.
+PyTorch only supplies device memory and the stream.  There is no CPU
+implementation behind this module: a missing library or a CPU tensor raises.
+
+FP8 tensors are ``torch.uint8`` holding OCP E4M3 / E5M2 codes; E8M0 block
+scales are ``torch.uint8`` codes; biases are ``torch.int32`` device scalars.
+Matrices are 2-D row-major (``stride(1) == 1``); the leading dimension is
+``stride(0)``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "E4M3", "E5M2", "load_library", "library_path", "Fp8Error",
+    "fp8_amax", "fp8_compute_scale", "fp8_history_init", "fp8_history_push",
+    "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize",
+    "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string", "fp8_abi_version",
+]
+
+E4M3 = 0
+E5M2 = 1
+_DT_BF16 = 0
+_DT_F32 = 1
+_FMT_NAMES = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_i64 = ctypes.c_int64
+
+_SIGNATURES = {
+    "fp8_status_string": ([_i], ctypes.c_char_p),
+    "fp8_abi_version": ([], _i),
+    "fp8_amax": ([_p, _i, _i64, _i64, _i64, _p, _p], _i),
+    "fp8_compute_scale": ([_p, _i, _i, _p, _p, _p, _p], _i),
+    "fp8_history_init": ([_p, _p, _i, _p], _i),
+    "fp8_history_push": ([_p, _p, _i, _p, _p], _i),
+    "fp8_compute_scale_delayed": ([_p, _p, _i, _i, _i, _p, _p, _p, _p], _i),
+    "fp8_quantize": ([_p, _i, _i64, _i64, _i64, _i, _p, _p, _i64, _p, _i64, _p, _p], _i),
+    "mx_quantize": ([_p, _i, _i64, _i64, _i64, _i, _p, _i64, _p, _i64, _p], _i),
+    "fp8_scaled_gemm": ([_i64, _i64, _i64, _p, _i, _i, _i64, _p, _p, _i, _i, _i64, _p,
+                         _p, _i, _i64, _p, _p], _i),
+    "mx_scaled_gemm": ([_i64, _i64, _i64, _p, _i, _i64, _p, _i64, _p, _i, _i64, _p, _i64,
+                        _p, _i, _i64, _p, _p], _i),
+}
+
+
+class Fp8Error(RuntimeError):
+    """A library call returned a negative status."""
+
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status} ({fp8_status_string(status)})")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libscaled_fp8.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libscaled_fp8.so (built in-tree); raise if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m scaled_quantize_fp8_amd.build` "
+                "(there is no fallback implementation)")
+        lib = ctypes.CDLL(path)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _LIB = lib
+    return _LIB
+
+
+def fp8_status_string(status: int) -> str:
+    return load_library().fp8_status_string(int(status)).decode()
+
+
+def fp8_abi_version() -> int:
+    return int(load_library().fp8_abi_version())
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise Fp8Error(fn, status)
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device}); there is no CPU path")
+    return t
+
+
+def _mat(t: torch.Tensor, name: str):
+    _dev(t, name)
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.shape[0] > 0 and t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must be row-major (stride(1) == 1)")
+    ld = t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+    return t.shape[0], t.shape[1], ld
+
+
+def _dtype_code(t: torch.Tensor, name: str) -> int:
+    if t.dtype == torch.bfloat16:
+        return _DT_BF16
+    if t.dtype == torch.float32:
+        return _DT_F32
+    raise ValueError(f"{name} must be bfloat16 or float32, got {t.dtype}")
+
+
+def _fmt(fmt) -> int:
+    if fmt not in _FMT_NAMES:
+        raise ValueError(f"unknown FP8 format {fmt!r}")
+    return _FMT_NAMES[fmt]
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _u8(t: torch.Tensor, name: str) -> torch.Tensor:
+    _dev(t, name)
+    if t.dtype != torch.uint8:
+        raise ValueError(f"{name} must be uint8 (FP8 / E8M0 codes), got {t.dtype}")
+    return t
+
+
+def _scalar(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
+    _dev(t, name)
+    if t.dtype != dtype or t.numel() < 1:
+        raise ValueError(f"{name} must be a {dtype} device tensor with at least one element")
+    return t
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def fp8_amax(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """max |x| of a 2-D bf16/f32 tensor, as a float32 device tensor of shape [1]."""
+    rows, cols, ld = _mat(x, "x")
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _scalar(out, torch.float32, "out")
+    _check("fp8_amax", load_library().fp8_amax(
+        _ptr(x), _dtype_code(x, "x"), rows, cols, ld, _ptr(out), _stream(x)))
+    return out
+
+
+def fp8_compute_scale(amax: torch.Tensor, fmt, margin: int = 0, bias_out=None,
+                      scale_out=None, scale_inv_out=None):
+    """Bias floor(log2(fmax/amax)) - margin; returns (bias int32[1],
+    scale float32[1], scale_inv float32[1])."""
+    _scalar(amax, torch.float32, "amax")
+    dev = amax.device
+    bias_out = torch.empty(1, dtype=torch.int32, device=dev) if bias_out is None else bias_out
+    scale_out = torch.empty(1, dtype=torch.float32, device=dev) if scale_out is None else scale_out
+    scale_inv_out = torch.empty(1, dtype=torch.float32, device=dev) if scale_inv_out is None else scale_inv_out
+    _check("fp8_compute_scale", load_library().fp8_compute_scale(
+        _ptr(amax), _fmt(fmt), int(margin), _ptr(bias_out), _ptr(scale_out),
+        _ptr(scale_inv_out), _stream(amax)))
+    return bias_out, scale_out, scale_inv_out
+
+
+def fp8_history_init(hist: torch.Tensor, state: torch.Tensor) -> None:
+    """Zero a delayed-scaling history (float32[window]) and its state (int32[2])."""
+    _scalar(hist, torch.float32, "hist")
+    _scalar(state, torch.int32, "state")
+    _check("fp8_history_init", load_library().fp8_history_init(
+        _ptr(hist), _ptr(state), hist.numel(), _stream(hist)))
+
+
+def fp8_history_push(hist: torch.Tensor, state: torch.Tensor, amax: torch.Tensor) -> None:
+    """Append one step's amax to the history ring."""
+    _scalar(hist, torch.float32, "hist")
+    _scalar(state, torch.int32, "state")
+    _scalar(amax, torch.float32, "amax")
+    _check("fp8_history_push", load_library().fp8_history_push(
+        _ptr(hist), _ptr(state), hist.numel(), _ptr(amax), _stream(hist)))
+
+
+def fp8_compute_scale_delayed(hist: torch.Tensor, state: torch.Tensor, fmt, margin: int = 0,
+                              bias_out=None, scale_out=None, scale_inv_out=None):
+    """Bias from the maximum over the history window; returns (bias, scale, scale_inv)."""
+    _scalar(hist, torch.float32, "hist")
+    _scalar(state, torch.int32, "state")
+    dev = hist.device
+    bias_out = torch.empty(1, dtype=torch.int32, device=dev) if bias_out is None else bias_out
+    scale_out = torch.empty(1, dtype=torch.float32, device=dev) if scale_out is None else scale_out
+    scale_inv_out = torch.empty(1, dtype=torch.float32, device=dev) if scale_inv_out is None else scale_inv_out
+    _check("fp8_compute_scale_delayed", load_library().fp8_compute_scale_delayed(
+        _ptr(hist), _ptr(state), hist.numel(), _fmt(fmt), int(margin), _ptr(bias_out),
+        _ptr(scale_out), _ptr(scale_inv_out), _stream(hist)))
+    return bias_out, scale_out, scale_inv_out
+
+
+def fp8_quantize(x: torch.Tensor, fmt, bias: torch.Tensor, q: torch.Tensor | None = None,
+                 transpose: bool = False, qT: torch.Tensor | None = None,
+                 want_amax: bool = False, amax_out: torch.Tensor | None = None):
+    """Per-tensor cast q = sat_RNE(x * 2**bias).  Returns (q, qT or None,
+    amax of x or None); ``transpose`` also writes qT = q^T, ``want_amax`` fuses
+    the input amax into the same pass."""
+    rows, cols, ld = _mat(x, "x")
+    _scalar(bias, torch.int32, "bias")
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    _u8(q, "q")
+    qr, qc, ldq = _mat(q, "q")
+    if (qr, qc) != (rows, cols):
+        raise ValueError("q must have the shape of x")
+    ldqT = 0
+    if transpose or qT is not None:
+        if qT is None:
+            qT = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+        _u8(qT, "qT")
+        tr, tc, ldqT = _mat(qT, "qT")
+        if (tr, tc) != (cols, rows):
+            raise ValueError("qT must have the transposed shape of x")
+    if want_amax or amax_out is not None:
+        if amax_out is None:
+            amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
+        _scalar(amax_out, torch.float32, "amax_out")
+    _check("fp8_quantize", load_library().fp8_quantize(
+        _ptr(x), _dtype_code(x, "x"), rows, cols, ld, _fmt(fmt), _ptr(bias), _ptr(q), ldq,
+        _ptr(qT), ldqT, _ptr(amax_out), _stream(x)))
+    return q, qT, amax_out
+
+
+def mx_quantize(x: torch.Tensor, fmt=E4M3, q: torch.Tensor | None = None,
+                scales: torch.Tensor | None = None):
+    """Per-block (1 x 32 along cols) cast; returns (q [R x C] codes, scales
+    [R x C/32] E8M0 codes)."""
+    rows, cols, ld = _mat(x, "x")
+    if cols % 32:
+        raise ValueError("mx_quantize needs cols % 32 == 0")
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    _u8(q, "q")
+    _u8(scales, "scales")
+    _, _, ldq = _mat(q, "q")
+    _, _, lds = _mat(scales, "scales")
+    _check("mx_quantize", load_library().mx_quantize(
+        _ptr(x), _dtype_code(x, "x"), rows, cols, ld, _fmt(fmt), _ptr(q), ldq, _ptr(scales),
+        lds, _stream(x)))
+    return q, scales
+
+
+def _out_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return _DT_BF16
+    if dtype == torch.float32:
+        return _DT_F32
+    raise ValueError("out dtype must be bfloat16 or float32")
+
+
+def fp8_scaled_gemm(A: torch.Tensor, fmt_a, bias_a: torch.Tensor, B: torch.Tensor, fmt_b,
+                    bias_b: torch.Tensor, trans_a: bool = False, trans_b: bool = False,
+                    out_dtype: torch.dtype = torch.bfloat16, want_amax: bool = False,
+                    out: torch.Tensor | None = None, amax_out: torch.Tensor | None = None):
+    """C = 2**-(bias_a + bias_b) * op(A) @ op(B)^T with op(A) [M x K], op(B)
+    [N x K]; A is stored [M x K] (or [K x M] with trans_a), B [N x K] (or
+    [K x N] with trans_b).  Returns (C, amax of C or None)."""
+    _u8(A, "A")
+    _u8(B, "B")
+    _scalar(bias_a, torch.int32, "bias_a")
+    _scalar(bias_b, torch.int32, "bias_b")
+    ar, ac, lda = _mat(A, "A")
+    br, bc, ldb = _mat(B, "B")
+    M, K = (ac, ar) if trans_a else (ar, ac)
+    N, Kb = (bc, br) if trans_b else (br, bc)
+    if K != Kb:
+        raise ValueError(f"inner dimensions differ: {K} vs {Kb}")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    _dev(out, "out")
+    orow, ocol, ldc = _mat(out, "out")
+    if (orow, ocol) != (M, N):
+        raise ValueError("out must be [M x N]")
+    if want_amax or amax_out is not None:
+        if amax_out is None:
+            amax_out = torch.empty(1, dtype=torch.float32, device=A.device)
+        _scalar(amax_out, torch.float32, "amax_out")
+    _check("fp8_scaled_gemm", load_library().fp8_scaled_gemm(
+        M, N, K, _ptr(A), _fmt(fmt_a), int(bool(trans_a)), lda, _ptr(bias_a),
+        _ptr(B), _fmt(fmt_b), int(bool(trans_b)), ldb, _ptr(bias_b),
+        _ptr(out), _out_code(out.dtype), ldc, _ptr(amax_out), _stream(A)))
+    return out, amax_out
+
+
+def mx_scaled_gemm(A: torch.Tensor, fmt_a, A_scales: torch.Tensor, B: torch.Tensor, fmt_b,
+                   B_scales: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                   want_amax: bool = False, out: torch.Tensor | None = None,
+                   amax_out: torch.Tensor | None = None):
+    """Block-scaled C = A @ B^T with A [M x K], B [N x K] and E8M0 scales
+    [M x K/32], [N x K/32].  Returns (C, amax of C or None)."""
+    _u8(A, "A")
+    _u8(B, "B")
+    _u8(A_scales, "A_scales")
+    _u8(B_scales, "B_scales")
+    M, K, lda = _mat(A, "A")
+    N, Kb, ldb = _mat(B, "B")
+    if K != Kb:
+        raise ValueError(f"inner dimensions differ: {K} vs {Kb}")
+    _, _, lds_a = _mat(A_scales, "A_scales")
+    _, _, lds_b = _mat(B_scales, "B_scales")
+    if tuple(A_scales.shape) != (M, K // 32) or tuple(B_scales.shape) != (N, K // 32):
+        raise ValueError("scales must be [rows x K/32]")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    _dev(out, "out")
+    orow, ocol, ldc = _mat(out, "out")
+    if (orow, ocol) != (M, N):
+        raise ValueError("out must be [M x N]")
+    if want_amax or amax_out is not None:
+        if amax_out is None:
+            amax_out = torch.empty(1, dtype=torch.float32, device=A.device)
+        _scalar(amax_out, torch.float32, "amax_out")
+    _check("mx_scaled_gemm", load_library().mx_scaled_gemm(
+        M, N, K, _ptr(A), _fmt(fmt_a), lda, _ptr(A_scales), lds_a, _ptr(B), _fmt(fmt_b), ldb,
+        _ptr(B_scales), lds_b, _ptr(out), _out_code(out.dtype), ldc, _ptr(amax_out), _stream(A)))
+    return out, amax_out

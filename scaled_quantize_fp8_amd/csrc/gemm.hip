@@ -1,0 +1,504 @@
+// Scaled FP8 GEMMs for gfx950: per-tensor (unscale in the epilogue) and
+// block-scaled MX (E8M0 scales applied by the MFMA itself), both with fp32
+// accumulation, bf16 or fp32 output and the output amax fused into the
+// epilogue.
+//
+// "Training and inference of large language models using 8-bit floating
+// point" (paper review), "Proposed method": the matrix multiplication runs on
+// the FP8 operands and is unscaled afterwards; gradients (E5) meet weights
+// or activations (E4) in the backward products.  "Per-Tensor and Per-Block
+// Scaling Strategies for Effective FP8 Training" (summary), "Key Questions
+// Answered": per-block scaling, each block with its own factor.
+//
+// CDNA4 mapping.
+//   * Macro tile 256 (M) x 256 (N) x 128 (K bytes), 256 lanes = 4 waves in a
+//     2 x 2 arrangement, each wave owning 128 x 128 of C as 8 x 8
+//     v_mfma_f32_16x16x128_f8f6f4 blocks (256 fp32 accumulators per lane).
+//   * Operands are staged in LDS, double-buffered (2 x 64 KiB of the 160 KiB),
+//     K-contiguous: row r of a tile is 128 bytes, its 16-byte chunk c stored
+//     at chunk c ^ ((r ^ (r >> 4)) & 7) so that the MFMA fragment reads
+//     (16 rows, same chunk) and the staging writes are bank-conflict free.
+//   * A lane's MFMA operand is two 16-byte K chunks of one row (lane group g
+//     holds K [16g, 16g+16) and [64+16g, 64+16g+16)); the block-scaled MFMA
+//     reads the E8M0 scale of (row, 32-wide K block j) from lane 16 j + row.
+//   * The MFMA's first operand is a W (op(B)) fragment and its second an X
+//     (op(A)) fragment, so a lane's four accumulators are four consecutive
+//     n of one output row m: the epilogue stores 8 (bf16) or 16 (fp32)
+//     contiguous bytes per lane.
+//   * Transposed operands ([K x M] storage) are loaded 16 M-bytes at a time
+//     for four consecutive k and transposed 4 x 4 bytes in registers
+//     (v_perm_b32) on their way into the K-contiguous LDS layout.
+//   * Workgroup -> tile mapping is XCD-aware: consecutive workgroup ids land
+//     on different XCDs, so ids are remapped to give each XCD a contiguous
+//     range of tiles, walked in groups of 8 tile-rows for L2 reuse.
+#include "common.hpp"
+#include "host.hpp"
+
+namespace sfp8 {
+
+constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int kGemmThreads = 256;
+constexpr int kGroupM = 8;
+constexpr int kTileBytes = BM * BK;          // 32 KiB per operand per stage
+
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 4)) & 7; }
+
+// Offset of byte k (0..127) of tile row `row` in the swizzled layout.
+__device__ __forceinline__ int lds_off(int row, int k) {
+  return row * BK + ((((k >> 4) ^ swz(row)) << 4) | (k & 15));
+}
+
+struct GemmArgs {
+  int64_t M, N, K;
+  const uint8_t* A;
+  int64_t lda;
+  const uint8_t* B;
+  int64_t ldb;
+  const int32_t* bias_a;
+  const int32_t* bias_b;
+  const uint8_t* sa;       // MX scales of op(A) rows [M x K/32]
+  int64_t lds_a;
+  const uint8_t* sb;       // MX scales of op(B) rows [N x K/32]
+  int64_t lds_b;
+  void* C;
+  int64_t ldc;
+  float* out_amax;
+  int out_f32;
+  int vec_store;
+  int sa_dword;            // scale rows 4-byte aligned: one dword per stage
+  int sb_dword;
+};
+
+// ---- buffer resources ------------------------------------------------------
+// Raw buffer descriptors give range-checked loads: an offset at or past
+// num_records reads zeros, which is how ragged tile edges are zero-filled.
+constexpr uint32_t kOOB = 0x80000000u;       // offset that is always out of range
+constexpr int kRsrcWord3 = 0x00020000;       // raw (untyped) buffer, gfx9 family
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t rec = bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)rec, kRsrcWord3);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// ---- K-contiguous operand: global -> LDS directly ----------------------------
+// The tile is 32 blocks of 8 rows x 128 bytes (1 KiB).  Wave w fills blocks
+// 8w .. 8w+7 with one buffer_load_dwordx4 ... lds each: lane L lands at byte
+// 16 L of the block, i.e. row L/8, stored chunk L%8, so it fetches logical
+// chunk (L%8) ^ swz(row) of that row (8 lanes = one 128-byte row segment).
+__device__ __forceinline__ void dma_tile_k(uint8_t* S, __amdgpu_buffer_rsrc_t rsrc, int64_t ld, int64_t rows_left,
+                                           int64_t k0, int64_t K) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int blk = wave * 8 + i;
+    const int row = blk * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz(row);
+    const int64_t gk = k0 + 16 * c;
+    const uint32_t off = (row < rows_left && gk < K) ? (uint32_t)(row * ld + gk) : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(S + blk * 1024), 16, off, 0, 0, 0);
+  }
+}
+
+// ---- transposed operand: global -> registers -> (transpose) -> LDS ---------
+// Stored [K x R] (R contiguous): a lane loads 16 R-bytes for 4 consecutive k,
+// twice (kg = lane/16 and lane/16 + 16).
+__device__ __forceinline__ void load_tile_t(__amdgpu_buffer_rsrc_t rsrc, int64_t ld, int64_t rows_left,
+                                            int64_t k0, int64_t K, uint4 (&reg)[8]) {
+  const int t = threadIdx.x;
+  const int r16 = t & 15;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int kg = (t >> 4) + 16 * u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t gk = k0 + 4 * kg + j;
+      const uint32_t off = (gk < K && 16 * r16 < rows_left) ? (uint32_t)(gk * ld + 16 * r16) : kOOB;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
+      reg[4 * u + j] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+// 4 x 4 byte transpose: a_k holds bytes (r0..r3) of k-row k; d_j gets bytes
+// (k0..k3) of row j.
+__device__ __forceinline__ void transpose4x4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint32_t& d0,
+                                             uint32_t& d1, uint32_t& d2, uint32_t& d3) {
+  const uint32_t x0 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);   // a0b0 a1b0 a0b1 a1b1
+  const uint32_t x1 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);   // a0b2 a1b2 a0b3 a1b3
+  const uint32_t y0 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);   // a2b0 a3b0 a2b1 a3b1
+  const uint32_t y1 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);   // a2b2 a3b2 a2b3 a3b3
+  d0 = __builtin_amdgcn_perm(y0, x0, 0x05040100u);                  // a0b0 a1b0 a2b0 a3b0
+  d1 = __builtin_amdgcn_perm(y0, x0, 0x07060302u);                  // a0b1 a1b1 a2b1 a3b1
+  d2 = __builtin_amdgcn_perm(y1, x1, 0x05040100u);
+  d3 = __builtin_amdgcn_perm(y1, x1, 0x07060302u);
+}
+
+__device__ __forceinline__ void store_tile_t(uint8_t* S, const uint4 (&reg)[8]) {
+  const int t = threadIdx.x;
+  const int r16 = t & 15;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int kg = (t >> 4) + 16 * u;
+    const int k = 4 * kg;
+    const uint4 a0 = reg[4 * u + 0], a1 = reg[4 * u + 1], a2 = reg[4 * u + 2], a3 = reg[4 * u + 3];
+    const uint32_t w0[4] = {a0.x, a0.y, a0.z, a0.w};
+    const uint32_t w1[4] = {a1.x, a1.y, a1.z, a1.w};
+    const uint32_t w2[4] = {a2.x, a2.y, a2.z, a2.w};
+    const uint32_t w3[4] = {a3.x, a3.y, a3.z, a3.w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t d[4];
+      transpose4x4(w0[w], w1[w], w2[w], w3[w], d[0], d[1], d[2], d[3]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * r16 + 4 * w + j;
+        *reinterpret_cast<uint32_t*>(S + lds_off(row, k)) = d[j];
+      }
+    }
+  }
+}
+
+// MX scales of a stage: lane t loads the four E8M0 codes of tile row t (one
+// dword when the four blocks exist, bytes at the K tail); rows past the
+// matrix and blocks past K get code 127 (scale 1) next to their zero data.
+__device__ __forceinline__ uint32_t load_scales(const uint8_t* __restrict__ S, int64_t lds, int64_t row0,
+                                                int64_t R, int64_t k0, int64_t K, bool dword_ok) {
+  const int64_t gr = row0 + threadIdx.x;
+  const int64_t kb0 = k0 / 32;
+  const int64_t nkb = K / 32;
+  if (gr >= R) return 0x7f7f7f7fu;
+  const uint8_t* p = S + gr * lds + kb0;
+  if (dword_ok && kb0 + 4 <= nkb) return *reinterpret_cast<const uint32_t*>(p);
+  uint32_t v = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v |= (uint32_t)(kb0 + j < nkb ? p[j] : 0x7fu) << (8 * j);
+  return v;
+}
+
+// MFMA operand of v_mfma_*_16x16x128_f8f6f4 for tile rows row0 .. row0+15:
+// lane l (g = l / 16) holds row row0 + l % 16, K bytes [16g, 16g + 16) in its
+// first four registers and [64 + 16g, 64 + 16g + 16) in the last four.  The
+// block-scaled form takes the E8M0 scale of (row l % 16, K block l / 16)
+// from lane l, so the two chunks a lane holds need not share its block.
+__device__ __forceinline__ v8i load_frag(const uint8_t* S, int row0, int lane) {
+  const int row = row0 + (lane & 15);
+  const int c = lane >> 4;
+  const uint4 lo = *reinterpret_cast<const uint4*>(S + row * BK + ((c ^ swz(row)) << 4));
+  const uint4 hi = *reinterpret_cast<const uint4*>(S + row * BK + (((c + 4) ^ swz(row)) << 4));
+  v8i f;
+  f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
+  f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
+  return f;
+}
+
+// Output tile mapping: XCD-aware remap, then groups of kGroupM tile-rows.
+__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
+  const int64_t T = tiles_m * tiles_n;
+  const int64_t bid = blockIdx.x;
+  const int64_t xcd = bid % 8, local = bid / 8;
+  const int64_t q = T / 8, r = T % 8;
+  const int64_t lin = (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  const int64_t per_group = kGroupM * tiles_n;
+  const int64_t group = lin / per_group;
+  const int64_t first_m = group * kGroupM;
+  const int64_t gm = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
+  const int64_t in_group = lin % per_group;
+  tm = first_m + in_group % gm;
+  tn = in_group / gm;
+}
+
+template <int FA, int FB, bool MX, bool TA, bool TB>
+__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];
+  __shared__ uint32_t s_scale[MX ? 2 * 2 * BM : 1];
+  __shared__ uint32_t red[kGemmThreads / kWave];
+
+  const int64_t tiles_m = (g.M + BM - 1) / BM;
+  const int64_t tiles_n = (g.N + BN - 1) / BN;
+  int64_t tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  v4f acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // stage b: op(A) tile at smem + 2b * kTileBytes, op(B) tile right after it
+
+  uint4 ra[TA ? 8 : 1], rb[TB ? 8 : 1];
+  uint32_t rsa = 0, rsb = 0;
+  const int64_t nk = (g.K + BK - 1) / BK;
+  const int64_t rows_a = g.M - m0, rows_b = g.N - n0;
+  // op(A) / op(B) tiles: K-contiguous ones read rows [m0, m0+256) x K,
+  // transposed ones read columns [m0, m0+256) of a [K x M] matrix.
+  const __amdgpu_buffer_rsrc_t rs_a =
+      TA ? make_rsrc(g.A + m0, (g.K - 1) * g.lda + (rows_a < BM ? rows_a : BM))
+         : make_rsrc(g.A + m0 * g.lda, ((rows_a < BM ? rows_a : BM) - 1) * g.lda + g.K);
+  const __amdgpu_buffer_rsrc_t rs_b =
+      TB ? make_rsrc(g.B + n0, (g.K - 1) * g.ldb + (rows_b < BN ? rows_b : BN))
+         : make_rsrc(g.B + n0 * g.ldb, ((rows_b < BN ? rows_b : BN) - 1) * g.ldb + g.K);
+
+  // issue the global reads of stage kt (DMA straight into buffer `buf` for
+  // K-contiguous operands, registers for transposed ones and scales)
+  auto gload = [&](int64_t kt, int buf) {
+    const int64_t k0 = kt * BK;
+    uint8_t* sa_ = smem + 2 * buf * kTileBytes;
+    uint8_t* sb_ = sa_ + kTileBytes;
+    if constexpr (TA) load_tile_t(rs_a, g.lda, rows_a, k0, g.K, ra);
+    else dma_tile_k(sa_, rs_a, g.lda, rows_a, k0, g.K);
+    if constexpr (TB) load_tile_t(rs_b, g.ldb, rows_b, k0, g.K, rb);
+    else dma_tile_k(sb_, rs_b, g.ldb, rows_b, k0, g.K);
+    if constexpr (MX) {
+      rsa = load_scales(g.sa, g.lds_a, m0, g.M, k0, g.K, g.sa_dword);
+      rsb = load_scales(g.sb, g.lds_b, n0, g.N, k0, g.K, g.sb_dword);
+    }
+  };
+  // finish stage `buf` from registers (transposes, scales)
+  auto sstore = [&](int buf) {
+    uint8_t* sa_ = smem + 2 * buf * kTileBytes;
+    uint8_t* sb_ = sa_ + kTileBytes;
+    if constexpr (TA) store_tile_t(sa_, ra);
+    if constexpr (TB) store_tile_t(sb_, rb);
+    if constexpr (MX) {
+      s_scale[buf * 2 * BM + threadIdx.x] = rsa;
+      s_scale[buf * 2 * BM + BM + threadIdx.x] = rsb;
+    }
+  };
+
+  if (nk > 0) {
+    gload(0, 0);
+    sstore(0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int cur = (int)(kt & 1);
+    // buffer cur^1 was last read in iteration kt-1, which every wave has
+    // left (barrier below), so stage kt+1 may land in it now
+    if (kt + 1 < nk) gload(kt + 1, cur ^ 1);
+
+    const uint8_t* A_ = smem + 2 * cur * kTileBytes;
+    const uint8_t* B_ = A_ + kTileBytes;
+    v8i xf[8];
+    // MX: this lane's E8M0 codes for the 8 op(A) fragments, 4 per register;
+    // the MFMA's op_sel immediate picks the byte of fragment mb.
+    int xs[2] = {0, 0};
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      xf[mb] = load_frag(A_, wm * 128 + mb * 16, lane);
+      if constexpr (MX) {
+        const uint32_t code =
+            (s_scale[cur * 2 * BM + wm * 128 + mb * 16 + (lane & 15)] >> (8 * (lane >> 4))) & 0xffu;
+        xs[mb >> 2] |= (int)(code << (8 * (mb & 3)));
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const v8i wf = load_frag(B_, wn * 128 + nb * 16, lane);
+      int ws = 0;
+      if constexpr (MX)
+        ws = (int)((s_scale[cur * 2 * BM + BM + wn * 128 + nb * 16 + (lane & 15)] >> (8 * (lane >> 4))) & 0xffu);
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        if constexpr (MX) {
+          if ((mb & 3) == 0)
+            acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, xf[mb], acc[nb][mb], FB, FA, 0, ws,
+                                                                           0, xs[mb >> 2]);
+          else if ((mb & 3) == 1)
+            acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, xf[mb], acc[nb][mb], FB, FA, 0, ws,
+                                                                           1, xs[mb >> 2]);
+          else if ((mb & 3) == 2)
+            acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, xf[mb], acc[nb][mb], FB, FA, 0, ws,
+                                                                           2, xs[mb >> 2]);
+          else
+            acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, xf[mb], acc[nb][mb], FB, FA, 0, ws,
+                                                                           3, xs[mb >> 2]);
+        } else {
+          acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, xf[mb], acc[nb][mb], FB, FA, 0, 0, 0, 0);
+        }
+      }
+    }
+
+    if (kt + 1 < nk) sstore(cur ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // ---- epilogue: unscale, round, store, fused |C| max ----------------------
+  const int e = MX ? 0 : -(*g.bias_a + *g.bias_b);
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+      const int64_t m = m0 + wm * 128 + mb * 16 + (lane & 15);
+      const int64_t n = n0 + wn * 128 + nb * 16 + 4 * (lane >> 4);
+      if (m >= g.M) continue;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = MX ? acc[nb][mb][r] : __builtin_amdgcn_ldexpf(acc[nb][mb][r], e);
+      if (g.out_f32) {
+        float* crow = reinterpret_cast<float*>(g.C) + m * g.ldc;
+        if (g.vec_store && n + 3 < g.N) {
+          *reinterpret_cast<float4*>(crow + n) = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t ab = __float_as_uint(v[r]) & 0x7fffffffu;
+            amax_bits = amax_bits > ab ? amax_bits : ab;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (n + r < g.N) {
+              crow[n + r] = v[r];
+              const uint32_t ab = __float_as_uint(v[r]) & 0x7fffffffu;
+              amax_bits = amax_bits > ab ? amax_bits : ab;
+            }
+          }
+        }
+      } else {
+        uint16_t h[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) h[r] = __builtin_bit_cast(uint16_t, (__bf16)v[r]);
+        uint16_t* crow = reinterpret_cast<uint16_t*>(g.C) + m * g.ldc;
+        if (g.vec_store && n + 3 < g.N) {
+          *reinterpret_cast<uint2*>(crow + n) =
+              make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t ab = ((uint32_t)h[r] & 0x7fffu) << 16;
+            amax_bits = amax_bits > ab ? amax_bits : ab;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (n + r < g.N) {
+              crow[n + r] = h[r];
+              const uint32_t ab = ((uint32_t)h[r] & 0x7fffu) << 16;
+              amax_bits = amax_bits > ab ? amax_bits : ab;
+            }
+          }
+        }
+      }
+    }
+  }
+  if (g.out_amax) block_max_to_global(amax_bits, red, g.out_amax);
+}
+
+template <int FA, int FB, bool MX, bool TA, bool TB>
+static void launch_gemm(const GemmArgs& g, hipStream_t s) {
+  const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_kernel<FA, FB, MX, TA, TB>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, g);
+}
+
+template <int FA, int FB>
+static void dispatch_trans(const GemmArgs& g, bool ta, bool tb, hipStream_t s) {
+  if (!ta && !tb) launch_gemm<FA, FB, false, false, false>(g, s);
+  else if (!ta && tb) launch_gemm<FA, FB, false, false, true>(g, s);
+  else if (ta && !tb) launch_gemm<FA, FB, false, true, false>(g, s);
+  else launch_gemm<FA, FB, false, true, true>(g, s);
+}
+
+// 16-byte loads need 16-byte aligned rows; buffer offsets are 32-bit, so a
+// K-contiguous tile (256 rows) or a transposed operand (K rows) must span
+// less than 2 GiB.
+static int check_operand(const uint8_t* p, int64_t ld, bool trans, int64_t K) {
+  if (!aligned(p, 16) || (ld % 16) != 0) return FP8_ERR_ALIGN;
+  if (trans ? (K * ld >= (1LL << 31) - 4096) : (ld >= (1LL << 23))) return FP8_ERR_UNSUPPORTED;
+  return FP8_OK;
+}
+
+}  // namespace sfp8
+
+using namespace sfp8;
+
+extern "C" {
+
+int fp8_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int fmt_a, int trans_a, int64_t lda,
+                    const int32_t* bias_a, const uint8_t* B, int fmt_b, int trans_b, int64_t ldb,
+                    const int32_t* bias_b, void* C, int out_dtype, int64_t ldc, float* out_amax,
+                    hipStream_t stream) {
+  if (!bias_a || !bias_b) return FP8_ERR_NULL;
+  if (!valid_fmt(fmt_a) || !valid_fmt(fmt_b)) return FP8_ERR_FORMAT;
+  if (!valid_dtype(out_dtype)) return FP8_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || (K % 16) != 0) return FP8_ERR_SHAPE;
+  if (trans_a ? (lda < M || (M % 16) != 0) : (lda < K)) return FP8_ERR_SHAPE;
+  if (trans_b ? (ldb < N || (N % 16) != 0) : (ldb < K)) return FP8_ERR_SHAPE;
+  if (ldc < N) return FP8_ERR_SHAPE;
+  if (M > 0 && N > 0 && !C) return FP8_ERR_NULL;
+  if (M > 0 && N > 0 && K > 0 && (!A || !B)) return FP8_ERR_NULL;
+  if (M > 0 && N > 0 && K > 0) {
+    int st = check_operand(A, lda, trans_a != 0, K);
+    if (st) return st;
+    st = check_operand(B, ldb, trans_b != 0, K);
+    if (st) return st;
+  }
+  if (out_amax) zero_float_async(out_amax, stream);
+  if (M == 0 || N == 0) return launch_status();
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (tiles > 0x7fffffffLL) return FP8_ERR_SHAPE;
+  GemmArgs g;
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda; g.B = B; g.ldb = ldb;
+  g.bias_a = bias_a; g.bias_b = bias_b;
+  g.sa = nullptr; g.lds_a = 0; g.sb = nullptr; g.lds_b = 0;
+  g.sa_dword = 0; g.sb_dword = 0;
+  g.C = C; g.ldc = ldc; g.out_amax = out_amax;
+  g.out_f32 = out_dtype == FP8_DT_F32;
+  g.vec_store = g.out_f32 ? (aligned(C, 16) && ldc % 4 == 0) : (aligned(C, 8) && ldc % 4 == 0);
+  const bool ta = trans_a != 0, tb = trans_b != 0;
+  if (fmt_a == FP8_E4M3 && fmt_b == FP8_E4M3) dispatch_trans<FP8_E4M3, FP8_E4M3>(g, ta, tb, stream);
+  else if (fmt_a == FP8_E5M2 && fmt_b == FP8_E4M3) dispatch_trans<FP8_E5M2, FP8_E4M3>(g, ta, tb, stream);
+  else if (fmt_a == FP8_E4M3 && fmt_b == FP8_E5M2) dispatch_trans<FP8_E4M3, FP8_E5M2>(g, ta, tb, stream);
+  else dispatch_trans<FP8_E5M2, FP8_E5M2>(g, ta, tb, stream);
+  return launch_status();
+}
+
+int mx_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int fmt_a, int64_t lda,
+                   const uint8_t* A_scales, int64_t lds_a, const uint8_t* B, int fmt_b, int64_t ldb,
+                   const uint8_t* B_scales, int64_t lds_b, void* C, int out_dtype, int64_t ldc, float* out_amax,
+                   hipStream_t stream) {
+  if (!valid_fmt(fmt_a) || !valid_fmt(fmt_b)) return FP8_ERR_FORMAT;
+  if (!valid_dtype(out_dtype)) return FP8_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || (K % 32) != 0) return FP8_ERR_SHAPE;
+  if (lda < K || ldb < K || ldc < N || lds_a < K / 32 || lds_b < K / 32) return FP8_ERR_SHAPE;
+  if (M > 0 && N > 0 && !C) return FP8_ERR_NULL;
+  if (M > 0 && N > 0 && K > 0) {
+    if (!A || !B || !A_scales || !B_scales) return FP8_ERR_NULL;
+    int st = check_operand(A, lda, false, K);
+    if (st) return st;
+    st = check_operand(B, ldb, false, K);
+    if (st) return st;
+  }
+  if (out_amax) zero_float_async(out_amax, stream);
+  if (M == 0 || N == 0) return launch_status();
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (tiles > 0x7fffffffLL) return FP8_ERR_SHAPE;
+  GemmArgs g;
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda; g.B = B; g.ldb = ldb;
+  g.bias_a = nullptr; g.bias_b = nullptr;
+  g.sa = A_scales; g.lds_a = lds_a; g.sb = B_scales; g.lds_b = lds_b;
+  g.sa_dword = aligned(A_scales, 4) && (lds_a % 4) == 0;
+  g.sb_dword = aligned(B_scales, 4) && (lds_b % 4) == 0;
+  g.C = C; g.ldc = ldc; g.out_amax = out_amax;
+  g.out_f32 = out_dtype == FP8_DT_F32;
+  g.vec_store = g.out_f32 ? (aligned(C, 16) && ldc % 4 == 0) : (aligned(C, 8) && ldc % 4 == 0);
+  if (fmt_a == FP8_E4M3 && fmt_b == FP8_E4M3) launch_gemm<FP8_E4M3, FP8_E4M3, true, false, false>(g, stream);
+  else if (fmt_a == FP8_E5M2 && fmt_b == FP8_E4M3) launch_gemm<FP8_E5M2, FP8_E4M3, true, false, false>(g, stream);
+  else if (fmt_a == FP8_E4M3 && fmt_b == FP8_E5M2) launch_gemm<FP8_E4M3, FP8_E5M2, true, false, false>(g, stream);
+  else launch_gemm<FP8_E5M2, FP8_E5M2, true, false, false>(g, stream);
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Host-side helpers for the C entry points: argument checks that run before
+// any HIP call, launch-error mapping, and launch-shape choices.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/scaled_fp8.h"
+
+namespace sfp8 {
+
+inline bool valid_fmt(int f) { return f == FP8_E4M3 || f == FP8_E5M2; }
+inline bool valid_dtype(int d) { return d == FP8_DT_BF16 || d == FP8_DT_F32; }
+inline int dtype_size(int d) { return d == FP8_DT_BF16 ? 2 : 4; }
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// rows x cols matrix with leading dimension ld: sizes non-negative, ld >= cols
+// (ld is irrelevant when rows <= 1 but must still be >= cols if rows > 1).
+inline int check_matrix(int64_t rows, int64_t cols, int64_t ld) {
+  if (rows < 0 || cols < 0 || ld < 0) return FP8_ERR_SHAPE;
+  if (rows > 1 && ld < cols) return FP8_ERR_SHAPE;
+  return FP8_OK;
+}
+
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? FP8_OK : FP8_ERR_LAUNCH;
+}
+
+// Workgroups for a streaming kernel over `units` work items of `per_block`
+// items each, capped so that a grid-stride loop keeps each lane busy with a
+// few iterations (256 CUs x 16 workgroups in flight).
+inline unsigned stream_blocks(int64_t units, int64_t per_block) {
+  int64_t b = (units + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  if (b > 4096) b = 4096;
+  return (unsigned)b;
+}
+
+// Zero one float on `stream` with a tiny fill kernel (not hipMemsetAsync, so
+// that the call sequence can be captured into a HIP graph safely).
+void zero_float_async(float* p, hipStream_t stream);
+
+}  // namespace sfp8

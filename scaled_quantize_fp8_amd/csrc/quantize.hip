@@ -1,0 +1,490 @@
+// Per-tensor and per-block (MX) FP8 casts for gfx950, plus the read-only amax
+// pass, all HBM-bound streaming kernels.
+//
+// "Training and inference of large language models using 8-bit floating
+// point" (paper review), "Proposed method": inputs are multiplied by their
+// power-of-two scale, then cast to FP8 (E4 for weights/activations, E5 for
+// gradients).  "Per-Tensor and Per-Block Scaling Strategies for Effective FP8
+// Training" (summary), "Key Questions Answered": per-block scaling gives each
+// block its own factor (here 1 x 32 along K with an E8M0 power of two).
+//
+// Design for CDNA4: each lane moves 16-byte chunks (global_load_dwordx4) with
+// U chunks in flight, consecutive lanes own consecutive chunks so every wave
+// instruction is one contiguous 1 KiB span, the cast is 4 VALU ops per
+// element (unpack, v_ldexp, v_med3 clamp, half a v_cvt_pk), maxima are taken
+// on integer bit patterns (packed u16 for bf16) and leave each workgroup as
+// one atomicMax.  The per-block maximum of an MX block is a 4-lane (bf16) or
+// 8-lane (f32) DPP reduction: no LDS, no barrier.
+#include "common.hpp"
+#include "host.hpp"
+#include "stream_kernels.hpp"
+
+namespace sfp8 {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+
+template <int DT> struct In;
+template <> struct In<FP8_DT_BF16> {
+  static constexpr int kEsz = 2;
+  static constexpr int kEpc = 8;    // elements per 16-byte chunk
+};
+template <> struct In<FP8_DT_F32> {
+  static constexpr int kEsz = 4;
+  static constexpr int kEpc = 4;
+};
+
+// |x| bits of one element in float32 layout, and the element as a float.
+template <int DT>
+__device__ __forceinline__ uint32_t load_elem(const void* row, int64_t i, float* f) {
+  if constexpr (DT == FP8_DT_BF16) {
+    const uint32_t h = reinterpret_cast<const uint16_t*>(row)[i];
+    *f = __uint_as_float(h << 16);
+    return h << 16;
+  } else {
+    const uint32_t u = reinterpret_cast<const uint32_t*>(row)[i];
+    *f = __uint_as_float(u);
+    return u;
+  }
+}
+
+// Cast of one element given its float32-layout bits (NaN handled here).
+template <int FMT>
+__device__ __forceinline__ uint32_t cast_elem(uint32_t bits, int e) {
+  if ((bits & 0x7fffffffu) > 0x7f800000u) return nan_code_f32(bits);
+  return cvt1<FMT>(__builtin_amdgcn_ldexpf(__uint_as_float(bits), e));
+}
+
+// Cast of one 16-byte chunk; returns the packed codes (8 bytes for bf16, 4
+// for f32) and the chunk's max |x| bits (float32 layout) in *amax_bits.
+template <int DT, int FMT>
+__device__ __forceinline__ uint2 cast_chunk(uint4 v, int e, uint32_t* amax_bits, bool want_codes) {
+  uint2 o = make_uint2(0u, 0u);
+  if constexpr (DT == FP8_DT_BF16) {
+    const us2 m2 = max_us2(max_us2(abs_bf16x2(v.x), abs_bf16x2(v.y)),
+                           max_us2(abs_bf16x2(v.z), abs_bf16x2(v.w)));
+    const uint32_t m = hmax_us2(m2);
+    *amax_bits = m << 16;
+    if (want_codes) {
+      o.x = cvt4<FMT>(__builtin_amdgcn_ldexpf(bf16_lo(v.x), e), __builtin_amdgcn_ldexpf(bf16_hi(v.x), e),
+                      __builtin_amdgcn_ldexpf(bf16_lo(v.y), e), __builtin_amdgcn_ldexpf(bf16_hi(v.y), e));
+      o.y = cvt4<FMT>(__builtin_amdgcn_ldexpf(bf16_lo(v.z), e), __builtin_amdgcn_ldexpf(bf16_hi(v.z), e),
+                      __builtin_amdgcn_ldexpf(bf16_lo(v.w), e), __builtin_amdgcn_ldexpf(bf16_hi(v.w), e));
+      if (__builtin_expect(m > 0x7f80u, 0)) {      // a NaN in the chunk: patch its bytes
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+          if ((h & 0x7fffu) > 0x7f80u) {
+            const int sh = 8 * (i & 3);
+            uint32_t& dst = (i < 4) ? o.x : o.y;
+            dst = (dst & ~(0xffu << sh)) | (nan_code_bf16(h) << sh);
+          }
+        }
+      }
+    }
+  } else {
+    const uint32_t a0 = v.x & 0x7fffffffu, a1 = v.y & 0x7fffffffu;
+    const uint32_t a2 = v.z & 0x7fffffffu, a3 = v.w & 0x7fffffffu;
+    const uint32_t m01 = a0 > a1 ? a0 : a1, m23 = a2 > a3 ? a2 : a3;
+    const uint32_t m = m01 > m23 ? m01 : m23;
+    *amax_bits = m;
+    if (want_codes) {
+      o.x = cvt4<FMT>(__builtin_amdgcn_ldexpf(__uint_as_float(v.x), e),
+                      __builtin_amdgcn_ldexpf(__uint_as_float(v.y), e),
+                      __builtin_amdgcn_ldexpf(__uint_as_float(v.z), e),
+                      __builtin_amdgcn_ldexpf(__uint_as_float(v.w), e));
+      if (__builtin_expect(m > 0x7f800000u, 0)) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if ((w[i] & 0x7fffffffu) > 0x7f800000u) {
+            const int sh = 8 * i;
+            o.x = (o.x & ~(0xffu << sh)) | (nan_code_f32(w[i]) << sh);
+          }
+        }
+      }
+    }
+  }
+  return o;
+}
+
+template <int DT>
+__device__ __forceinline__ void store_codes(uint8_t* qrow, int64_t chunk, uint2 o) {
+  if constexpr (DT == FP8_DT_BF16) {
+    reinterpret_cast<uint2*>(qrow)[chunk] = o;
+  } else {
+    reinterpret_cast<uint32_t*>(qrow)[chunk] = o.x;
+  }
+}
+
+// Streaming pass: rows are walked by gridDim.y, 16-byte chunks of a row by a
+// grid-stride loop over x with kUnroll loads in flight per lane.
+template <int DT, int FMT, bool VEC, bool WQ, bool AMAX>
+__global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
+  __shared__ uint32_t red[kThreads / kWave];
+  constexpr int ESZ = In<DT>::kEsz;
+  constexpr int EPC = In<DT>::kEpc;
+  const int e = WQ ? *a.bias : 0;
+  uint32_t amax_bits = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (int64_t r = blockIdx.y; r < a.rows; r += gridDim.y) {
+    const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ld * ESZ;
+    uint8_t* qr = WQ ? a.q + r * a.ldq : nullptr;
+    int64_t e0 = 0;
+    if constexpr (VEC) {
+      const int64_t cpr = a.cols / EPC;
+      const uint4* x4 = reinterpret_cast<const uint4*>(xr);
+      int64_t c = tid;
+      for (; c + (kUnroll - 1) * stride < cpr; c += kUnroll * stride) {
+        uint4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = x4[c + u * stride];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          uint32_t m;
+          const uint2 o = cast_chunk<DT, FMT>(v[u], e, &m, WQ);
+          if (AMAX) amax_bits = amax_bits > m ? amax_bits : m;
+          if (WQ) store_codes<DT>(qr, c + u * stride, o);
+        }
+      }
+      for (; c < cpr; c += stride) {
+        uint32_t m;
+        const uint2 o = cast_chunk<DT, FMT>(x4[c], e, &m, WQ);
+        if (AMAX) amax_bits = amax_bits > m ? amax_bits : m;
+        if (WQ) store_codes<DT>(qr, c, o);
+      }
+      e0 = cpr * EPC;
+    }
+    for (int64_t i = e0 + tid; i < a.cols; i += stride) {   // tail (or all, when !VEC)
+      float f;
+      const uint32_t bits = load_elem<DT>(xr, i, &f);
+      const uint32_t ab = bits & 0x7fffffffu;
+      if (AMAX) amax_bits = amax_bits > ab ? amax_bits : ab;
+      if (WQ) qr[i] = (uint8_t)cast_elem<FMT>(bits, e);
+    }
+  }
+  if (AMAX) block_max_to_global(amax_bits, red, a.amax);
+}
+
+template <int DT, int FMT, bool VEC, bool WQ, bool AMAX>
+static void launch_t(const StreamArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((stream_kernel<DT, FMT, VEC, WQ, AMAX>), grid, dim3(kThreads), 0, s, a);
+}
+
+template <int DT, int FMT>
+static void launch_vec_mode(const StreamArgs& a, bool vec, bool wq, bool am, dim3 grid, hipStream_t s) {
+  if (vec) {
+    if (wq && am) launch_t<DT, FMT, true, true, true>(a, grid, s);
+    else if (wq) launch_t<DT, FMT, true, true, false>(a, grid, s);
+    else launch_t<DT, FMT, true, false, true>(a, grid, s);
+  } else {
+    if (wq && am) launch_t<DT, FMT, false, true, true>(a, grid, s);
+    else if (wq) launch_t<DT, FMT, false, true, false>(a, grid, s);
+    else launch_t<DT, FMT, false, false, true>(a, grid, s);
+  }
+}
+
+void launch_stream_pass(StreamArgs a, int dtype, int fmt, bool write_q, bool amax, hipStream_t stream) {
+  const int esz = dtype_size(dtype);
+  const int epc = 16 / esz;
+  // contiguous matrix -> one long row
+  if (a.rows > 1 && a.ld == a.cols && (!write_q || a.ldq == a.cols)) {
+    a.cols *= a.rows;
+    a.rows = 1;
+    a.ld = a.cols;
+    a.ldq = a.cols;
+  }
+  bool vec = aligned(a.x, 16) && (a.rows == 1 || (a.ld * esz) % 16 == 0);
+  if (write_q) vec = vec && aligned(a.q, epc) && (a.rows == 1 || a.ldq % epc == 0);
+  const int64_t units = vec ? (a.cols / epc) : a.cols;
+  unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? kUnroll : 1));
+  unsigned gy = (unsigned)(a.rows < 65535 ? a.rows : 65535);
+  if (gy < 1) gy = 1;
+  // keep the whole grid near 4096 workgroups
+  while ((uint64_t)gx * gy > 8192 && gy > 1) gy = (gy + 1) / 2;
+  const dim3 grid(gx, gy);
+  if (dtype == FP8_DT_BF16) {
+    if (fmt == FP8_E4M3) launch_vec_mode<FP8_DT_BF16, FP8_E4M3>(a, vec, write_q, amax, grid, stream);
+    else launch_vec_mode<FP8_DT_BF16, FP8_E5M2>(a, vec, write_q, amax, grid, stream);
+  } else {
+    if (fmt == FP8_E4M3) launch_vec_mode<FP8_DT_F32, FP8_E4M3>(a, vec, write_q, amax, grid, stream);
+    else launch_vec_mode<FP8_DT_F32, FP8_E5M2>(a, vec, write_q, amax, grid, stream);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cast-transpose: 64 x 64 tiles; writes q [rows x cols] and qT [cols x rows]
+// (the transposed copy a GEMM contracting over `rows` reads K-contiguous).
+// Each of the 256 lanes casts 16 consecutive elements of one tile row, the
+// bytes go through a padded LDS tile, and each lane then writes 16 bytes of
+// one qT row.
+// ---------------------------------------------------------------------------
+constexpr int kTT = 64;
+
+template <int DT, int FMT, bool AMAX>
+__global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
+    const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, const int32_t* __restrict__ bias,
+    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ amax) {
+  __shared__ uint32_t tile[kTT][kTT / 4 + 1];     // 64 rows x 64 bytes, padded by one dword
+  __shared__ uint32_t red[kThreads / kWave];
+  constexpr int ESZ = In<DT>::kEsz;
+  const int e = *bias;
+  const int64_t r0 = (int64_t)blockIdx.y * kTT;
+  const int64_t c0 = (int64_t)blockIdx.x * kTT;
+  const int tr = threadIdx.x / 4;            // tile row 0..63
+  const int tc = (threadIdx.x % 4) * 16;     // first tile column of this lane
+  uint32_t amax_bits = 0;
+  const int64_t r = r0 + tr;
+  uint32_t packed[4] = {0u, 0u, 0u, 0u};
+  if (r < rows) {
+    const char* xr = reinterpret_cast<const char*>(x) + r * ld * ESZ;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int64_t c = c0 + tc + j;
+      uint32_t code = 0;
+      if (c < cols) {
+        float f;
+        const uint32_t bits = load_elem<DT>(xr, c, &f);
+        const uint32_t ab = bits & 0x7fffffffu;
+        if (AMAX) amax_bits = amax_bits > ab ? amax_bits : ab;
+        code = cast_elem<FMT>(bits, e);
+        q[r * ldq + c] = (uint8_t)code;
+      }
+      packed[j / 4] |= code << (8 * (j % 4));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) tile[tr][tc / 4 + j] = packed[j];
+  __syncthreads();
+  // qT row (c0 + tr) gets tile column tr, tile rows tc .. tc+15
+  const int64_t cT = c0 + tr;
+  if (cT < cols) {
+    uint8_t* dst = qT + cT * ldqT + r0 + tc;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (r0 + tc + j < rows) {
+        const uint32_t w = tile[tc + j][tr / 4];
+        dst[j] = (uint8_t)((w >> (8 * (tr % 4))) & 0xffu);
+      }
+    }
+  }
+  if (AMAX) block_max_to_global(amax_bits, red, amax);
+}
+
+// ---------------------------------------------------------------------------
+// MX cast: 1 x 32 blocks along cols.  Vector kernel: a block is 4 lanes
+// (bf16) or 8 lanes (f32) of 16-byte chunks; the block max is a DPP
+// reduction inside the lane group, the group's first lane stores the E8M0
+// code.  Scalar kernel (unaligned operands): one lane per block.
+// ---------------------------------------------------------------------------
+struct MxArgs {
+  const void* x;
+  int64_t rows, cols, ld;
+  uint8_t* q;
+  int64_t ldq;
+  uint8_t* scales;
+  int64_t lds;
+};
+
+template <int FMT>
+__device__ __forceinline__ void block_exponent(uint32_t bmax_bits, int* e, uint32_t* code) {
+  if (bmax_bits > 0x7f800000u) {        // NaN in the block
+    *e = 0;
+    *code = 0xffu;
+  } else {
+    *e = bias_from_amax_bits(bmax_bits, Fmt<FMT>::kEmax, 0, -127, 127);
+    *code = (uint32_t)(127 - *e);
+  }
+}
+
+template <int DT, int FMT>
+__global__ __launch_bounds__(kThreads) void mx_vec_kernel(MxArgs a) {
+  constexpr int ESZ = In<DT>::kEsz;
+  constexpr int EPC = In<DT>::kEpc;
+  constexpr int L = 32 / EPC;           // lanes per block
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t cpr = a.cols / EPC;
+  for (int64_t r = blockIdx.y; r < a.rows; r += gridDim.y) {
+    const uint4* x4 = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.x) + r * a.ld * ESZ);
+    uint8_t* qr = a.q + r * a.ldq;
+    uint8_t* sr = a.scales + r * a.lds;
+    int64_t c = tid;
+    // every lane of a block's group takes the same branch: stride and cpr
+    // are multiples of L and the group's chunks share c / L
+    for (; c + (kUnroll - 1) * stride < cpr; c += kUnroll * stride) {
+      uint4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) v[u] = x4[c + u * stride];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        uint32_t m;
+        cast_chunk<DT, FMT>(v[u], 0, &m, false);
+        const uint32_t bm = (L == 4) ? group4_max(m) : group8_max(m);
+        int e;
+        uint32_t code;
+        block_exponent<FMT>(bm, &e, &code);
+        const uint2 o = cast_chunk<DT, FMT>(v[u], e, &m, true);
+        store_codes<DT>(qr, c + u * stride, o);
+        if ((threadIdx.x % L) == 0) sr[(c + u * stride) / L] = (uint8_t)code;
+      }
+    }
+    for (; c < cpr; c += stride) {
+      uint32_t m;
+      const uint4 v = x4[c];
+      cast_chunk<DT, FMT>(v, 0, &m, false);
+      const uint32_t bm = (L == 4) ? group4_max(m) : group8_max(m);
+      int e;
+      uint32_t code;
+      block_exponent<FMT>(bm, &e, &code);
+      const uint2 o = cast_chunk<DT, FMT>(v, e, &m, true);
+      store_codes<DT>(qr, c, o);
+      if ((threadIdx.x % L) == 0) sr[c / L] = (uint8_t)code;
+    }
+  }
+}
+
+template <int DT, int FMT>
+__global__ __launch_bounds__(kThreads) void mx_scalar_kernel(MxArgs a) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t nb = a.cols / 32;
+  for (int64_t r = blockIdx.y; r < a.rows; r += gridDim.y) {
+    const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ld * In<DT>::kEsz;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
+      uint32_t m = 0;
+      for (int j = 0; j < 32; ++j) {
+        float f;
+        const uint32_t ab = load_elem<DT>(xr, b * 32 + j, &f) & 0x7fffffffu;
+        m = m > ab ? m : ab;
+      }
+      int e;
+      uint32_t code;
+      block_exponent<FMT>(m, &e, &code);
+      for (int j = 0; j < 32; ++j) {
+        float f;
+        const uint32_t bits = load_elem<DT>(xr, b * 32 + j, &f);
+        a.q[r * a.ldq + b * 32 + j] = (uint8_t)cast_elem<FMT>(bits, e);
+      }
+      a.scales[r * a.lds + b] = (uint8_t)code;
+    }
+  }
+}
+
+template <int DT, int FMT>
+static void launch_mx(const MxArgs& a, bool vec, hipStream_t s) {
+  const int epc = 16 / In<DT>::kEsz;
+  const int64_t units = vec ? a.cols / epc : a.cols / 32;
+  const unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? kUnroll : 1));
+  unsigned gy = (unsigned)(a.rows < 65535 ? a.rows : 65535);
+  if (gy < 1) gy = 1;
+  while ((uint64_t)gx * gy > 8192 && gy > 1) gy = (gy + 1) / 2;
+  if (vec)
+    hipLaunchKernelGGL((mx_vec_kernel<DT, FMT>), dim3(gx, gy), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((mx_scalar_kernel<DT, FMT>), dim3(gx, gy), dim3(kThreads), 0, s, a);
+}
+
+}  // namespace sfp8
+
+using namespace sfp8;
+
+extern "C" {
+
+int fp8_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                 const int32_t* bias, uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT, float* amax_out,
+                 hipStream_t stream) {
+  if (!bias || !q) return FP8_ERR_NULL;
+  if (!valid_dtype(dtype)) return FP8_ERR_DTYPE;
+  if (!valid_fmt(fmt)) return FP8_ERR_FORMAT;
+  int st = check_matrix(rows, cols, ld);
+  if (st) return st;
+  st = check_matrix(rows, cols, ldq);
+  if (st) return st;
+  if (qT && check_matrix(cols, rows, ldqT)) return FP8_ERR_SHAPE;
+  const int64_t n = rows * cols;
+  if (n > 0 && !x) return FP8_ERR_NULL;
+  if (amax_out) zero_float_async(amax_out, stream);
+  if (n == 0) return launch_status();
+  if (qT) {
+    const dim3 grid((unsigned)((cols + kTT - 1) / kTT), (unsigned)((rows + kTT - 1) / kTT));
+    if (grid.y > 65535) return FP8_ERR_SHAPE;
+#define SFP8_CT(DT, FMT)                                                                                   \
+  do {                                                                                                     \
+    if (amax_out)                                                                                          \
+      hipLaunchKernelGGL((cast_transpose_kernel<DT, FMT, true>), grid, dim3(kThreads), 0, stream, x, rows, \
+                         cols, ld, bias, q, ldq, qT, ldqT, amax_out);                                      \
+    else                                                                                                   \
+      hipLaunchKernelGGL((cast_transpose_kernel<DT, FMT, false>), grid, dim3(kThreads), 0, stream, x,      \
+                         rows, cols, ld, bias, q, ldq, qT, ldqT, amax_out);                                \
+  } while (0)
+    if (dtype == FP8_DT_BF16) {
+      if (fmt == FP8_E4M3) SFP8_CT(FP8_DT_BF16, FP8_E4M3);
+      else SFP8_CT(FP8_DT_BF16, FP8_E5M2);
+    } else {
+      if (fmt == FP8_E4M3) SFP8_CT(FP8_DT_F32, FP8_E4M3);
+      else SFP8_CT(FP8_DT_F32, FP8_E5M2);
+    }
+#undef SFP8_CT
+    return launch_status();
+  }
+  StreamArgs a;
+  a.x = x;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.bias = bias;
+  a.q = q;
+  a.ldq = ldq;
+  a.amax = amax_out;
+  launch_stream_pass(a, dtype, fmt, /*write_q=*/true, /*amax=*/amax_out != nullptr, stream);
+  return launch_status();
+}
+
+int mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, uint8_t* q,
+                int64_t ldq, uint8_t* scales, int64_t ld_scales, hipStream_t stream) {
+  if (!q || !scales) return FP8_ERR_NULL;
+  if (!valid_dtype(dtype)) return FP8_ERR_DTYPE;
+  if (!valid_fmt(fmt)) return FP8_ERR_FORMAT;
+  if (cols % 32) return FP8_ERR_SHAPE;
+  int st = check_matrix(rows, cols, ld);
+  if (st) return st;
+  st = check_matrix(rows, cols, ldq);
+  if (st) return st;
+  st = check_matrix(rows, cols / 32, ld_scales);
+  if (st) return st;
+  if (rows * cols == 0) return FP8_OK;
+  if (!x) return FP8_ERR_NULL;
+  MxArgs a;
+  a.x = x;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.q = q;
+  a.ldq = ldq;
+  a.scales = scales;
+  a.lds = ld_scales;
+  const int esz = dtype_size(dtype);
+  const int epc = 16 / esz;
+  // contiguous -> one long row (blocks never straddle rows since cols % 32 == 0)
+  if (a.rows > 1 && a.ld == a.cols && a.ldq == a.cols && a.lds == a.cols / 32) {
+    a.cols *= a.rows;
+    a.rows = 1;
+    a.ld = a.cols;
+    a.ldq = a.cols;
+    a.lds = a.cols / 32;
+  }
+  const bool vec = aligned(a.x, 16) && (a.rows == 1 || (a.ld * esz) % 16 == 0) && aligned(a.q, epc) &&
+                   (a.rows == 1 || a.ldq % epc == 0);
+  if (dtype == FP8_DT_BF16) {
+    if (fmt == FP8_E4M3) launch_mx<FP8_DT_BF16, FP8_E4M3>(a, vec, stream);
+    else launch_mx<FP8_DT_BF16, FP8_E5M2>(a, vec, stream);
+  } else {
+    if (fmt == FP8_E4M3) launch_mx<FP8_DT_F32, FP8_E4M3>(a, vec, stream);
+    else launch_mx<FP8_DT_F32, FP8_E5M2>(a, vec, stream);
+  }
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,160 @@
+// Per-tensor amax, exponent bias and delayed-scaling history for gfx950.
+//
+// "Training and inference of large language models using 8-bit floating
+// point" (paper review), "Proposed method": per-tensor scaling biases come
+// from each tensor's maximum absolute value through log2(format max / amax)
+// with a configurable margin.  "Per-Tensor and Per-Block Scaling Strategies
+// for Effective FP8 Training" (summary), "Key Questions Answered": delayed
+// scaling takes the amax over a window of past iterations.
+//
+// The amax reduction itself shares the streaming kernel of quantize.hip
+// (a pass that only reads); this file holds the scalar kernels and the
+// entry points fp8_amax, fp8_compute_scale, fp8_history_*.
+#include "common.hpp"
+#include "host.hpp"
+#include "stream_kernels.hpp"
+
+namespace sfp8 {
+
+__global__ void zero_float_kernel(float* p) { *p = 0.0f; }
+
+void zero_float_async(float* p, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_float_kernel, dim3(1), dim3(1), 0, stream, p);
+}
+
+// One thread: bias and optional scales from one amax.
+__global__ void compute_scale_kernel(const float* __restrict__ amax, int emax, int margin,
+                                     int32_t* __restrict__ bias_out, float* __restrict__ scale_out,
+                                     float* __restrict__ scale_inv_out) {
+  const int b = bias_from_amax_bits(__float_as_uint(*amax), emax, margin, -126, 126);
+  *bias_out = b;
+  if (scale_out) *scale_out = pow2f(b);
+  if (scale_inv_out) *scale_inv_out = pow2f(-b);
+}
+
+__global__ void history_init_kernel(float* __restrict__ hist, int32_t* __restrict__ state, int window) {
+  for (int i = threadIdx.x; i < window; i += blockDim.x) hist[i] = 0.0f;
+  if (threadIdx.x == 0) {
+    state[0] = 0;
+    state[1] = 0;
+  }
+}
+
+__global__ void history_push_kernel(float* __restrict__ hist, int32_t* __restrict__ state, int window,
+                                    const float* __restrict__ amax) {
+  int count = state[0];
+  int head = state[1];
+  // a corrupted state is repaired into range rather than indexing outside hist
+  head = (head < 0 || head >= window) ? 0 : head;
+  count = count < 0 ? 0 : (count > window ? window : count);
+  hist[head] = *amax;
+  state[1] = (head + 1) % window;
+  state[0] = count + 1 > window ? window : count + 1;
+}
+
+// Window maximum over the valid entries, then the bias rule.  The entries
+// are amaxes (non-negative or NaN), so an unsigned compare of their bits is
+// the float max with NaN on top.
+__global__ void compute_scale_delayed_kernel(const float* __restrict__ hist, const int32_t* __restrict__ state,
+                                             int window, int emax, int margin, int32_t* __restrict__ bias_out,
+                                             float* __restrict__ scale_out, float* __restrict__ scale_inv_out) {
+  __shared__ uint32_t red[4];
+  int count = state[0];
+  count = count < 0 ? 0 : (count > window ? window : count);
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < count; i += blockDim.x) {
+    const uint32_t v = __float_as_uint(hist[i]) & 0x7fffffffu;
+    m = m > v ? m : v;
+  }
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x / 64] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 1; i < (int)(blockDim.x / 64); ++i) m = m > red[i] ? m : red[i];
+    m = m > red[0] ? m : red[0];
+    const int b = bias_from_amax_bits(m, emax, margin, -126, 126);
+    *bias_out = b;
+    if (scale_out) *scale_out = pow2f(b);
+    if (scale_inv_out) *scale_inv_out = pow2f(-b);
+  }
+}
+
+}  // namespace sfp8
+
+using namespace sfp8;
+
+extern "C" {
+
+const char* fp8_status_string(int status) {
+  switch (status) {
+    case FP8_OK: return "ok";
+    case FP8_ERR_NULL: return "null pointer";
+    case FP8_ERR_SHAPE: return "bad shape or leading dimension";
+    case FP8_ERR_ALIGN: return "misaligned operand (16-byte base and leading dimension required)";
+    case FP8_ERR_DTYPE: return "unknown data type";
+    case FP8_ERR_FORMAT: return "unknown FP8 format";
+    case FP8_ERR_LAUNCH: return "HIP launch failure";
+    case FP8_ERR_UNSUPPORTED: return "unsupported combination";
+    default: return "unknown status";
+  }
+}
+
+int fp8_abi_version(void) { return 1; }
+
+int fp8_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, float* amax_out,
+             hipStream_t stream) {
+  if (!amax_out) return FP8_ERR_NULL;
+  if (!valid_dtype(dtype)) return FP8_ERR_DTYPE;
+  int st = check_matrix(rows, cols, ld);
+  if (st) return st;
+  if (rows * cols > 0 && !x) return FP8_ERR_NULL;
+  zero_float_async(amax_out, stream);
+  if (rows * cols > 0) {
+    StreamArgs a;
+    a.x = x;
+    a.rows = rows;
+    a.cols = cols;
+    a.ld = ld;
+    a.bias = nullptr;
+    a.q = nullptr;
+    a.ldq = 0;
+    a.amax = amax_out;
+    launch_stream_pass(a, dtype, FP8_E4M3, /*write_q=*/false, /*amax=*/true, stream);
+  }
+  return launch_status();
+}
+
+int fp8_compute_scale(const float* amax, int fmt, int margin, int32_t* bias_out, float* scale_out,
+                      float* scale_inv_out, hipStream_t stream) {
+  if (!amax || !bias_out) return FP8_ERR_NULL;
+  if (!valid_fmt(fmt)) return FP8_ERR_FORMAT;
+  hipLaunchKernelGGL(compute_scale_kernel, dim3(1), dim3(1), 0, stream, amax, fmt == FP8_E4M3 ? 8 : 15,
+                     margin, bias_out, scale_out, scale_inv_out);
+  return launch_status();
+}
+
+int fp8_history_init(float* hist, int32_t* state, int window, hipStream_t stream) {
+  if (!hist || !state) return FP8_ERR_NULL;
+  if (window < 1 || window > 4096) return FP8_ERR_SHAPE;
+  hipLaunchKernelGGL(history_init_kernel, dim3(1), dim3(256), 0, stream, hist, state, window);
+  return launch_status();
+}
+
+int fp8_history_push(float* hist, int32_t* state, int window, const float* amax, hipStream_t stream) {
+  if (!hist || !state || !amax) return FP8_ERR_NULL;
+  if (window < 1 || window > 4096) return FP8_ERR_SHAPE;
+  hipLaunchKernelGGL(history_push_kernel, dim3(1), dim3(1), 0, stream, hist, state, window, amax);
+  return launch_status();
+}
+
+int fp8_compute_scale_delayed(const float* hist, const int32_t* state, int window, int fmt, int margin,
+                              int32_t* bias_out, float* scale_out, float* scale_inv_out, hipStream_t stream) {
+  if (!hist || !state || !bias_out) return FP8_ERR_NULL;
+  if (window < 1 || window > 4096) return FP8_ERR_SHAPE;
+  if (!valid_fmt(fmt)) return FP8_ERR_FORMAT;
+  hipLaunchKernelGGL(compute_scale_delayed_kernel, dim3(1), dim3(256), 0, stream, hist, state, window,
+                     fmt == FP8_E4M3 ? 8 : 15, margin, bias_out, scale_out, scale_inv_out);
+  return launch_status();
+}
+
+}  // extern "C"

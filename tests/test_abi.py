@@ -1,0 +1,128 @@
+"""C-ABI checks that run without a GPU: the library loads, exports every
+function ``include/scaled_fp8.h`` declares, and rejects bad arguments with
+the documented status codes before making any HIP call (so no call here
+touches a device: every one of them fails host-side validation)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import scaled_quantize_fp8_amd as sq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "scaled_fp8.h")
+
+OK, NULL, SHAPE, ALIGN, DTYPE, FORMAT, LAUNCH, UNSUP = 0, -1, -2, -3, -4, -5, -6, -7
+FAKE = 0x10000          # 16-byte aligned, never dereferenced (validation fails first)
+S = None                # default stream
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sq.library_path()):
+        pytest.skip("libscaled_fp8.so not built")
+    return sq.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(fp8_\w+|mx_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for want in ["fp8_amax", "fp8_compute_scale", "fp8_history_init", "fp8_history_push",
+                 "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize",
+                 "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string", "fp8_abi_version"]:
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert sq.fp8_status_string(OK) == "ok"
+    for code in (NULL, SHAPE, ALIGN, DTYPE, FORMAT, LAUNCH, UNSUP):
+        assert sq.fp8_status_string(code) not in ("ok", "unknown status")
+    assert sq.fp8_status_string(-99) == "unknown status"
+    assert sq.fp8_abi_version() >= 1
+
+
+def test_amax_validation(lib):
+    assert lib.fp8_amax(FAKE, 0, 4, 4, 4, None, S) == NULL
+    assert lib.fp8_amax(FAKE, 7, 4, 4, 4, FAKE, S) == DTYPE
+    assert lib.fp8_amax(FAKE, 0, 4, 8, 4, FAKE, S) == SHAPE          # ld < cols
+    assert lib.fp8_amax(FAKE, 0, -1, 8, 8, FAKE, S) == SHAPE
+    assert lib.fp8_amax(None, 0, 4, 4, 4, FAKE, S) == NULL
+
+
+def test_scale_and_history_validation(lib):
+    assert lib.fp8_compute_scale(None, 0, 0, FAKE, None, None, S) == NULL
+    assert lib.fp8_compute_scale(FAKE, 0, 0, None, None, None, S) == NULL
+    assert lib.fp8_compute_scale(FAKE, 2, 0, FAKE, None, None, S) == FORMAT
+    assert lib.fp8_history_init(None, FAKE, 16, S) == NULL
+    assert lib.fp8_history_init(FAKE, FAKE, 0, S) == SHAPE
+    assert lib.fp8_history_init(FAKE, FAKE, 4097, S) == SHAPE
+    assert lib.fp8_history_push(FAKE, FAKE, 16, None, S) == NULL
+    assert lib.fp8_history_push(FAKE, FAKE, -3, FAKE, S) == SHAPE
+    assert lib.fp8_compute_scale_delayed(FAKE, FAKE, 16, 9, 0, FAKE, None, None, S) == FORMAT
+    assert lib.fp8_compute_scale_delayed(FAKE, None, 16, 0, 0, FAKE, None, None, S) == NULL
+    assert lib.fp8_compute_scale_delayed(FAKE, FAKE, 0, 0, 0, FAKE, None, None, S) == SHAPE
+
+
+def test_quantize_validation(lib):
+    q = lib.fp8_quantize
+    assert q(FAKE, 0, 4, 4, 4, 0, None, FAKE, 4, None, 0, None, S) == NULL      # bias
+    assert q(FAKE, 0, 4, 4, 4, 0, FAKE, None, 4, None, 0, None, S) == NULL      # q
+    assert q(FAKE, 3, 4, 4, 4, 0, FAKE, FAKE, 4, None, 0, None, S) == DTYPE
+    assert q(FAKE, 0, 4, 4, 4, 5, FAKE, FAKE, 4, None, 0, None, S) == FORMAT
+    assert q(FAKE, 0, 4, 4, 2, 0, FAKE, FAKE, 4, None, 0, None, S) == SHAPE     # ld
+    assert q(FAKE, 0, 4, 4, 4, 0, FAKE, FAKE, 3, None, 0, None, S) == SHAPE     # ldq
+    assert q(FAKE, 0, 4, 8, 8, 0, FAKE, FAKE, 8, FAKE, 2, None, S) == SHAPE     # ldqT < rows
+    assert q(None, 0, 4, 4, 4, 0, FAKE, FAKE, 4, None, 0, None, S) == NULL
+    m = lib.mx_quantize
+    assert m(FAKE, 0, 4, 48, 48, 0, FAKE, 48, FAKE, 2, S) == SHAPE              # cols % 32
+    assert m(FAKE, 0, 4, 64, 64, 0, None, 64, FAKE, 2, S) == NULL
+    assert m(FAKE, 0, 4, 64, 64, 0, FAKE, 64, None, 2, S) == NULL
+    assert m(FAKE, 0, 4, 64, 64, 0, FAKE, 64, FAKE, 1, S) == SHAPE              # ld_scales
+    assert m(FAKE, 2, 4, 64, 64, 0, FAKE, 64, FAKE, 2, S) == DTYPE
+    assert m(FAKE, 0, 4, 64, 64, 2, FAKE, 64, FAKE, 2, S) == FORMAT
+
+
+def test_gemm_validation(lib):
+    g = lib.fp8_scaled_gemm
+    # M, N, K, A, fa, ta, lda, ba, B, fb, tb, ldb, bb, C, dt, ldc, amax, s
+    assert g(64, 64, 64, FAKE, 0, 0, 64, None, FAKE, 0, 0, 64, FAKE, FAKE, 0, 64, None, S) == NULL
+    assert g(64, 64, 64, FAKE, 4, 0, 64, FAKE, FAKE, 0, 0, 64, FAKE, FAKE, 0, 64, None, S) == FORMAT
+    assert g(64, 64, 64, FAKE, 0, 0, 64, FAKE, FAKE, 0, 0, 64, FAKE, FAKE, 9, 64, None, S) == DTYPE
+    assert g(64, 64, 40, FAKE, 0, 0, 48, FAKE, FAKE, 0, 0, 48, FAKE, FAKE, 0, 64, None, S) == SHAPE
+    assert g(64, 64, 64, FAKE, 0, 0, 32, FAKE, FAKE, 0, 0, 64, FAKE, FAKE, 0, 64, None, S) == SHAPE
+    assert g(64, 64, 64, FAKE, 0, 0, 64, FAKE, FAKE, 0, 0, 64, FAKE, FAKE, 0, 32, None, S) == SHAPE
+    assert g(40, 64, 64, FAKE, 0, 1, 48, FAKE, FAKE, 0, 0, 64, FAKE, FAKE, 0, 64, None, S) == SHAPE
+    assert g(64, 64, 64, FAKE + 8, 0, 0, 64, FAKE, FAKE, 0, 0, 64, FAKE, FAKE, 0, 64, None, S) == ALIGN
+    assert g(64, 64, 64, FAKE, 0, 0, 72, FAKE, FAKE, 0, 0, 64, FAKE, FAKE, 0, 64, None, S) == ALIGN
+    assert g(64, 64, 64, None, 0, 0, 64, FAKE, FAKE, 0, 0, 64, FAKE, FAKE, 0, 64, None, S) == NULL
+    assert g(64, 64, 64, FAKE, 0, 0, 64, FAKE, FAKE, 0, 0, 64, FAKE, None, 0, 64, None, S) == NULL
+    assert g(64, 64, 64, FAKE, 0, 0, 1 << 23, FAKE, FAKE, 0, 0, 64, FAKE, FAKE, 0, 64, None, S) == UNSUP
+    mg = lib.mx_scaled_gemm
+    # M, N, K, A, fa, lda, As, ldsa, B, fb, ldb, Bs, ldsb, C, dt, ldc, amax, s
+    assert mg(64, 64, 48, FAKE, 0, 48, FAKE, 4, FAKE, 0, 48, FAKE, 4, FAKE, 0, 64, None, S) == SHAPE
+    assert mg(64, 64, 64, FAKE, 0, 64, None, 4, FAKE, 0, 64, FAKE, 4, FAKE, 0, 64, None, S) == NULL
+    assert mg(64, 64, 64, FAKE, 0, 64, FAKE, 1, FAKE, 0, 64, FAKE, 4, FAKE, 0, 64, None, S) == SHAPE
+    assert mg(64, 64, 64, FAKE + 4, 0, 64, FAKE, 4, FAKE, 0, 64, FAKE, 4, FAKE, 0, 64, None, S) == ALIGN
+    assert mg(64, 64, 64, FAKE, 0, 64, FAKE, 2, FAKE, 0, 72, FAKE, 4, FAKE, 0, 64, None, S) == ALIGN
+    assert mg(64, 64, 64, FAKE, 3, 64, FAKE, 4, FAKE, 0, 64, FAKE, 4, FAKE, 0, 64, None, S) == FORMAT
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 4, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sq.fp8_amax(x)
+    with pytest.raises(ValueError):
+        sq.mx_quantize(torch.zeros(4, 32, dtype=torch.bfloat16))

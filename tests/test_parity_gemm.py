@@ -1,0 +1,289 @@
+"""GPU parity of the scaled FP8 GEMMs against the oracle's float64 sums.
+
+Operands are FP8 codes, biases and E8M0 scales produced by the ORACLE from
+the workload generators' bf16 inputs, so expected values never depend on the
+HIP path.  Acceptance: |C - C_ref| <= 1e-5 * sum_k |a_k b_k| (fp32 output),
+plus one bf16 ulp of C_ref (bf16 output); the workload configurations (the
+256x768x768 layer, the 7B-MLP backward products, the 70B-MLP forward) are held
+to exactly that.  Short-K synthetic edge cases add the FP8 MFMA's in-group
+truncation allowance (``mfma_group_term``), a property of the instruction
+measured on gfx950.  The fused output amax must equal max |C| over the
+stored output bit for bit."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scaled_quantize_fp8_amd as sq
+from oracle import E4M3, E5M2
+from workloads import f32_to_bf16_bits, make
+
+from gpu_helpers import (DEV, assert_gemm_close, bf16_dev, f32_bits_of, host, host_f64, i32_dev,
+                         mfma_group_term, need_gpu, oracle_mx_chunked, oracle_quantize_chunked,
+                         oracle_amax_chunked, say, u8_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _operand(rng, shape, std, fmt):
+    bits = f32_to_bf16_bits((rng.standard_normal(shape) * std).astype(np.float32))
+    vals = oracle.bf16_bits_to_f64(bits)
+    b = oracle.compute_bias(oracle.amax(vals), fmt)
+    return oracle.quantize(vals, fmt, b), b
+
+
+def _check_amax(C, amax_out):
+    ref = np.max(np.abs(host_f64(C))) if C.numel() else 0.0
+    assert host(amax_out)[0] == ref
+    assert f32_bits_of(amax_out) == f32_bits_of(sq.fp8_amax(C))
+
+
+def _run_pt(qa, fa, ba, qb, fb, bb, ta, tb, out_dtype):
+    """qa/qb are op(A) [M,K] / op(B) [N,K]; stored transposed when ta/tb."""
+    A = u8_dev(qa.T if ta else qa)
+    B = u8_dev(qb.T if tb else qb)
+    return sq.fp8_scaled_gemm(A, fa.code, i32_dev(ba), B, fb.code, i32_dev(bb), trans_a=ta, trans_b=tb,
+                              out_dtype=out_dtype, want_amax=True)
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("fa,fb", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2), (E5M2, E5M2)],
+                         ids=["e4e4", "e5e4", "e4e5", "e5e5"])
+def test_gemm_ragged_tiles(fa, fb, out_dtype):
+    """M=300, N=520, K=400: 2 x 3 macro tiles with ragged M, N and K tails."""
+    rng = np.random.default_rng(21)
+    M, N, K = 300, 520, 400
+    qa, ba = _operand(rng, (M, K), 1.0, fa)
+    qb, bb = _operand(rng, (N, K), 0.02, fb)
+    say(f"gemm ragged {fa.name}x{fb.name} {out_dtype}")
+    C, am = _run_pt(qa, fa, ba, qb, fb, bb, False, False, out_dtype)
+    ref = oracle.scaled_gemm_ref(qa, fa, ba, qb, fb, bb)
+    s = oracle.abs_product_sum(qa, fa, ba, qb, fb, bb)
+    gt = mfma_group_term(oracle.dequantize(qa, fa, ba), oracle.dequantize(qb, fb, bb))
+    assert_gemm_close(host_f64(C), ref, s, out_dtype == torch.bfloat16, "ragged", gt)
+    _check_amax(C, am)
+
+
+@pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)], ids=["NT", "TN", "TT"])
+def test_gemm_transposed_operands(ta, tb):
+    """Transposed storage for op(A) / op(B) (the backward products): M, N
+    multiples of 16, K ragged (K = 272)."""
+    rng = np.random.default_rng(22)
+    M, N, K = 272, 528, 272
+    qa, ba = _operand(rng, (M, K), 1e-4, E5M2)
+    qb, bb = _operand(rng, (N, K), 0.02, E4M3)
+    say(f"gemm transposed ta={ta} tb={tb}")
+    C, am = _run_pt(qa, E5M2, ba, qb, E4M3, bb, ta, tb, torch.float32)
+    ref = oracle.scaled_gemm_ref(qa, E5M2, ba, qb, E4M3, bb)
+    s = oracle.abs_product_sum(qa, E5M2, ba, qb, E4M3, bb)
+    gt = mfma_group_term(oracle.dequantize(qa, E5M2, ba), oracle.dequantize(qb, E4M3, bb))
+    assert_gemm_close(host_f64(C), ref, s, False, f"trans {ta}{tb}", gt)
+    _check_amax(C, am)
+
+
+def test_gemm_degenerate_shapes():
+    rng = np.random.default_rng(23)
+    qa, ba = _operand(rng, (64, 32), 1.0, E4M3)
+    qb, bb = _operand(rng, (48, 32), 1.0, E4M3)
+    # K = 0: C = 0, amax 0
+    A0 = torch.zeros((64, 0), dtype=torch.uint8, device=DEV)
+    B0 = torch.zeros((48, 0), dtype=torch.uint8, device=DEV)
+    C, am = sq.fp8_scaled_gemm(A0, 0, i32_dev(0), B0, 0, i32_dev(0), out_dtype=torch.float32, want_amax=True)
+    assert np.all(host(C) == 0) and host(am)[0] == 0.0
+    # M = 0
+    C, am = sq.fp8_scaled_gemm(torch.zeros((0, 32), dtype=torch.uint8, device=DEV), 0, i32_dev(0),
+                               u8_dev(qb), 0, i32_dev(bb), want_amax=True)
+    assert C.shape == (0, 48) and host(am)[0] == 0.0
+    # K = 16 (one partial MFMA block), tiny M, N
+    qa1, ba1 = _operand(rng, (3, 16), 1.0, E4M3)
+    qb1, bb1 = _operand(rng, (5, 16), 1.0, E4M3)
+    C, am = _run_pt(qa1, E4M3, ba1, qb1, E4M3, bb1, False, False, torch.float32)
+    assert_gemm_close(host_f64(C), oracle.scaled_gemm_ref(qa1, E4M3, ba1, qb1, E4M3, bb1),
+                      oracle.abs_product_sum(qa1, E4M3, ba1, qb1, E4M3, bb1), False, "K=16",
+                      mfma_group_term(oracle.dequantize(qa1, E4M3, ba1), oracle.dequantize(qb1, E4M3, bb1)))
+    # identity B: C = dequantized A exactly (fp32 out)
+    one = oracle.encode(np.array([1.0]), E4M3)[0]
+    eye = np.where(np.eye(32, dtype=bool), one, 0).astype(np.uint8)
+    C, _ = _run_pt(qa, E4M3, ba, eye, E4M3, 0, False, False, torch.float32)
+    assert np.array_equal(host_f64(C), oracle.dequantize(qa, E4M3, ba))
+    # strided output with padding columns untouched
+    big = torch.full((64, 64), -7.0, dtype=torch.float32, device=DEV)
+    sq.fp8_scaled_gemm(u8_dev(qa), 0, i32_dev(ba), u8_dev(qb), 0, i32_dev(bb), out=big[:, 8:56])
+    hb = host(big)
+    assert np.all(hb[:, :8] == -7.0) and np.all(hb[:, 56:] == -7.0)
+    assert_gemm_close(hb[:, 8:56].astype(np.float64), oracle.scaled_gemm_ref(qa, E4M3, ba, qb, E4M3, bb),
+                      oracle.abs_product_sum(qa, E4M3, ba, qb, E4M3, bb), False, "strided out",
+                      mfma_group_term(oracle.dequantize(qa, E4M3, ba), oracle.dequantize(qb, E4M3, bb)))
+
+
+def test_gemm_deterministic():
+    rng = np.random.default_rng(24)
+    qa, ba = _operand(rng, (512, 1024), 1.0, E4M3)
+    qb, bb = _operand(rng, (768, 1024), 0.02, E4M3)
+    C1, a1 = _run_pt(qa, E4M3, ba, qb, E4M3, bb, False, False, torch.bfloat16)
+    C2, a2 = _run_pt(qa, E4M3, ba, qb, E4M3, bb, False, False, torch.bfloat16)
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+    assert f32_bits_of(a1) == f32_bits_of(a2)
+
+
+def test_gemm_config_c1_full():
+    """X[256x768] W[768x768], current scaling, E4M3, Y = X W^T, bf16 and fp32."""
+    xb, wb = make("c1", "X"), make("c1", "W")
+    xv, wv = oracle.bf16_bits_to_f64(xb), oracle.bf16_bits_to_f64(wb)
+    bx, bw = oracle.compute_bias(oracle.amax(xv), E4M3), oracle.compute_bias(oracle.amax(wv), E4M3)
+    qx, qw = oracle.quantize(xv, E4M3, bx), oracle.quantize(wv, E4M3, bw)
+    ref = oracle.scaled_gemm_ref(qx, E4M3, bx, qw, E4M3, bw)
+    s = oracle.abs_product_sum(qx, E4M3, bx, qw, E4M3, bw)
+    for dt in (torch.bfloat16, torch.float32):
+        C, am = _run_pt(qx, E4M3, bx, qw, E4M3, bw, False, False, dt)
+        assert_gemm_close(host_f64(C), ref, s, dt == torch.bfloat16, "c1")
+        _check_amax(C, am)
+
+
+@pytest.mark.parametrize("fa,fb", [(E4M3, E4M3), (E5M2, E4M3)], ids=["e4e4", "e5e4"])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_mx_gemm_ragged(fa, fb, out_dtype):
+    """M=300, N=260, K=352 (K % 128 = 96: a partial last stage of blocks)."""
+    xb = make("c4", "X", shape=(300, 352))
+    wb = make("c4", "W", shape=(260, 352))
+    qa, sa = oracle.mx_quantize(oracle.bf16_bits_to_f64(xb), fa)
+    qb, sb = oracle.mx_quantize(oracle.bf16_bits_to_f64(wb), fb)
+    say(f"mx gemm {fa.name}x{fb.name} {out_dtype}")
+    C, am = sq.mx_scaled_gemm(u8_dev(qa), fa.code, u8_dev(sa), u8_dev(qb), fb.code, u8_dev(sb),
+                              out_dtype=out_dtype, want_amax=True)
+    ref = oracle.mx_gemm_ref(qa, sa, fa, qb, sb, fb)
+    s = oracle.mx_abs_product_sum(qa, sa, fa, qb, sb, fb)
+    gt = mfma_group_term(oracle.mx_dequantize(qa, sa, fa), oracle.mx_dequantize(qb, sb, fb))
+    assert_gemm_close(host_f64(C), ref, s, out_dtype == torch.bfloat16, "mx ragged", gt)
+    _check_amax(C, am)
+
+
+def test_mx_gemm_extreme_block_scales():
+    """Per-block codes spread over a wide range (2^-40 .. 2^40 per block), so a
+    wrong block <-> scale pairing cannot hide inside the tolerance."""
+    rng = np.random.default_rng(25)
+    M, N, K = 64, 80, 256
+    qa = rng.integers(0, 0x7E, (M, K)).astype(np.uint8) | (rng.integers(0, 2, (M, K)) << 7).astype(np.uint8)
+    qb = rng.integers(0, 0x7E, (N, K)).astype(np.uint8)
+    sa = rng.integers(87, 168, (M, K // 32)).astype(np.uint8)
+    sb = rng.integers(87, 168, (N, K // 32)).astype(np.uint8)
+    C, _ = sq.mx_scaled_gemm(u8_dev(qa), 0, u8_dev(sa), u8_dev(qb), 0, u8_dev(sb), out_dtype=torch.float32)
+    ref = oracle.mx_gemm_ref(qa, sa, E4M3, qb, sb, E4M3)
+    s = oracle.mx_abs_product_sum(qa, sa, E4M3, qb, sb, E4M3)
+    gt = mfma_group_term(oracle.mx_dequantize(qa, sa, E4M3), oracle.mx_dequantize(qb, sb, E4M3))
+    assert_gemm_close(host_f64(C), ref, s, False, "mx scales", gt)
+
+
+def test_mx_gemm_uniform_scales_match_per_tensor():
+    rng = np.random.default_rng(26)
+    qa, ba = _operand(rng, (130, 256), 1.0, E4M3)
+    qb, bb = _operand(rng, (70, 256), 1.0, E4M3)
+    sa = np.full((130, 8), 127 - ba, dtype=np.uint8)
+    sb = np.full((70, 8), 127 - bb, dtype=np.uint8)
+    Cm, _ = sq.mx_scaled_gemm(u8_dev(qa), 0, u8_dev(sa), u8_dev(qb), 0, u8_dev(sb), out_dtype=torch.float32)
+    Cp, _ = _run_pt(qa, E4M3, ba, qb, E4M3, bb, False, False, torch.float32)
+    ref = oracle.scaled_gemm_ref(qa, E4M3, ba, qb, E4M3, bb)
+    s = oracle.abs_product_sum(qa, E4M3, ba, qb, E4M3, bb)
+    gt = mfma_group_term(oracle.dequantize(qa, E4M3, ba), oracle.dequantize(qb, E4M3, bb))
+    assert_gemm_close(host_f64(Cm), ref, s, False, "mx uniform", gt)
+    assert_gemm_close(host_f64(Cp), ref, s, False, "pt uniform", gt)
+    # same codes, same arithmetic: the two kernels agree bit for bit
+    assert torch.equal(Cm, Cp)
+
+
+def _sample_idx(rng, M, N, n=2048):
+    rows = np.concatenate([rng.integers(0, M, n), [0, M - 1, 0, M - 1]])
+    cols = np.concatenate([rng.integers(0, N, n), [0, N - 1, N - 1, 0]])
+    return rows, cols
+
+
+def _sample_pairs(rng, M, N, nr=192, n=2048):
+    """n (row, col) output positions drawn from nr distinct rows and columns
+    (plus the four corners), so the oracle casts only those operand rows."""
+    rs = np.unique(np.concatenate([rng.integers(0, M, nr), [0, M - 1]]))
+    cs = np.unique(np.concatenate([rng.integers(0, N, nr), [0, N - 1]]))
+    ri = np.concatenate([rng.integers(0, rs.size, n), [0, rs.size - 1, 0, rs.size - 1]])
+    ci = np.concatenate([rng.integers(0, cs.size, n), [0, cs.size - 1, cs.size - 1, 0]])
+    return rs, cs, ri, ci
+
+
+def test_full_size_70b_mlp_end_to_end_sampled():
+    """X[16384 x 8192], W[28672 x 8192] through the whole hot path on the GPU,
+    in the benchmark's launch sequence: amax -> bias -> E4M3 cast -> per-tensor
+    GEMM (bf16 out, fused amax), and MX cast -> MX GEMM.  The oracle recomputes
+    amax and bias from the generator's bf16 tensors, casts only the sampled
+    operand rows and forms 2052 sampled outputs of each GEMM; the fused output
+    amax must equal a standalone reduction over the GPU's own output."""
+    xb, wb = make("c5", "X"), make("c5", "W")
+    x, w = bf16_dev(xb), bf16_dev(wb)
+    say("c5 gpu per-tensor path")
+    ax, aw = sq.fp8_amax(x), sq.fp8_amax(w)
+    bx, _, _ = sq.fp8_compute_scale(ax, 0, 0)
+    bw, _, _ = sq.fp8_compute_scale(aw, 0, 0)
+    qx, _, _ = sq.fp8_quantize(x, 0, bx)
+    qw, _, _ = sq.fp8_quantize(w, 0, bw)
+    C, am = sq.fp8_scaled_gemm(qx, 0, bx, qw, 0, bw, want_amax=True)
+    am_ref = sq.fp8_amax(C)
+    rng = np.random.default_rng(27)
+    rs, cs, ri, ci = _sample_pairs(rng, xb.shape[0], wb.shape[0])
+    got = host_f64(C[torch.from_numpy(rs[ri]).to(DEV), torch.from_numpy(cs[ci]).to(DEV)])
+    assert f32_bits_of(am) == f32_bits_of(am_ref)
+    del C, qx, qw
+    torch.cuda.empty_cache()
+    say("c5 oracle (per-tensor)")
+    rbx = oracle.compute_bias(oracle_amax_chunked(xb), E4M3)
+    rbw = oracle.compute_bias(oracle_amax_chunked(wb), E4M3)
+    assert int(host(bx)[0]) == rbx and int(host(bw)[0]) == rbw
+    oqx = oracle_quantize_chunked(xb, E4M3, rbx, rs)
+    oqw = oracle_quantize_chunked(wb, E4M3, rbw, cs)
+    y, s = oracle.gemm_sample_ref(oqx, E4M3, rbx, oqw, E4M3, rbw, ri, ci)
+    assert_gemm_close(got, y, s, True, "c5 per-tensor")
+    say("c5 gpu mx path")
+    mqx, msx = sq.mx_quantize(x, 0)
+    mqw, msw = sq.mx_quantize(w, 0)
+    C, am = sq.mx_scaled_gemm(mqx, 0, msx, mqw, 0, msw, want_amax=True)
+    got = host_f64(C[torch.from_numpy(rs[ri]).to(DEV), torch.from_numpy(cs[ci]).to(DEV)])
+    assert f32_bits_of(am) == f32_bits_of(sq.fp8_amax(C))
+    del C
+    say("c5 oracle (mx)")
+    oqxm, osxm = oracle_mx_chunked(xb, E4M3, rs)
+    oqwm, oswm = oracle_mx_chunked(wb, E4M3, cs)
+    y, s = oracle.mx_gemm_sample_ref(oqxm, osxm, E4M3, oqwm, oswm, E4M3, ri, ci)
+    assert_gemm_close(got, y, s, True, "c5 mx")
+
+
+def test_backward_shapes_7b_mlp_sampled():
+    """dX = dY W (A = dY [4096 x 11008] E5M2, B = W stored [11008 x 4096] ->
+    trans_b) and dW = dY^T X (A = dY^T, B = X^T, both stored transposed)."""
+    dyb, wb, xb = make("c3", "dY"), make("c3", "W"), make("c3", "X")
+    say("c3 oracle casts")
+    bdy = oracle.compute_bias(oracle_amax_chunked(dyb), E5M2)
+    bw = oracle.compute_bias(oracle_amax_chunked(wb), E4M3)
+    bx = oracle.compute_bias(oracle_amax_chunked(xb), E4M3)
+    qdy = oracle_quantize_chunked(dyb, E5M2, bdy)
+    qw = oracle_quantize_chunked(wb, E4M3, bw)
+    qx = oracle_quantize_chunked(xb, E4M3, bx)
+    rng = np.random.default_rng(28)
+    say("c3 dX")
+    dX, _ = sq.fp8_scaled_gemm(u8_dev(qdy), 1, i32_dev(bdy), u8_dev(qw), 0, i32_dev(bw), trans_b=True,
+                               out_dtype=torch.float32)
+    rows, cols = _sample_idx(rng, 4096, 4096, 1024)
+    qwT = np.ascontiguousarray(qw.T)
+    y, s = oracle.gemm_sample_ref(qdy, E5M2, bdy, qwT, E4M3, bw, rows, cols)
+    assert_gemm_close(host_f64(dX[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)]), y, s,
+                      False, "dX")
+    del dX
+    say("c3 dW")
+    dW, _ = sq.fp8_scaled_gemm(u8_dev(qdy), 1, i32_dev(bdy), u8_dev(qx), 0, i32_dev(bx), trans_a=True,
+                               trans_b=True, out_dtype=torch.float32)
+    rows, cols = _sample_idx(rng, 11008, 4096, 1024)
+    y, s = oracle.gemm_sample_ref(np.ascontiguousarray(qdy.T), E5M2, bdy, np.ascontiguousarray(qx.T), E4M3, bx,
+                                  rows, cols)
+    assert_gemm_close(host_f64(dW[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)]), y, s,
+                      False, "dW")

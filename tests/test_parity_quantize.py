@@ -1,0 +1,212 @@
+"""GPU parity of amax, bias, per-tensor and per-block casts against the
+oracle: bit-exact bytes, biases, float32 amaxes and E8M0 codes."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scaled_quantize_fp8_amd as sq
+from oracle import E4M3, E5M2
+from workloads import all_bf16_patterns, make
+
+from gpu_helpers import (DEV, bf16_dev, f32_bits_of, f32_dev, host, i32_dev, need_gpu,
+                         oracle_amax_chunked, oracle_mx_chunked, oracle_quantize_chunked, say, u8_dev)
+
+pytestmark = pytest.mark.gpu
+FMTS = [E4M3, E5M2]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: f.name)
+def test_cast_every_bf16_pattern_every_bias(fmt):
+    """All 65,536 bf16 bit patterns x every bias in [-126, 126]: the GPU bytes
+    equal the oracle's (NaN -> 0x7F|sign, saturation, -0, subnormals)."""
+    bits = all_bf16_patterns().reshape(256, 256)
+    x = bf16_dev(bits)
+    vals = oracle.bf16_bits_to_f64(bits)
+    mism = []
+    for b in range(-126, 127):
+        say(f"cast sweep fmt={fmt.name} bias={b}") if b % 50 == 0 else None
+        q, _, _ = sq.fp8_quantize(x, fmt.code, i32_dev(b))
+        ref = oracle.quantize(vals, fmt, b)
+        got = host(q)
+        if not np.array_equal(got, ref):
+            d = np.argwhere(got != ref)[:3]
+            mism.append((b, [(hex(int(bits[tuple(i)])), hex(int(got[tuple(i)])), hex(int(ref[tuple(i)]))) for i in d]))
+    assert not mism, mism[:5]
+
+
+def test_cast_f32_inputs_bit_exact():
+    rng = np.random.default_rng(3)
+    u = rng.integers(0, 2**32, size=(128, 256), dtype=np.uint64).astype(np.uint32)
+    u[0, :8] = [0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00001, 0x00000001, 0x80000001, 0, 0x80000000]
+    vals = oracle.f32_bits_to_f64(u)
+    x = f32_dev(u)
+    for fmt in FMTS:
+        for b in (-100, -20, 0, 7, 40, 126):
+            q, _, am = sq.fp8_quantize(x, fmt.code, i32_dev(b), want_amax=True)
+            assert np.array_equal(host(q), oracle.quantize(vals, fmt, b)), (fmt.name, b)
+    assert np.isnan(host(am)[0])
+
+
+def test_amax_exact_and_nan():
+    bits = all_bf16_patterns()
+    finite = bits[np.isfinite(oracle.bf16_bits_to_f64(bits))].reshape(1, -1)
+    a = sq.fp8_amax(bf16_dev(finite))
+    assert host(a)[0] == oracle.amax(oracle.bf16_bits_to_f64(finite))
+    assert np.isnan(host(sq.fp8_amax(bf16_dev(bits.reshape(256, 256))))[0])
+    x = make("c1", "X")
+    a = sq.fp8_amax(bf16_dev(x))
+    assert host(a)[0] == oracle.amax(oracle.bf16_bits_to_f64(x))
+    z = torch.zeros((0, 5), dtype=torch.bfloat16, device=DEV)
+    assert host(sq.fp8_amax(z))[0] == 0.0
+
+
+def test_compute_scale_matches_oracle():
+    rng = np.random.default_rng(4)
+    vals = list(np.exp(rng.uniform(-90, 90, 300)).astype(np.float32))
+    vals += [0.0, np.inf, np.nan, 448.0, 449.0, 57344.0, 57345.0, 1.75, 1.7500001, 1e-45, 1e-40,
+             3.4e38, 2.0 ** -126, 2.0 ** -149, 0.875, 7.0, 224.0]
+    for v in vals:
+        a = torch.tensor([v], dtype=torch.float32, device=DEV)
+        for fmt in FMTS:
+            for margin in (0, 1, 3):
+                b, s, si = sq.fp8_compute_scale(a, fmt.code, margin)
+                ref = oracle.compute_bias(float(np.float32(v)), fmt, margin)
+                assert int(host(b)[0]) == ref, (v, fmt.name, margin)
+                assert host(s)[0] == 2.0 ** ref and host(si)[0] == 2.0 ** -ref
+
+
+def test_current_scaling_config_c1():
+    """amax -> bias -> cast of X[256x768] and W[768x768], E4M3, margin 0."""
+    for name in ("X", "W"):
+        bits = make("c1", name)
+        x = bf16_dev(bits)
+        a = sq.fp8_amax(x)
+        b, _, _ = sq.fp8_compute_scale(a, E4M3.code, 0)
+        q, _, fused = sq.fp8_quantize(x, E4M3.code, b, want_amax=True)
+        vals = oracle.bf16_bits_to_f64(bits)
+        ref_a = oracle.amax(vals)
+        ref_b = oracle.compute_bias(ref_a, E4M3)
+        assert host(a)[0] == ref_a and f32_bits_of(fused) == f32_bits_of(a)
+        assert int(host(b)[0]) == ref_b
+        assert np.array_equal(host(q), oracle.quantize(vals, E4M3, ref_b))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_cast_strided_ragged_and_unaligned(dtype):
+    """Leading dimensions larger than cols, ragged tails and unaligned bases
+    take the non-vector paths; results stay bit-exact."""
+    rng = np.random.default_rng(5)
+    full = (rng.standard_normal((41, 136)) * 3).astype(np.float32)
+    if dtype == "bf16":
+        from workloads import f32_to_bf16_bits
+        fb = f32_to_bf16_bits(full)
+        t = bf16_dev(fb)
+        vals_full = oracle.bf16_bits_to_f64(fb)
+    else:
+        t = f32_dev(full)
+        vals_full = full.astype(np.float64)
+    for (r0, c0, c1) in [(0, 0, 128), (0, 0, 136), (1, 3, 100), (2, 1, 131), (0, 5, 5 + 64), (3, 8, 136)]:
+        sub = t[r0:, c0:c1]
+        vals = vals_full[r0:, c0:c1]
+        say(f"strided cast {dtype} view rows {r0}: cols {c0}:{c1}")
+        for fmt in FMTS:
+            bias = oracle.compute_bias(oracle.amax(vals), fmt)
+            q, _, am = sq.fp8_quantize(sub, fmt.code, i32_dev(bias), want_amax=True)
+            assert np.array_equal(host(q), oracle.quantize(vals, fmt, bias))
+            assert host(am)[0] == oracle.amax(vals)
+            assert host(sq.fp8_amax(sub))[0] == oracle.amax(vals)
+            # strided output too
+            big = torch.full((sub.shape[0], sub.shape[1] + 9), 0xAA, dtype=torch.uint8, device=DEV)
+            q2, _, _ = sq.fp8_quantize(sub, fmt.code, i32_dev(bias), q=big[:, 3:3 + sub.shape[1]])
+            hb = host(big)
+            assert np.array_equal(hb[:, 3:3 + sub.shape[1]], oracle.quantize(vals, fmt, bias))
+            assert np.all(hb[:, :3] == 0xAA) and np.all(hb[:, 3 + sub.shape[1]:] == 0xAA)
+
+
+@pytest.mark.parametrize("shape", [(256, 768), (130, 200), (1, 77), (64, 64), (300, 17)])
+def test_cast_transpose(shape):
+    rng = np.random.default_rng(6)
+    from workloads import f32_to_bf16_bits
+    bits = f32_to_bf16_bits((rng.standard_normal(shape) * 0.02).astype(np.float32))
+    vals = oracle.bf16_bits_to_f64(bits)
+    x = bf16_dev(bits)
+    for fmt in FMTS:
+        bias = oracle.compute_bias(oracle.amax(vals), fmt)
+        q, qT, am = sq.fp8_quantize(x, fmt.code, i32_dev(bias), transpose=True, want_amax=True)
+        ref = oracle.quantize(vals, fmt, bias)
+        assert np.array_equal(host(q), ref)
+        assert np.array_equal(host(qT), ref.T)
+        assert host(am)[0] == oracle.amax(vals)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: f.name)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mx_cast_bit_exact(fmt, dtype):
+    bits = make("c4", "X", shape=(96, 640))
+    bits[0, :32] = 0                                   # all-zero block
+    bits[1, 40] = 0x7FC0                               # NaN block
+    bits[2, 64:96] = 0x0001                            # subnormal-only block
+    bits[3, 100] = 0x7F80                              # Inf block
+    bits[4, 128:160] = 0x7F7F                          # bf16 max
+    vals = oracle.bf16_bits_to_f64(bits)
+    x = bf16_dev(bits) if dtype == "bf16" else f32_dev(vals.astype(np.float32))
+    q, s = sq.mx_quantize(x, fmt.code)
+    rq, rs = oracle.mx_quantize(vals, fmt)
+    assert np.array_equal(host(s), rs)
+    assert np.array_equal(host(q), rq)
+    # strided / unaligned views (scalar path) on the same data
+    sub = x[5:, 32:32 + 512]
+    q2, s2 = sq.mx_quantize(sub, fmt.code)
+    rq2, rs2 = oracle.mx_quantize(vals[5:, 32:32 + 512], fmt)
+    assert np.array_equal(host(s2), rs2) and np.array_equal(host(q2), rq2)
+    if dtype == "bf16":
+        odd = torch.empty(bits.size + 1, dtype=torch.bfloat16, device=DEV)[1:].view(bits.shape)
+        odd.copy_(x)
+        q3, s3 = sq.mx_quantize(odd, fmt.code)
+        assert np.array_equal(host(s3), rs) and np.array_equal(host(q3), rq)
+
+
+def test_mx_rmse_below_per_tensor_c4_shape():
+    bits = make("c4", "X", shape=(256, 1024))
+    vals = oracle.bf16_bits_to_f64(bits)
+    q, s = sq.mx_quantize(bf16_dev(bits), E4M3.code)
+    rq, rs = oracle.mx_quantize(vals, E4M3)
+    assert np.array_equal(host(q), rq) and np.array_equal(host(s), rs)
+    b = oracle.compute_bias(oracle.amax(vals), E4M3)
+    pt = oracle.dequantize(oracle.quantize(vals, E4M3, b), E4M3, b)
+    mx = oracle.mx_dequantize(host(q), host(s), E4M3)
+    assert oracle.rmse(vals, mx) <= oracle.rmse(vals, pt)
+
+
+@pytest.mark.parametrize("name", ["X", "W"])
+def test_full_size_70b_mlp_sampled_rows(name):
+    """The 70B-MLP tensors at full size, in the launch configuration the
+    benchmark times: amax exact, bias exact, per-tensor and MX bytes exact on
+    sampled rows (first, last and 62 random rows)."""
+    bits = make("c5", name)
+    say(f"full-size c5 {name} {bits.shape}")
+    x = bf16_dev(bits)
+    a = sq.fp8_amax(x)
+    ref_a = oracle_amax_chunked(bits)
+    assert host(a)[0] == ref_a
+    b, _, _ = sq.fp8_compute_scale(a, E4M3.code, 0)
+    ref_b = oracle.compute_bias(ref_a, E4M3)
+    assert int(host(b)[0]) == ref_b
+    q, _, fused = sq.fp8_quantize(x, E4M3.code, b, want_amax=True)
+    assert f32_bits_of(fused) == f32_bits_of(a)
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, bits.shape[0] - 1], rng.integers(0, bits.shape[0], 62)]))
+    assert np.array_equal(host(q[torch.from_numpy(rows).to(DEV)]),
+                          oracle_quantize_chunked(bits, E4M3, ref_b, rows))
+    mq, ms = sq.mx_quantize(x, E4M3.code)
+    rq, rs = oracle_mx_chunked(bits, E4M3, rows)
+    idx = torch.from_numpy(rows).to(DEV)
+    assert np.array_equal(host(ms[idx]), rs)
+    assert np.array_equal(host(mq[idx]), rq)
