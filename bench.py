@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before the steps, run a plain 1 GiB device-to-device copy (known bytes) "
+                         "to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
 
 
@@ -169,6 +172,14 @@ def main():
         sq.mx_scaled_gemm(mqx, sq.E4M3, msx, mqw, sq.E4M3, msw, out=ym, amax_out=aym)
         mark(10)
 
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)                 # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -206,16 +217,24 @@ def main():
     }
     dom = "gemm_pt" if per["gemm_pt"] >= per["gemm_mx"] else "gemm_mx"
     achieved = gemm_flops / per[dom] / 1e9
+    # HBM-side bytes per launch from the committed rocprofv3 FETCH_SIZE /
+    # WRITE_SIZE runs; null once the GEMM source differs from the profiled one
     traffic = None
     tr_path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if os.path.exists(tr_path):
+        import hashlib
         try:
             with open(tr_path) as f:
-                traffic = json.load(f).get(dom)
+                tr = json.load(f)
+            with open(os.path.join(ROOT, "scaled_quantize_fp8_amd", "csrc", "gemm.hip"), "rb") as f:
+                same = hashlib.sha256(f.read()).hexdigest() == tr.get("gemm_source_sha256")
+            traffic = tr.get(dom) if same else None
         except Exception:
             traffic = None
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic,
+                "traffic_unit": "GB per launch (HBM-side read+write, copy-calibrated rocprofv3 counters)",
+                "algorithmic_GB": round((M * K + N * K + 2 * M * N) / 1e9, 3)}
 
     cpu = None
     if not args.no_cpu_baseline:
