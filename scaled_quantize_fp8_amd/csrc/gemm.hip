@@ -10,7 +10,15 @@
 // Scaling Strategies for Effective FP8 Training" (summary), "Key Questions
 // Answered": per-block scaling, each block with its own factor.
 //
-// CDNA4 mapping.
+// Two kernels.
+//   * gemm_fwd_kernel: both operands K-contiguous and K % 128 == 0 (the
+//     forward product Y = X W^T and every MX product of that shape): 32x32x64
+//     MFMAs fed from a two-slot LDS pipeline with asynchronous global -> LDS
+//     copies; described where it is defined.
+//   * gemm_kernel: every other layout (transposed operands, a K tail) with
+//     the design below.
+//
+// gemm_kernel's CDNA4 mapping.
 //   * Macro tile 256 (M) x 256 (N) x 128 (K bytes), 256 lanes = 4 waves in a
 //     2 x 2 arrangement, each wave owning 128 x 128 of C as 8 x 8
 //     v_mfma_f32_16x16x128_f8f6f4 blocks (256 fp32 accumulators per lane).
@@ -28,9 +36,12 @@
 //   * Transposed operands ([K x M] storage) are loaded 16 M-bytes at a time
 //     for four consecutive k and transposed 4 x 4 bytes in registers
 //     (v_perm_b32) on their way into the K-contiguous LDS layout.
-//   * Workgroup -> tile mapping is XCD-aware: consecutive workgroup ids land
-//     on different XCDs, so ids are remapped to give each XCD a contiguous
-//     range of tiles, walked in groups of 8 tile-rows for L2 reuse.
+//
+// Both kernels map workgroups to tiles XCD-aware: consecutive workgroup ids
+// land on different XCDs, so ids are remapped to give each XCD a contiguous
+// range of tiles, walked in groups of 8 tile-rows for L2 reuse.
+#include <type_traits>
+
 #include "common.hpp"
 #include "host.hpp"
 
@@ -67,6 +78,7 @@ struct GemmArgs {
   int vec_store;
   int sa_dword;            // scale rows 4-byte aligned: one dword per stage
   int sb_dword;
+  int scales_dma;          // both scale matrices dword-aligned rows and K % 128 == 0
 };
 
 // ---- buffer resources ------------------------------------------------------
@@ -278,7 +290,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
     gload(0, 0);
     sstore(0);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
   __syncthreads();
 
   for (int64_t kt = 0; kt < nk; ++kt) {
@@ -330,7 +342,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
     }
 
     if (kt + 1 < nk) sstore(cur ^ 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
     __syncthreads();
   }
 
@@ -395,10 +407,378 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
   if (g.out_amax) block_max_to_global(amax_bits, red, g.out_amax);
 }
 
+
+// ===========================================================================
+// Forward-layout kernel (both operands K-contiguous, K % 128 == 0).
+// ===========================================================================
+// Global -> LDS copies are issued as inline assembly
+// (buffer_load_dwordx4 ... lds): for the compiler's own LDS-DMA builtin, its
+// waitcnt pass waits for every outstanding copy before any later LDS read,
+// which would serialise the prefetch with the MFMAs.  Completion is tracked
+// explicitly with s_waitcnt vmcnt (issued through the builtin, so that the
+// pass knows about it and adds no waits of its own).
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (base, stride 0, num_records, gfx9 raw format) in
+// SGPRs for the inline-assembly loads below.
+__device__ __forceinline__ v4i make_srd(const void* base, int64_t bytes) {
+  const int64_t rec = bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)((a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)rec);
+  r[3] = kRsrcWord3;
+  return r;
+}
+
+// 32-bit LDS byte offset of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// 16 bytes per lane from buffer offset off + soff to LDS lds_addr + 16 * lane
+// (lds_addr and soff wave-uniform).
+__device__ __forceinline__ void dma_b128_so(v4i srd, uint32_t lds_addr, uint32_t off, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
+               :: "v"(off), "s"(lds_addr), "s"(srd), "s"(soff) : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N> __device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// 32x32x64 MFMA with E8M0 scales picked by byte (op_sel) from packed registers.
+template <int FA_, int FB_>
+__device__ __forceinline__ v16f mfma32(v8i a, v8i b, v16f c, int sa, int oa, int sb, int ob) {
+#define SFP8_M(OA, OB) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA_, FB_, OA, sa, OB, sb)
+  switch (oa * 4 + ob) {
+    case 0: SFP8_M(0, 0); case 1: SFP8_M(0, 1); case 2: SFP8_M(0, 2); case 3: SFP8_M(0, 3);
+    case 4: SFP8_M(1, 0); case 5: SFP8_M(1, 1); case 6: SFP8_M(1, 2); case 7: SFP8_M(1, 3);
+    case 8: SFP8_M(2, 0); case 9: SFP8_M(2, 1); case 10: SFP8_M(2, 2); case 11: SFP8_M(2, 3);
+    case 12: SFP8_M(3, 0); case 13: SFP8_M(3, 1); case 14: SFP8_M(3, 2); default: SFP8_M(3, 3);
+  }
+#undef SFP8_M
+}
+
+// ---------------------------------------------------------------------------
+// Forward-layout kernel.
+//   * Macro tile 256 x 256, K stages of 128 bytes, 4 waves in 2 x 2, each
+//     wave owning 128 x 128 of C as 4 x 4 v_mfma_f32_32x32x64_f8f6f4 blocks
+//     (256 fp32 accumulators per lane, all in AGPRs).
+//   * LDS: op(A) stages at [0, 64K) (slot s at 32K s), op(B) stages at
+//     [64K, 128K); a stage is 256 rows x 128 bytes, the 16-byte chunk c of
+//     row r stored at chunk c ^ (r & 7).  Every fragment read is a
+//     loop-invariant per-lane base plus an immediate (slot, fragment).
+//   * Pipeline, two slots: a stage is two 64-byte K sub-steps.  Phase A runs
+//     sub-step 0's 16 MFMAs while reading sub-step 1's fragments; the wave
+//     then waits for its own copies of stage kt+1 and the workgroup meets at
+//     one barrier; phase B runs sub-step 1's MFMAs while reading stage kt+1's
+//     sub-step 0 fragments and issuing stage kt+2's copies (one per MFMA) into
+//     the slot stage kt has just released.
+//   * Past the last stage the copies re-load stage nk-1 into the free slot
+//     (never read), so the loop body has no branches; the wave drains them
+//     before the epilogue.
+// ---------------------------------------------------------------------------
+// 32x32x64 operand: K sub-step h (bytes 64h..64h+63) of rows row0 + (l % 32);
+// lane l (g = l / 32) holds chunk 4h + g then 4h + 2 + g.  `base_lo/hi` are
+// the lane's byte offsets for fragment 0 of slot 0; slot and fragment are
+// immediates.
+template <int OFF>
+__device__ __forceinline__ v8i frag_at(const uint8_t* lds, uint32_t base_lo, uint32_t base_hi) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(lds + base_lo + OFF);
+  const uint4 hi = *reinterpret_cast<const uint4*>(lds + base_hi + OFF);
+  v8i f;
+  f[0] = (int)lo.x; f[1] = (int)lo.y; f[2] = (int)lo.z; f[3] = (int)lo.w;
+  f[4] = (int)hi.x; f[5] = (int)hi.y; f[6] = (int)hi.z; f[7] = (int)hi.w;
+  return f;
+}
+
+template <int FA, int FB, bool MX, bool SDMA>
+__global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t s_scale[(MX && SDMA) ? 2 * 2 * BM : 1];
+  __shared__ uint32_t red[kGemmThreads / kWave];
+  constexpr int kRegB = 2 * kTileBytes;             // op(B) region offset (64 KiB)
+  constexpr int kSlot = kTileBytes;                 // 32 KiB per slot per operand
+  constexpr int kFrag = 32 * BK;                    // 4 KiB between 32-row fragments
+
+  const int64_t tiles_m = (g.M + BM - 1) / BM;
+  const int64_t tiles_n = (g.N + BN - 1) / BN;
+  int64_t tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: SGPR
+  const int wm = wave >> 1, wn = wave & 1;
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int64_t nk = (g.K + BK - 1) / BK;          // 128-byte K stages
+  const int64_t nkb = g.K / 32;
+  const int64_t rows_a = g.M - m0, rows_b = g.N - n0;
+  const int64_t ra_ = rows_a < BM ? rows_a : BM, rb_ = rows_b < BN ? rows_b : BN;
+  const v4i rs_a = make_srd(g.A + m0 * g.lda, (ra_ - 1) * g.lda + g.K);
+  const v4i rs_b = make_srd(g.B + n0 * g.ldb, (rb_ - 1) * g.ldb + g.K);
+  v4i ss_a = rs_a, ss_b = rs_b;
+  if constexpr (MX && SDMA) {
+    ss_a = make_srd(g.sa + m0 * g.lds_a, (ra_ - 1) * g.lds_a + nkb);
+    ss_b = make_srd(g.sb + n0 * g.lds_b, (rb_ - 1) * g.lds_b + nkb);
+  }
+  // DMA: wave w fills 1 KiB blocks 8w..8w+7 (8 rows each) of each operand;
+  // lane L lands at row 8 blk + L/8, stored chunk L%8, so it fetches logical
+  // chunk (L%8) ^ (L/8).  The stage's K offset rides in soffset.
+  const int cl = (lane & 7) ^ (lane >> 3);
+  uint32_t offa[8], offb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = (wave * 8 + i) * 8 + (lane >> 3);
+    offa[i] = row < rows_a ? (uint32_t)(row * g.lda + 16 * cl) : kOOB;
+    offb[i] = row < rows_b ? (uint32_t)(row * g.ldb + 16 * cl) : kOOB;
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
+  uint32_t offsa = kOOB, offsb = kOOB, ldss = 0;
+  if constexpr (MX && SDMA) {
+    const int row = wave * 64 + lane;
+    offsa = row < rows_a ? (uint32_t)(row * g.lds_a) : kOOB;
+    offsb = row < rows_b ? (uint32_t)(row * g.lds_b) : kOOB;
+    ldss = __builtin_amdgcn_readfirstlane(lds_offset(s_scale));
+  }
+  constexpr int LPS = (MX && SDMA) ? 18 : 16;      // DMA instructions per stage per wave
+
+  // Stage indices past the end re-load stage nk-1 into the slot that is free
+  // at that point: the copy is never read, and the loop stays branch-free.
+  auto dma = [&](int64_t kt, int t) {
+    const int slot = (int)(kt & 1);
+    const int64_t ks = kt < nk ? kt : nk - 1;
+    const uint32_t k0 = (uint32_t)(ks * BK);
+    if (t < 16) {
+      const int i = t & 7;
+      const bool isb = t >= 8;
+      const uint32_t off = isb ? offb[i] : offa[i];     // K % 128 == 0: no K tail
+      const uint32_t la = lds0 + (uint32_t)((isb ? kRegB : 0) + slot * kSlot + (wave * 8 + i) * 1024);
+      if (isb) dma_b128_so(rs_b, la, off, k0);
+      else dma_b128_so(rs_a, la, off, k0);
+    } else {
+      const bool isb = t == 17;
+      const uint32_t la = ldss + (uint32_t)((slot * 2 * BM + (isb ? BM : 0) + wave * 64) * 4);
+      const uint32_t so = (uint32_t)(4 * ks);
+      if (isb)
+        asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %0, %2, %3 offen lds"
+                     :: "v"(offsb), "s"(la), "s"(ss_b), "s"(so) : "memory", "m0");
+      else
+        asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %0, %2, %3 offen lds"
+                     :: "v"(offsa), "s"(la), "s"(ss_a), "s"(so) : "memory", "m0");
+    }
+  };
+  // E8M0 codes of this lane's fragments for sub-step h of stage kt
+  auto read_scales = [&](int64_t kt, int h, int& xs, int& ws) {
+    xs = 0;
+    ws = 0;
+    if constexpr (MX) {
+      const int slot = (int)(kt & 1);
+      const int gq = lane >> 5;
+      const int64_t kb = 4 * kt + 2 * h + gq;
+      const int sub = 2 * h + gq;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t ca, cb;
+        if constexpr (SDMA) {
+          ca = (s_scale[slot * 2 * BM + wm * 128 + j * 32 + (lane & 31)] >> (8 * sub)) & 0xffu;
+          cb = (s_scale[slot * 2 * BM + BM + wn * 128 + j * 32 + (lane & 31)] >> (8 * sub)) & 0xffu;
+        } else {
+          const int64_t ra = m0 + wm * 128 + j * 32 + (lane & 31);
+          const int64_t rb = n0 + wn * 128 + j * 32 + (lane & 31);
+          ca = (ra < g.M && kb < nkb) ? g.sa[ra * g.lds_a + kb] : 127u;
+          cb = (rb < g.N && kb < nkb) ? g.sb[rb * g.lds_b + kb] : 127u;
+        }
+        if (kb >= nkb) { ca = 127u; cb = 127u; }
+        xs |= (int)(ca << (8 * j));
+        ws |= (int)(cb << (8 * j));
+      }
+    }
+  };
+
+  // per-lane fragment bases (slot 0, fragment 0) for sub-steps 0 and 1
+  const int s7 = lane & 7, gq = lane >> 5;
+  const uint32_t rowa = (uint32_t)((wm * 128 + (lane & 31)) * BK);
+  const uint32_t rowb = (uint32_t)(kRegB + (wn * 128 + (lane & 31)) * BK);
+  const uint32_t a0lo = rowa + (((0 + gq) ^ s7) << 4), a0hi = rowa + (((2 + gq) ^ s7) << 4);
+  const uint32_t a1lo = rowa + (((4 + gq) ^ s7) << 4), a1hi = rowa + (((6 + gq) ^ s7) << 4);
+  const uint32_t b0lo = rowb + (((0 + gq) ^ s7) << 4), b0hi = rowb + (((2 + gq) ^ s7) << 4);
+  const uint32_t b1lo = rowb + (((4 + gq) ^ s7) << 4), b1hi = rowb + (((6 + gq) ^ s7) << 4);
+
+  // prologue: stages 0 and 1 in flight, stage 0 published, its sub-step 0 fragments read
+#pragma unroll
+  for (int t = 0; t < LPS; ++t) dma(0, t);
+#pragma unroll
+  for (int t = 0; t < LPS; ++t) dma(1, t);
+  wait_vm<LPS>();
+  __syncthreads();
+  v8i x0[4], w0[4], x1[4], w1[4];
+  int xs0 = 0, ws0 = 0, xs1 = 0, ws1 = 0;
+  if (nk > 0) {
+    x0[0] = frag_at<0 * kFrag>(smem, a0lo, a0hi); x0[1] = frag_at<1 * kFrag>(smem, a0lo, a0hi);
+    x0[2] = frag_at<2 * kFrag>(smem, a0lo, a0hi); x0[3] = frag_at<3 * kFrag>(smem, a0lo, a0hi);
+    w0[0] = frag_at<0 * kFrag>(smem, b0lo, b0hi); w0[1] = frag_at<1 * kFrag>(smem, b0lo, b0hi);
+    w0[2] = frag_at<2 * kFrag>(smem, b0lo, b0hi); w0[3] = frag_at<3 * kFrag>(smem, b0lo, b0hi);
+    read_scales(0, 0, xs0, ws0);
+  }
+
+  // One stage in slot SLOT: phase A = sub-step 0 MFMAs (set 0) while reading
+  // sub-step 1 (set 1); publish stage kt+1 (wait own DMA, barrier); phase B =
+  // sub-step 1 MFMAs while reading stage kt+1's sub-step 0 (set 0) and
+  // issuing stage kt+2's DMA into the slot stage kt released.
+  auto stage = [&](int64_t kt, auto slot_c) {
+    constexpr int SLOT = decltype(slot_c)::value;
+    constexpr int NSL = 1 - SLOT;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int i = t >> 2, j = t & 3;
+      switch (t) {
+        case 0: x1[0] = frag_at<SLOT * kSlot + 0 * kFrag>(smem, a1lo, a1hi); break;
+        case 1: x1[1] = frag_at<SLOT * kSlot + 1 * kFrag>(smem, a1lo, a1hi); break;
+        case 2: x1[2] = frag_at<SLOT * kSlot + 2 * kFrag>(smem, a1lo, a1hi); break;
+        case 3: x1[3] = frag_at<SLOT * kSlot + 3 * kFrag>(smem, a1lo, a1hi); break;
+        case 4: w1[0] = frag_at<SLOT * kSlot + 0 * kFrag>(smem, b1lo, b1hi); break;
+        case 5: w1[1] = frag_at<SLOT * kSlot + 1 * kFrag>(smem, b1lo, b1hi); break;
+        case 6: w1[2] = frag_at<SLOT * kSlot + 2 * kFrag>(smem, b1lo, b1hi); break;
+        case 7: w1[3] = frag_at<SLOT * kSlot + 3 * kFrag>(smem, b1lo, b1hi); break;
+        case 8: read_scales(kt, 1, xs1, ws1); break;
+        default: break;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MX)
+        acc[i][j] = mfma32<FB, FA>(w0[i], x0[j], acc[i][j], ws0, i, xs0, j);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w0[i], x0[j], acc[i][j], FB, FA, 0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm<0>();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int i = t >> 2, j = t & 3;
+      {
+        switch (t) {
+          case 0: x0[0] = frag_at<NSL * kSlot + 0 * kFrag>(smem, a0lo, a0hi); break;
+          case 1: x0[1] = frag_at<NSL * kSlot + 1 * kFrag>(smem, a0lo, a0hi); break;
+          case 2: x0[2] = frag_at<NSL * kSlot + 2 * kFrag>(smem, a0lo, a0hi); break;
+          case 3: x0[3] = frag_at<NSL * kSlot + 3 * kFrag>(smem, a0lo, a0hi); break;
+          case 4: w0[0] = frag_at<NSL * kSlot + 0 * kFrag>(smem, b0lo, b0hi); break;
+          case 5: w0[1] = frag_at<NSL * kSlot + 1 * kFrag>(smem, b0lo, b0hi); break;
+          case 6: w0[2] = frag_at<NSL * kSlot + 2 * kFrag>(smem, b0lo, b0hi); break;
+          case 7: w0[3] = frag_at<NSL * kSlot + 3 * kFrag>(smem, b0lo, b0hi); break;
+          case 8: read_scales(kt + 1, 0, xs0, ws0); break;
+          default: break;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MX)
+        acc[i][j] = mfma32<FB, FA>(w1[i], x1[j], acc[i][j], ws1, i, xs1, j);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w1[i], x1[j], acc[i][j], FB, FA, 0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      dma(kt + 2, t);
+      if (t < LPS - 16) dma(kt + 2, 16 + t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  int64_t kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    stage(kt, std::integral_constant<int, 0>{});
+    stage(kt + 1, std::integral_constant<int, 1>{});
+  }
+  if (kt < nk) stage(kt, std::integral_constant<int, 0>{});
+  wait_vm<0>();                                     // drain the trailing re-loads
+
+  // epilogue: lane l of block (i, j) holds n = 8q + 4(l/32) + 0..3 of column m = l%32
+  const int e = MX ? 0 : -(*g.bias_a + *g.bias_b);
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t m = m0 + wm * 128 + j * 32 + (lane & 31);
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = n0 + wn * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = MX ? acc[i][j][4 * q + r] : __builtin_amdgcn_ldexpf(acc[i][j][4 * q + r], e);
+        if (g.out_f32) {
+          float* crow = reinterpret_cast<float*>(g.C) + m * g.ldc;
+          if (g.vec_store && n + 3 < g.N) {
+            *reinterpret_cast<float4*>(crow + n) = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t ab = __float_as_uint(v[r]) & 0x7fffffffu;
+              amax_bits = amax_bits > ab ? amax_bits : ab;
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (n + r < g.N) {
+                crow[n + r] = v[r];
+                const uint32_t ab = __float_as_uint(v[r]) & 0x7fffffffu;
+                amax_bits = amax_bits > ab ? amax_bits : ab;
+              }
+          }
+        } else {
+          uint16_t h[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h[r] = __builtin_bit_cast(uint16_t, (__bf16)v[r]);
+          uint16_t* crow = reinterpret_cast<uint16_t*>(g.C) + m * g.ldc;
+          if (g.vec_store && n + 3 < g.N) {
+            *reinterpret_cast<uint2*>(crow + n) =
+                make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const uint32_t ab = ((uint32_t)h[r] & 0x7fffu) << 16;
+              amax_bits = amax_bits > ab ? amax_bits : ab;
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (n + r < g.N) {
+                crow[n + r] = h[r];
+                const uint32_t ab = ((uint32_t)h[r] & 0x7fffu) << 16;
+                amax_bits = amax_bits > ab ? amax_bits : ab;
+              }
+          }
+        }
+      }
+    }
+  }
+  if (g.out_amax) block_max_to_global(amax_bits, red, g.out_amax);
+}
+
 template <int FA, int FB, bool MX, bool TA, bool TB>
 static void launch_gemm(const GemmArgs& g, hipStream_t s) {
   const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<FA, FB, MX, TA, TB>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, g);
+  if (!TA && !TB && g.K > 0 && (g.K % 128) == 0) {
+    const bool sdma = MX && g.scales_dma;
+    if (sdma)
+      hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, true>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, g);
+    else
+      hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, false>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, g);
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<FA, FB, MX, TA, TB>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, g);
+  }
 }
 
 template <int FA, int FB>
@@ -452,7 +832,7 @@ int fp8_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int fmt_a
   g.A = A; g.lda = lda; g.B = B; g.ldb = ldb;
   g.bias_a = bias_a; g.bias_b = bias_b;
   g.sa = nullptr; g.lds_a = 0; g.sb = nullptr; g.lds_b = 0;
-  g.sa_dword = 0; g.sb_dword = 0;
+  g.sa_dword = 0; g.sb_dword = 0; g.scales_dma = 0;
   g.C = C; g.ldc = ldc; g.out_amax = out_amax;
   g.out_f32 = out_dtype == FP8_DT_F32;
   g.vec_store = g.out_f32 ? (aligned(C, 16) && ldc % 4 == 0) : (aligned(C, 8) && ldc % 4 == 0);
@@ -491,6 +871,7 @@ int mx_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int fmt_a,
   g.sa = A_scales; g.lds_a = lds_a; g.sb = B_scales; g.lds_b = lds_b;
   g.sa_dword = aligned(A_scales, 4) && (lds_a % 4) == 0;
   g.sb_dword = aligned(B_scales, 4) && (lds_b % 4) == 0;
+  g.scales_dma = g.sa_dword && g.sb_dword && (K % 128) == 0 && lds_a < (1LL << 23) && lds_b < (1LL << 23);
   g.C = C; g.ldc = ldc; g.out_amax = out_amax;
   g.out_f32 = out_dtype == FP8_DT_F32;
   g.vec_store = g.out_f32 ? (aligned(C, 16) && ldc % 4 == 0) : (aligned(C, 8) && ldc % 4 == 0);

@@ -70,6 +70,37 @@ def test_gemm_ragged_tiles(fa, fb, out_dtype):
     _check_amax(C, am)
 
 
+@pytest.mark.parametrize("K", [128, 384, 1024], ids=["K128", "K384", "K1024"])
+@pytest.mark.parametrize("fa,fb", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2), (E5M2, E5M2)],
+                         ids=["e4e4", "e5e4", "e4e5", "e5e5"])
+def test_gemm_k_multiple_of_128(fa, fb, K):
+    """K a multiple of the 128-byte stage (one stage, an odd count, an even
+    count) with ragged M = 300, N = 520, then a 40 x 24 problem far smaller
+    than one tile, read from operands whose rows are padded (lda = K + 48)."""
+    rng = np.random.default_rng(29 + K)
+    qa, ba = _operand(rng, (300, K), 1.0, fa)
+    qb, bb = _operand(rng, (520, K), 0.02, fb)
+    say(f"gemm K%128 {fa.name}x{fb.name} K={K}")
+    for dt in (torch.bfloat16, torch.float32):
+        C, am = _run_pt(qa, fa, ba, qb, fb, bb, False, False, dt)
+        ref = oracle.scaled_gemm_ref(qa, fa, ba, qb, fb, bb)
+        s = oracle.abs_product_sum(qa, fa, ba, qb, fb, bb)
+        gt = mfma_group_term(oracle.dequantize(qa, fa, ba), oracle.dequantize(qb, fb, bb))
+        assert_gemm_close(host_f64(C), ref, s, dt == torch.bfloat16, f"K={K}", gt)
+        _check_amax(C, am)
+    pa = np.zeros((40, K + 48), dtype=np.uint8)
+    pb = np.zeros((24, K + 48), dtype=np.uint8)
+    pa[:, :K], pb[:, :K] = qa[:40], qb[:24]
+    A, B = u8_dev(pa)[:, :K], u8_dev(pb)[:, :K]
+    C, am = sq.fp8_scaled_gemm(A, fa.code, i32_dev(ba), B, fb.code, i32_dev(bb), out_dtype=torch.float32,
+                               want_amax=True)
+    ref = oracle.scaled_gemm_ref(qa[:40], fa, ba, qb[:24], fb, bb)
+    s = oracle.abs_product_sum(qa[:40], fa, ba, qb[:24], fb, bb)
+    gt = mfma_group_term(oracle.dequantize(qa[:40], fa, ba), oracle.dequantize(qb[:24], fb, bb))
+    assert_gemm_close(host_f64(C), ref, s, False, f"small K={K}", gt)
+    _check_amax(C, am)
+
+
 @pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)], ids=["NT", "TN", "TT"])
 def test_gemm_transposed_operands(ta, tb):
     """Transposed storage for op(A) / op(B) (the backward products): M, N
@@ -162,6 +193,33 @@ def test_mx_gemm_ragged(fa, fb, out_dtype):
     gt = mfma_group_term(oracle.mx_dequantize(qa, sa, fa), oracle.mx_dequantize(qb, sb, fb))
     assert_gemm_close(host_f64(C), ref, s, out_dtype == torch.bfloat16, "mx ragged", gt)
     _check_amax(C, am)
+
+
+@pytest.mark.parametrize("K", [128, 384, 1024], ids=["K128", "K384", "K1024"])
+@pytest.mark.parametrize("fa,fb", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2), (E5M2, E5M2)],
+                         ids=["e4e4", "e5e4", "e4e5", "e5e5"])
+def test_mx_gemm_k_multiple_of_128(fa, fb, K):
+    """K a multiple of 128 with ragged M = 300, N = 260; scales passed twice:
+    packed rows (K/32 bytes each, dword-aligned) and rows padded to an odd
+    stride (K/32 + 1 bytes), which the kernel must read byte by byte."""
+    xb = make("c4", "X", shape=(300, K))
+    wb = make("c4", "W", shape=(260, K))
+    qa, sa = oracle.mx_quantize(oracle.bf16_bits_to_f64(xb), fa)
+    qb, sb = oracle.mx_quantize(oracle.bf16_bits_to_f64(wb), fb)
+    ref = oracle.mx_gemm_ref(qa, sa, fa, qb, sb, fb)
+    s = oracle.mx_abs_product_sum(qa, sa, fa, qb, sb, fb)
+    gt = mfma_group_term(oracle.mx_dequantize(qa, sa, fa), oracle.mx_dequantize(qb, sb, fb))
+    nb = K // 32
+    psa = np.zeros((300, nb + 1), dtype=np.uint8)
+    psb = np.zeros((260, nb + 1), dtype=np.uint8)
+    psa[:, :nb], psb[:, :nb] = sa, sb
+    for what, SA, SB, dt in (("packed", u8_dev(sa), u8_dev(sb), torch.bfloat16),
+                             ("odd stride", u8_dev(psa)[:, :nb], u8_dev(psb)[:, :nb], torch.float32)):
+        say(f"mx gemm K%128 {fa.name}x{fb.name} K={K} {what}")
+        C, am = sq.mx_scaled_gemm(u8_dev(qa), fa.code, SA, u8_dev(qb), fb.code, SB, out_dtype=dt,
+                                  want_amax=True)
+        assert_gemm_close(host_f64(C), ref, s, dt == torch.bfloat16, f"mx K={K} {what}", gt)
+        _check_amax(C, am)
 
 
 def test_mx_gemm_extreme_block_scales():
