@@ -40,6 +40,7 @@
 // Both kernels map workgroups to tiles XCD-aware: consecutive workgroup ids
 // land on different XCDs, so ids are remapped to give each XCD a contiguous
 // range of tiles, walked in groups of 8 tile-rows for L2 reuse.
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -78,7 +79,7 @@ struct GemmArgs {
   int vec_store;
   int sa_dword;            // scale rows 4-byte aligned: one dword per stage
   int sb_dword;
-  int scales_dma;          // both scale matrices dword-aligned rows and K % 128 == 0
+  int scales_dma;          // both scale matrices dword-aligned rows, K % 128 == 0, K >= 512
 };
 
 // ---- buffer resources ------------------------------------------------------
@@ -437,6 +438,16 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
+// A descriptor held in SGPRs (its words are wave-uniform by construction).
+__device__ __forceinline__ v4i uniform_srd(v4i r) {
+  v4i u;
+  u[0] = __builtin_amdgcn_readfirstlane(r[0]);
+  u[1] = __builtin_amdgcn_readfirstlane(r[1]);
+  u[2] = __builtin_amdgcn_readfirstlane(r[2]);
+  u[3] = __builtin_amdgcn_readfirstlane(r[3]);
+  return u;
+}
+
 // 16 bytes per lane from buffer offset off + soff to LDS lds_addr + 16 * lane
 // (lds_addr and soff wave-uniform).
 __device__ __forceinline__ void dma_b128_so(v4i srd, uint32_t lds_addr, uint32_t off, uint32_t soff) {
@@ -471,22 +482,40 @@ __device__ __forceinline__ v16f mfma32(v8i a, v8i b, v16f c, int sa, int oa, int
 //     (256 fp32 accumulators per lane, all in AGPRs).
 //   * LDS: op(A) stages at [0, 64K) (slot s at 32K s), op(B) stages at
 //     [64K, 128K); a stage is 256 rows x 128 bytes, the 16-byte chunk c of
-//     row r stored at chunk c ^ (r & 7).  Every fragment read is a
-//     loop-invariant per-lane base plus an immediate (slot, fragment).
+//     row r stored at chunk c ^ fswz(r), fswz(r) = (r & 7) ^ ((r >> 3) & 1).
+//     A fragment read has 16 lanes on 16 consecutive rows and one logical
+//     chunk; with 64 four-byte banks two 128-byte rows share a bank window,
+//     so the 16 (row parity, stored chunk) pairs must differ: plain r & 7
+//     repeats them at rows r and r + 8 (2-way conflicts on every read),
+//     fswz does not (and stays a bijection within 8 rows).  Every fragment
+//     read is a loop-invariant per-lane base plus an immediate (slot,
+//     fragment).
 //   * Pipeline, two slots: a stage is two 64-byte K sub-steps.  Phase A runs
 //     sub-step 0's 16 MFMAs while reading sub-step 1's fragments; the wave
 //     then waits for its own copies of stage kt+1 and the workgroup meets at
 //     one barrier; phase B runs sub-step 1's MFMAs while reading stage kt+1's
 //     sub-step 0 fragments and issuing stage kt+2's copies (one per MFMA) into
 //     the slot stage kt has just released.
-//   * Past the last stage the copies re-load stage nk-1 into the free slot
-//     (never read), so the loop body has no branches; the wave drains them
-//     before the epilogue.
+//   * The loop is unrolled by 2 (by 4 for MX, whose scale codes are copied
+//     4 stages at a time) and always runs whole iterations: stages past nk
+//     copy zeros through zero-sized buffer descriptors and add nothing, so
+//     the loop body has no branches.  The wave drains its copies before the
+//     epilogue.
 // ---------------------------------------------------------------------------
 // 32x32x64 operand: K sub-step h (bytes 64h..64h+63) of rows row0 + (l % 32);
 // lane l (g = l / 32) holds chunk 4h + g then 4h + 2 + g.  `base_lo/hi` are
 // the lane's byte offsets for fragment 0 of slot 0; slot and fragment are
 // immediates.
+typedef unsigned short us2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to bf16 (RNE), packed low / high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  const f2v f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2v));
+}
+
 template <int OFF>
 __device__ __forceinline__ v8i frag_at(const uint8_t* lds, uint32_t base_lo, uint32_t base_hi) {
   const uint4 lo = *reinterpret_cast<const uint4*>(lds + base_lo + OFF);
@@ -497,120 +526,179 @@ __device__ __forceinline__ v8i frag_at(const uint8_t* lds, uint32_t base_lo, uin
   return f;
 }
 
-template <int FA, int FB, bool MX, bool SDMA>
+// Workgroup -> tile mapping of virtual block id vb (32-bit): XCD-aware remap,
+// then groups of kGroupM tile-rows (the mapping tile_coords gives blockIdx).
+__device__ __forceinline__ void tile_coords_vb(int vb, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int T = tiles_m * tiles_n;
+  const int xcd = vb & 7, local = vb >> 3;
+  const int q = T >> 3, r = T & 7;
+  const int lin = (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+  const int per_group = kGroupM * tiles_n;
+  const int group = lin / per_group;
+  const int first_m = group * kGroupM;
+  const int gm = (tiles_m - first_m) < kGroupM ? (tiles_m - first_m) : kGroupM;
+  const int in_group = lin - group * per_group;
+  tm = first_m + in_group % gm;
+  tn = in_group / gm;
+}
+
+// Buffer descriptors of one output tile's operand panels (and MX scale
+// panels).  A panel's size ends at its last existing row, so rows past the
+// matrix are out of range for tile-independent per-lane offsets; a tile
+// past the end gets size-0 descriptors (every copy reads zeros).
+struct TileSrd {
+  v4i a, b, sa, sb;
+};
+
+template <int FA, int FB, bool MX>
 __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint32_t s_scale[(MX && SDMA) ? 2 * 2 * BM : 1];
+  // MX scales, 4 stages per copy: [group slot][operand][tile row][4 dwords]
+  __shared__ __attribute__((aligned(16))) uint32_t s_scale[MX ? 2 * 2 * BM * 4 : 1];
   __shared__ uint32_t red[kGemmThreads / kWave];
   constexpr int kRegB = 2 * kTileBytes;             // op(B) region offset (64 KiB)
   constexpr int kSlot = kTileBytes;                 // 32 KiB per slot per operand
   constexpr int kFrag = 32 * BK;                    // 4 KiB between 32-row fragments
-
-  const int64_t tiles_m = (g.M + BM - 1) / BM;
-  const int64_t tiles_n = (g.N + BN - 1) / BN;
-  int64_t tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = tm * BM, n0 = tn * BN;
+  constexpr int U = MX ? 4 : 2;                     // stages per loop iteration
+  constexpr int LPS = 16;                           // data copies per stage per wave
+  // Per-tensor: persistent, one workgroup per compute unit walking tiles.
+  // MX: one tile per workgroup (its scale copies leave no SGPRs for a second
+  // tile's descriptors).
+  constexpr bool PERSIST = !MX;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: SGPR
   const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = (int)((g.M + BM - 1) / BM);
+  const int tiles_n = (int)((g.N + BN - 1) / BN);
+  const int tiles = tiles_m * tiles_n;
+  const int P = gridDim.x;                          // persistent: tiles vb, vb + P, ...
+  const int nk = (int)(g.K / BK);                   // K % 128 == 0, nk < 2^24
+  const int nkb = 4 * nk;                           // 32-wide K blocks
+  const int nkU = (nk + U - 1) / U * U;             // stages run per tile (zero stages past nk)
+  const int ngroups = nkU / 4;                      // MX scale copies per tile
+  const int last_g = (nk - 1) >> 2;                 // last group holding real stages
 
-  v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto make_tile = [&](int vb, TileSrd& T) {
+    if (vb < tiles && (PERSIST || vb == (int)blockIdx.x)) {
+      int tm, tn;
+      tile_coords_vb(vb, tiles_m, tiles_n, tm, tn);
+      const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+      const int64_t ra = g.M - m0 < BM ? g.M - m0 : BM, rb = g.N - n0 < BN ? g.N - n0 : BN;
+      T.a = make_srd(g.A + m0 * g.lda, (ra - 1) * g.lda + g.K);
+      T.b = make_srd(g.B + n0 * g.ldb, (rb - 1) * g.ldb + g.K);
+      if constexpr (MX) {
+        T.sa = make_srd(g.sa + m0 * g.lds_a, (ra - 1) * g.lds_a + nkb);
+        T.sb = make_srd(g.sb + n0 * g.lds_b, (rb - 1) * g.lds_b + nkb);
+      } else {
+        T.sa = T.a;
+        T.sb = T.b;
+      }
+    } else {
+      T.a = make_srd(g.A, 0);
+      T.b = make_srd(g.B, 0);
+      T.sa = T.a;
+      T.sb = T.b;
+    }
+  };
 
-  const int64_t nk = (g.K + BK - 1) / BK;          // 128-byte K stages
-  const int64_t nkb = g.K / 32;
-  const int64_t rows_a = g.M - m0, rows_b = g.N - n0;
-  const int64_t ra_ = rows_a < BM ? rows_a : BM, rb_ = rows_b < BN ? rows_b : BN;
-  const v4i rs_a = make_srd(g.A + m0 * g.lda, (ra_ - 1) * g.lda + g.K);
-  const v4i rs_b = make_srd(g.B + n0 * g.ldb, (rb_ - 1) * g.ldb + g.K);
-  v4i ss_a = rs_a, ss_b = rs_b;
-  if constexpr (MX && SDMA) {
-    ss_a = make_srd(g.sa + m0 * g.lds_a, (ra_ - 1) * g.lds_a + nkb);
-    ss_b = make_srd(g.sb + n0 * g.lds_b, (rb_ - 1) * g.lds_b + nkb);
-  }
   // DMA: wave w fills 1 KiB blocks 8w..8w+7 (8 rows each) of each operand;
   // lane L lands at row 8 blk + L/8, stored chunk L%8, so it fetches logical
-  // chunk (L%8) ^ (L/8).  The stage's K offset rides in soffset.
-  const int cl = (lane & 7) ^ (lane >> 3);
+  // chunk (L%8) ^ fswz(row) = (L%8) ^ (L/8) ^ (blk & 1).  The stage's K
+  // offset rides in soffset.  Offsets do not depend on the tile: a row past
+  // the matrix has offset >= ra * ld >= (ra - 1) * ld + K, the panel's size.
+  const int cl = (lane & 7) ^ (lane >> 3);          // ^ (blk & 1) = ^ (i & 1) below
   uint32_t offa[8], offb[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = (wave * 8 + i) * 8 + (lane >> 3);
-    offa[i] = row < rows_a ? (uint32_t)(row * g.lda + 16 * cl) : kOOB;
-    offb[i] = row < rows_b ? (uint32_t)(row * g.ldb + 16 * cl) : kOOB;
+    offa[i] = (uint32_t)(row * g.lda + 16 * (cl ^ (i & 1)));
+    offb[i] = (uint32_t)(row * g.ldb + 16 * (cl ^ (i & 1)));
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
-  uint32_t offsa = kOOB, offsb = kOOB, ldss = 0;
-  if constexpr (MX && SDMA) {
+  // MX scales: lane L of wave w copies 16 bytes (the codes of 4 stages) of
+  // tile row 64 w + L of each operand.  Group G covers stages 4G .. 4G+3 and
+  // is read from byte min(16 G, nkb - 16) of the row, so the last, partial
+  // group never reads past the row's end (nkb >= 16 is required).
+  uint32_t offsa = 0, offsb = 0, ldss = 0;
+  if constexpr (MX) {
     const int row = wave * 64 + lane;
-    offsa = row < rows_a ? (uint32_t)(row * g.lds_a) : kOOB;
-    offsb = row < rows_b ? (uint32_t)(row * g.lds_b) : kOOB;
+    offsa = (uint32_t)(row * g.lds_a);
+    offsb = (uint32_t)(row * g.lds_b);
     ldss = __builtin_amdgcn_readfirstlane(lds_offset(s_scale));
   }
-  constexpr int LPS = (MX && SDMA) ? 18 : 16;      // DMA instructions per stage per wave
 
-  // Stage indices past the end re-load stage nk-1 into the slot that is free
-  // at that point: the copy is never read, and the loop stays branch-free.
-  auto dma = [&](int64_t kt, int t) {
-    const int slot = (int)(kt & 1);
-    const int64_t ks = kt < nk ? kt : nk - 1;
-    const uint32_t k0 = (uint32_t)(ks * BK);
-    if (t < 16) {
-      const int i = t & 7;
-      const bool isb = t >= 8;
-      const uint32_t off = isb ? offb[i] : offa[i];     // K % 128 == 0: no K tail
-      const uint32_t la = lds0 + (uint32_t)((isb ? kRegB : 0) + slot * kSlot + (wave * 8 + i) * 1024);
-      if (isb) dma_b128_so(rs_b, la, off, k0);
-      else dma_b128_so(rs_a, la, off, k0);
-    } else {
-      const bool isb = t == 17;
-      const uint32_t la = ldss + (uint32_t)((slot * 2 * BM + (isb ? BM : 0) + wave * 64) * 4);
-      const uint32_t so = (uint32_t)(4 * ks);
-      if (isb)
-        asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %0, %2, %3 offen lds"
-                     :: "v"(offsb), "s"(la), "s"(ss_b), "s"(so) : "memory", "m0");
-      else
-        asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %0, %2, %3 offen lds"
-                     :: "v"(offsa), "s"(la), "s"(ss_a), "s"(so) : "memory", "m0");
+  int vb = blockIdx.x;
+  TileSrd cur, nxt;
+  make_tile(vb, cur);
+  if constexpr (PERSIST) make_tile(vb + P, nxt);
+  int gbase = 0;                                    // scale groups of earlier tiles (slot parity)
+
+  // Copies of stage s of the current tile, 0 <= s < nkU + 2: s < nk real,
+  // nk <= s < nkU zeros (size-0 descriptor), s >= nkU the next tile's
+  // stage s - nkU.  nkU is even, so slot parity runs on across tiles.
+  auto dma = [&](int s, int t) {
+    const int slot = s & 1;
+    const bool nx = PERSIST && s >= nkU;
+    const bool live = s < nk || nx;
+    const uint32_t k0 = (uint32_t)((nx ? s - nkU : s) * BK);
+    const int i = t & 7;
+    const bool isb = t >= 8;
+    const uint32_t off = isb ? offb[i] : offa[i];
+    const uint32_t la = lds0 + (uint32_t)((isb ? kRegB : 0) + slot * kSlot + (wave * 8 + i) * 1024);
+    v4i srd = isb ? cur.b : cur.a;
+    if constexpr (PERSIST) srd = nx ? (isb ? nxt.b : nxt.a) : srd;
+    srd[2] = live ? srd[2] : 0;
+    dma_b128_so(uniform_srd(srd), __builtin_amdgcn_readfirstlane(la), off, __builtin_amdgcn_readfirstlane(k0));
+  };
+  // Scale group G of the current tile, 0 <= G <= ngroups (G == ngroups: the
+  // next tile's group 0, whose copy starts at block 0).
+  auto scale_dma = [&](int G) {
+    if constexpr (MX) {
+      const bool nx = G >= ngroups;
+      const uint32_t so = (uint32_t)(nx ? 0 : (G < last_g ? 16 * G : nkb - 16));
+      const uint32_t la = ldss + (uint32_t)((((gbase + G) & 1) * 2 * BM + wave * 64) * 16);
+      v4i sa = cur.sa, sb = cur.sb;
+      if constexpr (PERSIST) {
+        sa = nx ? nxt.sa : sa;
+        sb = nx ? nxt.sb : sb;
+      } else {
+        sa[2] = nx ? 0 : sa[2];                     // no next tile: zeros
+        sb[2] = nx ? 0 : sb[2];
+      }
+      dma_b128_so(uniform_srd(sa), __builtin_amdgcn_readfirstlane(la), offsa, __builtin_amdgcn_readfirstlane(so));
+      dma_b128_so(uniform_srd(sb), __builtin_amdgcn_readfirstlane(la + BM * 16), offsb,
+                  __builtin_amdgcn_readfirstlane(so));
     }
   };
-  // E8M0 codes of this lane's fragments for sub-step h of stage kt
-  auto read_scales = [&](int64_t kt, int h, int& xs, int& ws) {
-    xs = 0;
-    ws = 0;
+  // E8M0 codes of stage s (0 <= s <= nkU; nkU: the next tile's stage 0) for
+  // this lane: one dword per 32-row fragment holding the row's four block
+  // codes (sc[0..3]: op(A) fragments j, sc[4..7]: op(B) fragments i).
+  // Shifted right by 8 * (lane / 32) when the stage starts, byte 2h is the
+  // code of the block this lane's group scales in sub-step h (op_sel = 2h
+  // picks it); the shift is left until then so that no wait for these reads
+  // lands between the MFMAs.  Zero stages reuse stage nk-1's codes (finite
+  // codes times zero data, or a NaN code the row already carries).
+  auto read_scales = [&](int s, int (&sc)[8]) {
     if constexpr (MX) {
-      const int slot = (int)(kt & 1);
-      const int gq = lane >> 5;
-      const int64_t kb = 4 * kt + 2 * h + gq;
-      const int sub = 2 * h + gq;
+      // selects only: a branch here would split the stage's basic block
+      const bool nx = s >= nkU;
+      const int kc = s < nk ? s : nk - 1;
+      const int G0 = kc >> 2;
+      const int d0 = G0 < last_g ? (kc & 3) : kc - (nk - 4);  // dword of stage kc in its copy
+      const int G = nx ? ngroups : G0;
+      const int d = nx ? 0 : d0;
+      const int gs = (gbase + G) & 1;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t ca, cb;
-        if constexpr (SDMA) {
-          ca = (s_scale[slot * 2 * BM + wm * 128 + j * 32 + (lane & 31)] >> (8 * sub)) & 0xffu;
-          cb = (s_scale[slot * 2 * BM + BM + wn * 128 + j * 32 + (lane & 31)] >> (8 * sub)) & 0xffu;
-        } else {
-          const int64_t ra = m0 + wm * 128 + j * 32 + (lane & 31);
-          const int64_t rb = n0 + wn * 128 + j * 32 + (lane & 31);
-          ca = (ra < g.M && kb < nkb) ? g.sa[ra * g.lds_a + kb] : 127u;
-          cb = (rb < g.N && kb < nkb) ? g.sb[rb * g.lds_b + kb] : 127u;
-        }
-        if (kb >= nkb) { ca = 127u; cb = 127u; }
-        xs |= (int)(ca << (8 * j));
-        ws |= (int)(cb << (8 * j));
+        sc[j] = (int)s_scale[((gs * 2 * BM) + wm * 128 + j * 32 + (lane & 31)) * 4 + d];
+        sc[4 + j] = (int)s_scale[((gs * 2 + 1) * BM + wn * 128 + j * 32 + (lane & 31)) * 4 + d];
       }
     }
   };
 
   // per-lane fragment bases (slot 0, fragment 0) for sub-steps 0 and 1
-  const int s7 = lane & 7, gq = lane >> 5;
+  const int s7 = (lane & 7) ^ ((lane >> 3) & 1), gq = lane >> 5;   // fswz of the lane's rows
   const uint32_t rowa = (uint32_t)((wm * 128 + (lane & 31)) * BK);
   const uint32_t rowb = (uint32_t)(kRegB + (wn * 128 + (lane & 31)) * BK);
   const uint32_t a0lo = rowa + (((0 + gq) ^ s7) << 4), a0hi = rowa + (((2 + gq) ^ s7) << 4);
@@ -618,7 +706,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   const uint32_t b0lo = rowb + (((0 + gq) ^ s7) << 4), b0hi = rowb + (((2 + gq) ^ s7) << 4);
   const uint32_t b1lo = rowb + (((4 + gq) ^ s7) << 4), b1hi = rowb + (((6 + gq) ^ s7) << 4);
 
-  // prologue: stages 0 and 1 in flight, stage 0 published, its sub-step 0 fragments read
+  // prologue (first tile only; later tiles are prefetched by the previous
+  // tile's last two stages): stages 0 and 1 in flight, stage 0 published,
+  // its sub-step 0 fragments read
+  scale_dma(0);
 #pragma unroll
   for (int t = 0; t < LPS; ++t) dma(0, t);
 #pragma unroll
@@ -626,22 +717,28 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   wait_vm<LPS>();
   __syncthreads();
   v8i x0[4], w0[4], x1[4], w1[4];
-  int xs0 = 0, ws0 = 0, xs1 = 0, ws1 = 0;
-  if (nk > 0) {
-    x0[0] = frag_at<0 * kFrag>(smem, a0lo, a0hi); x0[1] = frag_at<1 * kFrag>(smem, a0lo, a0hi);
-    x0[2] = frag_at<2 * kFrag>(smem, a0lo, a0hi); x0[3] = frag_at<3 * kFrag>(smem, a0lo, a0hi);
-    w0[0] = frag_at<0 * kFrag>(smem, b0lo, b0hi); w0[1] = frag_at<1 * kFrag>(smem, b0lo, b0hi);
-    w0[2] = frag_at<2 * kFrag>(smem, b0lo, b0hi); w0[3] = frag_at<3 * kFrag>(smem, b0lo, b0hi);
-    read_scales(0, 0, xs0, ws0);
-  }
+  int sc[2][8] = {};                                 // scales of the stages in slots 0 and 1
+  x0[0] = frag_at<0 * kFrag>(smem, a0lo, a0hi); x0[1] = frag_at<1 * kFrag>(smem, a0lo, a0hi);
+  x0[2] = frag_at<2 * kFrag>(smem, a0lo, a0hi); x0[3] = frag_at<3 * kFrag>(smem, a0lo, a0hi);
+  w0[0] = frag_at<0 * kFrag>(smem, b0lo, b0hi); w0[1] = frag_at<1 * kFrag>(smem, b0lo, b0hi);
+  w0[2] = frag_at<2 * kFrag>(smem, b0lo, b0hi); w0[3] = frag_at<3 * kFrag>(smem, b0lo, b0hi);
+  read_scales(0, sc[0]);
 
+  v16f acc[4][4];
   // One stage in slot SLOT: phase A = sub-step 0 MFMAs (set 0) while reading
   // sub-step 1 (set 1); publish stage kt+1 (wait own DMA, barrier); phase B =
   // sub-step 1 MFMAs while reading stage kt+1's sub-step 0 (set 0) and
   // issuing stage kt+2's DMA into the slot stage kt released.
-  auto stage = [&](int64_t kt, auto slot_c) {
+  auto stage = [&](int kt, auto slot_c, auto scales_c) {
     constexpr int SLOT = decltype(slot_c)::value;
     constexpr int NSL = 1 - SLOT;
+    constexpr bool SCALES = decltype(scales_c)::value;  // issue the next scale group
+    int cs[8];
+    if constexpr (MX) {
+      const int sh = 8 * (lane >> 5);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) cs[k] = (int)((uint32_t)sc[SLOT][k] >> sh);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
@@ -655,12 +752,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
         case 5: w1[1] = frag_at<SLOT * kSlot + 1 * kFrag>(smem, b1lo, b1hi); break;
         case 6: w1[2] = frag_at<SLOT * kSlot + 2 * kFrag>(smem, b1lo, b1hi); break;
         case 7: w1[3] = frag_at<SLOT * kSlot + 3 * kFrag>(smem, b1lo, b1hi); break;
-        case 8: read_scales(kt, 1, xs1, ws1); break;
         default: break;
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (MX)
-        acc[i][j] = mfma32<FB, FA>(w0[i], x0[j], acc[i][j], ws0, i, xs0, j);
+        acc[i][j] = mfma32<FB, FA>(w0[i], x0[j], acc[i][j], cs[4 + i], 0, cs[j], 0);
       else
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w0[i], x0[j], acc[i][j], FB, FA, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -681,101 +777,192 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
           case 5: w0[1] = frag_at<NSL * kSlot + 1 * kFrag>(smem, b0lo, b0hi); break;
           case 6: w0[2] = frag_at<NSL * kSlot + 2 * kFrag>(smem, b0lo, b0hi); break;
           case 7: w0[3] = frag_at<NSL * kSlot + 3 * kFrag>(smem, b0lo, b0hi); break;
-          case 8: read_scales(kt + 1, 0, xs0, ws0); break;
+          case 8: read_scales(kt + 1, sc[NSL]); break;
           default: break;
         }
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (MX)
-        acc[i][j] = mfma32<FB, FA>(w1[i], x1[j], acc[i][j], ws1, i, xs1, j);
+        acc[i][j] = mfma32<FB, FA>(w1[i], x1[j], acc[i][j], cs[4 + i], 2, cs[j], 2);
       else
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w1[i], x1[j], acc[i][j], FB, FA, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       dma(kt + 2, t);
-      if (t < LPS - 16) dma(kt + 2, 16 + t);
+      if constexpr (SCALES)
+        if (t == 15) scale_dma((kt >> 2) + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  int64_t kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    stage(kt, std::integral_constant<int, 0>{});
-    stage(kt + 1, std::integral_constant<int, 1>{});
-  }
-  if (kt < nk) stage(kt, std::integral_constant<int, 0>{});
-  wait_vm<0>();                                     // drain the trailing re-loads
-
-  // epilogue: lane l of block (i, j) holds n = 8q + 4(l/32) + 0..3 of column m = l%32
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
   const int e = MX ? 0 : -(*g.bias_a + *g.bias_b);
   uint32_t amax_bits = 0;
+  for (;;) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t m = m0 + wm * 128 + j * 32 + (lane & 31);
-      if (m >= g.M) continue;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t n = n0 + wn * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
-        float v[4];
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // Unrolled by 2 (slot indices become immediates), by 4 for MX (the scale
+    // group copy lands in a fixed stage).  The last two stages prefetch the
+    // next tile's first two.
+    for (int kt = 0; kt < nkU; kt += U) {
+      stage(kt, S0{}, std::bool_constant<MX>{});
+      stage(kt + 1, S1{}, std::false_type{});
+      if constexpr (MX) {
+        stage(kt + 2, S0{}, std::false_type{});
+        stage(kt + 3, S1{}, std::false_type{});
+      }
+    }
+
+    int tm, tn;
+    tile_coords_vb(vb, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    // Epilogue.  Lane l of block (i, j) holds n = 8q + 4(l/32) + 0..3 of row
+    // m = l%32.  An interior tile (all of it inside C, rows allowing vector
+    // stores) takes a straight-line path: one row pointer per block row,
+    // immediate column offsets, bf16 maxima as packed 16-bit maxima of |h|;
+    // edge tiles check every element.
+    if (m0 + BM <= g.M && n0 + BN <= g.N && g.vec_store) {
+      us2v pmax = {0, 0};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = MX ? acc[i][j][4 * q + r] : __builtin_amdgcn_ldexpf(acc[i][j][4 * q + r], e);
+      for (int j = 0; j < 4; ++j) {
+        const int64_t m = m0 + wm * 128 + j * 32 + (lane & 31);
+        const int64_t nb = n0 + wn * 128 + 4 * (lane >> 5);
         if (g.out_f32) {
-          float* crow = reinterpret_cast<float*>(g.C) + m * g.ldc;
-          if (g.vec_store && n + 3 < g.N) {
-            *reinterpret_cast<float4*>(crow + n) = make_float4(v[0], v[1], v[2], v[3]);
+          float* crow = reinterpret_cast<float*>(g.C) + m * g.ldc + nb;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const uint32_t ab = __float_as_uint(v[r]) & 0x7fffffffu;
-              amax_bits = amax_bits > ab ? amax_bits : ab;
-            }
-          } else {
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (n + r < g.N) {
-                crow[n + r] = v[r];
+            for (int q = 0; q < 4; ++q) {
+              float v[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                v[r] = MX ? acc[i][j][4 * q + r] : __builtin_amdgcn_ldexpf(acc[i][j][4 * q + r], e);
+              *reinterpret_cast<float4*>(crow + i * 32 + 8 * q) = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
                 const uint32_t ab = __float_as_uint(v[r]) & 0x7fffffffu;
                 amax_bits = amax_bits > ab ? amax_bits : ab;
               }
-          }
-        } else {
-          uint16_t h[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = __builtin_bit_cast(uint16_t, (__bf16)v[r]);
-          uint16_t* crow = reinterpret_cast<uint16_t*>(g.C) + m * g.ldc;
-          if (g.vec_store && n + 3 < g.N) {
-            *reinterpret_cast<uint2*>(crow + n) =
-                make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const uint32_t ab = ((uint32_t)h[r] & 0x7fffu) << 16;
-              amax_bits = amax_bits > ab ? amax_bits : ab;
             }
-          } else {
+        } else {
+          uint16_t* crow = reinterpret_cast<uint16_t*>(g.C) + m * g.ldc + nb;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (n + r < g.N) {
-                crow[n + r] = h[r];
-                const uint32_t ab = ((uint32_t)h[r] & 0x7fffu) << 16;
-                amax_bits = amax_bits > ab ? amax_bits : ab;
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float v[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                v[r] = MX ? acc[i][j][4 * q + r] : __builtin_amdgcn_ldexpf(acc[i][j][4 * q + r], e);
+              const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+              *reinterpret_cast<uint2*>(crow + i * 32 + 8 * q) = make_uint2(lo, hi);
+              pmax = __builtin_elementwise_max(pmax, __builtin_bit_cast(us2v, lo & 0x7fff7fffu));
+              pmax = __builtin_elementwise_max(pmax, __builtin_bit_cast(us2v, hi & 0x7fff7fffu));
+            }
+        }
+      }
+      const uint32_t pm = ((uint32_t)(pmax[0] > pmax[1] ? pmax[0] : pmax[1])) << 16;
+      amax_bits = amax_bits > pm ? amax_bits : pm;
+    } else {
+      // epilogue: lane l of block (i, j) holds n = 8q + 4(l/32) + 0..3 of column m = l%32
+    #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+    #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t m = m0 + wm * 128 + j * 32 + (lane & 31);
+          if (m >= g.M) continue;
+    #pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t n = n0 + wn * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
+            float v[4];
+    #pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = MX ? acc[i][j][4 * q + r] : __builtin_amdgcn_ldexpf(acc[i][j][4 * q + r], e);
+            if (g.out_f32) {
+              float* crow = reinterpret_cast<float*>(g.C) + m * g.ldc;
+              if (g.vec_store && n + 3 < g.N) {
+                *reinterpret_cast<float4*>(crow + n) = make_float4(v[0], v[1], v[2], v[3]);
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const uint32_t ab = __float_as_uint(v[r]) & 0x7fffffffu;
+                  amax_bits = amax_bits > ab ? amax_bits : ab;
+                }
+              } else {
+    #pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (n + r < g.N) {
+                    crow[n + r] = v[r];
+                    const uint32_t ab = __float_as_uint(v[r]) & 0x7fffffffu;
+                    amax_bits = amax_bits > ab ? amax_bits : ab;
+                  }
               }
+            } else {
+              uint16_t h[4];
+    #pragma unroll
+              for (int r = 0; r < 4; ++r) h[r] = __builtin_bit_cast(uint16_t, (__bf16)v[r]);
+              uint16_t* crow = reinterpret_cast<uint16_t*>(g.C) + m * g.ldc;
+              if (g.vec_store && n + 3 < g.N) {
+                *reinterpret_cast<uint2*>(crow + n) =
+                    make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const uint32_t ab = ((uint32_t)h[r] & 0x7fffu) << 16;
+                  amax_bits = amax_bits > ab ? amax_bits : ab;
+                }
+              } else {
+    #pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  if (n + r < g.N) {
+                    crow[n + r] = h[r];
+                    const uint32_t ab = ((uint32_t)h[r] & 0x7fffu) << 16;
+                    amax_bits = amax_bits > ab ? amax_bits : ab;
+                  }
+              }
+            }
           }
         }
       }
     }
+    vb += P;
+    if (!PERSIST || vb >= tiles) break;
+    if constexpr (PERSIST) {
+      cur = nxt;
+      make_tile(vb + P, nxt);
+    }
+    gbase += ngroups;
   }
+  wait_vm<0>();                                     // drain the zero copies past the last tile
   if (g.out_amax) block_max_to_global(amax_bits, red, g.out_amax);
+}
+
+// Compute units of the current device: the persistent grid size.  Cached per
+// device (concurrent first calls store the same value).
+static int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 template <int FA, int FB, bool MX, bool TA, bool TB>
 static void launch_gemm(const GemmArgs& g, hipStream_t s) {
   const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  if (!TA && !TB && g.K > 0 && (g.K % 128) == 0) {
-    const bool sdma = MX && g.scales_dma;
-    if (sdma)
-      hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, true>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, g);
-    else
-      hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, false>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, g);
+  // the forward kernel stages MX scales with dword copies: scale rows must be
+  // 4-byte aligned (always true for packed rows once K % 128 == 0); it is
+  // persistent, one workgroup per compute unit walking tiles
+  if (!TA && !TB && g.K > 0 && (g.K % 128) == 0 && (!MX || g.scales_dma)) {
+    const int64_t cus = MX ? tiles : device_cu_count();
+    const int64_t grid = tiles < cus ? tiles : cus;
+    hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, g);
   } else {
     hipLaunchKernelGGL((gemm_kernel<FA, FB, MX, TA, TB>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, g);
   }
@@ -871,7 +1058,7 @@ int mx_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int fmt_a,
   g.sa = A_scales; g.lds_a = lds_a; g.sb = B_scales; g.lds_b = lds_b;
   g.sa_dword = aligned(A_scales, 4) && (lds_a % 4) == 0;
   g.sb_dword = aligned(B_scales, 4) && (lds_b % 4) == 0;
-  g.scales_dma = g.sa_dword && g.sb_dword && (K % 128) == 0 && lds_a < (1LL << 23) && lds_b < (1LL << 23);
+  g.scales_dma = g.sa_dword && g.sb_dword && (K % 128) == 0 && K >= 512 && lds_a < (1LL << 23) && lds_b < (1LL << 23);
   g.C = C; g.ldc = ldc; g.out_amax = out_amax;
   g.out_f32 = out_dtype == FP8_DT_F32;
   g.vec_store = g.out_f32 ? (aligned(C, 16) && ldc % 4 == 0) : (aligned(C, 8) && ldc % 4 == 0);
