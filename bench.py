@@ -199,6 +199,20 @@ def main():
     per = {nm: sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)) / args.steps
            for i, nm in enumerate(names)}
 
+    # empirically achievable HBM rate: a plain 1 GiB device-to-device copy,
+    # timed after (outside) the timed region
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_GBps = 2 * (1 << 30) * 5 / c0.elapsed_time(c1) / 1e6
+    del src, dst
+
     gemm_flops = 2.0 * M * N * K
     step_flops = 2 * gemm_flops
     bx_b, bw_b = M * K, N * K          # elements
@@ -211,6 +225,7 @@ def main():
         "mxq_w_GBps": (3 + 1 / 32) * bw_b / per["mxq_w"] / 1e6,
         "current_scaling_effective_GBps": 3 * (bx_b + bw_b) / (per["amax_x"] + per["amax_w"] + per["scale"]
                                                                + per["quant_x"] + per["quant_w"]) / 1e6,
+        "hbm_copy_GBps": copy_GBps,
         "gemm_pt_TFLOPs": gemm_flops / per["gemm_pt"] / 1e9,
         "gemm_mx_TFLOPs": gemm_flops / per["gemm_mx"] / 1e9,
         "ms": {k: round(v, 4) for k, v in per.items()},
@@ -236,6 +251,13 @@ def main():
                 "traffic_unit": "GB per launch (HBM-side read+write, copy-calibrated rocprofv3 counters)",
                 "algorithmic_GB": round((M * K + N * K + 2 * M * N) / 1e9, 3)}
 
+    # the HBM-bound kernels against the datasheet 8 TB/s and the copy ceiling
+    stream = {"bound": "hbm", "peak": PEAK_HBM_GBS, "copy_ceiling": round(copy_GBps, 1), "unit": "GB/s"}
+    for k in ("amax_w", "quant_w", "mxq_w", "amax_x", "quant_x", "mxq_x"):
+        v = breakdown[k + "_GBps"]
+        stream[k] = {"achieved": round(v, 1), "frac": round(v / PEAK_HBM_GBS, 4),
+                     "frac_of_copy": round(v / copy_GBps, 4)}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(xb, wb, args.cpu_seconds)
@@ -259,6 +281,7 @@ def main():
                            "MX cast (X,W), MX GEMM+out amax"},
         "breakdown": {k: (round(v, 1) if isinstance(v, float) else v) for k, v in breakdown.items()},
         "roofline": roofline,
+        "stream_roofline": stream,
         "cpu_baseline": cpu,
         "input_generation_s": round(gen_s, 1),
     }

@@ -22,7 +22,24 @@
 namespace sfp8 {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 4;         // 16-byte loads in flight per lane (casts)
+constexpr int kUnrollRead = 8;     // same for the read-only amax pass
+// Unrolled iterations per lane the grid is sized for.  Casts run fastest as
+// many short workgroups (one iteration each); a pass that reduces an amax
+// ends every workgroup with a reduction and one atomic, so it wants fewer,
+// longer ones (measured on the 70B-MLP W tensor: 6.15 TB/s cast, 6.27 TB/s amax).
+constexpr int kItersCast = 1;
+constexpr int kItersCastAmax = 4;
+constexpr int kItersRead = 8;
+
+// Streaming loads and stores with the non-temporal hint: every byte is
+// touched once, and keeping it out of the caches measured 10-20% faster.
+typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
+typedef unsigned v2u_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  const v4u_t v = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 template <int DT> struct In;
 template <> struct In<FP8_DT_BF16> {
@@ -112,19 +129,22 @@ __device__ __forceinline__ uint2 cast_chunk(uint4 v, int e, uint32_t* amax_bits,
 template <int DT>
 __device__ __forceinline__ void store_codes(uint8_t* qrow, int64_t chunk, uint2 o) {
   if constexpr (DT == FP8_DT_BF16) {
-    reinterpret_cast<uint2*>(qrow)[chunk] = o;
+    const v2u_t v = {o.x, o.y};
+    __builtin_nontemporal_store(v, reinterpret_cast<v2u_t*>(qrow) + chunk);
   } else {
-    reinterpret_cast<uint32_t*>(qrow)[chunk] = o.x;
+    __builtin_nontemporal_store(o.x, reinterpret_cast<uint32_t*>(qrow) + chunk);
   }
 }
 
 // Streaming pass: rows are walked by gridDim.y, 16-byte chunks of a row by a
-// grid-stride loop over x with kUnroll loads in flight per lane.
+// grid-stride loop over x with U (kUnroll, or kUnrollRead for the amax-only
+// pass) non-temporal loads in flight per lane.
 template <int DT, int FMT, bool VEC, bool WQ, bool AMAX>
 __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
   __shared__ uint32_t red[kThreads / kWave];
   constexpr int ESZ = In<DT>::kEsz;
   constexpr int EPC = In<DT>::kEpc;
+  constexpr int U = WQ ? kUnroll : kUnrollRead;
   const int e = WQ ? *a.bias : 0;
   uint32_t amax_bits = 0;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -137,12 +157,12 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
       const int64_t cpr = a.cols / EPC;
       const uint4* x4 = reinterpret_cast<const uint4*>(xr);
       int64_t c = tid;
-      for (; c + (kUnroll - 1) * stride < cpr; c += kUnroll * stride) {
-        uint4 v[kUnroll];
+      for (; c + (U - 1) * stride < cpr; c += U * stride) {
+        uint4 v[U];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = x4[c + u * stride];
+        for (int u = 0; u < U; ++u) v[u] = load_nt(x4 + c + u * stride);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
           uint32_t m;
           const uint2 o = cast_chunk<DT, FMT>(v[u], e, &m, WQ);
           if (AMAX) amax_bits = amax_bits > m ? amax_bits : m;
@@ -151,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
       }
       for (; c < cpr; c += stride) {
         uint32_t m;
-        const uint2 o = cast_chunk<DT, FMT>(x4[c], e, &m, WQ);
+        const uint2 o = cast_chunk<DT, FMT>(load_nt(x4 + c), e, &m, WQ);
         if (AMAX) amax_bits = amax_bits > m ? amax_bits : m;
         if (WQ) store_codes<DT>(qr, c, o);
       }
@@ -199,11 +219,13 @@ void launch_stream_pass(StreamArgs a, int dtype, int fmt, bool write_q, bool ama
   bool vec = aligned(a.x, 16) && (a.rows == 1 || (a.ld * esz) % 16 == 0);
   if (write_q) vec = vec && aligned(a.q, epc) && (a.rows == 1 || a.ldq % epc == 0);
   const int64_t units = vec ? (a.cols / epc) : a.cols;
-  unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? kUnroll : 1));
+  const int unroll = write_q ? kUnroll : kUnrollRead;
+  const int iters = !write_q ? kItersRead : (amax ? kItersCastAmax : kItersCast);
+  unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? unroll * iters : iters));
   unsigned gy = (unsigned)(a.rows < 65535 ? a.rows : 65535);
   if (gy < 1) gy = 1;
-  // keep the whole grid near 4096 workgroups
-  while ((uint64_t)gx * gy > 8192 && gy > 1) gy = (gy + 1) / 2;
+  // bound the grid for many short rows
+  while ((uint64_t)gx * gy > 32768 && gy > 1) gy = (gy + 1) / 2;
   const dim3 grid(gx, gy);
   if (dtype == FP8_DT_BF16) {
     if (fmt == FP8_E4M3) launch_vec_mode<FP8_DT_BF16, FP8_E4M3>(a, vec, write_q, amax, grid, stream);
@@ -317,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void mx_vec_kernel(MxArgs a) {
     for (; c + (kUnroll - 1) * stride < cpr; c += kUnroll * stride) {
       uint4 v[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = x4[c + u * stride];
+      for (int u = 0; u < kUnroll; ++u) v[u] = load_nt(x4 + c + u * stride);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         uint32_t m;
@@ -333,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void mx_vec_kernel(MxArgs a) {
     }
     for (; c < cpr; c += stride) {
       uint32_t m;
-      const uint4 v = x4[c];
+      const uint4 v = load_nt(x4 + c);
       cast_chunk<DT, FMT>(v, 0, &m, false);
       const uint32_t bm = (L == 4) ? group4_max(m) : group8_max(m);
       int e;
@@ -376,10 +398,10 @@ template <int DT, int FMT>
 static void launch_mx(const MxArgs& a, bool vec, hipStream_t s) {
   const int epc = 16 / In<DT>::kEsz;
   const int64_t units = vec ? a.cols / epc : a.cols / 32;
-  const unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? kUnroll : 1));
+  const unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? kUnroll * kItersCast : kItersCast));
   unsigned gy = (unsigned)(a.rows < 65535 ? a.rows : 65535);
   if (gy < 1) gy = 1;
-  while ((uint64_t)gx * gy > 8192 && gy > 1) gy = (gy + 1) / 2;
+  while ((uint64_t)gx * gy > 32768 && gy > 1) gy = (gy + 1) / 2;
   if (vec)
     hipLaunchKernelGGL((mx_vec_kernel<DT, FMT>), dim3(gx, gy), dim3(kThreads), 0, s, a);
   else
