@@ -64,7 +64,8 @@ enum {
   FP8_OK = 0,
   FP8_ERR_NULL = -1,        /* a required pointer is NULL */
   FP8_ERR_SHAPE = -2,       /* negative size, ld < cols, K % 16 (GEMM) or
-                               cols % 32 / K % 32 (MX) violated, bad window */
+                               cols % 32 / rows % 32 / K % 32 (MX) violated,
+                               bad window */
   FP8_ERR_ALIGN = -3,       /* GEMM operand base or leading dimension not a
                                multiple of 16 bytes (required by 16-byte loads) */
   FP8_ERR_DTYPE = -4,       /* unknown FP8_DT_* value */
@@ -158,6 +159,23 @@ int fp8_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
 int mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                 int fmt, uint8_t* q, int64_t ldq, uint8_t* scales,
                 int64_t ld_scales, hipStream_t stream);
+
+/*
+ * mx_quantize_t — per-block cast with the blocks along ROWS, written
+ * transposed ("Key Questions Answered": per-block scaling; the backward
+ * products contract over the token axis, so their MX operands need blocks
+ * along it).  Blocks are 32 x 1 (32 consecutive rows of one column); the
+ * result equals mx_quantize of x^T:
+ *   qT       [cols x rows] FP8 codes (fmt), leading dimension ldqT (bytes):
+ *            qT[c, r] = sat_RNE(x[r, c] * 2^e_b) for the block b of rows
+ *            32 floor(r/32) .. +31 in column c.
+ *   scalesT  [cols x rows/32] E8M0 codes, leading dimension ld_scales, by the
+ *            rule of mx_quantize.
+ * rows % 32 == 0 is required; any alignment is accepted.
+ */
+int mx_quantize_t(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                  int fmt, uint8_t* qT, int64_t ldqT, uint8_t* scalesT,
+                  int64_t ld_scales, hipStream_t stream);
 
 /*
  * fp8_scaled_gemm — per-tensor scaled FP8 GEMM with unscale ("Proposed

@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "E4M3", "E5M2", "load_library", "library_path", "Fp8Error",
     "fp8_amax", "fp8_compute_scale", "fp8_history_init", "fp8_history_push",
-    "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize",
+    "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize", "mx_quantize_t",
     "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string", "fp8_abi_version",
 ]
 
@@ -50,6 +50,7 @@ _SIGNATURES = {
     "fp8_compute_scale_delayed": ([_p, _p, _i, _i, _i, _p, _p, _p, _p], _i),
     "fp8_quantize": ([_p, _i, _i64, _i64, _i64, _i, _p, _p, _i64, _p, _i64, _p, _p], _i),
     "mx_quantize": ([_p, _i, _i64, _i64, _i64, _i, _p, _i64, _p, _i64, _p], _i),
+    "mx_quantize_t": ([_p, _i, _i64, _i64, _i64, _i, _p, _i64, _p, _i64, _p], _i),
     "fp8_scaled_gemm": ([_i64, _i64, _i64, _p, _i, _i, _i64, _p, _p, _i, _i, _i64, _p,
                          _p, _i, _i64, _p, _p], _i),
     "mx_scaled_gemm": ([_i64, _i64, _i64, _p, _i, _i64, _p, _i64, _p, _i, _i64, _p, _i64,
@@ -271,6 +272,28 @@ def mx_quantize(x: torch.Tensor, fmt=E4M3, q: torch.Tensor | None = None,
         _ptr(x), _dtype_code(x, "x"), rows, cols, ld, _fmt(fmt), _ptr(q), ldq, _ptr(scales),
         lds, _stream(x)))
     return q, scales
+
+
+def mx_quantize_t(x: torch.Tensor, fmt=E4M3, qT: torch.Tensor | None = None,
+                  scalesT: torch.Tensor | None = None):
+    """Per-block cast with 32 x 1 blocks along rows, written transposed;
+    returns (qT [C x R] codes, scalesT [C x R/32] E8M0 codes), the MX cast of
+    x^T."""
+    rows, cols, ld = _mat(x, "x")
+    if rows % 32:
+        raise ValueError("mx_quantize_t needs rows % 32 == 0")
+    if qT is None:
+        qT = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    if scalesT is None:
+        scalesT = torch.empty((cols, rows // 32), dtype=torch.uint8, device=x.device)
+    _u8(qT, "qT")
+    _u8(scalesT, "scalesT")
+    _, _, ldq = _mat(qT, "qT")
+    _, _, lds = _mat(scalesT, "scalesT")
+    _check("mx_quantize_t", load_library().mx_quantize_t(
+        _ptr(x), _dtype_code(x, "x"), rows, cols, ld, _fmt(fmt), _ptr(qT), ldq, _ptr(scalesT),
+        lds, _stream(x)))
+    return qT, scalesT
 
 
 def _out_code(dtype: torch.dtype) -> int:

@@ -408,6 +408,76 @@ static void launch_mx(const MxArgs& a, bool vec, hipStream_t s) {
     hipLaunchKernelGGL((mx_scalar_kernel<DT, FMT>), dim3(gx, gy), dim3(kThreads), 0, s, a);
 }
 
+// ---------------------------------------------------------------------------
+// Transposed MX cast: blocks of 32 consecutive ROWS of one column, written as
+// qT [cols x rows] with scalesT [cols x rows/32], i.e. the MX cast of x^T
+// (for a GEMM that contracts over `rows`, such as a weight gradient whose K
+// is the token axis).  64 x 64 tiles: each lane loads 16 consecutive elements
+// of one tile row into an LDS tile of fp32 bit patterns; then lane (c, q)
+// (q = lane / 64, one wave per quarter) takes rows 16q..16q+15 of tile
+// column c, the two quarters of a 32-row block exchange their maxima through
+// LDS, and each lane writes its 16 codes as 16 contiguous bytes of qT row c.
+// ---------------------------------------------------------------------------
+template <int DT, int FMT>
+__global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
+  __shared__ uint32_t tile[kTT][kTT + 1];          // fp32 bit patterns, padded
+  __shared__ uint32_t pmax[4][kTT];                // per-quarter column maxima
+  constexpr int ESZ = In<DT>::kEsz;
+  const int64_t r0 = (int64_t)blockIdx.y * kTT;
+  const int64_t c0 = (int64_t)blockIdx.x * kTT;
+  {
+    const int tr = threadIdx.x / 4;
+    const int tc = (threadIdx.x % 4) * 16;
+    const int64_t r = r0 + tr;
+    const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ld * ESZ;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int64_t c = c0 + tc + j;
+      uint32_t bits = 0;
+      if (r < a.rows && c < a.cols) {
+        float f;
+        bits = load_elem<DT>(xr, c, &f);
+      }
+      tile[tr][tc + j] = bits;
+    }
+  }
+  __syncthreads();
+  const int c = threadIdx.x % kTT;
+  const int qq = threadIdx.x / kTT;                // 0..3: rows 16 qq .. 16 qq + 15
+  uint32_t v[16];
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = tile[16 * qq + i][c];
+    const uint32_t ab = v[i] & 0x7fffffffu;
+    m = m > ab ? m : ab;
+  }
+  pmax[qq][c] = m;
+  __syncthreads();
+  const uint32_t o = pmax[qq ^ 1][c];
+  const uint32_t bm = m > o ? m : o;
+  int e;
+  uint32_t code;
+  block_exponent<FMT>(bm, &e, &code);
+  const int64_t col = c0 + c;                      // qT row
+  const int64_t rr = r0 + 16 * qq;                 // first qT column of this lane
+  if (col < a.cols && rr < a.rows) {               // rows % 32 == 0: all 16 rows exist
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = cast_elem<FMT>(v[4 * k], e) | (cast_elem<FMT>(v[4 * k + 1], e) << 8) |
+             (cast_elem<FMT>(v[4 * k + 2], e) << 16) | (cast_elem<FMT>(v[4 * k + 3], e) << 24);
+    uint8_t* dst = a.q + col * a.ldq + rr;
+    if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) dst[k] = (uint8_t)(w[k / 4] >> (8 * (k % 4)));
+    }
+    if ((qq & 1) == 0) a.scales[col * a.lds + rr / 32] = (uint8_t)code;
+  }
+}
+
 }  // namespace sfp8
 
 using namespace sfp8;
@@ -505,6 +575,42 @@ int mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
   } else {
     if (fmt == FP8_E4M3) launch_mx<FP8_DT_F32, FP8_E4M3>(a, vec, stream);
     else launch_mx<FP8_DT_F32, FP8_E5M2>(a, vec, stream);
+  }
+  return launch_status();
+}
+
+int mx_quantize_t(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, uint8_t* qT,
+                  int64_t ldqT, uint8_t* scalesT, int64_t ld_scales, hipStream_t stream) {
+  if (!qT || !scalesT) return FP8_ERR_NULL;
+  if (!valid_dtype(dtype)) return FP8_ERR_DTYPE;
+  if (!valid_fmt(fmt)) return FP8_ERR_FORMAT;
+  if (rows % 32) return FP8_ERR_SHAPE;
+  int st = check_matrix(rows, cols, ld);
+  if (st) return st;
+  st = check_matrix(cols, rows, ldqT);
+  if (st) return st;
+  st = check_matrix(cols, rows / 32, ld_scales);
+  if (st) return st;
+  if (rows * cols == 0) return FP8_OK;
+  if (!x) return FP8_ERR_NULL;
+  const int64_t gy = (rows + kTT - 1) / kTT;
+  if (gy > 65535) return FP8_ERR_SHAPE;
+  MxArgs a;
+  a.x = x;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.q = qT;
+  a.ldq = ldqT;
+  a.scales = scalesT;
+  a.lds = ld_scales;
+  const dim3 grid((unsigned)((cols + kTT - 1) / kTT), (unsigned)gy);
+  if (dtype == FP8_DT_BF16) {
+    if (fmt == FP8_E4M3) hipLaunchKernelGGL((mx_transpose_kernel<FP8_DT_BF16, FP8_E4M3>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((mx_transpose_kernel<FP8_DT_BF16, FP8_E5M2>), grid, dim3(kThreads), 0, stream, a);
+  } else {
+    if (fmt == FP8_E4M3) hipLaunchKernelGGL((mx_transpose_kernel<FP8_DT_F32, FP8_E4M3>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((mx_transpose_kernel<FP8_DT_F32, FP8_E5M2>), grid, dim3(kThreads), 0, stream, a);
   }
   return launch_status();
 }

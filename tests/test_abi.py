@@ -35,7 +35,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for want in ["fp8_amax", "fp8_compute_scale", "fp8_history_init", "fp8_history_push",
-                 "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize",
+                 "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize", "mx_quantize_t",
                  "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string", "fp8_abi_version"]:
         assert want in names
 
@@ -92,6 +92,17 @@ def test_quantize_validation(lib):
     assert m(FAKE, 0, 4, 64, 64, 0, FAKE, 64, FAKE, 1, S) == SHAPE              # ld_scales
     assert m(FAKE, 2, 4, 64, 64, 0, FAKE, 64, FAKE, 2, S) == DTYPE
     assert m(FAKE, 0, 4, 64, 64, 2, FAKE, 64, FAKE, 2, S) == FORMAT
+    t = lib.mx_quantize_t
+    # x, dtype, rows, cols, ld, fmt, qT, ldqT, scalesT, ld_scales, s
+    assert t(FAKE, 0, 48, 8, 8, 0, FAKE, 48, FAKE, 2, S) == SHAPE                # rows % 32
+    assert t(FAKE, 0, 64, 8, 8, 0, None, 64, FAKE, 2, S) == NULL
+    assert t(FAKE, 0, 64, 8, 8, 0, FAKE, 64, None, 2, S) == NULL
+    assert t(FAKE, 0, 64, 8, 8, 0, FAKE, 32, FAKE, 2, S) == SHAPE                # ldqT < rows
+    assert t(FAKE, 0, 64, 8, 8, 0, FAKE, 64, FAKE, 1, S) == SHAPE                # ld_scales
+    assert t(FAKE, 0, 64, 8, 4, 0, FAKE, 64, FAKE, 2, S) == SHAPE                # ld < cols
+    assert t(FAKE, 5, 64, 8, 8, 0, FAKE, 64, FAKE, 2, S) == DTYPE
+    assert t(FAKE, 0, 64, 8, 8, 3, FAKE, 64, FAKE, 2, S) == FORMAT
+    assert t(None, 0, 64, 8, 8, 0, FAKE, 64, FAKE, 2, S) == NULL
 
 
 def test_gemm_validation(lib):
@@ -126,3 +137,5 @@ def test_binding_refuses_cpu_tensors():
         sq.fp8_amax(x)
     with pytest.raises(ValueError):
         sq.mx_quantize(torch.zeros(4, 32, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        sq.mx_quantize_t(torch.zeros(32, 4, dtype=torch.bfloat16))

@@ -257,6 +257,27 @@ def test_mx_gemm_uniform_scales_match_per_tensor():
     assert torch.equal(Cm, Cp)
 
 
+def test_mx_weight_gradient_via_transposed_casts():
+    """dW = dY^T X with MX operands: both cast with blocks along the token
+    axis (mx_quantize_t), then the MX GEMM contracts over tokens (K = 1024).
+    dY is E5M2 (a gradient), X is E4M3; the oracle casts dY^T and X^T itself."""
+    dyb = make("c3", "dY", shape=(1024, 384))
+    xb = make("c3", "X", shape=(1024, 256))
+    say("mx dW via transposed casts")
+    qdy, sdy = sq.mx_quantize_t(bf16_dev(dyb), E5M2.code)
+    qx, sx = sq.mx_quantize_t(bf16_dev(xb), E4M3.code)
+    C, am = sq.mx_scaled_gemm(qdy, E5M2.code, sdy, qx, E4M3.code, sx, out_dtype=torch.float32, want_amax=True)
+    oqdy, osdy = oracle.mx_quantize(oracle.bf16_bits_to_f64(np.ascontiguousarray(dyb.T)), E5M2)
+    oqx, osx = oracle.mx_quantize(oracle.bf16_bits_to_f64(np.ascontiguousarray(xb.T)), E4M3)
+    assert np.array_equal(host(qdy), oqdy) and np.array_equal(host(sdy), osdy)
+    assert np.array_equal(host(qx), oqx) and np.array_equal(host(sx), osx)
+    ref = oracle.mx_gemm_ref(oqdy, osdy, E5M2, oqx, osx, E4M3)
+    s = oracle.mx_abs_product_sum(oqdy, osdy, E5M2, oqx, osx, E4M3)
+    gt = mfma_group_term(oracle.mx_dequantize(oqdy, osdy, E5M2), oracle.mx_dequantize(oqx, osx, E4M3))
+    assert_gemm_close(host_f64(C), ref, s, False, "mx dW", gt)
+    _check_amax(C, am)
+
+
 def _sample_idx(rng, M, N, n=2048):
     rows = np.concatenate([rng.integers(0, M, n), [0, M - 1, 0, M - 1]])
     cols = np.concatenate([rng.integers(0, N, n), [0, N - 1, N - 1, 0]])

@@ -173,6 +173,53 @@ def test_mx_cast_bit_exact(fmt, dtype):
         assert np.array_equal(host(s3), rs) and np.array_equal(host(q3), rq)
 
 
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: f.name)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mx_cast_transposed_bit_exact(fmt, dtype):
+    """Blocks of 32 rows, written transposed: equals the oracle's MX cast of
+    x^T byte for byte.  96 rows (a half tile at the end), 100 columns (a
+    ragged tile), blocks holding zeros, NaN, Inf, subnormals and the bf16
+    maximum; then a strided input view and strided outputs."""
+    bits = make("c4", "X", shape=(96, 100))
+    bits[:32, 0] = 0                                   # all-zero block
+    bits[40, 1] = 0x7FC0                               # NaN block
+    bits[64:96, 2] = 0x0001                            # subnormal-only block
+    bits[5, 3] = 0x7F80                                # Inf block
+    bits[32:64, 4] = 0x7F7F                            # bf16 max
+    bits[70, 5] = 0xFF80                               # -Inf
+    vals = oracle.bf16_bits_to_f64(bits)
+    x = bf16_dev(bits) if dtype == "bf16" else f32_dev(vals.astype(np.float32))
+    say(f"mx transposed cast {fmt.name} {dtype}")
+    qT, sT = sq.mx_quantize_t(x, fmt.code)
+    rq, rs = oracle.mx_quantize(np.ascontiguousarray(vals.T), fmt)
+    assert qT.shape == (100, 96) and sT.shape == (100, 3)
+    assert np.array_equal(host(sT), rs)
+    assert np.array_equal(host(qT), rq)
+    # strided input (ld = 100 + 28) and padded outputs (ldqT = 96 + 16, ld_scales = 5)
+    big = torch.zeros((96, 128), dtype=x.dtype, device=DEV)
+    big[:, :100] = x
+    qbig = torch.full((100, 112), 0xA5, dtype=torch.uint8, device=DEV)
+    sbig = torch.full((100, 5), 0x5A, dtype=torch.uint8, device=DEV)
+    sq.mx_quantize_t(big[:, :100], fmt.code, qT=qbig[:, :96], scalesT=sbig[:, :3])
+    assert np.array_equal(host(qbig[:, :96]), rq) and np.array_equal(host(sbig[:, :3]), rs)
+    assert np.all(host(qbig[:, 96:]) == 0xA5) and np.all(host(sbig[:, 3:]) == 0x5A)
+
+
+def test_mx_cast_transposed_full_size_sampled():
+    """X[16384 x 8192] of the 70B-MLP workload: qT [8192 x 16384] and its
+    scales exact on 64 sampled qT rows (columns of X)."""
+    bits = make("c5", "X")
+    x = bf16_dev(bits)
+    say("mx transposed cast c5 X")
+    qT, sT = sq.mx_quantize_t(x, E4M3.code)
+    rng = np.random.default_rng(11)
+    cols = np.unique(np.concatenate([[0, bits.shape[1] - 1], rng.integers(0, bits.shape[1], 62)]))
+    rq, rs = oracle.mx_quantize(oracle.bf16_bits_to_f64(np.ascontiguousarray(bits[:, cols].T)), E4M3)
+    idx = torch.from_numpy(cols).to(DEV)
+    assert np.array_equal(host(sT[idx]), rs)
+    assert np.array_equal(host(qT[idx]), rq)
+
+
 def test_mx_rmse_below_per_tensor_c4_shape():
     bits = make("c4", "X", shape=(256, 1024))
     vals = oracle.bf16_bits_to_f64(bits)
