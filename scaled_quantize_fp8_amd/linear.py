@@ -1,0 +1,177 @@
+"""FP8 linear layer, forward and backward, over the library's entry points.
+
+"Training and inference of large language models using 8-bit floating
+point" (paper review page), "Proposed method": every tensor of a linear
+layer gets a power-of-two scale from its amax, weights and activations are
+cast to E4M3 and gradients to E5M2, and the matrix products run on the FP8
+operands and are unscaled afterwards.  "Per-Tensor and Per-Block Scaling
+Strategies for Effective FP8 Training" (summary page), "Key Questions
+Answered": the scale may come from the amaxes of past iterations (delayed
+scaling) or from each block of the tensor (per-block, MX).
+
+Every step runs in the HIP library; this module only routes tensors between
+entry points.  The three products all read K-contiguous operands (the fast
+TN GEMM):
+
+    forward   Y  = X W^T      A = X   [T x in],   B = W   [out x in]
+    backward  dX = dY W       A = dY  [T x out],  B = W^T [in x out]
+              dW = dY^T X     A = dY^T [out x T], B = X^T [in x T]
+
+W^T and X^T are the transposed copies written by the forward casts (the
+per-tensor cast writes both layouts in one pass; MX casts W^T and X^T with
+blocks along their new contiguous axis), dY^T by the backward cast.
+
+Recipes:
+    "current"  per-tensor, bias from the tensor's own amax (two passes:
+               amax, then cast);
+    "delayed"  per-tensor, bias from the largest amax of the last `history`
+               steps; the cast also reduces the tensor's amax, which is
+               pushed into the history afterwards.  The first step has no
+               history and pushes its own amax first (current scaling);
+    "mx"       per-block: 1 x 32 blocks along each product's K axis, E8M0
+               block scales.
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import (E4M3, E5M2, fp8_amax, fp8_compute_scale, fp8_compute_scale_delayed,
+               fp8_history_init, fp8_history_push, fp8_quantize, fp8_scaled_gemm, mx_quantize,
+               mx_quantize_t, mx_scaled_gemm)
+
+RECIPES = ("current", "delayed", "mx")
+
+
+class _History:
+    """Delayed-scaling state of one tensor: `window` past amaxes and
+    {count, head}, in device memory (checkpointing copies these buffers)."""
+
+    def __init__(self, window: int, device):
+        self.window = window
+        self.hist = torch.empty(window, dtype=torch.float32, device=device)
+        self.state = torch.empty(2, dtype=torch.int32, device=device)
+        fp8_history_init(self.hist, self.state)
+        self.steps = 0
+
+
+def _per_tensor_cast(x2: torch.Tensor, fmt, recipe: str, margin: int, hist: _History | None,
+                     transpose: bool):
+    """Bias and FP8 codes (plus the transposed copy) of one tensor."""
+    if recipe == "current":
+        bias, _, _ = fp8_compute_scale(fp8_amax(x2), fmt, margin)
+        q, qT, _ = fp8_quantize(x2, fmt, bias, transpose=transpose)
+        return bias, q, qT
+    # delayed: the first step bootstraps the history with its own amax
+    if hist.steps == 0:
+        fp8_history_push(hist.hist, hist.state, fp8_amax(x2))
+    bias, _, _ = fp8_compute_scale_delayed(hist.hist, hist.state, fmt, margin)
+    q, qT, amax = fp8_quantize(x2, fmt, bias, transpose=transpose, want_amax=True)
+    if hist.steps > 0:
+        fp8_history_push(hist.hist, hist.state, amax)
+    hist.steps += 1
+    return bias, q, qT
+
+
+class Fp8LinearFunction(torch.autograd.Function):
+    """Y = X W^T with FP8 operands (no additive bias)."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, w: torch.Tensor, layer: "Fp8Linear"):
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, x.shape[-1])
+        if not x2.is_contiguous():
+            x2 = x2.contiguous()
+        recipe = layer.recipe
+        if recipe == "mx":
+            qx, sx = mx_quantize(x2, E4M3)
+            qw, sw = mx_quantize(w, E4M3)
+            y, amax = mx_scaled_gemm(qx, E4M3, sx, qw, E4M3, sw, out_dtype=x.dtype, want_amax=True)
+            if ctx.needs_input_grad[0] or ctx.needs_input_grad[1]:
+                # backward operands: blocks along out (W^T) and along tokens (X^T)
+                qwT, swT = mx_quantize_t(w, E4M3)
+                qxT, sxT = mx_quantize_t(x2, E4M3)
+                ctx.save_for_backward(qwT, swT, qxT, sxT)
+        else:
+            bx, qx, qxT = _per_tensor_cast(x2, E4M3, recipe, layer.margin, layer._hx, True)
+            bw, qw, qwT = _per_tensor_cast(w, E4M3, recipe, layer.margin, layer._hw, True)
+            y, amax = fp8_scaled_gemm(qx, E4M3, bx, qw, E4M3, bw, out_dtype=x.dtype, want_amax=True)
+            ctx.save_for_backward(qwT, bw, qxT, bx)
+        layer.last_output_amax = amax
+        ctx.layer = layer
+        ctx.lead = lead
+        ctx.dtype = x.dtype
+        return y.reshape(*lead, w.shape[0])
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        layer = ctx.layer
+        dy2 = dy.reshape(-1, dy.shape[-1])
+        if not dy2.is_contiguous():
+            dy2 = dy2.contiguous()
+        if dy2.dtype != ctx.dtype:
+            raise TypeError(f"gradient dtype {dy2.dtype} differs from the forward's {ctx.dtype}")
+        dx = dw = None
+        if layer.recipe == "mx":
+            qwT, swT, qxT, sxT = ctx.saved_tensors
+            if ctx.needs_input_grad[0]:
+                qdy, sdy = mx_quantize(dy2, E5M2)
+                dx, _ = mx_scaled_gemm(qdy, E5M2, sdy, qwT, E4M3, swT, out_dtype=ctx.dtype)
+            if ctx.needs_input_grad[1]:
+                qdyT, sdyT = mx_quantize_t(dy2, E5M2)
+                dw, _ = mx_scaled_gemm(qdyT, E5M2, sdyT, qxT, E4M3, sxT, out_dtype=ctx.dtype)
+        else:
+            qwT, bw, qxT, bx = ctx.saved_tensors
+            bdy, qdy, qdyT = _per_tensor_cast(dy2, E5M2, layer.recipe, layer.margin, layer._hdy,
+                                              ctx.needs_input_grad[1])
+            if ctx.needs_input_grad[0]:
+                dx, _ = fp8_scaled_gemm(qdy, E5M2, bdy, qwT, E4M3, bw, out_dtype=ctx.dtype)
+            if ctx.needs_input_grad[1]:
+                dw, _ = fp8_scaled_gemm(qdyT, E5M2, bdy, qxT, E4M3, bx, out_dtype=ctx.dtype)
+        if dx is not None:
+            dx = dx.reshape(*ctx.lead, dx.shape[-1])
+        return dx, dw, None
+
+
+class Fp8Linear(torch.nn.Module):
+    """Linear layer y = x W^T whose three products run in FP8 on the GPU.
+
+    in_features, out_features and the token count must be multiples of 32
+    (the MX block; the per-tensor path needs 16, and multiples of 128 take the
+    fastest GEMM).  `last_output_amax` holds max |y| of the latest forward,
+    reduced in the GEMM's epilogue, for a next layer's scale."""
+
+    def __init__(self, in_features: int, out_features: int, recipe: str = "current",
+                 margin: int = 0, history: int = 16, device=None, dtype=torch.bfloat16):
+        super().__init__()
+        if recipe not in RECIPES:
+            raise ValueError(f"recipe must be one of {RECIPES}")
+        if in_features % 32 or out_features % 32:
+            raise ValueError("in_features and out_features must be multiples of 32")
+        if dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("dtype must be bfloat16 or float32")
+        self.in_features, self.out_features = in_features, out_features
+        self.recipe, self.margin = recipe, int(margin)
+        self.weight = torch.nn.Parameter(torch.empty(out_features, in_features, device=device, dtype=dtype))
+        torch.nn.init.kaiming_uniform_(self.weight, a=math.sqrt(5))
+        self.last_output_amax = None
+        self._hx = self._hw = self._hdy = None
+        if recipe == "delayed":
+            dev = self.weight.device
+            self._hx, self._hw, self._hdy = (_History(history, dev), _History(history, dev),
+                                             _History(history, dev))
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        if x.shape[-1] != self.in_features:
+            raise ValueError(f"expected {self.in_features} input features, got {x.shape[-1]}")
+        tokens = x.numel() // self.in_features
+        if tokens % 32:
+            raise ValueError("the number of tokens must be a multiple of 32")
+        if x.dtype != self.weight.dtype:
+            raise TypeError("input and weight dtypes differ")
+        return Fp8LinearFunction.apply(x, self.weight, self)
+
+    def extra_repr(self) -> str:
+        return f"in_features={self.in_features}, out_features={self.out_features}, recipe={self.recipe}"

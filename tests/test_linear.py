@@ -1,0 +1,145 @@
+"""The FP8 linear layer (forward Y = X W^T, backward dX = dY W and
+dW = dY^T X) against the oracle's emulation of the same recipe: the oracle
+computes every amax, bias, per-tensor or MX cast itself from the bf16 inputs
+and forms the three products in float64; the GPU results must meet the GEMM
+acceptance bound of the parity tests.  CPU tests cover argument checks."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import scaled_quantize_fp8_amd as sq
+from oracle import E4M3, E5M2
+from scaled_quantize_fp8_amd.linear import Fp8Linear
+from workloads import make
+
+from gpu_helpers import DEV, assert_gemm_close, bf16_dev, host, host_f64, mfma_group_term, need_gpu, say
+
+T, IN, OUT = 256, 512, 384
+
+
+def _tensors(step=0, x_scale=1.0):
+    xb = make("c1", "X", step=step, shape=(T, IN))
+    x = oracle.bf16_bits_to_f64(xb) * x_scale                 # exact: power-of-two scales only
+    wb = make("c1", "W", shape=(OUT, IN))
+    dyb = make("c3", "dY", step=step, shape=(T, OUT))
+    return x, oracle.bf16_bits_to_f64(wb), oracle.bf16_bits_to_f64(dyb)
+
+
+def _dev(v):
+    return torch.from_numpy(v.astype(np.float32)).to(DEV).to(torch.bfloat16)
+
+
+def _run(layer, x, dy):
+    xt = _dev(x).requires_grad_(True)
+    y = layer(xt)
+    y.backward(_dev(dy))
+    return host_f64(y), host_f64(xt.grad), host_f64(layer.weight.grad), layer.last_output_amax
+
+
+def _check(what, got, ref, s, gt):
+    assert_gemm_close(got, ref, s, True, what, gt)
+
+
+def _check_pt(y, dx, dw, x, w, dy, bx, bw, bdy):
+    qx, qw, qdy = oracle.quantize(x, E4M3, bx), oracle.quantize(w, E4M3, bw), oracle.quantize(dy, E5M2, bdy)
+    qwT, qxT, qdyT = (np.ascontiguousarray(a.T) for a in (qw, qx, qdy))
+    for what, got, a, fa, ba, b, fb, bb in (("y", y, qx, E4M3, bx, qw, E4M3, bw),
+                                            ("dx", dx, qdy, E5M2, bdy, qwT, E4M3, bw),
+                                            ("dw", dw, qdyT, E5M2, bdy, qxT, E4M3, bx)):
+        ref = oracle.scaled_gemm_ref(a, fa, ba, b, fb, bb)
+        s = oracle.abs_product_sum(a, fa, ba, b, fb, bb)
+        gt = mfma_group_term(oracle.dequantize(a, fa, ba), oracle.dequantize(b, fb, bb))
+        _check(what, got, ref, s, gt)
+
+
+@pytest.mark.gpu
+def test_linear_current_scaling_matches_oracle():
+    need_gpu()
+    x, w, dy = _tensors()
+    layer = Fp8Linear(IN, OUT, recipe="current", device=DEV)
+    with torch.no_grad():
+        layer.weight.copy_(_dev(w))
+    say("fp8 linear, current scaling")
+    y, dx, dw, amax = _run(layer, x, dy)
+    bx, bw = oracle.compute_bias(oracle.amax(x), E4M3), oracle.compute_bias(oracle.amax(w), E4M3)
+    bdy = oracle.compute_bias(oracle.amax(dy), E5M2)
+    _check_pt(y, dx, dw, x, w, dy, bx, bw, bdy)
+    assert host(amax)[0] == np.max(np.abs(y))
+
+
+@pytest.mark.gpu
+def test_linear_delayed_scaling_three_steps():
+    """Activations whose scale jumps (x1, x16, x1/8): the layer's biases follow
+    the oracle's delayed-scaling history (step 0 current, later steps the
+    window maximum of earlier steps), forward and backward."""
+    need_gpu()
+    layer = Fp8Linear(IN, OUT, recipe="delayed", history=16, device=DEV)
+    hx, hw, hdy = oracle.DelayedScaling(16), oracle.DelayedScaling(16), oracle.DelayedScaling(16)
+    for step, xs in enumerate((1.0, 16.0, 0.125)):
+        x, w, dy = _tensors(step, xs)
+        if step == 0:
+            with torch.no_grad():
+                layer.weight.copy_(_dev(w))
+        layer.weight.grad = None
+        say(f"fp8 linear, delayed scaling step {step}")
+        y, dx, dw, _ = _run(layer, x, dy)
+        biases = []
+        for h, v, fmt in ((hx, x, E4M3), (hw, w, E4M3), (hdy, dy, E5M2)):
+            if step == 0:
+                h.push(oracle.amax(v))
+            biases.append(h.bias(fmt))
+            if step > 0:
+                h.push(oracle.amax(v))
+        _check_pt(y, dx, dw, x, w, dy, *biases)
+
+
+@pytest.mark.gpu
+def test_linear_mx_matches_oracle():
+    need_gpu()
+    x, w, dy = _tensors()
+    layer = Fp8Linear(IN, OUT, recipe="mx", device=DEV)
+    with torch.no_grad():
+        layer.weight.copy_(_dev(w))
+    say("fp8 linear, MX")
+    y, dx, dw, amax = _run(layer, x, dy)
+    qx, sx = oracle.mx_quantize(x, E4M3)
+    qw, sw = oracle.mx_quantize(w, E4M3)
+    qdy, sdy = oracle.mx_quantize(dy, E5M2)
+    qwT, swT = oracle.mx_quantize(np.ascontiguousarray(w.T), E4M3)
+    qdyT, sdyT = oracle.mx_quantize(np.ascontiguousarray(dy.T), E5M2)
+    qxT, sxT = oracle.mx_quantize(np.ascontiguousarray(x.T), E4M3)
+    for what, got, a, sa, fa, b, sb, fb in (("y", y, qx, sx, E4M3, qw, sw, E4M3),
+                                            ("dx", dx, qdy, sdy, E5M2, qwT, swT, E4M3),
+                                            ("dw", dw, qdyT, sdyT, E5M2, qxT, sxT, E4M3)):
+        ref = oracle.mx_gemm_ref(a, sa, fa, b, sb, fb)
+        s = oracle.mx_abs_product_sum(a, sa, fa, b, sb, fb)
+        gt = mfma_group_term(oracle.mx_dequantize(a, sa, fa), oracle.mx_dequantize(b, sb, fb))
+        _check(what, got, ref, s, gt)
+    assert host(amax)[0] == np.max(np.abs(y))
+
+
+@pytest.mark.gpu
+def test_linear_batched_input_shape():
+    need_gpu()
+    layer = Fp8Linear(IN, OUT, device=DEV)
+    x = bf16_dev(make("c1", "X", shape=(T, IN))).view(2, T // 2, IN).requires_grad_(True)
+    y = layer(x)
+    assert y.shape == (2, T // 2, OUT)
+    y.sum().backward()
+    assert x.grad.shape == x.shape and layer.weight.grad.shape == layer.weight.shape
+
+
+def test_linear_argument_checks():
+    with pytest.raises(ValueError):
+        Fp8Linear(IN, OUT, recipe="fp16")
+    with pytest.raises(ValueError):
+        Fp8Linear(100, OUT)
+    layer = Fp8Linear(IN, OUT)                       # CPU parameters: the product path refuses them
+    with pytest.raises(ValueError):
+        layer(torch.zeros(T, IN, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        layer(torch.zeros(T, IN + 32, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        layer(torch.zeros(T + 16, IN, dtype=torch.bfloat16))
