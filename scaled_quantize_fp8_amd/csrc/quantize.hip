@@ -296,6 +296,107 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Cast-transpose, vector form (bf16 input): 128 x 64 tiles.  Lane (cg, rg)
+// loads 16 bytes (8 columns) of 4 consecutive rows, casts them, stores the 4
+// x 8 codes of q directly (8 bytes per row), transposes them 4 x 4 bytes at a
+// time in registers and writes 8 dwords (4 rows each) into a column-major
+// LDS tile; then lane (j, s) writes 32 contiguous bytes of qT row j.  Tiles
+// reaching past the matrix take a per-element path with the same exchange.
+// ---------------------------------------------------------------------------
+constexpr int kCtR = 128, kCtC = 64;
+
+// d_k = byte k of a0, a1, a2, a3 (a 4 x 4 byte transpose)
+__device__ __forceinline__ void bytes_transpose4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                                 uint32_t (&d)[4]) {
+  const uint32_t lo01 = __builtin_amdgcn_perm(a1, a0, 0x05010400u);   // a0.0 a1.0 a0.1 a1.1
+  const uint32_t hi01 = __builtin_amdgcn_perm(a1, a0, 0x07030602u);   // a0.2 a1.2 a0.3 a1.3
+  const uint32_t lo23 = __builtin_amdgcn_perm(a3, a2, 0x05010400u);
+  const uint32_t hi23 = __builtin_amdgcn_perm(a3, a2, 0x07030602u);
+  d[0] = __builtin_amdgcn_perm(lo23, lo01, 0x05040100u);             // a0.0 a1.0 a2.0 a3.0
+  d[1] = __builtin_amdgcn_perm(lo23, lo01, 0x07060302u);
+  d[2] = __builtin_amdgcn_perm(hi23, hi01, 0x05040100u);
+  d[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
+}
+
+template <int FMT, bool AMAX>
+__global__ __launch_bounds__(kThreads) void cast_transpose_vec_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, const int32_t* __restrict__ bias,
+    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ amax) {
+  __shared__ uint32_t T[kCtC][kCtR / 4 + 1];       // codes, column-major, 4 rows per dword
+  __shared__ uint32_t red[kThreads / kWave];
+  const int e = *bias;
+  const int64_t r0 = (int64_t)blockIdx.y * kCtR, c0 = (int64_t)blockIdx.x * kCtC;
+  const int cg = threadIdx.x & 7, rg = threadIdx.x >> 3;
+  const bool interior = r0 + kCtR <= rows && c0 + kCtC <= cols;
+  uint32_t amax_bits = 0;
+  uint2 o[4];
+  if (interior) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = r0 + 4 * rg + i;
+      const uint4 v = load_nt(reinterpret_cast<const uint4*>(x + r * ld + c0 + 8 * cg));
+      uint32_t m;
+      o[i] = cast_chunk<FP8_DT_BF16, FMT>(v, e, &m, true);
+      if (AMAX) amax_bits = amax_bits > m ? amax_bits : m;
+      const v2u_t ov = {o[i].x, o[i].y};
+      __builtin_nontemporal_store(ov, reinterpret_cast<v2u_t*>(q + r * ldq + c0 + 8 * cg));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t r = r0 + 4 * rg + i;
+      uint32_t w[2] = {0u, 0u};
+      if (r < rows) {
+        const char* xr = reinterpret_cast<const char*>(x) + r * ld * 2;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int64_t c = c0 + 8 * cg + k;
+          if (c < cols) {
+            float f;
+            const uint32_t bits = load_elem<FP8_DT_BF16>(xr, c, &f);
+            const uint32_t ab = bits & 0x7fffffffu;
+            if (AMAX) amax_bits = amax_bits > ab ? amax_bits : ab;
+            const uint32_t code = cast_elem<FMT>(bits, e);
+            q[r * ldq + c] = (uint8_t)code;
+            w[k / 4] |= code << (8 * (k % 4));
+          }
+        }
+      }
+      o[i] = make_uint2(w[0], w[1]);
+    }
+  }
+  uint32_t d[8];
+  {
+    uint32_t t4[4];
+    bytes_transpose4(o[0].x, o[1].x, o[2].x, o[3].x, t4);
+    d[0] = t4[0]; d[1] = t4[1]; d[2] = t4[2]; d[3] = t4[3];
+    bytes_transpose4(o[0].y, o[1].y, o[2].y, o[3].y, t4);
+    d[4] = t4[0]; d[5] = t4[1]; d[6] = t4[2]; d[7] = t4[3];
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) T[8 * cg + k][rg] = d[k];
+  __syncthreads();
+  const int j = threadIdx.x >> 2, sgm = threadIdx.x & 3;
+  const int64_t cT = c0 + j;
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = T[j][8 * sgm + i];
+  if (interior) {
+    v4u_t* dst = reinterpret_cast<v4u_t*>(qT + cT * ldqT + r0 + 32 * sgm);
+    const v4u_t lo = {w[0], w[1], w[2], w[3]}, hi = {w[4], w[5], w[6], w[7]};
+    __builtin_nontemporal_store(lo, dst);
+    __builtin_nontemporal_store(hi, dst + 1);
+  } else if (cT < cols) {
+#pragma unroll
+    for (int b = 0; b < 32; ++b) {
+      const int64_t r = r0 + 32 * sgm + b;
+      if (r < rows) qT[cT * ldqT + r] = (uint8_t)(w[b / 4] >> (8 * (b % 4)));
+    }
+  }
+  if (AMAX) block_max_to_global(amax_bits, red, amax);
+}
+
+// ---------------------------------------------------------------------------
 // MX cast: 1 x 32 blocks along cols.  Vector kernel: a block is 4 lanes
 // (bf16) or 8 lanes (f32) of 16-byte chunks; the block max is a DPP
 // reduction inside the lane group, the group's first lane stores the E8M0
@@ -418,7 +519,7 @@ static void launch_mx(const MxArgs& a, bool vec, hipStream_t s) {
 // column c, the two quarters of a 32-row block exchange their maxima through
 // LDS, and each lane writes its 16 codes as 16 contiguous bytes of qT row c.
 // ---------------------------------------------------------------------------
-template <int DT, int FMT>
+template <int DT, int FMT, bool VEC>
 __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
   __shared__ uint32_t tile[kTT][kTT + 1];          // fp32 bit patterns, padded
   __shared__ uint32_t pmax[4][kTT];                // per-quarter column maxima
@@ -430,15 +531,40 @@ __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
     const int tc = (threadIdx.x % 4) * 16;
     const int64_t r = r0 + tr;
     const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ld * ESZ;
+    if (VEC && r < a.rows && c0 + tc + 16 <= a.cols) {      // 16 elements = 2 (bf16) or 4 (f32) chunks
+      const uint4* src = reinterpret_cast<const uint4*>(xr + (c0 + tc) * ESZ);
+      if constexpr (DT == FP8_DT_BF16) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int64_t c = c0 + tc + j;
-      uint32_t bits = 0;
-      if (r < a.rows && c < a.cols) {
-        float f;
-        bits = load_elem<DT>(xr, c, &f);
+        for (int h = 0; h < 2; ++h) {
+          const uint4 v = load_nt(src + h);
+          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            tile[tr][tc + 8 * h + 2 * k] = w4[k] << 16;
+            tile[tr][tc + 8 * h + 2 * k + 1] = w4[k] & 0xffff0000u;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint4 v = load_nt(src + h);
+          tile[tr][tc + 4 * h] = v.x;
+          tile[tr][tc + 4 * h + 1] = v.y;
+          tile[tr][tc + 4 * h + 2] = v.z;
+          tile[tr][tc + 4 * h + 3] = v.w;
+        }
       }
-      tile[tr][tc + j] = bits;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t c = c0 + tc + j;
+        uint32_t bits = 0;
+        if (r < a.rows && c < a.cols) {
+          float f;
+          bits = load_elem<DT>(xr, c, &f);
+        }
+        tile[tr][tc + j] = bits;
+      }
     }
   }
   __syncthreads();
@@ -499,6 +625,24 @@ int fp8_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
   if (n > 0 && !x) return FP8_ERR_NULL;
   if (amax_out) zero_float_async(amax_out, stream);
   if (n == 0) return launch_status();
+  if (qT && dtype == FP8_DT_BF16 && aligned(x, 16) && ld % 8 == 0 && aligned(q, 8) && ldq % 8 == 0 &&
+      aligned(qT, 16) && ldqT % 16 == 0 && (rows + kCtR - 1) / kCtR <= 65535) {
+    const dim3 grid((unsigned)((cols + kCtC - 1) / kCtC), (unsigned)((rows + kCtR - 1) / kCtR));
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+#define SFP8_CTV(FMT)                                                                                         \
+  do {                                                                                                        \
+    if (amax_out)                                                                                             \
+      hipLaunchKernelGGL((cast_transpose_vec_kernel<FMT, true>), grid, dim3(kThreads), 0, stream, xb, rows,   \
+                         cols, ld, bias, q, ldq, qT, ldqT, amax_out);                                         \
+    else                                                                                                      \
+      hipLaunchKernelGGL((cast_transpose_vec_kernel<FMT, false>), grid, dim3(kThreads), 0, stream, xb, rows,  \
+                         cols, ld, bias, q, ldq, qT, ldqT, amax_out);                                         \
+  } while (0)
+    if (fmt == FP8_E4M3) SFP8_CTV(FP8_E4M3);
+    else SFP8_CTV(FP8_E5M2);
+#undef SFP8_CTV
+    return launch_status();
+  }
   if (qT) {
     const dim3 grid((unsigned)((cols + kTT - 1) / kTT), (unsigned)((rows + kTT - 1) / kTT));
     if (grid.y > 65535) return FP8_ERR_SHAPE;
@@ -605,13 +749,21 @@ int mx_quantize_t(const void* x, int dtype, int64_t rows, int64_t cols, int64_t 
   a.scales = scalesT;
   a.lds = ld_scales;
   const dim3 grid((unsigned)((cols + kTT - 1) / kTT), (unsigned)gy);
+  // 16-byte loads when every row start is 16-byte aligned
+  const bool vec = aligned(x, 16) && (ld * dtype_size(dtype)) % 16 == 0;
+#define SFP8_MXT(DT, FMT)                                                                              \
+  do {                                                                                                 \
+    if (vec) hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, true>), grid, dim3(kThreads), 0, stream, a); \
+    else hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, false>), grid, dim3(kThreads), 0, stream, a);   \
+  } while (0)
   if (dtype == FP8_DT_BF16) {
-    if (fmt == FP8_E4M3) hipLaunchKernelGGL((mx_transpose_kernel<FP8_DT_BF16, FP8_E4M3>), grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((mx_transpose_kernel<FP8_DT_BF16, FP8_E5M2>), grid, dim3(kThreads), 0, stream, a);
+    if (fmt == FP8_E4M3) SFP8_MXT(FP8_DT_BF16, FP8_E4M3);
+    else SFP8_MXT(FP8_DT_BF16, FP8_E5M2);
   } else {
-    if (fmt == FP8_E4M3) hipLaunchKernelGGL((mx_transpose_kernel<FP8_DT_F32, FP8_E4M3>), grid, dim3(kThreads), 0, stream, a);
-    else hipLaunchKernelGGL((mx_transpose_kernel<FP8_DT_F32, FP8_E5M2>), grid, dim3(kThreads), 0, stream, a);
+    if (fmt == FP8_E4M3) SFP8_MXT(FP8_DT_F32, FP8_E4M3);
+    else SFP8_MXT(FP8_DT_F32, FP8_E5M2);
   }
+#undef SFP8_MXT
   return launch_status();
 }
 

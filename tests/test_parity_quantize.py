@@ -130,8 +130,12 @@ def test_cast_strided_ragged_and_unaligned(dtype):
             assert np.all(hb[:, :3] == 0xAA) and np.all(hb[:, 3 + sub.shape[1]:] == 0xAA)
 
 
-@pytest.mark.parametrize("shape", [(256, 768), (130, 200), (1, 77), (64, 64), (300, 17)])
+@pytest.mark.parametrize("shape", [(256, 768), (130, 200), (1, 77), (64, 64), (300, 17), (384, 200),
+                                   (272, 1024)])
 def test_cast_transpose(shape):
+    """Vector kernel (aligned bf16 rows: whole 128 x 64 tiles, a ragged column
+    tile, ragged row tiles, a matrix smaller than one tile) and the generic
+    kernel (unaligned strides)."""
     rng = np.random.default_rng(6)
     from workloads import f32_to_bf16_bits
     bits = f32_to_bf16_bits((rng.standard_normal(shape) * 0.02).astype(np.float32))
@@ -144,6 +148,27 @@ def test_cast_transpose(shape):
         assert np.array_equal(host(q), ref)
         assert np.array_equal(host(qT), ref.T)
         assert host(am)[0] == oracle.amax(vals)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: f.name)
+def test_cast_transpose_special_values(fmt):
+    """NaN, +-Inf, -0, saturating and subnormal inputs through the vector
+    cast-transpose (256 x 128, bias 3), with the fused amax (NaN)."""
+    rng = np.random.default_rng(8)
+    from workloads import f32_to_bf16_bits
+    bits = f32_to_bf16_bits((rng.standard_normal((256, 128)) * 30).astype(np.float32))
+    bits[0, 0] = 0x7FC0
+    bits[5, 9] = 0xFF80
+    bits[17, 70] = 0x7F80
+    bits[100, 33] = 0x8000
+    bits[200, 127] = 0x0003
+    bits[255, 64] = 0x7F7F
+    vals = oracle.bf16_bits_to_f64(bits)
+    q, qT, am = sq.fp8_quantize(bf16_dev(bits), fmt.code, i32_dev(3), transpose=True, want_amax=True)
+    ref = oracle.quantize(vals, fmt, 3)
+    assert np.array_equal(host(q), ref)
+    assert np.array_equal(host(qT), ref.T)
+    assert np.isnan(host(am)[0])
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=lambda f: f.name)
