@@ -98,6 +98,64 @@ def cpu_baseline(xb, wb, target_s: float):
     }
 
 
+def backward_extras(dev, reps: int = 5):
+    """The 7B-MLP down-projection backward (dY [4096 x 11008], W [11008 x
+    4096], X [4096 x 4096]) as the linear layer runs it: transposed casts,
+    then dX = dY W and dW = dY^T X as K-contiguous (TN) products; per-tensor
+    (E5M2 gradient x E4M3) and MX.  Synthetic N(0, s) inputs drawn on the
+    device; timed outside the headline step."""
+    import torch
+    import scaled_quantize_fp8_amd as sq
+    T, H, F = 4096, 4096, 11008
+    dy = (torch.randn(T, F, device=dev) * 1e-3).to(torch.bfloat16)
+    w = (torch.randn(F, H, device=dev) * 0.02).to(torch.bfloat16)
+    x = torch.randn(T, H, device=dev).to(torch.bfloat16)
+    bdy = torch.tensor([10], dtype=torch.int32, device=dev)
+    bw = torch.tensor([4], dtype=torch.int32, device=dev)
+    bx = torch.tensor([6], dtype=torch.int32, device=dev)
+    qdy, qdyT = torch.empty(T, F, dtype=torch.uint8, device=dev), torch.empty(F, T, dtype=torch.uint8, device=dev)
+    qw, qwT = torch.empty(F, H, dtype=torch.uint8, device=dev), torch.empty(H, F, dtype=torch.uint8, device=dev)
+    qx, qxT = torch.empty(T, H, dtype=torch.uint8, device=dev), torch.empty(H, T, dtype=torch.uint8, device=dev)
+    dx = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    dw = torch.empty(F, H, dtype=torch.bfloat16, device=dev)
+    pt = [("cast_t_dY", lambda: sq.fp8_quantize(dy, sq.E5M2, bdy, q=qdy, qT=qdyT), 4 * T * F),
+          ("cast_t_W", lambda: sq.fp8_quantize(w, sq.E4M3, bw, q=qw, qT=qwT), 4 * F * H),
+          ("cast_t_X", lambda: sq.fp8_quantize(x, sq.E4M3, bx, q=qx, qT=qxT), 4 * T * H),
+          ("gemm_dX", lambda: sq.fp8_scaled_gemm(qdy, sq.E5M2, bdy, qwT, sq.E4M3, bw, out=dx), None),
+          ("gemm_dW", lambda: sq.fp8_scaled_gemm(qdyT, sq.E5M2, bdy, qxT, sq.E4M3, bx, out=dw), None)]
+    mq, ms_ = torch.empty(T, F, dtype=torch.uint8, device=dev), torch.empty(T, F // 32, dtype=torch.uint8, device=dev)
+    mqT, msT = torch.empty(F, T, dtype=torch.uint8, device=dev), torch.empty(F, T // 32, dtype=torch.uint8, device=dev)
+    mwT, mswT = torch.empty(H, F, dtype=torch.uint8, device=dev), torch.empty(H, F // 32, dtype=torch.uint8, device=dev)
+    mxT, msxT = torch.empty(H, T, dtype=torch.uint8, device=dev), torch.empty(H, T // 32, dtype=torch.uint8, device=dev)
+    mx = [("mx_cast_dY", lambda: sq.mx_quantize(dy, sq.E5M2, q=mq, scales=ms_), (3 + 1 / 32) * T * F),
+          ("mx_cast_t_dY", lambda: sq.mx_quantize_t(dy, sq.E5M2, qT=mqT, scalesT=msT), (3 + 1 / 32) * T * F),
+          ("mx_cast_t_W", lambda: sq.mx_quantize_t(w, sq.E4M3, qT=mwT, scalesT=mswT), (3 + 1 / 32) * F * H),
+          ("mx_cast_t_X", lambda: sq.mx_quantize_t(x, sq.E4M3, qT=mxT, scalesT=msxT), (3 + 1 / 32) * T * H),
+          ("mx_gemm_dX", lambda: sq.mx_scaled_gemm(mq, sq.E5M2, ms_, mwT, sq.E4M3, mswT, out=dx), None),
+          ("mx_gemm_dW", lambda: sq.mx_scaled_gemm(mqT, sq.E5M2, msT, mxT, sq.E4M3, msxT, out=dw), None)]
+    flops = 2.0 * T * H * F
+    out = {"shapes": "dY [4096 x 11008] E5M2, W [11008 x 4096], X [4096 x 4096] E4M3; bf16 out"}
+    for tag, ops in (("per_tensor", pt), ("mx", mx)):
+        total = 0.0
+        res = {}
+        for name, fn, byts in ops:
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            total += ms
+            res[name + ("_GBps" if byts else "_TFLOPs")] = round((byts / ms / 1e6) if byts else (flops / ms / 1e9), 1)
+        res["backward_TFLOPs"] = round(2 * flops / total / 1e9, 1)
+        res["ms"] = round(total, 4)
+        out[tag] = res
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -258,6 +316,8 @@ def main():
         stream[k] = {"achieved": round(v, 1), "frac": round(v / PEAK_HBM_GBS, 4),
                      "frac_of_copy": round(v / copy_GBps, 4)}
 
+    extras = {"backward_7b_mlp": backward_extras(dev)}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(xb, wb, args.cpu_seconds)
@@ -283,6 +343,7 @@ def main():
         "roofline": roofline,
         "stream_roofline": stream,
         "cpu_baseline": cpu,
+        "extras": extras,
         "input_generation_s": round(gen_s, 1),
     }
     print(json.dumps(out), flush=True)
