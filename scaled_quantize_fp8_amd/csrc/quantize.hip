@@ -513,95 +513,97 @@ static void launch_mx(const MxArgs& a, bool vec, hipStream_t s) {
 // Transposed MX cast: blocks of 32 consecutive ROWS of one column, written as
 // qT [cols x rows] with scalesT [cols x rows/32], i.e. the MX cast of x^T
 // (for a GEMM that contracts over `rows`, such as a weight gradient whose K
-// is the token axis).  64 x 64 tiles: each lane loads 16 consecutive elements
-// of one tile row into an LDS tile of fp32 bit patterns; then lane (c, q)
-// (q = lane / 64, one wave per quarter) takes rows 16q..16q+15 of tile
-// column c, the two quarters of a 32-row block exchange their maxima through
-// LDS, and each lane writes its 16 codes as 16 contiguous bytes of qT row c.
+// is the token axis).  128 x 64 tiles: the workgroup stages the tile as fp32
+// bit patterns in LDS (consecutive lanes load consecutive 16-byte chunks of
+// a row), then lane (c, b) owns the whole 32-row block b of tile column c:
+// it reduces the block's maximum, casts its 32 elements and writes them as
+// 32 contiguous bytes of qT row c, so each qT row receives one full 128-byte
+// line per workgroup.
 // ---------------------------------------------------------------------------
+constexpr int kMtR = 128, kMtC = 64;
+
 template <int DT, int FMT, bool VEC>
 __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
-  __shared__ uint32_t tile[kTT][kTT + 1];          // fp32 bit patterns, padded
-  __shared__ uint32_t pmax[4][kTT];                // per-quarter column maxima
+  // rows padded to 68 dwords: 16-byte aligned rows for the staging writes,
+  // and the column reads (one row per lane group) stay conflict-free
+  __shared__ __attribute__((aligned(16))) uint32_t tile[kMtR][kMtC + 4];
   constexpr int ESZ = In<DT>::kEsz;
-  const int64_t r0 = (int64_t)blockIdx.y * kTT;
-  const int64_t c0 = (int64_t)blockIdx.x * kTT;
-  {
-    const int tr = threadIdx.x / 4;
-    const int tc = (threadIdx.x % 4) * 16;
+  constexpr int EPC = In<DT>::kEpc;                // elements per 16-byte chunk
+  constexpr int CPR = kMtC / EPC;                  // chunks per tile row
+  const int64_t r0 = (int64_t)blockIdx.y * kMtR;
+  const int64_t c0 = (int64_t)blockIdx.x * kMtC;
+  const bool full_cols = c0 + kMtC <= a.cols;
+#pragma unroll
+  for (int k = 0; k < kMtR * CPR / kThreads; ++k) {
+    const int idx = threadIdx.x + k * kThreads;
+    const int tr = idx / CPR, ch = idx % CPR;
     const int64_t r = r0 + tr;
     const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ld * ESZ;
-    if (VEC && r < a.rows && c0 + tc + 16 <= a.cols) {      // 16 elements = 2 (bf16) or 4 (f32) chunks
-      const uint4* src = reinterpret_cast<const uint4*>(xr + (c0 + tc) * ESZ);
+    uint4* trow = reinterpret_cast<uint4*>(&tile[tr][ch * EPC]);
+    if (VEC && full_cols && r < a.rows) {
+      const uint4 v = load_nt(reinterpret_cast<const uint4*>(xr + (c0 + ch * EPC) * ESZ));
       if constexpr (DT == FP8_DT_BF16) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint4 v = load_nt(src + h);
-          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            tile[tr][tc + 8 * h + 2 * k] = w4[k] << 16;
-            tile[tr][tc + 8 * h + 2 * k + 1] = w4[k] & 0xffff0000u;
-          }
-        }
+        trow[0] = make_uint4(v.x << 16, v.x & 0xffff0000u, v.y << 16, v.y & 0xffff0000u);
+        trow[1] = make_uint4(v.z << 16, v.z & 0xffff0000u, v.w << 16, v.w & 0xffff0000u);
       } else {
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          const uint4 v = load_nt(src + h);
-          tile[tr][tc + 4 * h] = v.x;
-          tile[tr][tc + 4 * h + 1] = v.y;
-          tile[tr][tc + 4 * h + 2] = v.z;
-          tile[tr][tc + 4 * h + 3] = v.w;
-        }
+        trow[0] = v;
       }
     } else {
+      uint32_t w[EPC];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int64_t c = c0 + tc + j;
-        uint32_t bits = 0;
+      for (int j = 0; j < EPC; ++j) {
+        const int64_t c = c0 + ch * EPC + j;
+        w[j] = 0u;
         if (r < a.rows && c < a.cols) {
           float f;
-          bits = load_elem<DT>(xr, c, &f);
+          w[j] = load_elem<DT>(xr, c, &f);
         }
-        tile[tr][tc + j] = bits;
       }
+#pragma unroll
+      for (int h = 0; h < EPC / 4; ++h) trow[h] = make_uint4(w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]);
     }
   }
   __syncthreads();
-  const int c = threadIdx.x % kTT;
-  const int qq = threadIdx.x / kTT;                // 0..3: rows 16 qq .. 16 qq + 15
-  uint32_t v[16];
-  uint32_t m = 0;
+  const int c = threadIdx.x % kMtC;
+  const int blk = threadIdx.x / kMtC;              // 0..3: tile rows 32 blk .. 32 blk + 31
+  const int64_t col = c0 + c;                      // qT row
+  const int64_t rr = r0 + 32 * blk;                // first qT column of this block
+  if (col >= a.cols || rr >= a.rows) return;       // rows % 32 == 0: a block exists whole or not at all
+  uint32_t v[32];
+  uint32_t bm = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    v[i] = tile[16 * qq + i][c];
+  for (int i = 0; i < 32; ++i) {
+    v[i] = tile[32 * blk + i][c];
     const uint32_t ab = v[i] & 0x7fffffffu;
-    m = m > ab ? m : ab;
+    bm = bm > ab ? bm : ab;
   }
-  pmax[qq][c] = m;
-  __syncthreads();
-  const uint32_t o = pmax[qq ^ 1][c];
-  const uint32_t bm = m > o ? m : o;
   int e;
   uint32_t code;
   block_exponent<FMT>(bm, &e, &code);
-  const int64_t col = c0 + c;                      // qT row
-  const int64_t rr = r0 + 16 * qq;                 // first qT column of this lane
-  if (col < a.cols && rr < a.rows) {               // rows % 32 == 0: all 16 rows exist
-    uint32_t w[4];
+  uint32_t w[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      w[k] = cast_elem<FMT>(v[4 * k], e) | (cast_elem<FMT>(v[4 * k + 1], e) << 8) |
-             (cast_elem<FMT>(v[4 * k + 2], e) << 16) | (cast_elem<FMT>(v[4 * k + 3], e) << 24);
-    uint8_t* dst = a.q + col * a.ldq + rr;
-    if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-    } else {
+  for (int k = 0; k < 8; ++k)
+    w[k] = cvt4<FMT>(__builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k]), e),
+                     __builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k + 1]), e),
+                     __builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k + 2]), e),
+                     __builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k + 3]), e));
+  if (__builtin_expect(bm > 0x7f800000u, 0)) {      // a NaN in the block: patch its codes
 #pragma unroll
-      for (int k = 0; k < 16; ++k) dst[k] = (uint8_t)(w[k / 4] >> (8 * (k % 4)));
-    }
-    if ((qq & 1) == 0) a.scales[col * a.lds + rr / 32] = (uint8_t)code;
+    for (int i = 0; i < 32; ++i)
+      if ((v[i] & 0x7fffffffu) > 0x7f800000u)
+        w[i / 4] = (w[i / 4] & ~(0xffu << (8 * (i % 4)))) | (nan_code_f32(v[i]) << (8 * (i % 4)));
   }
+  // cached stores: the four blocks of a qT line come from four waves, and L2
+  // merges them into one full line before it is written back
+  uint8_t* dst = a.q + col * a.ldq + rr;
+  if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+    reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) dst[k] = (uint8_t)(w[k / 4] >> (8 * (k % 4)));
+  }
+  a.scales[col * a.lds + rr / 32] = (uint8_t)code;
 }
 
 }  // namespace sfp8
@@ -737,7 +739,7 @@ int mx_quantize_t(const void* x, int dtype, int64_t rows, int64_t cols, int64_t 
   if (st) return st;
   if (rows * cols == 0) return FP8_OK;
   if (!x) return FP8_ERR_NULL;
-  const int64_t gy = (rows + kTT - 1) / kTT;
+  const int64_t gy = (rows + kMtR - 1) / kMtR;
   if (gy > 65535) return FP8_ERR_SHAPE;
   MxArgs a;
   a.x = x;
@@ -748,7 +750,7 @@ int mx_quantize_t(const void* x, int dtype, int64_t rows, int64_t cols, int64_t 
   a.ldq = ldqT;
   a.scales = scalesT;
   a.lds = ld_scales;
-  const dim3 grid((unsigned)((cols + kTT - 1) / kTT), (unsigned)gy);
+  const dim3 grid((unsigned)((cols + kMtC - 1) / kMtC), (unsigned)gy);
   // 16-byte loads when every row start is 16-byte aligned
   const bool vec = aligned(x, 16) && (ld * dtype_size(dtype)) % 16 == 0;
 #define SFP8_MXT(DT, FMT)                                                                              \
