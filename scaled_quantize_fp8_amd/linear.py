@@ -29,7 +29,10 @@ Recipes:
                pushed into the history afterwards.  The first step has no
                history and pushes its own amax first (current scaling);
     "mx"       per-block: 1 x 32 blocks along each product's K axis, E8M0
-               block scales.
+               block scales;
+    "constant" one fixed bias for every tensor (the fixed-scaling baseline
+               the pages compare FP8-AMAX against, FP8-CSCALE; "Research
+               questions" / "Key findings" of the paper review page).
 """
 
 from __future__ import annotations
@@ -42,7 +45,7 @@ from . import (E4M3, E5M2, fp8_amax, fp8_compute_scale, fp8_compute_scale_delaye
                fp8_history_init, fp8_history_push, fp8_quantize, fp8_scaled_gemm, mx_quantize,
                mx_quantize_t, mx_scaled_gemm)
 
-RECIPES = ("current", "delayed", "mx")
+RECIPES = ("current", "delayed", "mx", "constant")
 
 
 class _History:
@@ -58,8 +61,11 @@ class _History:
 
 
 def _per_tensor_cast(x2: torch.Tensor, fmt, recipe: str, margin: int, hist: _History | None,
-                     transpose: bool):
+                     transpose: bool, const_bias: torch.Tensor | None = None):
     """Bias and FP8 codes (plus the transposed copy) of one tensor."""
+    if recipe == "constant":
+        q, qT, _ = fp8_quantize(x2, fmt, const_bias, transpose=transpose)
+        return const_bias, q, qT
     if recipe == "current":
         bias, _, _ = fp8_compute_scale(fp8_amax(x2), fmt, margin)
         q, qT, _ = fp8_quantize(x2, fmt, bias, transpose=transpose)
@@ -95,8 +101,8 @@ class Fp8LinearFunction(torch.autograd.Function):
                 qxT, sxT = mx_quantize_t(x2, E4M3)
                 ctx.save_for_backward(qwT, swT, qxT, sxT)
         else:
-            bx, qx, qxT = _per_tensor_cast(x2, E4M3, recipe, layer.margin, layer._hx, True)
-            bw, qw, qwT = _per_tensor_cast(w, E4M3, recipe, layer.margin, layer._hw, True)
+            bx, qx, qxT = _per_tensor_cast(x2, E4M3, recipe, layer.margin, layer._hx, True, layer._bias)
+            bw, qw, qwT = _per_tensor_cast(w, E4M3, recipe, layer.margin, layer._hw, True, layer._bias)
             y, amax = fp8_scaled_gemm(qx, E4M3, bx, qw, E4M3, bw, out_dtype=x.dtype, want_amax=True)
             ctx.save_for_backward(qwT, bw, qxT, bx)
         layer.last_output_amax = amax
@@ -125,7 +131,7 @@ class Fp8LinearFunction(torch.autograd.Function):
         else:
             qwT, bw, qxT, bx = ctx.saved_tensors
             bdy, qdy, qdyT = _per_tensor_cast(dy2, E5M2, layer.recipe, layer.margin, layer._hdy,
-                                              ctx.needs_input_grad[1])
+                                              ctx.needs_input_grad[1], layer._bias)
             if ctx.needs_input_grad[0]:
                 dx, _ = fp8_scaled_gemm(qdy, E5M2, bdy, qwT, E4M3, bw, out_dtype=ctx.dtype)
             if ctx.needs_input_grad[1]:
@@ -137,6 +143,8 @@ class Fp8LinearFunction(torch.autograd.Function):
 
 class Fp8Linear(torch.nn.Module):
     """Linear layer y = x W^T whose three products run in FP8 on the GPU.
+    `bias` is the fixed exponent bias of the "constant" recipe (scale 2^bias
+    for every tensor); the layer has no additive bias.
 
     in_features, out_features and the token count must be multiples of 32
     (the MX block; the per-tensor path needs 16, and multiples of 128 take the
@@ -144,7 +152,7 @@ class Fp8Linear(torch.nn.Module):
     reduced in the GEMM's epilogue, for a next layer's scale."""
 
     def __init__(self, in_features: int, out_features: int, recipe: str = "current",
-                 margin: int = 0, history: int = 16, device=None, dtype=torch.bfloat16):
+                 margin: int = 0, history: int = 16, bias: int = 0, device=None, dtype=torch.bfloat16):
         super().__init__()
         if recipe not in RECIPES:
             raise ValueError(f"recipe must be one of {RECIPES}")
@@ -158,6 +166,12 @@ class Fp8Linear(torch.nn.Module):
         torch.nn.init.kaiming_uniform_(self.weight, a=math.sqrt(5))
         self.last_output_amax = None
         self._hx = self._hw = self._hdy = None
+        if recipe == "constant":
+            if not -126 <= int(bias) <= 126:
+                raise ValueError("bias must lie in [-126, 126]")
+            self.register_buffer("_bias", torch.tensor([int(bias)], dtype=torch.int32, device=self.weight.device))
+        else:
+            self._bias = None
         if recipe == "delayed":
             dev = self.weight.device
             self._hx, self._hw, self._hdy = (_History(history, dev), _History(history, dev),

@@ -96,6 +96,19 @@ def test_linear_delayed_scaling_three_steps():
 
 
 @pytest.mark.gpu
+def test_linear_constant_bias_matches_oracle():
+    """The fixed-scaling recipe: bias -1 for every tensor, no amax pass."""
+    need_gpu()
+    x, w, dy = _tensors()
+    layer = Fp8Linear(IN, OUT, recipe="constant", bias=-1, device=DEV)
+    with torch.no_grad():
+        layer.weight.copy_(_dev(w))
+    say("fp8 linear, constant bias -1")
+    y, dx, dw, _ = _run(layer, x, dy)
+    _check_pt(y, dx, dw, x, w, dy, -1, -1, -1)
+
+
+@pytest.mark.gpu
 def test_linear_mx_matches_oracle():
     need_gpu()
     x, w, dy = _tensors()
@@ -134,6 +147,8 @@ def test_linear_batched_input_shape():
 def test_linear_argument_checks():
     with pytest.raises(ValueError):
         Fp8Linear(IN, OUT, recipe="fp16")
+    with pytest.raises(ValueError):
+        Fp8Linear(IN, OUT, recipe="constant", bias=200)
     with pytest.raises(ValueError):
         Fp8Linear(100, OUT)
     layer = Fp8Linear(IN, OUT)                       # CPU parameters: the product path refuses them
