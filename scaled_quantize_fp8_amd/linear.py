@@ -61,23 +61,29 @@ class _History:
 
 
 def _per_tensor_cast(x2: torch.Tensor, fmt, recipe: str, margin: int, hist: _History | None,
-                     transpose: bool, const_bias: torch.Tensor | None = None):
-    """Bias and FP8 codes (plus the transposed copy) of one tensor."""
+                     transpose: bool, const_bias: torch.Tensor | None = None, log=None, name: str = ""):
+    """Bias and FP8 codes (plus the transposed copy) of one tensor; with a
+    `log` list, appends (name, bias, amax) as device scalars (amax None for
+    the constant recipe)."""
+    amax = None
     if recipe == "constant":
-        q, qT, _ = fp8_quantize(x2, fmt, const_bias, transpose=transpose)
-        return const_bias, q, qT
-    if recipe == "current":
-        bias, _, _ = fp8_compute_scale(fp8_amax(x2), fmt, margin)
+        bias = const_bias
         q, qT, _ = fp8_quantize(x2, fmt, bias, transpose=transpose)
-        return bias, q, qT
-    # delayed: the first step bootstraps the history with its own amax
-    if hist.steps == 0:
-        fp8_history_push(hist.hist, hist.state, fp8_amax(x2))
-    bias, _, _ = fp8_compute_scale_delayed(hist.hist, hist.state, fmt, margin)
-    q, qT, amax = fp8_quantize(x2, fmt, bias, transpose=transpose, want_amax=True)
-    if hist.steps > 0:
-        fp8_history_push(hist.hist, hist.state, amax)
-    hist.steps += 1
+    elif recipe == "current":
+        amax = fp8_amax(x2)
+        bias, _, _ = fp8_compute_scale(amax, fmt, margin)
+        q, qT, _ = fp8_quantize(x2, fmt, bias, transpose=transpose)
+    else:
+        # delayed: the first step bootstraps the history with its own amax
+        if hist.steps == 0:
+            fp8_history_push(hist.hist, hist.state, fp8_amax(x2))
+        bias, _, _ = fp8_compute_scale_delayed(hist.hist, hist.state, fmt, margin)
+        q, qT, amax = fp8_quantize(x2, fmt, bias, transpose=transpose, want_amax=True)
+        if hist.steps > 0:
+            fp8_history_push(hist.hist, hist.state, amax)
+        hist.steps += 1
+    if log is not None:
+        log.append((name, bias.clone(), None if amax is None else amax.clone()))
     return bias, q, qT
 
 
@@ -101,8 +107,10 @@ class Fp8LinearFunction(torch.autograd.Function):
                 qxT, sxT = mx_quantize_t(x2, E4M3)
                 ctx.save_for_backward(qwT, swT, qxT, sxT)
         else:
-            bx, qx, qxT = _per_tensor_cast(x2, E4M3, recipe, layer.margin, layer._hx, True, layer._bias)
-            bw, qw, qwT = _per_tensor_cast(w, E4M3, recipe, layer.margin, layer._hw, True, layer._bias)
+            bx, qx, qxT = _per_tensor_cast(x2, E4M3, recipe, layer.margin, layer._hx, True, layer._bias,
+                                           layer._log, "x")
+            bw, qw, qwT = _per_tensor_cast(w, E4M3, recipe, layer.margin, layer._hw, True, layer._bias,
+                                           layer._log, "w")
             y, amax = fp8_scaled_gemm(qx, E4M3, bx, qw, E4M3, bw, out_dtype=x.dtype, want_amax=True)
             ctx.save_for_backward(qwT, bw, qxT, bx)
         layer.last_output_amax = amax
@@ -131,7 +139,7 @@ class Fp8LinearFunction(torch.autograd.Function):
         else:
             qwT, bw, qxT, bx = ctx.saved_tensors
             bdy, qdy, qdyT = _per_tensor_cast(dy2, E5M2, layer.recipe, layer.margin, layer._hdy,
-                                              ctx.needs_input_grad[1], layer._bias)
+                                              ctx.needs_input_grad[1], layer._bias, layer._log, "dy")
             if ctx.needs_input_grad[0]:
                 dx, _ = fp8_scaled_gemm(qdy, E5M2, bdy, qwT, E4M3, bw, out_dtype=ctx.dtype)
             if ctx.needs_input_grad[1]:
@@ -152,7 +160,8 @@ class Fp8Linear(torch.nn.Module):
     reduced in the GEMM's epilogue, for a next layer's scale."""
 
     def __init__(self, in_features: int, out_features: int, recipe: str = "current",
-                 margin: int = 0, history: int = 16, bias: int = 0, device=None, dtype=torch.bfloat16):
+                 margin: int = 0, history: int = 16, bias: int = 0, log_scales: bool = False,
+                 device=None, dtype=torch.bfloat16):
         super().__init__()
         if recipe not in RECIPES:
             raise ValueError(f"recipe must be one of {RECIPES}")
@@ -166,6 +175,9 @@ class Fp8Linear(torch.nn.Module):
         torch.nn.init.kaiming_uniform_(self.weight, a=math.sqrt(5))
         self.last_output_amax = None
         self._hx = self._hw = self._hdy = None
+        if log_scales and recipe == "mx":
+            raise ValueError("scale logging covers the per-tensor recipes")
+        self._log = [] if log_scales else None
         if recipe == "constant":
             if not -126 <= int(bias) <= 126:
                 raise ValueError("bias must lie in [-126, 126]")
@@ -186,6 +198,32 @@ class Fp8Linear(torch.nn.Module):
         if x.dtype != self.weight.dtype:
             raise TypeError("input and weight dtypes differ")
         return Fp8LinearFunction.apply(x, self.weight, self)
+
+    def scale_history(self) -> dict:
+        """Per-step (bias, amax) of each tensor ("x", "w", "dy") since the
+        layer was built or the log cleared, in step order; copies the logged
+        device scalars to the host (one synchronization)."""
+        if self._log is None:
+            raise RuntimeError("the layer was built without log_scales=True")
+        out = {"x": [], "w": [], "dy": []}
+        for name, b, a in self._log:
+            out[name].append((int(b.cpu()[0]), None if a is None else float(a.cpu()[0])))
+        return out
+
+    def bias_histogram(self) -> dict:
+        """Count of steps per bias value, for each tensor: the per-tensor scale
+        distribution over the logged steps."""
+        hist = {}
+        for name, rows in self.scale_history().items():
+            h = {}
+            for b, _ in rows:
+                h[b] = h.get(b, 0) + 1
+            hist[name] = dict(sorted(h.items()))
+        return hist
+
+    def clear_scale_log(self) -> None:
+        if self._log is not None:
+            self._log.clear()
 
     def extra_repr(self) -> str:
         return f"in_features={self.in_features}, out_features={self.out_features}, recipe={self.recipe}"

@@ -134,6 +134,40 @@ def test_linear_mx_matches_oracle():
 
 
 @pytest.mark.gpu
+def test_linear_scale_log_16_delayed_steps():
+    """The delayed-scaling workload of the 7B attention projection (activation
+    scales drawn per step, 0.1% outliers x50), 16 steps at 256 tokens: the
+    logged per-step biases and amaxes of x, w and dy equal the oracle's
+    history, and the histogram counts every step once."""
+    need_gpu()
+    layer = Fp8Linear(IN, OUT, recipe="delayed", history=16, log_scales=True, device=DEV)
+    wv = oracle.bf16_bits_to_f64(make("c2", "W", shape=(OUT, IN)))
+    with torch.no_grad():
+        layer.weight.copy_(_dev(wv))
+    hx, hw, hdy = oracle.DelayedScaling(16), oracle.DelayedScaling(16), oracle.DelayedScaling(16)
+    want = {"x": [], "w": [], "dy": []}
+    for step in range(16):
+        xv = oracle.bf16_bits_to_f64(make("c2", "X", step=step, shape=(T, IN)))
+        dyv = oracle.bf16_bits_to_f64(make("c3", "dY", step=step, shape=(T, OUT)))
+        layer.weight.grad = None
+        say(f"scale log step {step}")
+        _run(layer, xv, dyv)
+        for name, h, v, fmt in (("x", hx, xv, E4M3), ("w", hw, wv, E4M3), ("dy", hdy, dyv, E5M2)):
+            if step == 0:
+                h.push(oracle.amax(v))
+            want[name].append((h.bias(fmt), oracle.amax(v)))
+            if step > 0:
+                h.push(oracle.amax(v))
+    got = layer.scale_history()
+    for name in ("x", "w", "dy"):
+        assert [b for b, _ in got[name]] == [b for b, _ in want[name]], name
+        assert [a for _, a in got[name]] == [a for _, a in want[name]], name
+    hist = layer.bias_histogram()
+    assert all(sum(h.values()) == 16 for h in hist.values())
+    assert len(hist["x"]) > 1                      # the activation scale moved
+
+
+@pytest.mark.gpu
 def test_linear_batched_input_shape():
     need_gpu()
     layer = Fp8Linear(IN, OUT, device=DEV)
@@ -149,6 +183,10 @@ def test_linear_argument_checks():
         Fp8Linear(IN, OUT, recipe="fp16")
     with pytest.raises(ValueError):
         Fp8Linear(IN, OUT, recipe="constant", bias=200)
+    with pytest.raises(ValueError):
+        Fp8Linear(IN, OUT, recipe="mx", log_scales=True)
+    with pytest.raises(RuntimeError):
+        Fp8Linear(IN, OUT).scale_history()
     with pytest.raises(ValueError):
         Fp8Linear(100, OUT)
     layer = Fp8Linear(IN, OUT)                       # CPU parameters: the product path refuses them
