@@ -455,6 +455,12 @@ __device__ __forceinline__ void dma_b128_so(v4i srd, uint32_t lds_addr, uint32_t
                :: "v"(off), "s"(lds_addr), "s"(srd), "s"(soff) : "memory", "m0");
 }
 
+// 4 bytes per lane from buffer offset off + soff to LDS lds_addr + 4 * lane.
+__device__ __forceinline__ void dma_b32_so(v4i srd, uint32_t lds_addr, uint32_t off, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %0, %2, %3 offen lds"
+               :: "v"(off), "s"(lds_addr), "s"(srd), "s"(soff) : "memory", "m0");
+}
+
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N> __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
@@ -556,6 +562,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // MX scales, 4 stages per copy: [group slot][operand][tile row][4 dwords]
   __shared__ __attribute__((aligned(16))) uint32_t s_scale[MX ? 2 * 2 * BM * 4 : 1];
   __shared__ uint32_t red[kGemmThreads / kWave];
+  __shared__ uint32_t pf_sink[64];                  // landing words of the L2 prefetch (never read)
   constexpr int kRegB = 2 * kTileBytes;             // op(B) region offset (64 KiB)
   constexpr int kSlot = kTileBytes;                 // 32 KiB per slot per operand
   constexpr int kFrag = 32 * BK;                    // 4 KiB between 32-row fragments
@@ -620,6 +627,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // tile row 64 w + L of each operand.  Group G covers stages 4G .. 4G+3 and
   // is read from byte min(16 G, nkb - 16) of the row, so the last, partial
   // group never reads past the row's end (nkb >= 16 is required).
+  // L2 prefetch of op(B) (the weight panel): every stage of a tile touches a
+  // new K slice of it, and all XCDs walk the same panels in step, so its
+  // copies are the ones that wait on HBM.  One workgroup per group of kGroupM
+  // tile rows (the tiles that share the panel on an XCD) touches, 8 stages
+  // ahead, one 128-byte line per panel row (lane L of wave w: row 64 w + L),
+  // landing in pf_sink; the other workgroups issue the same load through a
+  // size-0 descriptor.  Measured: +5% per-tensor, +7% MX (prefetching from
+  // every workgroup, or both operands 2 stages ahead, was slower).
+  const uint32_t pfb = (uint32_t)((wave * 64 + lane) * g.ldb);
+  const uint32_t pf_lds = __builtin_amdgcn_readfirstlane(lds_offset(pf_sink));
   uint32_t offsa = 0, offsb = 0, ldss = 0;
   if constexpr (MX) {
     const int row = wave * 64 + lane;
@@ -629,6 +646,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   }
 
   int vb = blockIdx.x;
+  bool pf_owner = false;                            // this tile prefetches its B panel
+  auto owner_of = [&](int v) {
+    int tm, tn;
+    tile_coords_vb(v, tiles_m, tiles_n, tm, tn);
+    return (tm % kGroupM) == 0;
+  };
+  pf_owner = owner_of(vb);
   TileSrd cur, nxt;
   make_tile(vb, cur);
   if constexpr (PERSIST) make_tile(vb + P, nxt);
@@ -650,6 +674,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     if constexpr (PERSIST) srd = nx ? (isb ? nxt.b : nxt.a) : srd;
     srd[2] = live ? srd[2] : 0;
     dma_b128_so(uniform_srd(srd), __builtin_amdgcn_readfirstlane(la), off, __builtin_amdgcn_readfirstlane(k0));
+  };
+  // prefetch of op(B) stage s (descriptor choice as for the copies)
+  auto prefetch_b = [&](int s, bool owner) {
+    const bool nx = PERSIST && s >= nkU;
+    const bool live = owner && (s < nk || nx);
+    const uint32_t k0 = (uint32_t)((nx ? s - nkU : s) * BK);
+    v4i srd = cur.b;
+    if constexpr (PERSIST) srd = nx ? nxt.b : srd;
+    srd[2] = live ? srd[2] : 0;
+    dma_b32_so(uniform_srd(srd), pf_lds, pfb, __builtin_amdgcn_readfirstlane(k0));
   };
   // Scale group G of the current tile, 0 <= G <= ngroups (G == ngroups: the
   // next tile's group 0, whose copy starts at block 0).
@@ -761,7 +795,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w0[i], x0[j], acc[i][j], FB, FA, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vm<0>();
+    wait_vm<1>();                                     // all but the prefetch, issued last
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -790,6 +824,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
       dma(kt + 2, t);
       if constexpr (SCALES)
         if (t == 15) scale_dma((kt >> 2) + 1);
+      if (t == 15) prefetch_b(kt + 8, pf_owner);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -933,6 +968,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
       cur = nxt;
       make_tile(vb + P, nxt);
     }
+    pf_owner = owner_of(vb);
     gbase += ngroups;
   }
   wait_vm<0>();                                     // drain the zero copies past the last tile
