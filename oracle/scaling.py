@@ -124,7 +124,7 @@ def dequantize(q, fmt, bias: int) -> np.ndarray:
     return np.ldexp(decode(q, fmt), -int(bias))
 
 
-def mx_block_exponent(block_amax, fmt):
+def mx_block_exponent(block_amax, fmt, rule: str = "fmax"):
     """Per-block exponent e_b and its E8M0 code for an array of block maxima.
 
     "Per-Tensor and Per-Block Scaling Strategies for Effective FP8 Training"
@@ -137,18 +137,35 @@ def mx_block_exponent(block_amax, fmt):
     127 - e_b, so dequantization multiplies by 2**(code - 127) = 2**-e_b.  An
     all-zero (or Inf) block gets e_b = 0, code 127; a block holding a NaN gets
     code 0xFF (the E8M0 NaN) and its elements are cast with e_b = 0.
+
+    The option ``rule="ocp"`` follows the OCP MX shared-exponent rule
+    instead: the block's scale exponent is floor(log2 amax) minus the
+    exponent of the element format's largest binade, i.e. e_b = emax -
+    floor(log2 amax), so the block maximum lands in the largest binade and,
+    when its significand exceeds the format maximum's (1.75), saturates.
+    The conventions for zero, Inf, NaN and the clamp are the same.
     """
     a = np.asarray(block_amax, dtype=np.float64)
-    e = np.asarray(compute_bias(a, fmt, 0, lo=-127, hi=127), dtype=np.int64)
+    if rule == "fmax":
+        e = np.asarray(compute_bias(a, fmt, 0, lo=-127, hi=127), dtype=np.int64)
+    elif rule == "ocp":
+        fmt = _fmt(fmt)
+        finite = np.isfinite(a) & (a > 0)
+        _, ex = np.frexp(np.where(finite, a, 1.0))          # a = m 2^ex, 0.5 <= m < 1
+        e = np.where(finite, fmt.emax - (ex.astype(np.int64) - 1), 0)
+        e = np.clip(e, -127, 127).astype(np.int64)
+    else:
+        raise ValueError("rule must be 'fmax' or 'ocp'")
     codes = (E8M0_BIAS - e).astype(np.int64)
     codes = np.where(np.isnan(a), E8M0_NAN, codes).astype(np.uint8)
     return e, codes
 
 
-def mx_quantize(x, fmt=0):
+def mx_quantize(x, fmt=0, rule: str = "fmax"):
     """Per-block cast with 1 x 32 blocks along the last (K) axis.
 
-    Returns (codes[R, C], scales[R, C/32]) with scales as E8M0 codes.
+    Returns (codes[R, C], scales[R, C/32]) with scales as E8M0 codes; `rule`
+    picks the block exponent rule of ``mx_block_exponent``.
     Reading: blocks run along the contiguous K axis, which is the reduction
     axis of both GEMM operands, and C must be a multiple of 32.
     """
@@ -161,7 +178,7 @@ def mx_quantize(x, fmt=0):
         bmax = np.max(np.abs(blocks), axis=2)
     else:
         bmax = np.zeros((r, c // MX_BLOCK))
-    e, codes = mx_block_exponent(bmax, fmt)
+    e, codes = mx_block_exponent(bmax, fmt, rule)
     q = encode(np.ldexp(blocks, e[:, :, None]), fmt).reshape(r, c)
     return q, codes
 

@@ -209,3 +209,91 @@ def test_mx_uniform_codes_equal_per_tensor():
     q, s = oracle.mx_quantize(x, E4M3)
     assert np.all(s == s[0, 0])
     assert np.array_equal(q, oracle.quantize(x, E4M3, 127 - int(s[0, 0])))
+
+
+# --- the OCP MX shared-exponent rule ---------------------------------------
+
+def _scan_ocp_exponent(a, emax):
+    """Integer e with 2**emax <= a * 2**e < 2**(emax + 1), found by stepping
+    e (exact in float64): the block maximum lands in the element format's
+    top binade."""
+    e = -400
+    while a * 2.0 ** e < 2.0 ** emax:
+        e += 1
+    assert a * 2.0 ** e < 2.0 ** (emax + 1)
+    return e
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: f.name)
+def test_mx_ocp_exponent_matches_binade_scan(fmt):
+    rng = np.random.default_rng(3)
+    a = np.concatenate([np.ldexp(rng.uniform(1, 2, 200), rng.integers(-100, 100, 200)),
+                        [1.0, 1.75, 1.7500001, 1.9999999, 448.0, 57344.0, 2.0 ** -120]])
+    e, codes = oracle.mx_block_exponent(a, fmt, rule="ocp")
+    want = np.array([min(max(_scan_ocp_exponent(v, fmt.emax), -127), 127) for v in a])
+    assert np.array_equal(e, want)
+    assert np.array_equal(codes.astype(np.int64), 127 - want)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: f.name)
+def test_mx_ocp_rule_against_fmax_rule_all_bf16(fmt):
+    """Both formats' largest finite value has significand 1.75 (E4M3 448 =
+    1.75 * 2**8, E5M2 57344 = 1.75 * 2**15), so over every positive finite
+    bf16 amax the two rules agree when the amax significand is at most 1.75
+    and the OCP exponent is one larger above it (both before the clamp)."""
+    a = _positive_finite_bf16()
+    e_f, _ = oracle.mx_block_exponent(a, fmt)
+    e_o, _ = oracle.mx_block_exponent(a, fmt, rule="ocp")
+    m, _ = np.frexp(a)
+    over = 2 * m > 1.75
+    inside = (e_f > -127) & (e_f < 126)
+    assert np.array_equal(e_o[inside & ~over], e_f[inside & ~over])
+    assert np.array_equal(e_o[inside & over], e_f[inside & over] + 1)
+    assert np.count_nonzero(inside & over) > 1000
+
+
+def test_mx_ocp_worked_block():
+    """E4M3 block with max 1.8: the OCP rule scales by 2**8 (1.8 -> 460.8,
+    which saturates to 448, code 0x7E), the fmax rule by 2**7 (1.8 -> 230.4,
+    nearest E4M3 value 224); 1.0 lands on 256 and 128.  Codes for amax 1 are
+    127 - 8 = 119 (E4M3) and 127 - 15 = 112 (E5M2)."""
+    x = np.zeros((1, 32))
+    x[0, 0], x[0, 1] = 1.8, 1.0
+    q_o, s_o = oracle.mx_quantize(x, E4M3, rule="ocp")
+    q_f, s_f = oracle.mx_quantize(x, E4M3)
+    assert s_o[0, 0] == 119 and s_f[0, 0] == 120
+    assert q_o[0, 0] == 0x7E and decode(q_o[:, :1], E4M3)[0, 0] == 448.0
+    assert decode(q_f[:, :1], E4M3)[0, 0] == 224.0
+    assert decode(q_o[:, 1:2], E4M3)[0, 0] == 256.0 and decode(q_f[:, 1:2], E4M3)[0, 0] == 128.0
+    _, s5 = oracle.mx_quantize(np.ones((1, 32)), E5M2, rule="ocp")
+    assert s5[0, 0] == 112
+
+
+def test_mx_ocp_edge_blocks_and_bad_rule():
+    x = np.zeros((2, 96))
+    x[1, 5] = np.nan
+    x[1, 70] = np.inf
+    x[1, 64:70] = 1.0
+    q, s = oracle.mx_quantize(x, E4M3, rule="ocp")
+    assert s[0, 0] == 127 and s[1, 0] == 0xFF and s[1, 2] == 127
+    assert q[1, 5] == 0x7F and q[1, 70] == 0x7E
+    _, s2 = oracle.mx_quantize(np.full((1, 32), 2.0 ** -133), E4M3, rule="ocp")
+    assert s2[0, 0] == 0                               # exponent clamps at 127
+    with pytest.raises(ValueError):
+        oracle.mx_block_exponent(np.ones(2), E4M3, rule="floor")
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: f.name)
+def test_mx_ocp_clipping_bound(fmt):
+    """Under the OCP rule only elements whose scaled magnitude exceeds the
+    format maximum clip, to the maximum; the block maximum's relative error
+    is then below (2 - 1.75) / 2."""
+    x = oracle.bf16_bits_to_f64(make("c4", "X", shape=(64, 256)))
+    q, s = oracle.mx_quantize(x, fmt, rule="ocp")
+    deq = oracle.mx_dequantize(q, s, fmt)
+    e = (127 - s.astype(np.int64))[:, :, None]
+    scaled = np.abs(np.ldexp(x.reshape(64, -1, MX_BLOCK), e)).reshape(x.shape)
+    clipped = scaled > fmt.max
+    assert np.all(np.abs(decode(q, fmt))[clipped] == fmt.max)
+    assert np.all(np.abs(deq - x)[clipped] < 0.125 * np.abs(x)[clipped])
+    assert np.count_nonzero(clipped) > 0
