@@ -58,6 +58,8 @@ extern "C" {
 enum { FP8_E4M3 = 0, FP8_E5M2 = 1 };
 /* High-precision data types for inputs and GEMM outputs. */
 enum { FP8_DT_BF16 = 0, FP8_DT_F32 = 1 };
+/* MX block-exponent rules (see mx_quantize_rule). */
+enum { MX_RULE_FMAX = 0, MX_RULE_OCP = 1 };
 
 /* Status codes. */
 enum {
@@ -69,7 +71,7 @@ enum {
   FP8_ERR_ALIGN = -3,       /* GEMM operand base or leading dimension not a
                                multiple of 16 bytes (required by 16-byte loads) */
   FP8_ERR_DTYPE = -4,       /* unknown FP8_DT_* value */
-  FP8_ERR_FORMAT = -5,      /* unknown FP8_E* value */
+  FP8_ERR_FORMAT = -5,      /* unknown FP8_E* or MX_RULE_* value */
   FP8_ERR_LAUNCH = -6,      /* hipGetLastError reported a launch failure */
   FP8_ERR_UNSUPPORTED = -7  /* valid but not implemented combination */
 };
@@ -176,6 +178,33 @@ int mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
 int mx_quantize_t(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                   int fmt, uint8_t* qT, int64_t ldqT, uint8_t* scalesT,
                   int64_t ld_scales, hipStream_t stream);
+
+/*
+ * mx_quantize_rule / mx_quantize_t_rule — mx_quantize / mx_quantize_t with a
+ * choice of block-exponent rule.  The summary page ("Key Questions
+ * Answered") names MXFP8 block scaling but not how a block's scale is
+ * chosen; MX_RULE_OCP is the shared-scale rule of the OCP Microscaling (MX)
+ * specification that MXFP8 belongs to:
+ *   rule = MX_RULE_FMAX  e_b = floor(log2(fmax / block_amax)), exactly what
+ *                        mx_quantize / mx_quantize_t compute: the block
+ *                        maximum never exceeds the format maximum;
+ *   rule = MX_RULE_OCP   e_b = emax - floor(log2(block_amax)), emax being the
+ *                        exponent of the format's largest binade (8 for
+ *                        E4M3, 15 for E5M2): the block maximum lands in that
+ *                        binade and, when its significand exceeds 1.75 (the
+ *                        format maximum's), saturates to +-fmax.  It equals
+ *                        FMAX's e_b, or FMAX's e_b + 1 when the significand
+ *                        of block_amax is above 1.75.
+ * Both clamp e_b to [-127, 127] and share the zero, Inf and NaN conventions,
+ * layouts and argument rules of mx_quantize / mx_quantize_t; an unknown rule
+ * returns FP8_ERR_FORMAT.  The GEMM reads either rule's scales unchanged.
+ */
+int mx_quantize_rule(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                     int fmt, int rule, uint8_t* q, int64_t ldq, uint8_t* scales,
+                     int64_t ld_scales, hipStream_t stream);
+int mx_quantize_t_rule(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                       int fmt, int rule, uint8_t* qT, int64_t ldqT, uint8_t* scalesT,
+                       int64_t ld_scales, hipStream_t stream);
 
 /*
  * fp8_scaled_gemm — per-tensor scaled FP8 GEMM with unscale ("Proposed

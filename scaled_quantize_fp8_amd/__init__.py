@@ -24,6 +24,7 @@ __all__ = [
     "E4M3", "E5M2", "load_library", "library_path", "Fp8Error",
     "fp8_amax", "fp8_compute_scale", "fp8_history_init", "fp8_history_push",
     "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize", "mx_quantize_t",
+    "mx_quantize_rule", "mx_quantize_t_rule", "MX_RULE_FMAX", "MX_RULE_OCP",
     "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string", "fp8_abi_version",
 ]
 
@@ -32,6 +33,10 @@ E5M2 = 1
 _DT_BF16 = 0
 _DT_F32 = 1
 _FMT_NAMES = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
+MX_RULE_FMAX = 0
+MX_RULE_OCP = 1
+_RULE_NAMES = {"fmax": MX_RULE_FMAX, "ocp": MX_RULE_OCP, MX_RULE_FMAX: MX_RULE_FMAX,
+               MX_RULE_OCP: MX_RULE_OCP}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -51,6 +56,8 @@ _SIGNATURES = {
     "fp8_quantize": ([_p, _i, _i64, _i64, _i64, _i, _p, _p, _i64, _p, _i64, _p, _p], _i),
     "mx_quantize": ([_p, _i, _i64, _i64, _i64, _i, _p, _i64, _p, _i64, _p], _i),
     "mx_quantize_t": ([_p, _i, _i64, _i64, _i64, _i, _p, _i64, _p, _i64, _p], _i),
+    "mx_quantize_rule": ([_p, _i, _i64, _i64, _i64, _i, _i, _p, _i64, _p, _i64, _p], _i),
+    "mx_quantize_t_rule": ([_p, _i, _i64, _i64, _i64, _i, _i, _p, _i64, _p, _i64, _p], _i),
     "fp8_scaled_gemm": ([_i64, _i64, _i64, _p, _i, _i, _i64, _p, _p, _i, _i, _i64, _p,
                          _p, _i, _i64, _p, _p], _i),
     "mx_scaled_gemm": ([_i64, _i64, _i64, _p, _i, _i64, _p, _i64, _p, _i, _i64, _p, _i64,
@@ -253,13 +260,31 @@ def fp8_quantize(x: torch.Tensor, fmt, bias: torch.Tensor, q: torch.Tensor | Non
     return q, qT, amax_out
 
 
+def _rule(rule) -> int:
+    if rule not in _RULE_NAMES:
+        raise ValueError(f"unknown MX rule {rule!r} (use 'fmax' or 'ocp')")
+    return _RULE_NAMES[rule]
+
+
 def mx_quantize(x: torch.Tensor, fmt=E4M3, q: torch.Tensor | None = None,
                 scales: torch.Tensor | None = None):
     """Per-block (1 x 32 along cols) cast; returns (q [R x C] codes, scales
     [R x C/32] E8M0 codes)."""
+    return _mx_cast("mx_quantize", x, fmt, None, q, scales)
+
+
+def mx_quantize_rule(x: torch.Tensor, fmt=E4M3, rule="fmax", q: torch.Tensor | None = None,
+                     scales: torch.Tensor | None = None):
+    """mx_quantize with a choice of block-exponent rule: "fmax" (block max
+    at or below the format maximum) or "ocp" (the OCP MX rule: block max in
+    the format's top binade, saturating above the format maximum)."""
+    return _mx_cast("mx_quantize_rule", x, fmt, _rule(rule), q, scales)
+
+
+def _mx_cast(name, x, fmt, rule, q, scales):
     rows, cols, ld = _mat(x, "x")
     if cols % 32:
-        raise ValueError("mx_quantize needs cols % 32 == 0")
+        raise ValueError(f"{name} needs cols % 32 == 0")
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if scales is None:
@@ -268,8 +293,9 @@ def mx_quantize(x: torch.Tensor, fmt=E4M3, q: torch.Tensor | None = None,
     _u8(scales, "scales")
     _, _, ldq = _mat(q, "q")
     _, _, lds = _mat(scales, "scales")
-    _check("mx_quantize", load_library().mx_quantize(
-        _ptr(x), _dtype_code(x, "x"), rows, cols, ld, _fmt(fmt), _ptr(q), ldq, _ptr(scales),
+    fmt_rule = (_fmt(fmt),) if rule is None else (_fmt(fmt), rule)
+    _check(name, getattr(load_library(), name)(
+        _ptr(x), _dtype_code(x, "x"), rows, cols, ld, *fmt_rule, _ptr(q), ldq, _ptr(scales),
         lds, _stream(x)))
     return q, scales
 
@@ -279,9 +305,20 @@ def mx_quantize_t(x: torch.Tensor, fmt=E4M3, qT: torch.Tensor | None = None,
     """Per-block cast with 32 x 1 blocks along rows, written transposed;
     returns (qT [C x R] codes, scalesT [C x R/32] E8M0 codes), the MX cast of
     x^T."""
+    return _mx_cast_t("mx_quantize_t", x, fmt, None, qT, scalesT)
+
+
+def mx_quantize_t_rule(x: torch.Tensor, fmt=E4M3, rule="fmax", qT: torch.Tensor | None = None,
+                       scalesT: torch.Tensor | None = None):
+    """mx_quantize_t with a choice of block-exponent rule ("fmax" or "ocp",
+    as in mx_quantize_rule)."""
+    return _mx_cast_t("mx_quantize_t_rule", x, fmt, _rule(rule), qT, scalesT)
+
+
+def _mx_cast_t(name, x, fmt, rule, qT, scalesT):
     rows, cols, ld = _mat(x, "x")
     if rows % 32:
-        raise ValueError("mx_quantize_t needs rows % 32 == 0")
+        raise ValueError(f"{name} needs rows % 32 == 0")
     if qT is None:
         qT = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
     if scalesT is None:
@@ -290,8 +327,9 @@ def mx_quantize_t(x: torch.Tensor, fmt=E4M3, qT: torch.Tensor | None = None,
     _u8(scalesT, "scalesT")
     _, _, ldq = _mat(qT, "qT")
     _, _, lds = _mat(scalesT, "scalesT")
-    _check("mx_quantize_t", load_library().mx_quantize_t(
-        _ptr(x), _dtype_code(x, "x"), rows, cols, ld, _fmt(fmt), _ptr(qT), ldq, _ptr(scalesT),
+    fmt_rule = (_fmt(fmt),) if rule is None else (_fmt(fmt), rule)
+    _check(name, getattr(load_library(), name)(
+        _ptr(x), _dtype_code(x, "x"), rows, cols, ld, *fmt_rule, _ptr(qT), ldq, _ptr(scalesT),
         lds, _stream(x)))
     return qT, scalesT
 

@@ -40,8 +40,11 @@ __device__ __forceinline__ int fmt_emax(int fmt) { return fmt == FP8_E4M3 ? 8 : 
 // floor(log2(fmax/amax)) is emax - E - (m_amax > 1.75 ? 1 : 0), where
 // amax = m_amax * 2^E with m_amax in [1, 2); subnormal amax is normalised
 // with a count of leading zeros.  Pure integer arithmetic: exact.
+// With `top_binade` the correction term is dropped (emax - E - margin): the
+// OCP MX shared-exponent rule, which puts amax in the format's top binade
+// and lets a significand above the format maximum's saturate.
 __device__ __forceinline__ int bias_from_amax_bits(uint32_t abits, int emax, int margin,
-                                                   int lo, int hi) {
+                                                   int lo, int hi, bool top_binade = false) {
   abits &= 0x7fffffffu;
   if (abits == 0u || abits >= 0x7f800000u) return 0;
   int E;
@@ -55,7 +58,7 @@ __device__ __forceinline__ int bias_from_amax_bits(uint32_t abits, int emax, int
     E = (int)efield - 127;
     mfield = abits & 0x7fffffu;
   }
-  int b = emax - E - (mfield > kMaxMantissaField ? 1 : 0) - margin;
+  int b = emax - E - (!top_binade && mfield > kMaxMantissaField ? 1 : 0) - margin;
   b = b < lo ? lo : b;
   b = b > hi ? hi : b;
   return b;

@@ -10,6 +10,7 @@
 namespace sfp8 {
 
 inline bool valid_fmt(int f) { return f == FP8_E4M3 || f == FP8_E5M2; }
+inline bool valid_mx_rule(int r) { return r == MX_RULE_FMAX || r == MX_RULE_OCP; }
 inline bool valid_dtype(int d) { return d == FP8_DT_BF16 || d == FP8_DT_F32; }
 inline int dtype_size(int d) { return d == FP8_DT_BF16 ? 2 : 4; }
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }

@@ -411,18 +411,20 @@ struct MxArgs {
   int64_t lds;
 };
 
-template <int FMT>
+// Block exponent by the default rule (block max at or below the format
+// maximum) or, with OCP, the OCP MX rule (block max in the top binade).
+template <int FMT, bool OCP>
 __device__ __forceinline__ void block_exponent(uint32_t bmax_bits, int* e, uint32_t* code) {
   if (bmax_bits > 0x7f800000u) {        // NaN in the block
     *e = 0;
     *code = 0xffu;
   } else {
-    *e = bias_from_amax_bits(bmax_bits, Fmt<FMT>::kEmax, 0, -127, 127);
+    *e = bias_from_amax_bits(bmax_bits, Fmt<FMT>::kEmax, 0, -127, 127, OCP);
     *code = (uint32_t)(127 - *e);
   }
 }
 
-template <int DT, int FMT>
+template <int DT, int FMT, bool OCP>
 __global__ __launch_bounds__(kThreads) void mx_vec_kernel(MxArgs a) {
   constexpr int ESZ = In<DT>::kEsz;
   constexpr int EPC = In<DT>::kEpc;
@@ -448,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void mx_vec_kernel(MxArgs a) {
         const uint32_t bm = (L == 4) ? group4_max(m) : group8_max(m);
         int e;
         uint32_t code;
-        block_exponent<FMT>(bm, &e, &code);
+        block_exponent<FMT, OCP>(bm, &e, &code);
         const uint2 o = cast_chunk<DT, FMT>(v[u], e, &m, true);
         store_codes<DT>(qr, c + u * stride, o);
         if ((threadIdx.x % L) == 0) sr[(c + u * stride) / L] = (uint8_t)code;
@@ -461,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void mx_vec_kernel(MxArgs a) {
       const uint32_t bm = (L == 4) ? group4_max(m) : group8_max(m);
       int e;
       uint32_t code;
-      block_exponent<FMT>(bm, &e, &code);
+      block_exponent<FMT, OCP>(bm, &e, &code);
       const uint2 o = cast_chunk<DT, FMT>(v, e, &m, true);
       store_codes<DT>(qr, c, o);
       if ((threadIdx.x % L) == 0) sr[c / L] = (uint8_t)code;
@@ -469,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void mx_vec_kernel(MxArgs a) {
   }
 }
 
-template <int DT, int FMT>
+template <int DT, int FMT, bool OCP>
 __global__ __launch_bounds__(kThreads) void mx_scalar_kernel(MxArgs a) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t nb = a.cols / 32;
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void mx_scalar_kernel(MxArgs a) {
       }
       int e;
       uint32_t code;
-      block_exponent<FMT>(m, &e, &code);
+      block_exponent<FMT, OCP>(m, &e, &code);
       for (int j = 0; j < 32; ++j) {
         float f;
         const uint32_t bits = load_elem<DT>(xr, b * 32 + j, &f);
@@ -495,7 +497,7 @@ __global__ __launch_bounds__(kThreads) void mx_scalar_kernel(MxArgs a) {
   }
 }
 
-template <int DT, int FMT>
+template <int DT, int FMT, bool OCP>
 static void launch_mx(const MxArgs& a, bool vec, hipStream_t s) {
   const int epc = 16 / In<DT>::kEsz;
   const int64_t units = vec ? a.cols / epc : a.cols / 32;
@@ -504,9 +506,9 @@ static void launch_mx(const MxArgs& a, bool vec, hipStream_t s) {
   if (gy < 1) gy = 1;
   while ((uint64_t)gx * gy > 32768 && gy > 1) gy = (gy + 1) / 2;
   if (vec)
-    hipLaunchKernelGGL((mx_vec_kernel<DT, FMT>), dim3(gx, gy), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((mx_vec_kernel<DT, FMT, OCP>), dim3(gx, gy), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((mx_scalar_kernel<DT, FMT>), dim3(gx, gy), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((mx_scalar_kernel<DT, FMT, OCP>), dim3(gx, gy), dim3(kThreads), 0, s, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -522,7 +524,7 @@ static void launch_mx(const MxArgs& a, bool vec, hipStream_t s) {
 // ---------------------------------------------------------------------------
 constexpr int kMtR = 128, kMtC = 64;
 
-template <int DT, int FMT, bool VEC>
+template <int DT, int FMT, bool VEC, bool OCP>
 __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
   // rows padded to 68 dwords: 16-byte aligned rows for the staging writes,
   // and the column reads (one row per lane group) stay conflict-free
@@ -579,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
   }
   int e;
   uint32_t code;
-  block_exponent<FMT>(bm, &e, &code);
+  block_exponent<FMT, OCP>(bm, &e, &code);
   uint32_t w[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k)
@@ -680,11 +682,11 @@ int fp8_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
   return launch_status();
 }
 
-int mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, uint8_t* q,
-                int64_t ldq, uint8_t* scales, int64_t ld_scales, hipStream_t stream) {
+int mx_quantize_rule(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, int rule,
+                     uint8_t* q, int64_t ldq, uint8_t* scales, int64_t ld_scales, hipStream_t stream) {
   if (!q || !scales) return FP8_ERR_NULL;
   if (!valid_dtype(dtype)) return FP8_ERR_DTYPE;
-  if (!valid_fmt(fmt)) return FP8_ERR_FORMAT;
+  if (!valid_fmt(fmt) || !valid_mx_rule(rule)) return FP8_ERR_FORMAT;
   if (cols % 32) return FP8_ERR_SHAPE;
   int st = check_matrix(rows, cols, ld);
   if (st) return st;
@@ -715,21 +717,32 @@ int mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld
   }
   const bool vec = aligned(a.x, 16) && (a.rows == 1 || (a.ld * esz) % 16 == 0) && aligned(a.q, epc) &&
                    (a.rows == 1 || a.ldq % epc == 0);
+#define SFP8_MX(DT, FMT)                                       \
+  do {                                                         \
+    if (rule == MX_RULE_OCP) launch_mx<DT, FMT, true>(a, vec, stream); \
+    else launch_mx<DT, FMT, false>(a, vec, stream);            \
+  } while (0)
   if (dtype == FP8_DT_BF16) {
-    if (fmt == FP8_E4M3) launch_mx<FP8_DT_BF16, FP8_E4M3>(a, vec, stream);
-    else launch_mx<FP8_DT_BF16, FP8_E5M2>(a, vec, stream);
+    if (fmt == FP8_E4M3) SFP8_MX(FP8_DT_BF16, FP8_E4M3);
+    else SFP8_MX(FP8_DT_BF16, FP8_E5M2);
   } else {
-    if (fmt == FP8_E4M3) launch_mx<FP8_DT_F32, FP8_E4M3>(a, vec, stream);
-    else launch_mx<FP8_DT_F32, FP8_E5M2>(a, vec, stream);
+    if (fmt == FP8_E4M3) SFP8_MX(FP8_DT_F32, FP8_E4M3);
+    else SFP8_MX(FP8_DT_F32, FP8_E5M2);
   }
+#undef SFP8_MX
   return launch_status();
 }
 
-int mx_quantize_t(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, uint8_t* qT,
-                  int64_t ldqT, uint8_t* scalesT, int64_t ld_scales, hipStream_t stream) {
+int mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, uint8_t* q,
+                int64_t ldq, uint8_t* scales, int64_t ld_scales, hipStream_t stream) {
+  return mx_quantize_rule(x, dtype, rows, cols, ld, fmt, MX_RULE_FMAX, q, ldq, scales, ld_scales, stream);
+}
+
+int mx_quantize_t_rule(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, int rule,
+                       uint8_t* qT, int64_t ldqT, uint8_t* scalesT, int64_t ld_scales, hipStream_t stream) {
   if (!qT || !scalesT) return FP8_ERR_NULL;
   if (!valid_dtype(dtype)) return FP8_ERR_DTYPE;
-  if (!valid_fmt(fmt)) return FP8_ERR_FORMAT;
+  if (!valid_fmt(fmt) || !valid_mx_rule(rule)) return FP8_ERR_FORMAT;
   if (rows % 32) return FP8_ERR_SHAPE;
   int st = check_matrix(rows, cols, ld);
   if (st) return st;
@@ -755,8 +768,13 @@ int mx_quantize_t(const void* x, int dtype, int64_t rows, int64_t cols, int64_t 
   const bool vec = aligned(x, 16) && (ld * dtype_size(dtype)) % 16 == 0;
 #define SFP8_MXT(DT, FMT)                                                                              \
   do {                                                                                                 \
-    if (vec) hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, true>), grid, dim3(kThreads), 0, stream, a); \
-    else hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, false>), grid, dim3(kThreads), 0, stream, a);   \
+    if (rule == MX_RULE_OCP) {                                                                         \
+      if (vec) hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, true, true>), grid, dim3(kThreads), 0, stream, a); \
+      else hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, false, true>), grid, dim3(kThreads), 0, stream, a);   \
+    } else {                                                                                           \
+      if (vec) hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, true, false>), grid, dim3(kThreads), 0, stream, a); \
+      else hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, false, false>), grid, dim3(kThreads), 0, stream, a);   \
+    }                                                                                                  \
   } while (0)
   if (dtype == FP8_DT_BF16) {
     if (fmt == FP8_E4M3) SFP8_MXT(FP8_DT_BF16, FP8_E4M3);
@@ -767,6 +785,11 @@ int mx_quantize_t(const void* x, int dtype, int64_t rows, int64_t cols, int64_t 
   }
 #undef SFP8_MXT
   return launch_status();
+}
+
+int mx_quantize_t(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, uint8_t* qT,
+                  int64_t ldqT, uint8_t* scalesT, int64_t ld_scales, hipStream_t stream) {
+  return mx_quantize_t_rule(x, dtype, rows, cols, ld, fmt, MX_RULE_FMAX, qT, ldqT, scalesT, ld_scales, stream);
 }
 
 }  // extern "C"

@@ -29,7 +29,9 @@ Recipes:
                pushed into the history afterwards.  The first step has no
                history and pushes its own amax first (current scaling);
     "mx"       per-block: 1 x 32 blocks along each product's K axis, E8M0
-               block scales;
+               block scales; `mx_rule` picks the block-exponent rule
+               ("fmax": block max at or below the format maximum; "ocp": the
+               OCP MX rule, block max in the format's top binade);
     "constant" one fixed bias for every tensor (the fixed-scaling baseline
                the pages compare FP8-AMAX against, FP8-CSCALE; "Research
                questions" / "Key findings" of the paper review page).
@@ -41,9 +43,9 @@ import math
 
 import torch
 
-from . import (E4M3, E5M2, fp8_amax, fp8_compute_scale, fp8_compute_scale_delayed,
-               fp8_history_init, fp8_history_push, fp8_quantize, fp8_scaled_gemm, mx_quantize,
-               mx_quantize_t, mx_scaled_gemm)
+from . import (E4M3, E5M2, _rule, fp8_amax, fp8_compute_scale, fp8_compute_scale_delayed,
+               fp8_history_init, fp8_history_push, fp8_quantize, fp8_scaled_gemm, mx_quantize_rule,
+               mx_quantize_t_rule, mx_scaled_gemm)
 
 RECIPES = ("current", "delayed", "mx", "constant")
 
@@ -98,13 +100,14 @@ class Fp8LinearFunction(torch.autograd.Function):
             x2 = x2.contiguous()
         recipe = layer.recipe
         if recipe == "mx":
-            qx, sx = mx_quantize(x2, E4M3)
-            qw, sw = mx_quantize(w, E4M3)
+            rule = layer.mx_rule
+            qx, sx = mx_quantize_rule(x2, E4M3, rule)
+            qw, sw = mx_quantize_rule(w, E4M3, rule)
             y, amax = mx_scaled_gemm(qx, E4M3, sx, qw, E4M3, sw, out_dtype=x.dtype, want_amax=True)
             if ctx.needs_input_grad[0] or ctx.needs_input_grad[1]:
                 # backward operands: blocks along out (W^T) and along tokens (X^T)
-                qwT, swT = mx_quantize_t(w, E4M3)
-                qxT, sxT = mx_quantize_t(x2, E4M3)
+                qwT, swT = mx_quantize_t_rule(w, E4M3, rule)
+                qxT, sxT = mx_quantize_t_rule(x2, E4M3, rule)
                 ctx.save_for_backward(qwT, swT, qxT, sxT)
         else:
             bx, qx, qxT = _per_tensor_cast(x2, E4M3, recipe, layer.margin, layer._hx, True, layer._bias,
@@ -131,10 +134,10 @@ class Fp8LinearFunction(torch.autograd.Function):
         if layer.recipe == "mx":
             qwT, swT, qxT, sxT = ctx.saved_tensors
             if ctx.needs_input_grad[0]:
-                qdy, sdy = mx_quantize(dy2, E5M2)
+                qdy, sdy = mx_quantize_rule(dy2, E5M2, layer.mx_rule)
                 dx, _ = mx_scaled_gemm(qdy, E5M2, sdy, qwT, E4M3, swT, out_dtype=ctx.dtype)
             if ctx.needs_input_grad[1]:
-                qdyT, sdyT = mx_quantize_t(dy2, E5M2)
+                qdyT, sdyT = mx_quantize_t_rule(dy2, E5M2, layer.mx_rule)
                 dw, _ = mx_scaled_gemm(qdyT, E5M2, sdyT, qxT, E4M3, sxT, out_dtype=ctx.dtype)
         else:
             qwT, bw, qxT, bx = ctx.saved_tensors
@@ -161,7 +164,7 @@ class Fp8Linear(torch.nn.Module):
 
     def __init__(self, in_features: int, out_features: int, recipe: str = "current",
                  margin: int = 0, history: int = 16, bias: int = 0, log_scales: bool = False,
-                 device=None, dtype=torch.bfloat16):
+                 mx_rule: str = "fmax", device=None, dtype=torch.bfloat16):
         super().__init__()
         if recipe not in RECIPES:
             raise ValueError(f"recipe must be one of {RECIPES}")
@@ -171,6 +174,8 @@ class Fp8Linear(torch.nn.Module):
             raise ValueError("dtype must be bfloat16 or float32")
         self.in_features, self.out_features = in_features, out_features
         self.recipe, self.margin = recipe, int(margin)
+        _rule(mx_rule)                                   # validates the name
+        self.mx_rule = mx_rule
         self.weight = torch.nn.Parameter(torch.empty(out_features, in_features, device=device, dtype=dtype))
         torch.nn.init.kaiming_uniform_(self.weight, a=math.sqrt(5))
         self.last_output_amax = None
@@ -226,4 +231,5 @@ class Fp8Linear(torch.nn.Module):
             self._log.clear()
 
     def extra_repr(self) -> str:
-        return f"in_features={self.in_features}, out_features={self.out_features}, recipe={self.recipe}"
+        extra = f", mx_rule={self.mx_rule}" if self.recipe == "mx" else ""
+        return f"in_features={self.in_features}, out_features={self.out_features}, recipe={self.recipe}{extra}"

@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for want in ["fp8_amax", "fp8_compute_scale", "fp8_history_init", "fp8_history_push",
                  "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize", "mx_quantize_t",
-                 "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string", "fp8_abi_version"]:
+                 "mx_quantize_rule", "mx_quantize_t_rule", "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string", "fp8_abi_version"]:
         assert want in names
 
 
@@ -105,6 +105,26 @@ def test_quantize_validation(lib):
     assert t(None, 0, 64, 8, 8, 0, FAKE, 64, FAKE, 2, S) == NULL
 
 
+def test_mx_rule_validation(lib):
+    m = lib.mx_quantize_rule
+    # x, dtype, rows, cols, ld, fmt, rule, q, ldq, scales, ld_scales, s
+    assert m(FAKE, 0, 4, 64, 64, 0, 2, FAKE, 64, FAKE, 2, S) == FORMAT          # unknown rule
+    assert m(FAKE, 0, 4, 64, 64, 0, -1, FAKE, 64, FAKE, 2, S) == FORMAT
+    assert m(FAKE, 0, 4, 64, 64, 2, 1, FAKE, 64, FAKE, 2, S) == FORMAT
+    assert m(FAKE, 0, 4, 48, 48, 0, 1, FAKE, 48, FAKE, 2, S) == SHAPE           # cols % 32
+    assert m(FAKE, 0, 4, 64, 64, 0, 1, None, 64, FAKE, 2, S) == NULL
+    assert m(FAKE, 2, 4, 64, 64, 0, 1, FAKE, 64, FAKE, 2, S) == DTYPE
+    assert m(FAKE, 0, 4, 64, 64, 0, 1, FAKE, 64, FAKE, 1, S) == SHAPE           # ld_scales
+    assert m(None, 0, 4, 64, 64, 0, 1, FAKE, 64, FAKE, 2, S) == NULL
+    assert m(None, 0, 0, 64, 64, 0, 1, FAKE, 64, FAKE, 2, S) == OK              # empty: no launch
+    t = lib.mx_quantize_t_rule
+    assert t(FAKE, 0, 64, 8, 8, 0, 7, FAKE, 64, FAKE, 2, S) == FORMAT
+    assert t(FAKE, 0, 48, 8, 8, 0, 1, FAKE, 48, FAKE, 2, S) == SHAPE            # rows % 32
+    assert t(FAKE, 0, 64, 8, 8, 0, 1, FAKE, 64, None, 2, S) == NULL
+    assert t(FAKE, 0, 64, 8, 8, 0, 1, FAKE, 32, FAKE, 2, S) == SHAPE            # ldqT < rows
+    assert t(None, 0, 64, 8, 8, 0, 1, FAKE, 64, FAKE, 2, S) == NULL
+
+
 def test_gemm_validation(lib):
     g = lib.fp8_scaled_gemm
     # M, N, K, A, fa, ta, lda, ba, B, fb, tb, ldb, bb, C, dt, ldc, amax, s
@@ -139,3 +159,9 @@ def test_binding_refuses_cpu_tensors():
         sq.mx_quantize(torch.zeros(4, 32, dtype=torch.bfloat16))
     with pytest.raises(ValueError):
         sq.mx_quantize_t(torch.zeros(32, 4, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        sq.mx_quantize_rule(torch.zeros(4, 32, dtype=torch.bfloat16), rule="ocp")
+    with pytest.raises(ValueError):
+        sq.mx_quantize_rule(torch.zeros(4, 32, dtype=torch.bfloat16), rule="nearest")
+    with pytest.raises(ValueError):
+        sq.mx_quantize_t_rule(torch.zeros(32, 4, dtype=torch.bfloat16), rule="ocp")

@@ -109,20 +109,21 @@ def test_linear_constant_bias_matches_oracle():
 
 
 @pytest.mark.gpu
-def test_linear_mx_matches_oracle():
+@pytest.mark.parametrize("rule", ["fmax", "ocp"])
+def test_linear_mx_matches_oracle(rule):
     need_gpu()
     x, w, dy = _tensors()
-    layer = Fp8Linear(IN, OUT, recipe="mx", device=DEV)
+    layer = Fp8Linear(IN, OUT, recipe="mx", mx_rule=rule, device=DEV)
     with torch.no_grad():
         layer.weight.copy_(_dev(w))
-    say("fp8 linear, MX")
+    say(f"fp8 linear, MX, rule {rule}")
     y, dx, dw, amax = _run(layer, x, dy)
-    qx, sx = oracle.mx_quantize(x, E4M3)
-    qw, sw = oracle.mx_quantize(w, E4M3)
-    qdy, sdy = oracle.mx_quantize(dy, E5M2)
-    qwT, swT = oracle.mx_quantize(np.ascontiguousarray(w.T), E4M3)
-    qdyT, sdyT = oracle.mx_quantize(np.ascontiguousarray(dy.T), E5M2)
-    qxT, sxT = oracle.mx_quantize(np.ascontiguousarray(x.T), E4M3)
+    qx, sx = oracle.mx_quantize(x, E4M3, rule)
+    qw, sw = oracle.mx_quantize(w, E4M3, rule)
+    qdy, sdy = oracle.mx_quantize(dy, E5M2, rule)
+    qwT, swT = oracle.mx_quantize(np.ascontiguousarray(w.T), E4M3, rule)
+    qdyT, sdyT = oracle.mx_quantize(np.ascontiguousarray(dy.T), E5M2, rule)
+    qxT, sxT = oracle.mx_quantize(np.ascontiguousarray(x.T), E4M3, rule)
     for what, got, a, sa, fa, b, sb, fb in (("y", y, qx, sx, E4M3, qw, sw, E4M3),
                                             ("dx", dx, qdy, sdy, E5M2, qwT, swT, E4M3),
                                             ("dw", dw, qdyT, sdyT, E5M2, qxT, sxT, E4M3)):
@@ -185,6 +186,8 @@ def test_linear_argument_checks():
         Fp8Linear(IN, OUT, recipe="constant", bias=200)
     with pytest.raises(ValueError):
         Fp8Linear(IN, OUT, recipe="mx", log_scales=True)
+    with pytest.raises(ValueError):
+        Fp8Linear(IN, OUT, recipe="mx", mx_rule="round")
     with pytest.raises(RuntimeError):
         Fp8Linear(IN, OUT).scale_history()
     with pytest.raises(ValueError):

@@ -245,6 +245,70 @@ def test_mx_cast_transposed_full_size_sampled():
     assert np.array_equal(host(qT[idx]), rq)
 
 
+def _every_bf16_as_block_max(seed=21):
+    """[2048 x 1024] bf16 bits: block i (1 x 32) holds bf16 pattern i and 31
+    elements of smaller or equal magnitude field (the pattern's field minus
+    0..127, floored at 0), each with a random sign, so every one of the
+    65,536 patterns is the maximum of its own block."""
+    rng = np.random.default_rng(seed)
+    p = all_bf16_patterns().astype(np.int64)
+    mag = (p & 0x7FFF)[:, None] - rng.integers(0, 128, (p.size, 31))
+    rest = np.maximum(mag, 0) | (rng.integers(0, 2, (p.size, 31)) << 15)
+    return np.concatenate([p[:, None], rest], axis=1).astype(np.uint16).reshape(2048, 1024)
+
+
+@pytest.mark.parametrize("rule", ["fmax", "ocp"])
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: f.name)
+def test_mx_rule_every_bf16_block_max(fmt, rule):
+    """Both block-exponent rules on blocks whose maxima run over every bf16
+    pattern (zeros, subnormals, the 1.75 significand boundary, Inf, NaN):
+    codes and scales equal the oracle's, for the row-block and the
+    transposed (column-block) entry points."""
+    bits = _every_bf16_as_block_max()
+    vals = oracle.bf16_bits_to_f64(bits)
+    say(f"mx rule {rule} {fmt.name}: every bf16 pattern as a block max")
+    rq, rs = oracle.mx_quantize(vals, fmt, rule=rule)
+    x = bf16_dev(bits)
+    q, s = sq.mx_quantize_rule(x, fmt.code, rule)
+    assert np.array_equal(host(s), rs)
+    assert np.array_equal(host(q), rq)
+    qT, sT = sq.mx_quantize_t_rule(x.T.contiguous(), fmt.code, rule)
+    assert np.array_equal(host(sT), rs)
+    assert np.array_equal(host(qT), rq)
+    if rule == "fmax":
+        q0, s0 = sq.mx_quantize(x, fmt.code)
+        assert np.array_equal(host(q0), rq) and np.array_equal(host(s0), rs)
+    else:
+        _, rs_f = oracle.mx_quantize(vals, fmt)
+        assert np.count_nonzero(rs != rs_f) > 1000         # the rules differ on many blocks
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: f.name)
+def test_mx_ocp_rule_f32_significand_boundary(fmt):
+    """f32 block maxima at and around significand 1.75 (the last ulp below,
+    1.75 itself, one ulp above, and just below 2) across binades, plus
+    strided and unaligned views, under the OCP rule."""
+    rng = np.random.default_rng(5)
+    sig = np.array([1.75 - 2.0 ** -23, 1.75, 1.75 + 2.0 ** -23, 2 - 2.0 ** -23, 1.0, 1.5])
+    exps = rng.integers(-140, 120, 64)
+    bmax = np.ldexp(sig[None, :], exps[:, None]).astype(np.float32).ravel()        # 384 blocks
+    blocks = bmax[:, None] * rng.uniform(-1, 1, (bmax.size, 32)).astype(np.float32)
+    blocks[:, 7] = bmax
+    vals = blocks.astype(np.float32).reshape(96, 128).astype(np.float64)
+    say(f"mx ocp rule {fmt.name}: f32 significand boundary")
+    rq, rs = oracle.mx_quantize(vals, fmt, rule="ocp")
+    x = f32_dev(vals.astype(np.float32))
+    q, s = sq.mx_quantize_rule(x, fmt.code, "ocp")
+    assert np.array_equal(host(s), rs) and np.array_equal(host(q), rq)
+    sub = x[3:, 32:96]                                   # strided: the scalar path
+    q2, s2 = sq.mx_quantize_rule(sub, fmt.code, "ocp")
+    rq2, rs2 = oracle.mx_quantize(vals[3:, 32:96], fmt, rule="ocp")
+    assert np.array_equal(host(s2), rs2) and np.array_equal(host(q2), rq2)
+    qT, sT = sq.mx_quantize_t_rule(x[:, 32:96], fmt.code, "ocp")   # strided transposed input
+    rqT, rsT = oracle.mx_quantize(np.ascontiguousarray(vals[:, 32:96].T), fmt, rule="ocp")
+    assert np.array_equal(host(sT), rsT) and np.array_equal(host(qT), rqT)
+
+
 def test_mx_rmse_below_per_tensor_c4_shape():
     bits = make("c4", "X", shape=(256, 1024))
     vals = oracle.bf16_bits_to_f64(bits)
