@@ -77,6 +77,7 @@ struct GemmArgs {
   float* out_amax;
   int out_f32;
   int vec_store;
+  int row16;                 // C and every row start 16-byte aligned (full-line bf16 stores)
   int sa_dword;            // scale rows 4-byte aligned: one dword per stage
   int sb_dword;
   int scales_dma;          // both scale matrices dword-aligned rows, K % 128 == 0, K >= 512
@@ -507,6 +508,12 @@ __device__ __forceinline__ v16f mfma32(v8i a, v8i b, v16f c, int sa, int oa, int
 //     copy zeros through zero-sized buffer descriptors and add nothing, so
 //     the loop body has no branches.  The wave drains its copies before the
 //     epilogue.
+//   * bf16 epilogue of an interior tile: a lane's accumulators are 4 n of
+//     one row, so direct stores would write 16 bytes in each of 32 rows per
+//     instruction; instead each 32 x 64 quarter of a wave's block row is
+//     staged in 4 KiB of LDS and written back as whole 128-byte row segments
+//     (measured +3% per-tensor, +5% MX on the 70B-MLP shape with every CU
+//     writing its tile at once).
 // ---------------------------------------------------------------------------
 // 32x32x64 operand: K sub-step h (bytes 64h..64h+63) of rows row0 + (l % 32);
 // lane l (g = l / 32) holds chunk 4h + g then 4h + 2 + g.  `base_lo/hi` are
@@ -563,6 +570,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint32_t s_scale[MX ? 2 * 2 * BM * 4 : 1];
   __shared__ uint32_t red[kGemmThreads / kWave];
   __shared__ uint32_t pf_sink[64];                  // landing words of the L2 prefetch (never read)
+  // bf16 epilogue staging, 4 KiB per wave (32 rows x 128 bytes of C).  MX
+  // has room for two waves' areas only: waves 0 and 1 stage in the scale
+  // slot the finished tile has released.
+  constexpr int kStage = 32 * 128;
+  __shared__ __attribute__((aligned(16))) uint8_t cstage[(MX ? 2 : 4) * kStage];
   constexpr int kRegB = 2 * kTileBytes;             // op(B) region offset (64 KiB)
   constexpr int kSlot = kTileBytes;                 // 32 KiB per slot per operand
   constexpr int kFrag = 32 * BK;                    // 4 KiB between 32-row fragments
@@ -861,8 +873,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     // stores) takes a straight-line path: one row pointer per block row,
     // immediate column offsets, bf16 maxima as packed 16-bit maxima of |h|;
     // edge tiles check every element.
-    if (m0 + BM <= g.M && n0 + BN <= g.N && g.vec_store) {
+    if (m0 + BM <= g.M && n0 + BN <= g.N && (g.out_f32 ? g.vec_store : g.row16)) {
       us2v pmax = {0, 0};
+      uint8_t* stg = cstage + (MX ? 0 : wave * kStage);
+      if constexpr (MX) {
+        const int fs = (gbase + ngroups - 1) & 1;     // scale slot of the tile's last group: free now
+        stg = wave < 2 ? reinterpret_cast<uint8_t*>(s_scale) + fs * (2 * BM * 16) + wave * kStage
+                       : cstage + (wave - 2) * kStage;
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t m = m0 + wm * 128 + j * 32 + (lane & 31);
@@ -885,20 +903,49 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
               }
             }
         } else {
-          uint16_t* crow = reinterpret_cast<uint16_t*>(g.C) + m * g.ldc + nb;
+          // bf16: each 32-row x 64-column quarter of the block row goes
+          // through the wave's LDS staging area so that a store instruction
+          // writes 8 whole 128-byte rows (one lane per 16 bytes) instead of
+          // 16 bytes in each of 32 rows.  Staging row r holds its 16-byte
+          // chunk c at chunk c ^ ((r >> 1) & 7): conflict-free for the 8-byte
+          // writes (16 rows per access) and the 16-byte reads (2 rows).
+          // lane-derived addresses are recomputed here: hoisted out of the
+          // tile loop they would be spilled and reloaded from scratch
+          int ln = lane;
+          asm volatile("" : "+v"(ln));
+          const uint32_t wr = (uint32_t)(ln & 31);
+          const uint32_t wbase = wr * 128 + 8 * (ln >> 5);
+          const uint32_t wsw = (wr >> 1) & 7;
+          // stores: the wave's C block base (uniform) plus a 32-bit byte
+          // offset (the host admits this path only if 128 rows span < 4 GiB)
+          uint8_t* const cw = reinterpret_cast<uint8_t*>(g.C) + ((m0 + wm * 128) * g.ldc + n0 + wn * 128) * 2;
+          const uint32_t ldcb = (uint32_t)g.ldc * 2u;
+          const uint32_t lr = (uint32_t)(ln >> 3), ch = (uint32_t)(ln & 7);
+          const uint32_t goff = lr * ldcb + 16u * ch;
+          const uint32_t rsw0 = lr * 128 + 16 * (ch ^ (lr >> 1)), rsw1 = lr * 128 + 16 * (ch ^ (lr >> 1) ^ 4u);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int p = 0; p < 2; ++p) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              float v[4];
+            for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                v[r] = MX ? acc[i][j][4 * q + r] : __builtin_amdgcn_ldexpf(acc[i][j][4 * q + r], e);
-              const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
-              *reinterpret_cast<uint2*>(crow + i * 32 + 8 * q) = make_uint2(lo, hi);
-              pmax = __builtin_elementwise_max(pmax, __builtin_bit_cast(us2v, lo & 0x7fff7fffu));
-              pmax = __builtin_elementwise_max(pmax, __builtin_bit_cast(us2v, hi & 0x7fff7fffu));
+              for (int q = 0; q < 4; ++q) {
+                const int i = 2 * p + ii;
+                float v[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  v[r] = MX ? acc[i][j][4 * q + r] : __builtin_amdgcn_ldexpf(acc[i][j][4 * q + r], e);
+                const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+                *reinterpret_cast<uint2*>(stg + wbase + 16 * ((uint32_t)(4 * ii + q) ^ wsw)) = make_uint2(lo, hi);
+                pmax = __builtin_elementwise_max(pmax, __builtin_bit_cast(us2v, lo & 0x7fff7fffu));
+                pmax = __builtin_elementwise_max(pmax, __builtin_bit_cast(us2v, hi & 0x7fff7fffu));
+              }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              // row 8k + lr, chunk ch; its swizzle (row >> 1) & 7 = (lr >> 1) ^ 4 (k & 1)
+              const uint4 d = *reinterpret_cast<const uint4*>(stg + 8 * k * 128 + ((k & 1) ? rsw1 : rsw0));
+              *reinterpret_cast<uint4*>(cw + goff + (uint32_t)(j * 32 + 8 * k) * ldcb + p * 128) = d;
             }
+          }
         }
       }
       const uint32_t pm = ((uint32_t)(pmax[0] > pmax[1] ? pmax[0] : pmax[1])) << 16;
@@ -1059,6 +1106,7 @@ int fp8_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int fmt_a
   g.C = C; g.ldc = ldc; g.out_amax = out_amax;
   g.out_f32 = out_dtype == FP8_DT_F32;
   g.vec_store = g.out_f32 ? (aligned(C, 16) && ldc % 4 == 0) : (aligned(C, 8) && ldc % 4 == 0);
+  g.row16 = aligned(C, 16) && (ldc * (g.out_f32 ? 4 : 2)) % 16 == 0 && ldc * 2 * BM < (1LL << 32);
   const bool ta = trans_a != 0, tb = trans_b != 0;
   if (fmt_a == FP8_E4M3 && fmt_b == FP8_E4M3) dispatch_trans<FP8_E4M3, FP8_E4M3>(g, ta, tb, stream);
   else if (fmt_a == FP8_E5M2 && fmt_b == FP8_E4M3) dispatch_trans<FP8_E5M2, FP8_E4M3>(g, ta, tb, stream);
@@ -1098,6 +1146,7 @@ int mx_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int fmt_a,
   g.C = C; g.ldc = ldc; g.out_amax = out_amax;
   g.out_f32 = out_dtype == FP8_DT_F32;
   g.vec_store = g.out_f32 ? (aligned(C, 16) && ldc % 4 == 0) : (aligned(C, 8) && ldc % 4 == 0);
+  g.row16 = aligned(C, 16) && (ldc * (g.out_f32 ? 4 : 2)) % 16 == 0 && ldc * 2 * BM < (1LL << 32);
   if (fmt_a == FP8_E4M3 && fmt_b == FP8_E4M3) launch_gemm<FP8_E4M3, FP8_E4M3, true, false, false>(g, stream);
   else if (fmt_a == FP8_E5M2 && fmt_b == FP8_E4M3) launch_gemm<FP8_E5M2, FP8_E4M3, true, false, false>(g, stream);
   else if (fmt_a == FP8_E4M3 && fmt_b == FP8_E5M2) launch_gemm<FP8_E4M3, FP8_E5M2, true, false, false>(g, stream);

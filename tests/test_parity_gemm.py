@@ -101,6 +101,46 @@ def test_gemm_k_multiple_of_128(fa, fb, K):
     _check_amax(C, am)
 
 
+@pytest.mark.parametrize("mx", [False, True], ids=["pt", "mx"])
+def test_gemm_bf16_padded_outputs(mx):
+    """bf16 C written into padded views, 2 x 2 interior tiles: row stride
+    N + 8 (rows 16-byte aligned: whole-row staged stores) and an 8-byte
+    offset with stride N + 4 (rows only 8-byte aligned: per-element path).
+    Results equal the oracle's and the padding is left untouched."""
+    rng = np.random.default_rng(41)
+    M, N, K = 512, 512, 512                 # K >= 512: MX also takes the forward kernel
+    qa, ba = _operand(rng, (M, K), 1.0, E4M3)
+    qb, bb = _operand(rng, (N, K), 0.02, E4M3)
+    if mx:
+        sa = rng.integers(118, 136, (M, K // 32)).astype(np.uint8)
+        sb = rng.integers(118, 136, (N, K // 32)).astype(np.uint8)
+        ref = oracle.mx_gemm_ref(qa, sa, E4M3, qb, sb, E4M3)
+        s = oracle.mx_abs_product_sum(qa, sa, E4M3, qb, sb, E4M3)
+        gt = mfma_group_term(oracle.mx_dequantize(qa, sa, E4M3), oracle.mx_dequantize(qb, sb, E4M3))
+    else:
+        ref = oracle.scaled_gemm_ref(qa, E4M3, ba, qb, E4M3, bb)
+        s = oracle.abs_product_sum(qa, E4M3, ba, qb, E4M3, bb)
+        gt = mfma_group_term(oracle.dequantize(qa, E4M3, ba), oracle.dequantize(qb, E4M3, bb))
+    for pad, off in ((8, 0), (4, 4)):
+        say(f"gemm bf16 padded out mx={mx} stride N+{pad} offset {off}")
+        big = torch.full((M, N + pad + off), -7.0, dtype=torch.bfloat16, device=DEV)
+        flat = big.view(-1)[off:off + M * (N + pad)].view(M, N + pad)
+        out = flat[:, :N]
+        if mx:
+            _, am = sq.mx_scaled_gemm(u8_dev(qa), E4M3.code, u8_dev(sa), u8_dev(qb), E4M3.code, u8_dev(sb),
+                                      out=out, want_amax=True)
+        else:
+            _, am = sq.fp8_scaled_gemm(u8_dev(qa), E4M3.code, i32_dev(ba), u8_dev(qb), E4M3.code, i32_dev(bb),
+                                       out=out, want_amax=True)
+        assert_gemm_close(host_f64(out), ref, s, True, f"padded out N+{pad}", gt)
+        _check_amax(out, am)
+        hb = host_f64(big).ravel()
+        written = np.zeros(hb.size, dtype=bool)
+        idx = off + np.arange(M)[:, None] * (N + pad) + np.arange(N)[None, :]
+        written[idx.ravel()] = True
+        assert np.all(hb[~written] == -7.0)
+
+
 @pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)], ids=["NT", "TN", "TT"])
 def test_gemm_transposed_operands(ta, tb):
     """Transposed storage for op(A) / op(B) (the backward products): M, N
