@@ -449,17 +449,30 @@ __device__ __forceinline__ v4i uniform_srd(v4i r) {
   return u;
 }
 
+// The compiler's hazard checks do not look inside inline assembly, so the
+// copies below carry the wait states themselves: an LDS DMA needs one after
+// the SALU write of M0, and a VMEM instruction needs five after a VALU
+// (v_readfirstlane) wrote one of its SGPR operands.  W is the number of wait
+// states placed between the M0 write and the load: 5 where the descriptor or
+// soffset may have just come from v_readfirstlane (the first copy of each
+// operand in a stage, where the compiler re-materialises descriptors it has
+// moved to VGPRs; the scale copies; the prefetch), 1 elsewhere.
+//
 // 16 bytes per lane from buffer offset off + soff to LDS lds_addr + 16 * lane
 // (lds_addr and soff wave-uniform).
+template <int W>
 __device__ __forceinline__ void dma_b128_so(v4i srd, uint32_t lds_addr, uint32_t off, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
-               :: "v"(off), "s"(lds_addr), "s"(srd), "s"(soff) : "memory", "m0");
+  static_assert(W >= 1 && W <= 16, "wait states");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop %4\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
+               :: "v"(off), "s"(lds_addr), "s"(srd), "s"(soff), "i"(W - 1) : "memory", "m0");
 }
 
 // 4 bytes per lane from buffer offset off + soff to LDS lds_addr + 4 * lane.
+template <int W>
 __device__ __forceinline__ void dma_b32_so(v4i srd, uint32_t lds_addr, uint32_t off, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dword %0, %2, %3 offen lds"
-               :: "v"(off), "s"(lds_addr), "s"(srd), "s"(soff) : "memory", "m0");
+  static_assert(W >= 1 && W <= 16, "wait states");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop %4\n\tbuffer_load_dword %0, %2, %3 offen lds"
+               :: "v"(off), "s"(lds_addr), "s"(srd), "s"(soff), "i"(W - 1) : "memory", "m0");
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight.
@@ -685,7 +698,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     v4i srd = isb ? cur.b : cur.a;
     if constexpr (PERSIST) srd = nx ? (isb ? nxt.b : nxt.a) : srd;
     srd[2] = live ? srd[2] : 0;
-    dma_b128_so(uniform_srd(srd), __builtin_amdgcn_readfirstlane(la), off, __builtin_amdgcn_readfirstlane(k0));
+    if ((t & 7) == 0)
+      dma_b128_so<5>(uniform_srd(srd), __builtin_amdgcn_readfirstlane(la), off, __builtin_amdgcn_readfirstlane(k0));
+    else
+      dma_b128_so<1>(uniform_srd(srd), __builtin_amdgcn_readfirstlane(la), off, __builtin_amdgcn_readfirstlane(k0));
   };
   // prefetch of op(B) stage s (descriptor choice as for the copies)
   auto prefetch_b = [&](int s, bool owner) {
@@ -695,7 +711,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     v4i srd = cur.b;
     if constexpr (PERSIST) srd = nx ? nxt.b : srd;
     srd[2] = live ? srd[2] : 0;
-    dma_b32_so(uniform_srd(srd), pf_lds, pfb, __builtin_amdgcn_readfirstlane(k0));
+    dma_b32_so<5>(uniform_srd(srd), pf_lds, pfb, __builtin_amdgcn_readfirstlane(k0));
   };
   // Scale group G of the current tile, 0 <= G <= ngroups (G == ngroups: the
   // next tile's group 0, whose copy starts at block 0).
@@ -712,8 +728,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
         sa[2] = nx ? 0 : sa[2];                     // no next tile: zeros
         sb[2] = nx ? 0 : sb[2];
       }
-      dma_b128_so(uniform_srd(sa), __builtin_amdgcn_readfirstlane(la), offsa, __builtin_amdgcn_readfirstlane(so));
-      dma_b128_so(uniform_srd(sb), __builtin_amdgcn_readfirstlane(la + BM * 16), offsb,
+      dma_b128_so<5>(uniform_srd(sa), __builtin_amdgcn_readfirstlane(la), offsa, __builtin_amdgcn_readfirstlane(so));
+      dma_b128_so<5>(uniform_srd(sb), __builtin_amdgcn_readfirstlane(la + BM * 16), offsb,
                   __builtin_amdgcn_readfirstlane(so));
     }
   };
@@ -760,7 +776,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   for (int t = 0; t < LPS; ++t) dma(0, t);
 #pragma unroll
   for (int t = 0; t < LPS; ++t) dma(1, t);
-  wait_vm<LPS>();
+  // Every stage's copy wait (wait_vm<1>) leaves one copy in flight: the L2
+  // prefetch each stage issues last.  The prologue ends with one too (stage
+  // 7's, which no stage prefetches), so that stage 0's wait covers all of
+  // stage 1's copies; without it the last copy of stage 1 could still be in
+  // flight when the barrier publishes the stage.
+  prefetch_b(7, pf_owner);
+  wait_vm<LPS + 1>();
   __syncthreads();
   v8i x0[4], w0[4], x1[4], w1[4];
   int sc[2][8] = {};                                 // scales of the stages in slots 0 and 1

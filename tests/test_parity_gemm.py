@@ -408,3 +408,99 @@ def test_backward_shapes_7b_mlp_sampled():
                                   rows, cols)
     assert_gemm_close(host_f64(dW[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)]), y, s,
                       False, "dW")
+
+
+def _repeat_identical(fn, reps, what):
+    """Run fn(out) `reps` times into NaN-filled outputs; every run must give
+    the first run's output and fused amax bit for bit."""
+    ref, ref_am = None, None
+    for r in range(reps):
+        out = ref if ref is None else torch.empty_like(ref)
+        out = fn(out)
+        C, am = out
+        torch.cuda.synchronize()
+        if ref is None:
+            ref, ref_am = C, f32_bits_of(am)
+            continue
+        nd = int((C.view(torch.int16) != ref.view(torch.int16)).sum())
+        assert nd == 0, f"{what}: repeat {r} differs from the first run in {nd} outputs"
+        assert f32_bits_of(am) == ref_am, f"{what}: repeat {r} fused amax differs"
+        del C
+
+
+@pytest.mark.parametrize("mx", [False, True], ids=["pt", "mx"])
+def test_full_size_70b_mlp_gemm_repeat_bit_identical(mx):
+    """Run-to-run determinism of the 70B-MLP GEMMs (16384 x 28672 x 8192,
+    bf16 out) over every output element: eight launches on the same operands
+    must agree bit for bit.  Each launch writes into a NaN-filled buffer, so an
+    output the kernel failed to write also shows.  (A missing copy wait once
+    left one 8-row block of a stage unpublished in rare tiles: ~1e-5 of the
+    outputs changed from run to run, which sampled parity could not see.)"""
+    g = torch.Generator(device=DEV).manual_seed(5)
+    x = torch.randn(16384, 8192, device=DEV, dtype=torch.bfloat16, generator=g)
+    w = torch.randn(28672, 8192, device=DEV, dtype=torch.bfloat16, generator=g) * 0.015
+    if mx:
+        qx, sx = sq.mx_quantize(x, 0)
+        qw, sw = sq.mx_quantize(w, 0)
+    else:
+        bx, _, _ = sq.fp8_compute_scale(sq.fp8_amax(x), 0, 0)
+        bw, _, _ = sq.fp8_compute_scale(sq.fp8_amax(w), 0, 0)
+        qx, _, _ = sq.fp8_quantize(x, 0, bx)
+        qw, _, _ = sq.fp8_quantize(w, 0, bw)
+    del x, w
+    torch.cuda.empty_cache()
+
+    def launch(out):
+        if out is None:
+            out = torch.empty(16384, 28672, device=DEV, dtype=torch.bfloat16)
+        out.fill_(float("nan"))
+        if mx:
+            return sq.mx_scaled_gemm(qx, 0, sx, qw, 0, sw, out=out, want_amax=True)
+        return sq.fp8_scaled_gemm(qx, 0, bx, qw, 0, bw, out=out, want_amax=True)
+
+    say(f"70b-mlp {'mx' if mx else 'per-tensor'} gemm x8 determinism")
+    _repeat_identical(launch, 8, "mx" if mx else "per-tensor")
+
+
+@pytest.mark.parametrize("mx", [False, True], ids=["pt", "mx"])
+def test_backward_7b_mlp_gemms_repeat_bit_identical(mx):
+    """Run-to-run determinism of the transposed-operand products of the 7B-MLP
+    backward (dX = dY W: 4096 x 4096 x 11008 with op(B) stored transposed;
+    dW = dY^T X: 11008 x 4096 x 4096 with both stored transposed), and of the
+    MX products over the transposed casts, four launches each."""
+    g = torch.Generator(device=DEV).manual_seed(6)
+    dy = torch.randn(4096, 11008, device=DEV, dtype=torch.bfloat16, generator=g) * 1e-4
+    w = torch.randn(11008, 4096, device=DEV, dtype=torch.bfloat16, generator=g) * 0.02
+    x = torch.randn(4096, 4096, device=DEV, dtype=torch.bfloat16, generator=g)
+    if mx:
+        qdy, sdy = sq.mx_quantize(dy, 1)
+        qwt, swt = sq.mx_quantize_t(w, 0)           # W^T [4096 x 11008]: blocks along 11008
+        qdyt, sdyt = sq.mx_quantize_t(dy, 1)        # dY^T [11008 x 4096]
+        qxt, sxt = sq.mx_quantize_t(x, 0)           # X^T [4096 x 4096]
+        cases = [
+            ("mx dX", lambda out: sq.mx_scaled_gemm(qdy, 1, sdy, qwt, 0, swt, out=out, want_amax=True),
+             (4096, 4096)),
+            ("mx dW", lambda out: sq.mx_scaled_gemm(qdyt, 1, sdyt, qxt, 0, sxt, out=out, want_amax=True),
+             (11008, 4096)),
+        ]
+    else:
+        bdy, _, _ = sq.fp8_compute_scale(sq.fp8_amax(dy), 1, 0)
+        bw, _, _ = sq.fp8_compute_scale(sq.fp8_amax(w), 0, 0)
+        bx, _, _ = sq.fp8_compute_scale(sq.fp8_amax(x), 0, 0)
+        qdy, _, _ = sq.fp8_quantize(dy, 1, bdy)
+        qw, _, _ = sq.fp8_quantize(w, 0, bw)
+        qx, _, _ = sq.fp8_quantize(x, 0, bx)
+        cases = [
+            ("dX", lambda out: sq.fp8_scaled_gemm(qdy, 1, bdy, qw, 0, bw, trans_b=True, out=out, want_amax=True),
+             (4096, 4096)),
+            ("dW", lambda out: sq.fp8_scaled_gemm(qdy, 1, bdy, qx, 0, bx, trans_a=True, trans_b=True, out=out,
+                                                  want_amax=True), (11008, 4096)),
+        ]
+    for name, fn, shape in cases:
+        def launch(out, fn=fn, shape=shape):
+            if out is None:
+                out = torch.empty(shape, device=DEV, dtype=torch.bfloat16)
+            out.fill_(float("nan"))
+            return fn(out)
+        say(f"7b-mlp backward {name} x4 determinism")
+        _repeat_identical(launch, 4, name)
