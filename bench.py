@@ -37,8 +37,8 @@ WORKLOAD = "llama2_70b_mlp_16384x28672x8192"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
@@ -96,6 +96,18 @@ def cpu_baseline(xb, wb, target_s: float):
                    f"reference GEMMs for {t_gemm:.1f} s ({gemm_rate / 1e9:.1f} GFLOP/s, BLAS threads={threads}); "
                    f"extrapolated to the full step: {full_time:.0f} s"),
     }
+
+
+def gpu_sclk():
+    """Current shader clock as reported by rocm-smi (a child process, after
+    the timed region); None where the tool is missing or prints no sclk."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    lines = [ln.strip() for ln in r.stdout.splitlines() if "sclk" in ln.lower()]
+    return lines[0] if lines else None
 
 
 def backward_extras(dev, reps: int = 5):
@@ -254,8 +266,11 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
-    per = {nm: sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)) / args.steps
-           for i, nm in enumerate(names)}
+    samples = {nm: sorted(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps))
+               for i, nm in enumerate(names)}
+    per = {nm: sum(v) / len(v) for nm, v in samples.items()}
+    per_median = {nm: v[len(v) // 2] for nm, v in samples.items()}
+    per_min = {nm: v[0] for nm, v in samples.items()}
 
     # empirically achievable HBM rate: a plain 1 GiB device-to-device copy,
     # timed after (outside) the timed region
@@ -287,6 +302,8 @@ def main():
         "gemm_pt_TFLOPs": gemm_flops / per["gemm_pt"] / 1e9,
         "gemm_mx_TFLOPs": gemm_flops / per["gemm_mx"] / 1e9,
         "ms": {k: round(v, 4) for k, v in per.items()},
+        "ms_median": {k: round(v, 4) for k, v in per_median.items()},
+        "ms_min": {k: round(v, 4) for k, v in per_min.items()},
     }
     dom = "gemm_pt" if per["gemm_pt"] >= per["gemm_mx"] else "gemm_mx"
     achieved = gemm_flops / per[dom] / 1e9
@@ -321,6 +338,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(xb, wb, args.cpu_seconds)
+    sclk = gpu_sclk()
 
     out = {
         "metric": "scaled FP8 GEMM TFLOP/s + amax/quantize GB/s (per-tensor, MXFP8), 1 GPU",
@@ -345,6 +363,7 @@ def main():
         "cpu_baseline": cpu,
         "extras": extras,
         "input_generation_s": round(gen_s, 1),
+        "gpu_sclk": sclk,
     }
     print(json.dumps(out), flush=True)
 
