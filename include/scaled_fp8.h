@@ -249,6 +249,51 @@ int mx_scaled_gemm(int64_t M, int64_t N, int64_t K,
                    void* C, int out_dtype, int64_t ldc, float* out_amax,
                    hipStream_t stream);
 
+/*
+ * Packed E8M0 scale layout for the block-scaled GEMM.  The per-block scales of
+ * "Key Questions Answered" (summary page) are the same codes as mx_quantize
+ * writes; only their order in memory changes, so that the GEMM copies whole
+ * cache lines of them (a row-major [rows x K/32] matrix hands it 16 bytes per
+ * row, one cache line per row per 4 K-stages).
+ *
+ * Layout: rows are grouped in tiles of 256, K-blocks in groups of 16 (512 K
+ * elements); each (tile t, group g) is one 4096-byte block holding, for
+ * r = 0..255, the 16 codes of row 256 t + r, blocks 16 g .. 16 g + 15.  The
+ * code of (row, block j) sits at byte
+ *     ((row / 256) * G + j / 16) * 4096 + (row % 256) * 16 + j % 16,
+ * with G = ceil(kblocks / 16).  Positions past the matrix (rows >= rows,
+ * j >= kblocks) hold 127 (scale 1).
+ */
+
+/* Size in bytes of the packed layout of a [rows x kblocks] E8M0 matrix:
+ * ceil(rows / 256) * ceil(kblocks / 16) * 4096 (FP8_ERR_SHAPE if negative).
+ * Host-only; no HIP call. */
+int64_t mx_packed_scales_bytes(int64_t rows, int64_t kblocks);
+
+/*
+ * mx_pack_scales — rewrite row-major E8M0 codes scales [rows x kblocks]
+ * (leading dimension ld_scales bytes, any alignment) into the packed layout
+ * above.  packed: mx_packed_scales_bytes(rows, kblocks) bytes, 16-byte
+ * aligned (else FP8_ERR_ALIGN).  Every byte of `packed` is written, padding
+ * included.
+ */
+int mx_pack_scales(const uint8_t* scales, int64_t rows, int64_t kblocks, int64_t ld_scales,
+                   uint8_t* packed, hipStream_t stream);
+
+/*
+ * mx_scaled_gemm_packed — mx_scaled_gemm with both scale operands in the
+ * packed layout (A_packed from mx_pack_scales of A's [M x K/32] codes,
+ * B_packed of B's [N x K/32] codes).  Same result, bit for bit, as
+ * mx_scaled_gemm on the row-major codes.  Requirements: those of
+ * mx_scaled_gemm, plus K % 128 == 0 and K >= 512 (else FP8_ERR_UNSUPPORTED:
+ * use mx_scaled_gemm) and 16-byte aligned packed buffers (FP8_ERR_ALIGN).
+ */
+int mx_scaled_gemm_packed(int64_t M, int64_t N, int64_t K,
+                          const uint8_t* A, int fmt_a, int64_t lda, const uint8_t* A_packed,
+                          const uint8_t* B, int fmt_b, int64_t ldb, const uint8_t* B_packed,
+                          void* C, int out_dtype, int64_t ldc, float* out_amax,
+                          hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

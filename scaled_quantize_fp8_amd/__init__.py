@@ -26,6 +26,7 @@ __all__ = [
     "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize", "mx_quantize_t",
     "mx_quantize_rule", "mx_quantize_t_rule", "MX_RULE_FMAX", "MX_RULE_OCP",
     "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string", "fp8_abi_version",
+    "mx_packed_scales_bytes", "mx_pack_scales", "mx_scaled_gemm_packed",
 ]
 
 E4M3 = 0
@@ -62,6 +63,10 @@ _SIGNATURES = {
                          _p, _i, _i64, _p, _p], _i),
     "mx_scaled_gemm": ([_i64, _i64, _i64, _p, _i, _i64, _p, _i64, _p, _i, _i64, _p, _i64,
                         _p, _i, _i64, _p, _p], _i),
+    "mx_packed_scales_bytes": ([_i64, _i64], _i64),
+    "mx_pack_scales": ([_p, _i64, _i64, _i64, _p, _p], _i),
+    "mx_scaled_gemm_packed": ([_i64, _i64, _i64, _p, _i, _i64, _p, _p, _i, _i64, _p,
+                               _p, _i, _i64, _p, _p], _i),
 }
 
 
@@ -407,4 +412,66 @@ def mx_scaled_gemm(A: torch.Tensor, fmt_a, A_scales: torch.Tensor, B: torch.Tens
     _check("mx_scaled_gemm", load_library().mx_scaled_gemm(
         M, N, K, _ptr(A), _fmt(fmt_a), lda, _ptr(A_scales), lds_a, _ptr(B), _fmt(fmt_b), ldb,
         _ptr(B_scales), lds_b, _ptr(out), _out_code(out.dtype), ldc, _ptr(amax_out), _stream(A)))
+    return out, amax_out
+
+
+def mx_packed_scales_bytes(rows: int, kblocks: int) -> int:
+    """Bytes of the packed E8M0 layout of a [rows x kblocks] scale matrix:
+    ceil(rows / 256) * ceil(kblocks / 16) * 4096."""
+    n = load_library().mx_packed_scales_bytes(int(rows), int(kblocks))
+    if n < 0:
+        raise Fp8Error("mx_packed_scales_bytes", n)
+    return n
+
+
+def mx_pack_scales(scales: torch.Tensor, packed: torch.Tensor | None = None) -> torch.Tensor:
+    """E8M0 codes [rows x kblocks] (row-major, as mx_quantize writes them) in
+    the packed layout mx_scaled_gemm_packed reads: a 1-D uint8 tensor of
+    mx_packed_scales_bytes(rows, kblocks) bytes."""
+    _u8(scales, "scales")
+    rows, kb, ld = _mat(scales, "scales")
+    n = mx_packed_scales_bytes(rows, kb)
+    if packed is None:
+        packed = torch.empty(n, dtype=torch.uint8, device=scales.device)
+    _u8(packed, "packed")
+    if packed.dim() != 1 or packed.numel() != n or not packed.is_contiguous():
+        raise ValueError(f"packed must be a contiguous 1-D uint8 tensor of {n} bytes")
+    _check("mx_pack_scales", load_library().mx_pack_scales(_ptr(scales), rows, kb, ld, _ptr(packed),
+                                                           _stream(scales)))
+    return packed
+
+
+def mx_scaled_gemm_packed(A: torch.Tensor, fmt_a, A_packed: torch.Tensor, B: torch.Tensor, fmt_b,
+                          B_packed: torch.Tensor, out_dtype: torch.dtype = torch.bfloat16,
+                          want_amax: bool = False, out: torch.Tensor | None = None,
+                          amax_out: torch.Tensor | None = None):
+    """mx_scaled_gemm with both scale operands in the packed layout
+    (mx_pack_scales of A's [M x K/32] and B's [N x K/32] codes); needs
+    K % 128 == 0 and K >= 512.  Returns (C, amax of C or None)."""
+    _u8(A, "A")
+    _u8(B, "B")
+    _u8(A_packed, "A_packed")
+    _u8(B_packed, "B_packed")
+    M, K, lda = _mat(A, "A")
+    N, Kb, ldb = _mat(B, "B")
+    if K != Kb:
+        raise ValueError(f"inner dimensions differ: {K} vs {Kb}")
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    for t, rows, name in ((A_packed, M, "A_packed"), (B_packed, N, "B_packed")):
+        if t.numel() != mx_packed_scales_bytes(rows, K // 32) or not t.is_contiguous():
+            raise ValueError(f"{name} must be the packed scales of a [{rows} x {K // 32}] matrix")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    _dev(out, "out")
+    orow, ocol, ldc = _mat(out, "out")
+    if (orow, ocol) != (M, N):
+        raise ValueError("out must be [M x N]")
+    if want_amax or amax_out is not None:
+        if amax_out is None:
+            amax_out = torch.empty(1, dtype=torch.float32, device=A.device)
+        _scalar(amax_out, torch.float32, "amax_out")
+    _check("mx_scaled_gemm_packed", load_library().mx_scaled_gemm_packed(
+        M, N, K, _ptr(A), _fmt(fmt_a), lda, _ptr(A_packed), _ptr(B), _fmt(fmt_b), ldb, _ptr(B_packed),
+        _ptr(out), _out_code(out.dtype), ldc, _ptr(amax_out), _stream(A)))
     return out, amax_out

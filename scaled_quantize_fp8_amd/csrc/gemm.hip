@@ -52,6 +52,9 @@ constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int kGemmThreads = 256;
 constexpr int kGroupM = 8;
 constexpr int kTileBytes = BM * BK;          // 32 KiB per operand per stage
+// Packed E8M0 layout (mx_pack_scales): per 256-row tile and per group of 16
+// K-blocks (4 K stages), 256 rows x 16 codes = 4 KiB contiguous.
+constexpr int kPackRows = 256, kPackBlocks = 16, kPackTile = kPackRows * kPackBlocks;
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 4)) & 7; }
 
@@ -81,6 +84,8 @@ struct GemmArgs {
   int sa_dword;            // scale rows 4-byte aligned: one dword per stage
   int sb_dword;
   int scales_dma;          // both scale matrices dword-aligned rows, K % 128 == 0, K >= 512
+  int scales_packed;       // sa / sb in the tiled layout of mx_pack_scales (forward kernel only)
+  int64_t sgroups;         // packed layout: 16-block groups per row, ceil(K / 512)
 };
 
 // ---- buffer resources ------------------------------------------------------
@@ -610,6 +615,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   const int nkU = (nk + U - 1) / U * U;             // stages run per tile (zero stages past nk)
   const int ngroups = nkU / 4;                      // MX scale copies per tile
   const int last_g = (nk - 1) >> 2;                 // last group holding real stages
+  const bool pk = MX && g.scales_packed;            // tiled scale layout (uniform)
 
   auto make_tile = [&](int vb, TileSrd& T) {
     if (vb < tiles && (PERSIST || vb == (int)blockIdx.x)) {
@@ -620,8 +626,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
       T.a = make_srd(g.A + m0 * g.lda, (ra - 1) * g.lda + g.K);
       T.b = make_srd(g.B + n0 * g.ldb, (rb - 1) * g.ldb + g.K);
       if constexpr (MX) {
-        T.sa = make_srd(g.sa + m0 * g.lds_a, (ra - 1) * g.lds_a + nkb);
-        T.sb = make_srd(g.sb + n0 * g.lds_b, (rb - 1) * g.lds_b + nkb);
+        if (g.scales_packed) {
+          // one 256-row tile of the packed layout: sgroups x 4 KiB, rows past
+          // the matrix padded with code 127 by mx_pack_scales
+          const int64_t tb = g.sgroups * (int64_t)kPackTile;
+          T.sa = make_srd(g.sa + (int64_t)tm * tb, tb);
+          T.sb = make_srd(g.sb + (int64_t)tn * tb, tb);
+        } else {
+          T.sa = make_srd(g.sa + m0 * g.lds_a, (ra - 1) * g.lds_a + nkb);
+          T.sb = make_srd(g.sb + n0 * g.lds_b, (rb - 1) * g.lds_b + nkb);
+        }
       } else {
         T.sa = T.a;
         T.sb = T.b;
@@ -665,8 +679,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   uint32_t offsa = 0, offsb = 0, ldss = 0;
   if constexpr (MX) {
     const int row = wave * 64 + lane;
-    offsa = (uint32_t)(row * g.lds_a);
-    offsb = (uint32_t)(row * g.lds_b);
+    offsa = (uint32_t)(g.scales_packed ? row * 16 : row * g.lds_a);
+    offsb = (uint32_t)(g.scales_packed ? row * 16 : row * g.lds_b);
     ldss = __builtin_amdgcn_readfirstlane(lds_offset(s_scale));
   }
 
@@ -718,7 +732,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   auto scale_dma = [&](int G) {
     if constexpr (MX) {
       const bool nx = G >= ngroups;
-      const uint32_t so = (uint32_t)(nx ? 0 : (G < last_g ? 16 * G : nkb - 16));
+      // packed: group G is the 4 KiB block G of the tile (whole lines);
+      // row-major: bytes 16 G.. of each row, the last group clamped to end at
+      // the row's end
+      const uint32_t so = (uint32_t)(nx ? 0 : (pk ? G * kPackTile : (G < last_g ? 16 * G : nkb - 16)));
       const uint32_t la = ldss + (uint32_t)((((gbase + G) & 1) * 2 * BM + wave * 64) * 16);
       v4i sa = cur.sa, sb = cur.sb;
       if constexpr (PERSIST) {
@@ -747,7 +764,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
       const bool nx = s >= nkU;
       const int kc = s < nk ? s : nk - 1;
       const int G0 = kc >> 2;
-      const int d0 = G0 < last_g ? (kc & 3) : kc - (nk - 4);  // dword of stage kc in its copy
+      const int d0 = (pk || G0 < last_g) ? (kc & 3) : kc - (nk - 4);  // dword of stage kc in its copy
       const int G = nx ? ngroups : G0;
       const int d = nx ? 0 : d0;
       const int gs = (gbase + G) & 1;
@@ -1094,6 +1111,44 @@ static void dispatch_trans(const GemmArgs& g, bool ta, bool tb, hipStream_t s) {
   else launch_gemm<FA, FB, false, true, true>(g, s);
 }
 
+// Row-major E8M0 codes [rows x kb] -> the packed layout the forward MX GEMM
+// copies whole lines of: chunk c (16 bytes) = codes [16 grp, 16 grp + 16) of
+// row 256 t + r, with c = (t * sgroups + grp) * 256 + r; codes past the
+// matrix (rows >= rows, blocks >= kb) are 127 (scale 1).  One lane per chunk:
+// consecutive lanes write consecutive chunks.
+__global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restrict__ src, int64_t rows, int64_t kb,
+                                                          int64_t ld, uint8_t* __restrict__ dst, int64_t sgroups,
+                                                          int64_t nchunks, int vec) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= nchunks) return;
+  const int64_t r = c % kPackRows, tg = c / kPackRows;
+  const int64_t grp = tg % sgroups, t = tg / sgroups;
+  const int64_t row = t * kPackRows + r, j0 = grp * kPackBlocks;
+  uint4 v;
+  if (vec && row < rows && j0 + kPackBlocks <= kb) {
+    v = *reinterpret_cast<const uint4*>(src + row * ld + j0);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int64_t j = j0 + 4 * q + b;
+        const uint32_t code = (row < rows && j < kb) ? src[row * ld + j] : 0x7fu;
+        x |= code << (8 * b);
+      }
+      w[q] = x;
+    }
+    v = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  *reinterpret_cast<uint4*>(dst + c * 16) = v;
+}
+
+static int64_t packed_bytes(int64_t rows, int64_t kb) {
+  return ((rows + kPackRows - 1) / kPackRows) * ((kb + kPackBlocks - 1) / kPackBlocks) * (int64_t)kPackTile;
+}
+
 // 16-byte loads need 16-byte aligned rows; buffer offsets are 32-bit, so a
 // K-contiguous tile (256 rows) or a transposed operand (K rows) must span
 // less than 2 GiB.
@@ -1138,6 +1193,7 @@ int fp8_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int fmt_a
   g.bias_a = bias_a; g.bias_b = bias_b;
   g.sa = nullptr; g.lds_a = 0; g.sb = nullptr; g.lds_b = 0;
   g.sa_dword = 0; g.sb_dword = 0; g.scales_dma = 0;
+  g.scales_packed = 0; g.sgroups = 0;
   g.C = C; g.ldc = ldc; g.out_amax = out_amax;
   g.out_f32 = out_dtype == FP8_DT_F32;
   g.vec_store = g.out_f32 ? (aligned(C, 16) && ldc % 4 == 0) : (aligned(C, 8) && ldc % 4 == 0);
@@ -1178,6 +1234,67 @@ int mx_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int fmt_a,
   g.sa_dword = aligned(A_scales, 4) && (lds_a % 4) == 0;
   g.sb_dword = aligned(B_scales, 4) && (lds_b % 4) == 0;
   g.scales_dma = g.sa_dword && g.sb_dword && (K % 128) == 0 && K >= 512 && lds_a < (1LL << 23) && lds_b < (1LL << 23);
+  g.scales_packed = 0; g.sgroups = 0;
+  g.C = C; g.ldc = ldc; g.out_amax = out_amax;
+  g.out_f32 = out_dtype == FP8_DT_F32;
+  g.vec_store = g.out_f32 ? (aligned(C, 16) && ldc % 4 == 0) : (aligned(C, 8) && ldc % 4 == 0);
+  g.row16 = aligned(C, 16) && (ldc * (g.out_f32 ? 4 : 2)) % 16 == 0 && ldc * 2 * BM < (1LL << 32);
+  if (fmt_a == FP8_E4M3 && fmt_b == FP8_E4M3) launch_gemm<FP8_E4M3, FP8_E4M3, true, false, false>(g, stream);
+  else if (fmt_a == FP8_E5M2 && fmt_b == FP8_E4M3) launch_gemm<FP8_E5M2, FP8_E4M3, true, false, false>(g, stream);
+  else if (fmt_a == FP8_E4M3 && fmt_b == FP8_E5M2) launch_gemm<FP8_E4M3, FP8_E5M2, true, false, false>(g, stream);
+  else launch_gemm<FP8_E5M2, FP8_E5M2, true, false, false>(g, stream);
+  return launch_status();
+}
+
+int64_t mx_packed_scales_bytes(int64_t rows, int64_t kblocks) {
+  if (rows < 0 || kblocks < 0) return FP8_ERR_SHAPE;
+  return packed_bytes(rows, kblocks);
+}
+
+int mx_pack_scales(const uint8_t* scales, int64_t rows, int64_t kblocks, int64_t ld_scales, uint8_t* packed,
+                   hipStream_t stream) {
+  if (int st = check_matrix(rows, kblocks, ld_scales)) return st;
+  const int64_t bytes = packed_bytes(rows, kblocks);
+  if (bytes == 0) return FP8_OK;
+  if (!packed || (kblocks > 0 && !scales)) return FP8_ERR_NULL;
+  if (!aligned(packed, 16)) return FP8_ERR_ALIGN;
+  const int64_t nchunks = bytes / 16;
+  const int64_t blocks = (nchunks + 255) / 256;
+  if (blocks > 0x7fffffffLL) return FP8_ERR_SHAPE;
+  const int vec = aligned(scales, 16) && (ld_scales % 16) == 0;
+  hipLaunchKernelGGL(pack_scales_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, scales, rows, kblocks,
+                     ld_scales, packed, (kblocks + kPackBlocks - 1) / kPackBlocks, nchunks, vec);
+  return launch_status();
+}
+
+int mx_scaled_gemm_packed(int64_t M, int64_t N, int64_t K, const uint8_t* A, int fmt_a, int64_t lda,
+                          const uint8_t* A_packed, const uint8_t* B, int fmt_b, int64_t ldb, const uint8_t* B_packed,
+                          void* C, int out_dtype, int64_t ldc, float* out_amax, hipStream_t stream) {
+  if (!valid_fmt(fmt_a) || !valid_fmt(fmt_b)) return FP8_ERR_FORMAT;
+  if (!valid_dtype(out_dtype)) return FP8_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || (K % 32) != 0) return FP8_ERR_SHAPE;
+  if (lda < K || ldb < K || ldc < N) return FP8_ERR_SHAPE;
+  if (M > 0 && N > 0 && !C) return FP8_ERR_NULL;
+  if (M > 0 && N > 0) {
+    if ((K % 128) != 0 || K < 512) return FP8_ERR_UNSUPPORTED;
+    if (!A || !B || !A_packed || !B_packed) return FP8_ERR_NULL;
+    if (!aligned(A_packed, 16) || !aligned(B_packed, 16)) return FP8_ERR_ALIGN;
+    int st = check_operand(A, lda, false, K);
+    if (st) return st;
+    st = check_operand(B, ldb, false, K);
+    if (st) return st;
+  }
+  if (out_amax) zero_float_async(out_amax, stream);
+  if (M == 0 || N == 0) return launch_status();
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (tiles > 0x7fffffffLL) return FP8_ERR_SHAPE;
+  GemmArgs g;
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda; g.B = B; g.ldb = ldb;
+  g.bias_a = nullptr; g.bias_b = nullptr;
+  g.sa = A_packed; g.lds_a = 0; g.sb = B_packed; g.lds_b = 0;
+  g.sa_dword = 1; g.sb_dword = 1; g.scales_dma = 1;
+  g.scales_packed = 1; g.sgroups = (K / 32 + kPackBlocks - 1) / kPackBlocks;
   g.C = C; g.ldc = ldc; g.out_amax = out_amax;
   g.out_f32 = out_dtype == FP8_DT_F32;
   g.vec_store = g.out_f32 ? (aligned(C, 16) && ldc % 4 == 0) : (aligned(C, 8) && ldc % 4 == 0);

@@ -99,7 +99,7 @@ const char* fp8_status_string(int status) {
   }
 }
 
-int fp8_abi_version(void) { return 1; }
+int fp8_abi_version(void) { return 2; }
 
 int fp8_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, float* amax_out,
              hipStream_t stream) {

@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
     names = _declared_functions()
     for want in ["fp8_amax", "fp8_compute_scale", "fp8_history_init", "fp8_history_push",
                  "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize", "mx_quantize_t",
-                 "mx_quantize_rule", "mx_quantize_t_rule", "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string", "fp8_abi_version"]:
+                 "mx_quantize_rule", "mx_quantize_t_rule", "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string",
+                 "fp8_abi_version", "mx_packed_scales_bytes", "mx_pack_scales", "mx_scaled_gemm_packed"]:
         assert want in names
 
 
@@ -50,7 +51,7 @@ def test_status_strings(lib):
     for code in (NULL, SHAPE, ALIGN, DTYPE, FORMAT, LAUNCH, UNSUP):
         assert sq.fp8_status_string(code) not in ("ok", "unknown status")
     assert sq.fp8_status_string(-99) == "unknown status"
-    assert sq.fp8_abi_version() >= 1
+    assert sq.fp8_abi_version() >= 2
 
 
 def test_amax_validation(lib):
@@ -148,6 +149,39 @@ def test_gemm_validation(lib):
     assert mg(64, 64, 64, FAKE + 4, 0, 64, FAKE, 4, FAKE, 0, 64, FAKE, 4, FAKE, 0, 64, None, S) == ALIGN
     assert mg(64, 64, 64, FAKE, 0, 64, FAKE, 2, FAKE, 0, 72, FAKE, 4, FAKE, 0, 64, None, S) == ALIGN
     assert mg(64, 64, 64, FAKE, 3, 64, FAKE, 4, FAKE, 0, 64, FAKE, 4, FAKE, 0, 64, None, S) == FORMAT
+
+
+def test_packed_scales_size_and_validation(lib):
+    """Size formula of the packed E8M0 layout (256-row tiles x 16-block groups
+    x 4 KiB) and the host-side checks of the two packed entry points."""
+    assert sq.mx_packed_scales_bytes(0, 0) == 0
+    assert sq.mx_packed_scales_bytes(1, 1) == 4096
+    assert sq.mx_packed_scales_bytes(256, 16) == 4096
+    assert sq.mx_packed_scales_bytes(257, 16) == 8192
+    assert sq.mx_packed_scales_bytes(256, 17) == 8192
+    assert sq.mx_packed_scales_bytes(16384, 256) == 64 * 16 * 4096
+    assert sq.mx_packed_scales_bytes(300, 20) == 2 * 2 * 4096
+    assert lib.mx_packed_scales_bytes(-1, 4) == SHAPE
+    p = lib.mx_pack_scales
+    # scales, rows, kblocks, ld, packed, s
+    assert p(FAKE, 4, 8, 4, FAKE, S) == SHAPE
+    assert p(FAKE, -1, 8, 8, FAKE, S) == SHAPE
+    assert p(None, 4, 8, 8, FAKE, S) == NULL
+    assert p(FAKE, 4, 8, 8, None, S) == NULL
+    assert p(FAKE, 4, 8, 8, FAKE + 4, S) == ALIGN
+    assert p(None, 0, 0, 0, None, S) == OK
+    g = lib.mx_scaled_gemm_packed
+    # M, N, K, A, fa, lda, Ap, B, fb, ldb, Bp, C, dt, ldc, amax, s
+    assert g(64, 64, 256, FAKE, 0, 256, FAKE, FAKE, 0, 256, FAKE, FAKE, 0, 64, None, S) == UNSUP
+    assert g(64, 64, 576, FAKE, 0, 576, FAKE, FAKE, 0, 576, FAKE, FAKE, 0, 64, None, S) == UNSUP
+    assert g(64, 64, 48, FAKE, 0, 48, FAKE, FAKE, 0, 48, FAKE, FAKE, 0, 64, None, S) == SHAPE
+    assert g(64, 64, 512, FAKE, 0, 512, None, FAKE, 0, 512, FAKE, FAKE, 0, 64, None, S) == NULL
+    assert g(64, 64, 512, FAKE, 0, 512, FAKE, FAKE, 0, 512, FAKE + 4, FAKE, 0, 64, None, S) == ALIGN
+    assert g(64, 64, 512, FAKE + 4, 0, 512, FAKE, FAKE, 0, 512, FAKE, FAKE, 0, 64, None, S) == ALIGN
+    assert g(64, 64, 512, FAKE, 2, 512, FAKE, FAKE, 0, 512, FAKE, FAKE, 0, 64, None, S) == FORMAT
+    assert g(64, 64, 512, FAKE, 0, 512, FAKE, FAKE, 0, 512, FAKE, FAKE, 7, 64, None, S) == DTYPE
+    assert g(64, 64, 512, FAKE, 0, 512, FAKE, FAKE, 0, 512, FAKE, FAKE, 0, 32, None, S) == SHAPE
+    assert g(64, 64, 512, FAKE, 0, 512, FAKE, FAKE, 0, 512, FAKE, None, 0, 64, None, S) == NULL
 
 
 def test_binding_refuses_cpu_tensors():

@@ -264,6 +264,64 @@ def test_mx_gemm_k_multiple_of_128(fa, fb, K):
         _check_amax(C, am)
 
 
+def _pack_scales_host(sc):
+    """The packed E8M0 layout, straight from its definition in the header:
+    code (r, j) at ((r // 256) * G + j // 16) * 4096 + (r % 256) * 16 + j % 16,
+    G = ceil(kb / 16), 127 wherever the matrix has no code."""
+    rows, kb = sc.shape
+    T, G = -(-rows // 256), -(-kb // 16)
+    out = np.full(T * G * 4096, 127, dtype=np.uint8)
+    r = np.arange(rows)[:, None]
+    j = np.arange(kb)[None, :]
+    out[((r // 256) * G + j // 16) * 4096 + (r % 256) * 16 + j % 16] = sc
+    return out
+
+
+@pytest.mark.parametrize("rows,kb,pad", [(300, 20, 4), (256, 16, 0), (1, 1, 0), (513, 256, 0), (70, 36, 1)],
+                         ids=["300x20_ld24", "256x16", "1x1", "513x256", "70x36_ld37"])
+def test_mx_pack_scales_layout(rows, kb, pad):
+    """mx_pack_scales rewrites row-major E8M0 codes into the tiled layout byte
+    for byte, padding included (ragged rows and block groups; leading
+    dimensions that allow and that do not allow 16-byte loads)."""
+    rng = np.random.default_rng(rows * 1000 + kb)
+    full = rng.integers(0, 256, (rows, kb + pad)).astype(np.uint8)
+    sc = full[:, :kb]
+    got = sq.mx_pack_scales(u8_dev(full)[:, :kb])
+    torch.cuda.synchronize()
+    assert sq.mx_packed_scales_bytes(rows, kb) == got.numel()
+    assert np.array_equal(host(got), _pack_scales_host(sc))
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 260, 640), (256, 256, 512), (512, 768, 1152), (130, 1030, 2048)],
+                         ids=["300x260x640", "256x256x512", "512x768x1152", "130x1030x2048"])
+@pytest.mark.parametrize("fa,fb", [(E4M3, E4M3), (E5M2, E4M3)], ids=["e4e4", "e5e4"])
+def test_mx_gemm_packed_scales(fa, fb, M, N, K):
+    """The block-scaled GEMM reading packed scales (mx_pack_scales) equals the
+    row-major-scale GEMM bit for bit (bf16 and fp32 out, fused amax too) and
+    the oracle within tolerance: ragged M / N tiles, a partial last group of
+    16 blocks (K = 640, 1152), exactly one group (K = 512)."""
+    xb = make("c4", "X", shape=(M, K))
+    wb = make("c4", "W", shape=(N, K))
+    qa, sa = oracle.mx_quantize(oracle.bf16_bits_to_f64(xb), fa)
+    qb, sb = oracle.mx_quantize(oracle.bf16_bits_to_f64(wb), fb)
+    ref = oracle.mx_gemm_ref(qa, sa, fa, qb, sb, fb)
+    s = oracle.mx_abs_product_sum(qa, sa, fa, qb, sb, fb)
+    gt = mfma_group_term(oracle.mx_dequantize(qa, sa, fa), oracle.mx_dequantize(qb, sb, fb))
+    A, B, SA, SB = u8_dev(qa), u8_dev(qb), u8_dev(sa), u8_dev(sb)
+    PA, PB = sq.mx_pack_scales(SA), sq.mx_pack_scales(SB)
+    assert np.array_equal(host(PA), _pack_scales_host(sa)) and np.array_equal(host(PB), _pack_scales_host(sb))
+    for dt in (torch.bfloat16, torch.float32):
+        say(f"mx gemm packed {fa.name}x{fb.name} {M}x{N}x{K} {dt}")
+        Cp, amp = sq.mx_scaled_gemm_packed(A, fa.code, PA, B, fb.code, PB, out_dtype=dt, want_amax=True)
+        Cr, amr = sq.mx_scaled_gemm(A, fa.code, SA, B, fb.code, SB, out_dtype=dt, want_amax=True)
+        torch.cuda.synchronize()
+        assert torch.equal(Cp.view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                           Cr.view(torch.int16 if dt == torch.bfloat16 else torch.int32))
+        assert f32_bits_of(amp) == f32_bits_of(amr)
+        assert_gemm_close(host_f64(Cp), ref, s, dt == torch.bfloat16, f"mx packed {M}x{N}x{K}", gt)
+        _check_amax(Cp, amp)
+
+
 def test_mx_gemm_extreme_block_scales():
     """Per-block codes spread over a wide range (2^-40 .. 2^40 per block), so a
     wrong block <-> scale pairing cannot hide inside the tolerance."""
@@ -371,7 +429,12 @@ def test_full_size_70b_mlp_end_to_end_sampled():
     C, am = sq.mx_scaled_gemm(mqx, 0, msx, mqw, 0, msw, want_amax=True)
     got = host_f64(C[torch.from_numpy(rs[ri]).to(DEV), torch.from_numpy(cs[ci]).to(DEV)])
     assert f32_bits_of(am) == f32_bits_of(sq.fp8_amax(C))
-    del C
+    say("c5 gpu mx path, packed scales")
+    Cp, amp = sq.mx_scaled_gemm_packed(mqx, 0, sq.mx_pack_scales(msx), mqw, 0, sq.mx_pack_scales(msw),
+                                       want_amax=True)
+    assert torch.equal(Cp.view(torch.int16), C.view(torch.int16))
+    assert f32_bits_of(amp) == f32_bits_of(am)
+    del C, Cp
     say("c5 oracle (mx)")
     oqxm, osxm = oracle_mx_chunked(xb, E4M3, rs)
     oqwm, oswm = oracle_mx_chunked(wb, E4M3, cs)
@@ -428,7 +491,7 @@ def _repeat_identical(fn, reps, what):
         del C
 
 
-@pytest.mark.parametrize("mx", [False, True], ids=["pt", "mx"])
+@pytest.mark.parametrize("mx", [False, True, "packed"], ids=["pt", "mx", "mx_packed"])
 def test_full_size_70b_mlp_gemm_repeat_bit_identical(mx):
     """Run-to-run determinism of the 70B-MLP GEMMs (16384 x 28672 x 8192,
     bf16 out) over every output element: eight launches on the same operands
@@ -442,6 +505,8 @@ def test_full_size_70b_mlp_gemm_repeat_bit_identical(mx):
     if mx:
         qx, sx = sq.mx_quantize(x, 0)
         qw, sw = sq.mx_quantize(w, 0)
+        if mx == "packed":
+            sx, sw = sq.mx_pack_scales(sx), sq.mx_pack_scales(sw)
     else:
         bx, _, _ = sq.fp8_compute_scale(sq.fp8_amax(x), 0, 0)
         bw, _, _ = sq.fp8_compute_scale(sq.fp8_amax(w), 0, 0)
@@ -454,12 +519,15 @@ def test_full_size_70b_mlp_gemm_repeat_bit_identical(mx):
         if out is None:
             out = torch.empty(16384, 28672, device=DEV, dtype=torch.bfloat16)
         out.fill_(float("nan"))
+        if mx == "packed":
+            return sq.mx_scaled_gemm_packed(qx, 0, sx, qw, 0, sw, out=out, want_amax=True)
         if mx:
             return sq.mx_scaled_gemm(qx, 0, sx, qw, 0, sw, out=out, want_amax=True)
         return sq.fp8_scaled_gemm(qx, 0, bx, qw, 0, bw, out=out, want_amax=True)
 
-    say(f"70b-mlp {'mx' if mx else 'per-tensor'} gemm x8 determinism")
-    _repeat_identical(launch, 8, "mx" if mx else "per-tensor")
+    what = {False: "per-tensor", True: "mx", "packed": "mx packed scales"}[mx]
+    say(f"70b-mlp {what} gemm x8 determinism")
+    _repeat_identical(launch, 8, what)
 
 
 @pytest.mark.parametrize("mx", [False, True], ids=["pt", "mx"])
