@@ -55,6 +55,9 @@ constexpr int kTileBytes = BM * BK;          // 32 KiB per operand per stage
 // Packed E8M0 layout (mx_pack_scales): per 256-row tile and per group of 16
 // K-blocks (4 K stages), 256 rows x 16 codes = 4 KiB contiguous.
 constexpr int kPackRows = 256, kPackBlocks = 16, kPackTile = kPackRows * kPackBlocks;
+// Forward kernel launch: persistent per-tensor grid (true) or one tile per
+// workgroup (false, measured faster; see gemm_fwd_kernel).
+constexpr bool kFwdPersistent = false;
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 4)) & 7; }
 
@@ -524,8 +527,8 @@ __device__ __forceinline__ v16f mfma32(v8i a, v8i b, v16f c, int sa, int oa, int
 //   * The loop is unrolled by 2 (by 4 for MX, whose scale codes are copied
 //     4 stages at a time) and always runs whole iterations: stages past nk
 //     copy zeros through zero-sized buffer descriptors and add nothing, so
-//     the loop body has no branches.  The wave drains its copies before the
-//     epilogue.
+//     the loop body has no branches.  The workgroup's final wait covers
+//     every copy; the C stores issued after them may drain after it ends.
 //   * bf16 epilogue of an interior tile: a lane's accumulators are 4 n of
 //     one row, so direct stores would write 16 bytes in each of 32 rows per
 //     instruction; instead each 32 x 64 quarter of a wave's block row is
@@ -598,10 +601,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   constexpr int kFrag = 32 * BK;                    // 4 KiB between 32-row fragments
   constexpr int U = MX ? 4 : 2;                     // stages per loop iteration
   constexpr int LPS = 16;                           // data copies per stage per wave
-  // Per-tensor: persistent, one workgroup per compute unit walking tiles.
-  // MX: one tile per workgroup (its scale copies leave no SGPRs for a second
-  // tile's descriptors).
-  constexpr bool PERSIST = !MX;
+  // Launch shape (kFwdPersistent): one tile per workgroup, the dispatcher
+  // refilling each compute unit as a workgroup ends.  The persistent form
+  // (one workgroup per compute unit walking tiles, the last two stages of a
+  // tile prefetching the next tile's first two) is kept for the per-tensor
+  // product behind the switch; since a workgroup's final wait leaves its C
+  // stores in flight it measures slower (70B-MLP shape: -2.1% at K = 8192,
+  // -2.3% at K = 4096).  MX never runs persistent: its scale descriptors
+  // leave no SGPRs for a second tile's.
+  constexpr bool PERSIST = kFwdPersistent && !MX;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: SGPR
@@ -1092,10 +1100,11 @@ template <int FA, int FB, bool MX, bool TA, bool TB>
 static void launch_gemm(const GemmArgs& g, hipStream_t s) {
   const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   // the forward kernel stages MX scales with dword copies: scale rows must be
-  // 4-byte aligned (always true for packed rows once K % 128 == 0); it is
-  // persistent, one workgroup per compute unit walking tiles
+  // 4-byte aligned (always true for packed rows once K % 128 == 0); one tile
+  // per workgroup (or, with kFwdPersistent, per-tensor products walk tiles
+  // with one workgroup per compute unit)
   if (!TA && !TB && g.K > 0 && (g.K % 128) == 0 && (!MX || g.scales_dma)) {
-    const int64_t cus = MX ? tiles : device_cu_count();
+    const int64_t cus = (MX || !kFwdPersistent) ? tiles : device_cu_count();
     const int64_t grid = tiles < cus ? tiles : cus;
     hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, g);
   } else {
