@@ -110,6 +110,47 @@ def gpu_sclk():
     return lines[0] if lines else None
 
 
+def rmse_c4(dev):
+    """Quantization RMSE of the 13B-MLP up-projection tensors (X [8192 x 5120]
+    with log-normal column scales, W [13824 x 5120]), per-tensor E4M3 against
+    MX (1 x 32 blocks, E8M0): the library's casts on the GPU, then
+    sqrt(mean((dequant(q) - x)^2)) in float64 from the returned codes, decoded
+    through a 256-entry table taken from torch's CPU float8 type."""
+    import numpy as np
+    import torch
+    import scaled_quantize_fp8_amd as sq
+    from workloads import make
+    table = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().to(dev)
+    out = {"shapes": "X [8192 x 5120], W [13824 x 5120] bf16 -> E4M3"}
+    for name in ("X", "W"):
+        bits = make("c4", name)
+        x = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        xd = x.double()
+        b, _, _ = sq.fp8_compute_scale(sq.fp8_amax(x), sq.E4M3, 0)
+        q, _, _ = sq.fp8_quantize(x, sq.E4M3, b)
+        pt = table[q.long()] * (2.0 ** -int(b.item()))
+        mq, ms = sq.mx_quantize(x, sq.E4M3)
+        blk = torch.exp2(ms.double() - 127.0).repeat_interleave(32, dim=1)
+        mx = table[mq.long()] * blk
+        r_pt = float(torch.sqrt(torch.mean((pt - xd) ** 2)))
+        r_mx = float(torch.sqrt(torch.mean((mx - xd) ** 2)))
+        # RMSE is set by the large elements, which both schemes round with the
+        # same relative precision (E4M3 is a floating-point grid); the block
+        # scales matter where small values fall into the subnormals:
+        nz = xd != 0
+        n_nz = max(int(nz.sum()), 1)
+        out[name] = {"rmse_per_tensor": r_pt, "rmse_mx": r_mx, "rmse_mx_over_per_tensor": round(r_mx / r_pt, 6),
+                     "flushed_to_zero_per_tensor": int(((pt == 0) & nz).sum()) / n_nz,
+                     "flushed_to_zero_mx": int(((mx == 0) & nz).sum()) / n_nz,
+                     "mean_rel_err_per_tensor": float(((pt - xd).abs()[nz] / xd.abs()[nz]).mean()),
+                     "mean_rel_err_mx": float(((mx - xd).abs()[nz] / xd.abs()[nz]).mean()),
+                     "tensor_bias": int(b.item())}
+        del nz
+        del x, xd, q, pt, mq, ms, blk, mx
+    torch.cuda.empty_cache()
+    return out
+
+
 def backward_extras(dev, reps: int = 5):
     """The 7B-MLP down-projection backward (dY [4096 x 11008], W [11008 x
     4096], X [4096 x 4096]) as the linear layer runs it: transposed casts,
@@ -338,7 +379,7 @@ def main():
         stream[k] = {"achieved": round(v, 1), "frac": round(v / PEAK_HBM_GBS, 4),
                      "frac_of_copy": round(v / copy_GBps, 4)}
 
-    extras = {"backward_7b_mlp": backward_extras(dev)}
+    extras = {"backward_7b_mlp": backward_extras(dev), "rmse_13b_mlp_up": rmse_c4(dev)}
 
     cpu = None
     if not args.no_cpu_baseline:
