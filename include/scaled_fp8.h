@@ -281,9 +281,20 @@ int mx_pack_scales(const uint8_t* scales, int64_t rows, int64_t kblocks, int64_t
                    uint8_t* packed, hipStream_t stream);
 
 /*
+ * mx_quantize_packed — mx_quantize_rule writing its E8M0 codes straight into
+ * the packed layout (no separate mx_pack_scales pass).  q as for mx_quantize;
+ * packed: mx_packed_scales_bytes(rows, cols / 32) bytes, 16-byte aligned
+ * (else FP8_ERR_ALIGN); every byte is written (127 past the matrix).  The
+ * codes equal mx_pack_scales applied to mx_quantize_rule's, bit for bit.
+ */
+int mx_quantize_packed(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                       int fmt, int rule, uint8_t* q, int64_t ldq, uint8_t* packed,
+                       hipStream_t stream);
+
+/*
  * mx_scaled_gemm_packed — mx_scaled_gemm with both scale operands in the
- * packed layout (A_packed from mx_pack_scales of A's [M x K/32] codes,
- * B_packed of B's [N x K/32] codes).  Same result, bit for bit, as
+ * packed layout (A_packed from mx_pack_scales of A's [M x K/32] codes or from
+ * mx_quantize_packed, B_packed likewise for B's [N x K/32] codes).  Same result, bit for bit, as
  * mx_scaled_gemm on the row-major codes.  Requirements: those of
  * mx_scaled_gemm, plus K % 128 == 0 and K >= 512 (else FP8_ERR_UNSUPPORTED:
  * use mx_scaled_gemm) and 16-byte aligned packed buffers (FP8_ERR_ALIGN).

@@ -26,7 +26,7 @@ __all__ = [
     "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize", "mx_quantize_t",
     "mx_quantize_rule", "mx_quantize_t_rule", "MX_RULE_FMAX", "MX_RULE_OCP",
     "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string", "fp8_abi_version",
-    "mx_packed_scales_bytes", "mx_pack_scales", "mx_scaled_gemm_packed",
+    "mx_packed_scales_bytes", "mx_pack_scales", "mx_quantize_packed", "mx_scaled_gemm_packed",
 ]
 
 E4M3 = 0
@@ -65,6 +65,7 @@ _SIGNATURES = {
                         _p, _i, _i64, _p, _p], _i),
     "mx_packed_scales_bytes": ([_i64, _i64], _i64),
     "mx_pack_scales": ([_p, _i64, _i64, _i64, _p, _p], _i),
+    "mx_quantize_packed": ([_p, _i, _i64, _i64, _i64, _i, _i, _p, _i64, _p, _p], _i),
     "mx_scaled_gemm_packed": ([_i64, _i64, _i64, _p, _i, _i64, _p, _p, _i, _i64, _p,
                                _p, _i, _i64, _p, _p], _i),
 }
@@ -475,3 +476,30 @@ def mx_scaled_gemm_packed(A: torch.Tensor, fmt_a, A_packed: torch.Tensor, B: tor
         M, N, K, _ptr(A), _fmt(fmt_a), lda, _ptr(A_packed), _ptr(B), _fmt(fmt_b), ldb, _ptr(B_packed),
         _ptr(out), _out_code(out.dtype), ldc, _ptr(amax_out), _stream(A)))
     return out, amax_out
+
+
+def mx_quantize_packed(x: torch.Tensor, fmt=E4M3, rule="fmax", q: torch.Tensor | None = None,
+                       packed: torch.Tensor | None = None):
+    """Per-block cast (1 x 32 blocks along the rows, E8M0 codes) writing the
+    codes in the packed layout mx_scaled_gemm_packed reads; returns (q codes
+    [R x C], packed codes as a 1-D uint8 tensor of
+    mx_packed_scales_bytes(R, C / 32) bytes)."""
+    rows, cols, ld = _mat(x, "x")
+    dt = _dtype_code(x, "x")
+    if cols % 32:
+        raise ValueError("cols must be a multiple of 32")
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    _u8(q, "q")
+    qr, qc, ldq = _mat(q, "q")
+    if (qr, qc) != (rows, cols):
+        raise ValueError("q must have the shape of x")
+    n = mx_packed_scales_bytes(rows, cols // 32)
+    if packed is None:
+        packed = torch.empty(n, dtype=torch.uint8, device=x.device)
+    _u8(packed, "packed")
+    if packed.dim() != 1 or packed.numel() != n or not packed.is_contiguous():
+        raise ValueError(f"packed must be a contiguous 1-D uint8 tensor of {n} bytes")
+    _check("mx_quantize_packed", load_library().mx_quantize_packed(
+        _ptr(x), dt, rows, cols, ld, _fmt(fmt), _rule(rule), _ptr(q), ldq, _ptr(packed), _stream(x)))
+    return q, packed

@@ -52,9 +52,8 @@ constexpr int BM = 256, BN = 256, BK = 128;
 constexpr int kGemmThreads = 256;
 constexpr int kGroupM = 8;
 constexpr int kTileBytes = BM * BK;          // 32 KiB per operand per stage
-// Packed E8M0 layout (mx_pack_scales): per 256-row tile and per group of 16
-// K-blocks (4 K stages), 256 rows x 16 codes = 4 KiB contiguous.
-constexpr int kPackRows = 256, kPackBlocks = 16, kPackTile = kPackRows * kPackBlocks;
+// The packed E8M0 layout (kPackRows x kPackBlocks codes per 4 KiB block,
+// host.hpp): one group of 16 K-blocks is 4 K stages of this kernel.
 // Forward kernel launch: persistent per-tensor grid (true) or one tile per
 // workgroup (false, measured faster; see gemm_fwd_kernel).
 constexpr bool kFwdPersistent = false;
@@ -1152,10 +1151,6 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t* __restr
     v = make_uint4(w[0], w[1], w[2], w[3]);
   }
   *reinterpret_cast<uint4*>(dst + c * 16) = v;
-}
-
-static int64_t packed_bytes(int64_t rows, int64_t kb) {
-  return ((rows + kPackRows - 1) / kPackRows) * ((kb + kPackBlocks - 1) / kPackBlocks) * (int64_t)kPackTile;
 }
 
 // 16-byte loads need 16-byte aligned rows; buffer offsets are 32-bit, so a

@@ -37,6 +37,15 @@ inline unsigned stream_blocks(int64_t units, int64_t per_block) {
   return (unsigned)b;
 }
 
+// Packed E8M0 scale layout (mx_pack_scales, mx_quantize_packed,
+// mx_scaled_gemm_packed): per 256-row tile and group of 16 K-blocks, the
+// tile's 256 x 16 codes as one contiguous 4 KiB block.
+constexpr int kPackRows = 256, kPackBlocks = 16, kPackTile = kPackRows * kPackBlocks;
+inline int64_t packed_scale_groups(int64_t kb) { return (kb + kPackBlocks - 1) / kPackBlocks; }
+inline int64_t packed_bytes(int64_t rows, int64_t kb) {
+  return ((rows + kPackRows - 1) / kPackRows) * packed_scale_groups(kb) * (int64_t)kPackTile;
+}
+
 // Zero one float on `stream` with a tiny fill kernel (not hipMemsetAsync, so
 // that the call sequence can be captured into a HIP graph safely).
 void zero_float_async(float* p, hipStream_t stream);

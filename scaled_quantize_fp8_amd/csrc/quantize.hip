@@ -409,7 +409,25 @@ struct MxArgs {
   int64_t ldq;
   uint8_t* scales;
   int64_t lds;
+  int packed;          // scales in the packed layout (host.hpp), sgroups groups per row tile
+  int64_t sgroups;
 };
+
+// Where the E8M0 code of (row r, block j) goes: row-major (scales + r lds + j)
+// or the packed layout, ((r / 256) G + j / 16) 4096 + (r % 256) 16 + j % 16.
+__device__ __forceinline__ void store_scale(const MxArgs& a, int64_t r, int64_t j, uint32_t code) {
+  const int64_t off = a.packed ? ((r / kPackRows) * a.sgroups + j / kPackBlocks) * kPackTile +
+                                     (r % kPackRows) * kPackBlocks + j % kPackBlocks
+                               : r * a.lds + j;
+  a.scales[off] = (uint8_t)code;
+}
+
+// Fill n bytes (n % 16 == 0, p 16-byte aligned) with v: the padding of a
+// packed scale buffer.
+__global__ __launch_bounds__(256) void fill_u8_kernel(uint8_t* p, int64_t n16, uint32_t v4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n16) reinterpret_cast<uint4*>(p)[i] = make_uint4(v4, v4, v4, v4);
+}
 
 // Block exponent by the default rule (block max at or below the format
 // maximum) or, with OCP, the OCP MX rule (block max in the top binade).
@@ -435,7 +453,6 @@ __global__ __launch_bounds__(kThreads) void mx_vec_kernel(MxArgs a) {
   for (int64_t r = blockIdx.y; r < a.rows; r += gridDim.y) {
     const uint4* x4 = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.x) + r * a.ld * ESZ);
     uint8_t* qr = a.q + r * a.ldq;
-    uint8_t* sr = a.scales + r * a.lds;
     int64_t c = tid;
     // every lane of a block's group takes the same branch: stride and cpr
     // are multiples of L and the group's chunks share c / L
@@ -453,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void mx_vec_kernel(MxArgs a) {
         block_exponent<FMT, OCP>(bm, &e, &code);
         const uint2 o = cast_chunk<DT, FMT>(v[u], e, &m, true);
         store_codes<DT>(qr, c + u * stride, o);
-        if ((threadIdx.x % L) == 0) sr[(c + u * stride) / L] = (uint8_t)code;
+        if ((threadIdx.x % L) == 0) store_scale(a, r, (c + u * stride) / L, code);
       }
     }
     for (; c < cpr; c += stride) {
@@ -466,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void mx_vec_kernel(MxArgs a) {
       block_exponent<FMT, OCP>(bm, &e, &code);
       const uint2 o = cast_chunk<DT, FMT>(v, e, &m, true);
       store_codes<DT>(qr, c, o);
-      if ((threadIdx.x % L) == 0) sr[c / L] = (uint8_t)code;
+      if ((threadIdx.x % L) == 0) store_scale(a, r, c / L, code);
     }
   }
 }
@@ -492,7 +509,7 @@ __global__ __launch_bounds__(kThreads) void mx_scalar_kernel(MxArgs a) {
         const uint32_t bits = load_elem<DT>(xr, b * 32 + j, &f);
         a.q[r * a.ldq + b * 32 + j] = (uint8_t)cast_elem<FMT>(bits, e);
       }
-      a.scales[r * a.lds + b] = (uint8_t)code;
+      store_scale(a, r, b, code);
     }
   }
 }
@@ -682,8 +699,11 @@ int fp8_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
   return launch_status();
 }
 
-int mx_quantize_rule(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, int rule,
-                     uint8_t* q, int64_t ldq, uint8_t* scales, int64_t ld_scales, hipStream_t stream) {
+// Row-wise MX cast behind mx_quantize_rule (scales row-major, ld_scales) and
+// mx_quantize_packed (scales in the packed layout).
+static int mx_cast_rows(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, int rule,
+                        uint8_t* q, int64_t ldq, uint8_t* scales, int64_t ld_scales, bool packed,
+                        hipStream_t stream) {
   if (!q || !scales) return FP8_ERR_NULL;
   if (!valid_dtype(dtype)) return FP8_ERR_DTYPE;
   if (!valid_fmt(fmt) || !valid_mx_rule(rule)) return FP8_ERR_FORMAT;
@@ -692,8 +712,12 @@ int mx_quantize_rule(const void* x, int dtype, int64_t rows, int64_t cols, int64
   if (st) return st;
   st = check_matrix(rows, cols, ldq);
   if (st) return st;
-  st = check_matrix(rows, cols / 32, ld_scales);
-  if (st) return st;
+  if (!packed) {
+    st = check_matrix(rows, cols / 32, ld_scales);
+    if (st) return st;
+  } else if (!aligned(scales, 16)) {
+    return FP8_ERR_ALIGN;
+  }
   if (rows * cols == 0) return FP8_OK;
   if (!x) return FP8_ERR_NULL;
   MxArgs a;
@@ -705,10 +729,20 @@ int mx_quantize_rule(const void* x, int dtype, int64_t rows, int64_t cols, int64
   a.ldq = ldq;
   a.scales = scales;
   a.lds = ld_scales;
+  a.packed = packed;
+  a.sgroups = packed_scale_groups(cols / 32);
+  if (packed && ((rows % kPackRows) != 0 || ((cols / 32) % kPackBlocks) != 0)) {
+    // positions past the matrix hold 127 (scale 1): fill the whole buffer
+    // first, then the cast overwrites every code of the matrix
+    const int64_t n16 = packed_bytes(rows, cols / 32) / 16;
+    hipLaunchKernelGGL(fill_u8_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, stream, scales, n16,
+                       0x7f7f7f7fu);
+  }
   const int esz = dtype_size(dtype);
   const int epc = 16 / esz;
-  // contiguous -> one long row (blocks never straddle rows since cols % 32 == 0)
-  if (a.rows > 1 && a.ld == a.cols && a.ldq == a.cols && a.lds == a.cols / 32) {
+  // contiguous -> one long row (blocks never straddle rows since cols % 32 == 0);
+  // the packed layout needs the true row of every block
+  if (!packed && a.rows > 1 && a.ld == a.cols && a.ldq == a.cols && a.lds == a.cols / 32) {
     a.cols *= a.rows;
     a.rows = 1;
     a.ld = a.cols;
@@ -731,6 +765,16 @@ int mx_quantize_rule(const void* x, int dtype, int64_t rows, int64_t cols, int64
   }
 #undef SFP8_MX
   return launch_status();
+}
+
+int mx_quantize_rule(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, int rule,
+                     uint8_t* q, int64_t ldq, uint8_t* scales, int64_t ld_scales, hipStream_t stream) {
+  return mx_cast_rows(x, dtype, rows, cols, ld, fmt, rule, q, ldq, scales, ld_scales, false, stream);
+}
+
+int mx_quantize_packed(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, int rule,
+                       uint8_t* q, int64_t ldq, uint8_t* packed, hipStream_t stream) {
+  return mx_cast_rows(x, dtype, rows, cols, ld, fmt, rule, q, ldq, packed, 0, true, stream);
 }
 
 int mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, uint8_t* q,
@@ -763,6 +807,8 @@ int mx_quantize_t_rule(const void* x, int dtype, int64_t rows, int64_t cols, int
   a.ldq = ldqT;
   a.scales = scalesT;
   a.lds = ld_scales;
+  a.packed = 0;
+  a.sgroups = 0;
   const dim3 grid((unsigned)((cols + kMtC - 1) / kMtC), (unsigned)gy);
   // 16-byte loads when every row start is 16-byte aligned
   const bool vec = aligned(x, 16) && (ld * dtype_size(dtype)) % 16 == 0;

@@ -122,3 +122,16 @@ def assert_gemm_close(y_gpu: np.ndarray, y_ref: np.ndarray, s_ref: np.ndarray, b
         idx = np.argwhere(bad)[:5]
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; first "
                              f"{[(tuple(i), y_gpu[tuple(i)], y_ref[tuple(i)], tol[tuple(i)]) for i in idx]}")
+
+
+def pack_scales_host(sc):
+    """The packed E8M0 layout, straight from its definition in the header:
+    code (r, j) at ((r // 256) * G + j // 16) * 4096 + (r % 256) * 16 + j % 16,
+    G = ceil(kb / 16), 127 wherever the matrix has no code."""
+    rows, kb = sc.shape
+    T, G = -(-rows // 256), -(-kb // 16)
+    out = np.full(T * G * 4096, 127, dtype=np.uint8)
+    r = np.arange(rows)[:, None]
+    j = np.arange(kb)[None, :]
+    out[((r // 256) * G + j // 16) * 4096 + (r % 256) * 16 + j % 16] = sc
+    return out

@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
     for want in ["fp8_amax", "fp8_compute_scale", "fp8_history_init", "fp8_history_push",
                  "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize", "mx_quantize_t",
                  "mx_quantize_rule", "mx_quantize_t_rule", "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string",
-                 "fp8_abi_version", "mx_packed_scales_bytes", "mx_pack_scales", "mx_scaled_gemm_packed"]:
+                 "fp8_abi_version", "mx_packed_scales_bytes", "mx_pack_scales", "mx_quantize_packed",
+                 "mx_scaled_gemm_packed"]:
         assert want in names
 
 
@@ -170,6 +171,17 @@ def test_packed_scales_size_and_validation(lib):
     assert p(FAKE, 4, 8, 8, None, S) == NULL
     assert p(FAKE, 4, 8, 8, FAKE + 4, S) == ALIGN
     assert p(None, 0, 0, 0, None, S) == OK
+    c = lib.mx_quantize_packed
+    # x, dt, rows, cols, ld, fmt, rule, q, ldq, packed, s
+    assert c(FAKE, 0, 4, 64, 64, 0, 0, None, 64, FAKE, S) == NULL
+    assert c(FAKE, 0, 4, 64, 64, 0, 0, FAKE, 64, None, S) == NULL
+    assert c(FAKE, 0, 4, 48, 48, 0, 0, FAKE, 48, FAKE, S) == SHAPE
+    assert c(FAKE, 0, 4, 64, 32, 0, 0, FAKE, 64, FAKE, S) == SHAPE
+    assert c(FAKE, 0, 4, 64, 64, 0, 0, FAKE, 64, FAKE + 8, S) == ALIGN
+    assert c(FAKE, 5, 4, 64, 64, 0, 0, FAKE, 64, FAKE, S) == DTYPE
+    assert c(FAKE, 0, 4, 64, 64, 3, 0, FAKE, 64, FAKE, S) == FORMAT
+    assert c(FAKE, 0, 4, 64, 64, 0, 9, FAKE, 64, FAKE, S) == FORMAT
+    assert c(None, 0, 4, 64, 64, 0, 0, FAKE, 64, FAKE, S) == NULL
     g = lib.mx_scaled_gemm_packed
     # M, N, K, A, fa, lda, Ap, B, fb, ldb, Bp, C, dt, ldc, amax, s
     assert g(64, 64, 256, FAKE, 0, 256, FAKE, FAKE, 0, 256, FAKE, FAKE, 0, 64, None, S) == UNSUP

@@ -20,7 +20,7 @@ from oracle import E4M3, E5M2
 from workloads import f32_to_bf16_bits, make
 
 from gpu_helpers import (DEV, assert_gemm_close, bf16_dev, f32_bits_of, host, host_f64, i32_dev,
-                         mfma_group_term, need_gpu, oracle_mx_chunked, oracle_quantize_chunked,
+                         mfma_group_term, need_gpu, oracle_mx_chunked, oracle_quantize_chunked, pack_scales_host,
                          oracle_amax_chunked, say, u8_dev)
 
 pytestmark = pytest.mark.gpu
@@ -264,19 +264,6 @@ def test_mx_gemm_k_multiple_of_128(fa, fb, K):
         _check_amax(C, am)
 
 
-def _pack_scales_host(sc):
-    """The packed E8M0 layout, straight from its definition in the header:
-    code (r, j) at ((r // 256) * G + j // 16) * 4096 + (r % 256) * 16 + j % 16,
-    G = ceil(kb / 16), 127 wherever the matrix has no code."""
-    rows, kb = sc.shape
-    T, G = -(-rows // 256), -(-kb // 16)
-    out = np.full(T * G * 4096, 127, dtype=np.uint8)
-    r = np.arange(rows)[:, None]
-    j = np.arange(kb)[None, :]
-    out[((r // 256) * G + j // 16) * 4096 + (r % 256) * 16 + j % 16] = sc
-    return out
-
-
 @pytest.mark.parametrize("rows,kb,pad", [(300, 20, 4), (256, 16, 0), (1, 1, 0), (513, 256, 0), (70, 36, 1)],
                          ids=["300x20_ld24", "256x16", "1x1", "513x256", "70x36_ld37"])
 def test_mx_pack_scales_layout(rows, kb, pad):
@@ -289,7 +276,7 @@ def test_mx_pack_scales_layout(rows, kb, pad):
     got = sq.mx_pack_scales(u8_dev(full)[:, :kb])
     torch.cuda.synchronize()
     assert sq.mx_packed_scales_bytes(rows, kb) == got.numel()
-    assert np.array_equal(host(got), _pack_scales_host(sc))
+    assert np.array_equal(host(got), pack_scales_host(sc))
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 260, 640), (256, 256, 512), (512, 768, 1152), (130, 1030, 2048)],
@@ -309,7 +296,7 @@ def test_mx_gemm_packed_scales(fa, fb, M, N, K):
     gt = mfma_group_term(oracle.mx_dequantize(qa, sa, fa), oracle.mx_dequantize(qb, sb, fb))
     A, B, SA, SB = u8_dev(qa), u8_dev(qb), u8_dev(sa), u8_dev(sb)
     PA, PB = sq.mx_pack_scales(SA), sq.mx_pack_scales(SB)
-    assert np.array_equal(host(PA), _pack_scales_host(sa)) and np.array_equal(host(PB), _pack_scales_host(sb))
+    assert np.array_equal(host(PA), pack_scales_host(sa)) and np.array_equal(host(PB), pack_scales_host(sb))
     for dt in (torch.bfloat16, torch.float32):
         say(f"mx gemm packed {fa.name}x{fb.name} {M}x{N}x{K} {dt}")
         Cp, amp = sq.mx_scaled_gemm_packed(A, fa.code, PA, B, fb.code, PB, out_dtype=dt, want_amax=True)

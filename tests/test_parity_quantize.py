@@ -8,10 +8,11 @@ import torch
 import oracle
 import scaled_quantize_fp8_amd as sq
 from oracle import E4M3, E5M2
-from workloads import all_bf16_patterns, make
+from workloads import all_bf16_patterns, f32_to_bf16_bits, make
 
 from gpu_helpers import (DEV, bf16_dev, f32_bits_of, f32_dev, host, i32_dev, need_gpu,
-                         oracle_amax_chunked, oracle_mx_chunked, oracle_quantize_chunked, say, u8_dev)
+                         oracle_amax_chunked, oracle_mx_chunked, oracle_quantize_chunked, pack_scales_host, say,
+                         u8_dev)
 
 pytestmark = pytest.mark.gpu
 FMTS = [E4M3, E5M2]
@@ -346,3 +347,35 @@ def test_full_size_70b_mlp_sampled_rows(name):
     idx = torch.from_numpy(rows).to(DEV)
     assert np.array_equal(host(ms[idx]), rs)
     assert np.array_equal(host(mq[idx]), rq)
+    # the cast that writes the GEMM's packed scale layout: same codes, and
+    # scales equal to the row-major ones packed
+    pq, ps = sq.mx_quantize_packed(x, E4M3.code)
+    assert torch.equal(pq, mq)
+    assert torch.equal(ps, sq.mx_pack_scales(ms))
+
+
+@pytest.mark.parametrize("rows,cols,dtype,fmt,rule", [
+    (300, 640, "bf16", E4M3, "fmax"), (256, 512, "bf16", E4M3, "fmax"), (513, 1056, "f32", E5M2, "fmax"),
+    (70, 2048, "bf16", E4M3, "ocp"), (1, 32, "f32", E4M3, "fmax"), (257, 8192, "bf16", E5M2, "ocp")],
+    ids=["300x640", "256x512", "513x1056_f32_e5", "70x2048_ocp", "1x32", "257x8192_e5_ocp"])
+def test_mx_quantize_packed(rows, cols, dtype, fmt, rule):
+    """mx_quantize_packed: codes equal to the oracle's MX cast, scales equal
+    to the oracle's E8M0 codes in the packed layout (its definition in the
+    header, 127 padding), for ragged and whole 256-row tiles and 16-block
+    groups, bf16 and fp32 inputs, both block-exponent rules; also from a
+    strided input (no contiguous collapse)."""
+    rng = np.random.default_rng(rows * 7 + cols)
+    vals = rng.standard_normal((rows, cols)) * np.exp(rng.normal(0.0, 2.0, (1, cols)))
+    bits = f32_to_bf16_bits(vals.astype(np.float32))
+    xv = oracle.bf16_bits_to_f64(bits) if dtype == "bf16" else vals.astype(np.float32).astype(np.float64)
+    x = bf16_dev(bits) if dtype == "bf16" else f32_dev(vals.astype(np.float32))
+    rq, rs = oracle.mx_quantize(xv, fmt, rule=rule)
+    q, ps = sq.mx_quantize_packed(x, fmt.code, rule=rule)
+    assert np.array_equal(host(q), rq)
+    assert np.array_equal(host(ps), pack_scales_host(rs))
+    if cols >= 64:
+        sub = x[:, 32:]                                      # strided rows
+        q2, ps2 = sq.mx_quantize_packed(sub, fmt.code, rule=rule)
+        rq2, rs2 = oracle.mx_quantize(xv[:, 32:], fmt, rule=rule)
+        assert np.array_equal(host(q2), rq2)
+        assert np.array_equal(host(ps2), pack_scales_host(rs2))
