@@ -44,8 +44,8 @@ import math
 import torch
 
 from . import (E4M3, E5M2, _rule, fp8_amax, fp8_compute_scale, fp8_compute_scale_delayed,
-               fp8_history_init, fp8_history_push, fp8_quantize, fp8_scaled_gemm, mx_quantize_rule,
-               mx_quantize_t_rule, mx_scaled_gemm)
+               fp8_history_init, fp8_history_push, fp8_quantize, fp8_scaled_gemm, mx_quantize_packed,
+               mx_quantize_rule, mx_quantize_t_rule, mx_scaled_gemm, mx_scaled_gemm_packed)
 
 RECIPES = ("current", "delayed", "mx", "constant")
 
@@ -101,9 +101,17 @@ class Fp8LinearFunction(torch.autograd.Function):
         recipe = layer.recipe
         if recipe == "mx":
             rule = layer.mx_rule
-            qx, sx = mx_quantize_rule(x2, E4M3, rule)
-            qw, sw = mx_quantize_rule(w, E4M3, rule)
-            y, amax = mx_scaled_gemm(qx, E4M3, sx, qw, E4M3, sw, out_dtype=x.dtype, want_amax=True)
+            K = x2.shape[1]
+            if K % 128 == 0 and K >= 512 and x2.shape[0] > 0 and w.shape[0] > 0:
+                # the casts write the scales in the layout the GEMM copies
+                # whole cache lines of (same product, bit for bit)
+                qx, px = mx_quantize_packed(x2, E4M3, rule)
+                qw, pw = mx_quantize_packed(w, E4M3, rule)
+                y, amax = mx_scaled_gemm_packed(qx, E4M3, px, qw, E4M3, pw, out_dtype=x.dtype, want_amax=True)
+            else:
+                qx, sx = mx_quantize_rule(x2, E4M3, rule)
+                qw, sw = mx_quantize_rule(w, E4M3, rule)
+                y, amax = mx_scaled_gemm(qx, E4M3, sx, qw, E4M3, sw, out_dtype=x.dtype, want_amax=True)
             if ctx.needs_input_grad[0] or ctx.needs_input_grad[1]:
                 # backward operands: blocks along out (W^T) and along tokens (X^T)
                 qwT, swT = mx_quantize_t_rule(w, E4M3, rule)
