@@ -15,6 +15,8 @@
 // on integer bit patterns (packed u16 for bf16) and leave each workgroup as
 // one atomicMax.  The per-block maximum of an MX block is a 4-lane (bf16) or
 // 8-lane (f32) DPP reduction: no LDS, no barrier.
+#include <type_traits>
+
 #include "common.hpp"
 #include "host.hpp"
 #include "stream_kernels.hpp"
@@ -543,9 +545,14 @@ constexpr int kMtR = 128, kMtC = 64;
 
 template <int DT, int FMT, bool VEC, bool OCP>
 __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
-  // rows padded to 68 dwords: 16-byte aligned rows for the staging writes,
-  // and the column reads (one row per lane group) stay conflict-free
-  __shared__ __attribute__((aligned(16))) uint32_t tile[kMtR][kMtC + 4];
+  // The tile is staged in the input's own width (bf16 as 16-bit words, rows
+  // of 72: 144 bytes; fp32 rows of 68 dwords): 16-byte aligned rows for the
+  // staging writes, and a column read (64 lanes, one row) touches 64
+  // consecutive elements.  16-bit staging halves the LDS of a bf16 tile,
+  // so twice as many workgroups fit on a compute unit.
+  using TT = std::conditional_t<DT == FP8_DT_BF16, uint16_t, uint32_t>;
+  constexpr int PAD = DT == FP8_DT_BF16 ? 8 : 4;
+  __shared__ __attribute__((aligned(16))) TT tile[kMtR][kMtC + PAD];
   constexpr int ESZ = In<DT>::kEsz;
   constexpr int EPC = In<DT>::kEpc;                // elements per 16-byte chunk
   constexpr int CPR = kMtC / EPC;                  // chunks per tile row
@@ -558,28 +565,22 @@ __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
     const int tr = idx / CPR, ch = idx % CPR;
     const int64_t r = r0 + tr;
     const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ld * ESZ;
-    uint4* trow = reinterpret_cast<uint4*>(&tile[tr][ch * EPC]);
+    uint4* trow = reinterpret_cast<uint4*>(&tile[tr][ch * EPC]);   // one 16-byte chunk of the row
     if (VEC && full_cols && r < a.rows) {
-      const uint4 v = load_nt(reinterpret_cast<const uint4*>(xr + (c0 + ch * EPC) * ESZ));
-      if constexpr (DT == FP8_DT_BF16) {
-        trow[0] = make_uint4(v.x << 16, v.x & 0xffff0000u, v.y << 16, v.y & 0xffff0000u);
-        trow[1] = make_uint4(v.z << 16, v.z & 0xffff0000u, v.w << 16, v.w & 0xffff0000u);
-      } else {
-        trow[0] = v;
-      }
+      trow[0] = load_nt(reinterpret_cast<const uint4*>(xr + (c0 + ch * EPC) * ESZ));
     } else {
-      uint32_t w[EPC];
+      TT w[EPC];
 #pragma unroll
       for (int j = 0; j < EPC; ++j) {
         const int64_t c = c0 + ch * EPC + j;
-        w[j] = 0u;
+        w[j] = 0;
         if (r < a.rows && c < a.cols) {
           float f;
-          w[j] = load_elem<DT>(xr, c, &f);
+          const uint32_t bits = load_elem<DT>(xr, c, &f);
+          w[j] = (TT)(DT == FP8_DT_BF16 ? bits >> 16 : bits);
         }
       }
-#pragma unroll
-      for (int h = 0; h < EPC / 4; ++h) trow[h] = make_uint4(w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]);
+      trow[0] = *reinterpret_cast<const uint4*>(w);
     }
   }
   __syncthreads();
@@ -592,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
   uint32_t bm = 0;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    v[i] = tile[32 * blk + i][c];
+    v[i] = DT == FP8_DT_BF16 ? (uint32_t)tile[32 * blk + i][c] << 16 : (uint32_t)tile[32 * blk + i][c];
     const uint32_t ab = v[i] & 0x7fffffffu;
     bm = bm > ab ? bm : ab;
   }
