@@ -369,25 +369,29 @@ def _sample_idx(rng, M, N, n=2048):
     return rows, cols
 
 
-def _sample_pairs(rng, M, N, nr=192, n=2048):
-    """n (row, col) output positions drawn from nr distinct rows and columns
-    (plus the four corners), so the oracle casts only those operand rows."""
-    rs = np.unique(np.concatenate([rng.integers(0, M, nr), [0, M - 1]]))
-    cs = np.unique(np.concatenate([rng.integers(0, N, nr), [0, N - 1]]))
-    ri = np.concatenate([rng.integers(0, rs.size, n), [0, rs.size - 1, 0, rs.size - 1]])
-    ci = np.concatenate([rng.integers(0, cs.size, n), [0, cs.size - 1, cs.size - 1, 0]])
-    return rs, cs, ri, ci
+def _tile_rows(rng, n, extra=64):
+    """Two random indices inside every 256-wide tile of [0, n), the first and
+    last index, and `extra` more at random: sorted, unique."""
+    t = np.arange(0, n, 256)
+    per = np.concatenate([t + rng.integers(0, np.minimum(256, n - t)) for _ in range(2)])
+    return np.unique(np.concatenate([per, [0, n - 1], rng.integers(0, n, extra)]))
 
 
 def test_full_size_70b_mlp_end_to_end_sampled():
     """X[16384 x 8192], W[28672 x 8192] through the whole hot path on the GPU,
     in the benchmark's launch sequence: amax -> bias -> E4M3 cast -> per-tensor
-    GEMM (bf16 out, fused amax), and MX cast -> MX GEMM.  The oracle recomputes
-    amax and bias from the generator's bf16 tensors, casts only the sampled
-    operand rows and forms 2052 sampled outputs of each GEMM; the fused output
-    amax must equal a standalone reduction over the GPU's own output."""
+    GEMM (bf16 out, fused amax), and MX cast to packed scales -> MX GEMM.  The
+    oracle recomputes amax and bias from the generator's bf16 tensors, casts
+    the sampled operand rows (two in every 256-row tile of X and of W, plus
+    64 random ones each) and forms every output of those rows and columns in
+    float64: about 190 x 290 outputs per GEMM, at least four in each of the
+    7168 output tiles.  The fused output amax must equal a standalone
+    reduction over the GPU's own output."""
     xb, wb = make("c5", "X"), make("c5", "W")
     x, w = bf16_dev(xb), bf16_dev(wb)
+    rng = np.random.default_rng(27)
+    rs, cs = _tile_rows(rng, xb.shape[0]), _tile_rows(rng, wb.shape[0])
+    ri, ci = torch.from_numpy(rs).to(DEV), torch.from_numpy(cs).to(DEV)
     say("c5 gpu per-tensor path")
     ax, aw = sq.fp8_amax(x), sq.fp8_amax(w)
     bx, _, _ = sq.fp8_compute_scale(ax, 0, 0)
@@ -396,37 +400,40 @@ def test_full_size_70b_mlp_end_to_end_sampled():
     qw, _, _ = sq.fp8_quantize(w, 0, bw)
     C, am = sq.fp8_scaled_gemm(qx, 0, bx, qw, 0, bw, want_amax=True)
     am_ref = sq.fp8_amax(C)
-    rng = np.random.default_rng(27)
-    rs, cs, ri, ci = _sample_pairs(rng, xb.shape[0], wb.shape[0])
-    got = host_f64(C[torch.from_numpy(rs[ri]).to(DEV), torch.from_numpy(cs[ci]).to(DEV)])
+    got = host_f64(C[ri][:, ci])
     assert f32_bits_of(am) == f32_bits_of(am_ref)
     del C, qx, qw
     torch.cuda.empty_cache()
-    say("c5 oracle (per-tensor)")
+    say(f"c5 oracle (per-tensor), {rs.size} x {cs.size} outputs")
     rbx = oracle.compute_bias(oracle_amax_chunked(xb), E4M3)
     rbw = oracle.compute_bias(oracle_amax_chunked(wb), E4M3)
     assert int(host(bx)[0]) == rbx and int(host(bw)[0]) == rbw
     oqx = oracle_quantize_chunked(xb, E4M3, rbx, rs)
     oqw = oracle_quantize_chunked(wb, E4M3, rbw, cs)
-    y, s = oracle.gemm_sample_ref(oqx, E4M3, rbx, oqw, E4M3, rbw, ri, ci)
-    assert_gemm_close(got, y, s, True, "c5 per-tensor")
-    say("c5 gpu mx path")
-    mqx, msx = sq.mx_quantize(x, 0)
-    mqw, msw = sq.mx_quantize(w, 0)
-    C, am = sq.mx_scaled_gemm(mqx, 0, msx, mqw, 0, msw, want_amax=True)
-    got = host_f64(C[torch.from_numpy(rs[ri]).to(DEV), torch.from_numpy(cs[ci]).to(DEV)])
+    y = oracle.scaled_gemm_ref(oqx, E4M3, rbx, oqw, E4M3, rbw)
+    sabs = oracle.abs_product_sum(oqx, E4M3, rbx, oqw, E4M3, rbw)
+    assert_gemm_close(got, y, sabs, True, "c5 per-tensor")
+    tiles = {(int(r) // 256, int(c) // 256) for r in rs for c in cs}
+    assert len(tiles) == (xb.shape[0] // 256) * (wb.shape[0] // 256)
+    say("c5 gpu mx path (cast to packed scales)")
+    mqx, psx = sq.mx_quantize_packed(x, 0)
+    mqw, psw = sq.mx_quantize_packed(w, 0)
+    C, am = sq.mx_scaled_gemm_packed(mqx, 0, psx, mqw, 0, psw, want_amax=True)
+    got = host_f64(C[ri][:, ci])
     assert f32_bits_of(am) == f32_bits_of(sq.fp8_amax(C))
-    say("c5 gpu mx path, packed scales")
-    Cp, amp = sq.mx_scaled_gemm_packed(mqx, 0, sq.mx_pack_scales(msx), mqw, 0, sq.mx_pack_scales(msw),
-                                       want_amax=True)
-    assert torch.equal(Cp.view(torch.int16), C.view(torch.int16))
-    assert f32_bits_of(amp) == f32_bits_of(am)
-    del C, Cp
+    say("c5 gpu mx path, row-major scales: same bits")
+    _, msx = sq.mx_quantize(x, 0)
+    _, msw = sq.mx_quantize(w, 0)
+    Cr, amr = sq.mx_scaled_gemm(mqx, 0, msx, mqw, 0, msw, want_amax=True)
+    assert torch.equal(Cr.view(torch.int16), C.view(torch.int16))
+    assert f32_bits_of(amr) == f32_bits_of(am)
+    del C, Cr
     say("c5 oracle (mx)")
     oqxm, osxm = oracle_mx_chunked(xb, E4M3, rs)
     oqwm, oswm = oracle_mx_chunked(wb, E4M3, cs)
-    y, s = oracle.mx_gemm_sample_ref(oqxm, osxm, E4M3, oqwm, oswm, E4M3, ri, ci)
-    assert_gemm_close(got, y, s, True, "c5 mx")
+    y = oracle.mx_gemm_ref(oqxm, osxm, E4M3, oqwm, oswm, E4M3)
+    sabs = oracle.mx_abs_product_sum(oqxm, osxm, E4M3, oqwm, oswm, E4M3)
+    assert_gemm_close(got, y, sabs, True, "c5 mx")
 
 
 def test_backward_shapes_7b_mlp_sampled():
