@@ -176,16 +176,19 @@ def backward_extras(dev, reps: int = 5):
           ("cast_t_X", lambda: sq.fp8_quantize(x, sq.E4M3, bx, q=qx, qT=qxT), 4 * T * H),
           ("gemm_dX", lambda: sq.fp8_scaled_gemm(qdy, sq.E5M2, bdy, qwT, sq.E4M3, bw, out=dx), None),
           ("gemm_dW", lambda: sq.fp8_scaled_gemm(qdyT, sq.E5M2, bdy, qxT, sq.E4M3, bx, out=dw), None)]
-    mq, ms_ = torch.empty(T, F, dtype=torch.uint8, device=dev), torch.empty(T, F // 32, dtype=torch.uint8, device=dev)
-    mqT, msT = torch.empty(F, T, dtype=torch.uint8, device=dev), torch.empty(F, T // 32, dtype=torch.uint8, device=dev)
-    mwT, mswT = torch.empty(H, F, dtype=torch.uint8, device=dev), torch.empty(H, F // 32, dtype=torch.uint8, device=dev)
-    mxT, msxT = torch.empty(H, T, dtype=torch.uint8, device=dev), torch.empty(H, T // 32, dtype=torch.uint8, device=dev)
-    mx = [("mx_cast_dY", lambda: sq.mx_quantize(dy, sq.E5M2, q=mq, scales=ms_), (3 + 1 / 32) * T * F),
-          ("mx_cast_t_dY", lambda: sq.mx_quantize_t(dy, sq.E5M2, qT=mqT, scalesT=msT), (3 + 1 / 32) * T * F),
-          ("mx_cast_t_W", lambda: sq.mx_quantize_t(w, sq.E4M3, qT=mwT, scalesT=mswT), (3 + 1 / 32) * F * H),
-          ("mx_cast_t_X", lambda: sq.mx_quantize_t(x, sq.E4M3, qT=mxT, scalesT=msxT), (3 + 1 / 32) * T * H),
-          ("mx_gemm_dX", lambda: sq.mx_scaled_gemm(mq, sq.E5M2, ms_, mwT, sq.E4M3, mswT, out=dx), None),
-          ("mx_gemm_dW", lambda: sq.mx_scaled_gemm(mqT, sq.E5M2, msT, mxT, sq.E4M3, msxT, out=dw), None)]
+    # MX: every cast writes its E8M0 codes in the packed layout the products
+    # read (as Fp8Linear does when K % 128 == 0 and K >= 512)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    mq, ms_ = torch.empty(T, F, **u8), torch.empty(sq.mx_packed_scales_bytes(T, F // 32), **u8)
+    mqT, msT = torch.empty(F, T, **u8), torch.empty(sq.mx_packed_scales_bytes(F, T // 32), **u8)
+    mwT, mswT = torch.empty(H, F, **u8), torch.empty(sq.mx_packed_scales_bytes(H, F // 32), **u8)
+    mxT, msxT = torch.empty(H, T, **u8), torch.empty(sq.mx_packed_scales_bytes(H, T // 32), **u8)
+    mx = [("mx_cast_dY", lambda: sq.mx_quantize_packed(dy, sq.E5M2, q=mq, packed=ms_), (3 + 1 / 32) * T * F),
+          ("mx_cast_t_dY", lambda: sq.mx_quantize_t_packed(dy, sq.E5M2, qT=mqT, packed=msT), (3 + 1 / 32) * T * F),
+          ("mx_cast_t_W", lambda: sq.mx_quantize_t_packed(w, sq.E4M3, qT=mwT, packed=mswT), (3 + 1 / 32) * F * H),
+          ("mx_cast_t_X", lambda: sq.mx_quantize_t_packed(x, sq.E4M3, qT=mxT, packed=msxT), (3 + 1 / 32) * T * H),
+          ("mx_gemm_dX", lambda: sq.mx_scaled_gemm_packed(mq, sq.E5M2, ms_, mwT, sq.E4M3, mswT, out=dx), None),
+          ("mx_gemm_dW", lambda: sq.mx_scaled_gemm_packed(mqT, sq.E5M2, msT, mxT, sq.E4M3, msxT, out=dw), None)]
     flops = 2.0 * T * H * F
     out = {"shapes": "dY [4096 x 11008] E5M2, W [11008 x 4096], X [4096 x 4096] E4M3; bf16 out"}
     for tag, ops in (("per_tensor", pt), ("mx", mx)):

@@ -292,9 +292,21 @@ int mx_quantize_packed(const void* x, int dtype, int64_t rows, int64_t cols, int
                        hipStream_t stream);
 
 /*
+ * mx_quantize_t_packed — mx_quantize_t_rule (the MX cast of x^T: blocks of 32
+ * rows, qT [cols x rows]) writing the E8M0 codes of qT, a [cols x rows/32]
+ * matrix, in the packed layout: mx_packed_scales_bytes(cols, rows / 32)
+ * bytes, 16-byte aligned (else FP8_ERR_ALIGN); every byte is written (127
+ * past the matrix).  Equal to mx_pack_scales of mx_quantize_t_rule's codes.
+ */
+int mx_quantize_t_packed(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                         int fmt, int rule, uint8_t* qT, int64_t ldqT, uint8_t* packed,
+                         hipStream_t stream);
+
+/*
  * mx_scaled_gemm_packed — mx_scaled_gemm with both scale operands in the
  * packed layout (A_packed from mx_pack_scales of A's [M x K/32] codes or from
- * mx_quantize_packed, B_packed likewise for B's [N x K/32] codes).  Same result, bit for bit, as
+ * mx_quantize_packed / mx_quantize_t_packed, B_packed likewise for B's
+ * [N x K/32] codes).  Same result, bit for bit, as
  * mx_scaled_gemm on the row-major codes.  Requirements: those of
  * mx_scaled_gemm, plus K % 128 == 0 and K >= 512 (else FP8_ERR_UNSUPPORTED:
  * use mx_scaled_gemm) and 16-byte aligned packed buffers (FP8_ERR_ALIGN).

@@ -26,7 +26,8 @@ __all__ = [
     "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize", "mx_quantize_t",
     "mx_quantize_rule", "mx_quantize_t_rule", "MX_RULE_FMAX", "MX_RULE_OCP",
     "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string", "fp8_abi_version",
-    "mx_packed_scales_bytes", "mx_pack_scales", "mx_quantize_packed", "mx_scaled_gemm_packed",
+    "mx_packed_scales_bytes", "mx_pack_scales", "mx_quantize_packed", "mx_quantize_t_packed",
+    "mx_scaled_gemm_packed",
 ]
 
 E4M3 = 0
@@ -66,6 +67,7 @@ _SIGNATURES = {
     "mx_packed_scales_bytes": ([_i64, _i64], _i64),
     "mx_pack_scales": ([_p, _i64, _i64, _i64, _p, _p], _i),
     "mx_quantize_packed": ([_p, _i, _i64, _i64, _i64, _i, _i, _p, _i64, _p, _p], _i),
+    "mx_quantize_t_packed": ([_p, _i, _i64, _i64, _i64, _i, _i, _p, _i64, _p, _p], _i),
     "mx_scaled_gemm_packed": ([_i64, _i64, _i64, _p, _i, _i64, _p, _p, _i, _i64, _p,
                                _p, _i, _i64, _p, _p], _i),
 }
@@ -503,3 +505,29 @@ def mx_quantize_packed(x: torch.Tensor, fmt=E4M3, rule="fmax", q: torch.Tensor |
     _check("mx_quantize_packed", load_library().mx_quantize_packed(
         _ptr(x), dt, rows, cols, ld, _fmt(fmt), _rule(rule), _ptr(q), ldq, _ptr(packed), _stream(x)))
     return q, packed
+
+
+def mx_quantize_t_packed(x: torch.Tensor, fmt=E4M3, rule="fmax", qT: torch.Tensor | None = None,
+                         packed: torch.Tensor | None = None):
+    """MX cast of x^T (blocks of 32 rows of x, qT [C x R]) with the E8M0 codes
+    of qT in the packed layout; returns (qT, packed codes as a 1-D uint8
+    tensor of mx_packed_scales_bytes(C, R / 32) bytes)."""
+    rows, cols, ld = _mat(x, "x")
+    dt = _dtype_code(x, "x")
+    if rows % 32:
+        raise ValueError("rows must be a multiple of 32")
+    if qT is None:
+        qT = torch.empty((cols, rows), dtype=torch.uint8, device=x.device)
+    _u8(qT, "qT")
+    qr, qc, ldqT = _mat(qT, "qT")
+    if (qr, qc) != (cols, rows):
+        raise ValueError("qT must have the transposed shape of x")
+    n = mx_packed_scales_bytes(cols, rows // 32)
+    if packed is None:
+        packed = torch.empty(n, dtype=torch.uint8, device=x.device)
+    _u8(packed, "packed")
+    if packed.dim() != 1 or packed.numel() != n or not packed.is_contiguous():
+        raise ValueError(f"packed must be a contiguous 1-D uint8 tensor of {n} bytes")
+    _check("mx_quantize_t_packed", load_library().mx_quantize_t_packed(
+        _ptr(x), dt, rows, cols, ld, _fmt(fmt), _rule(rule), _ptr(qT), ldqT, _ptr(packed), _stream(x)))
+    return qT, packed

@@ -45,9 +45,17 @@ import torch
 
 from . import (E4M3, E5M2, _rule, fp8_amax, fp8_compute_scale, fp8_compute_scale_delayed,
                fp8_history_init, fp8_history_push, fp8_quantize, fp8_scaled_gemm, mx_quantize_packed,
-               mx_quantize_rule, mx_quantize_t_rule, mx_scaled_gemm, mx_scaled_gemm_packed)
+               mx_quantize_rule, mx_quantize_t_packed, mx_quantize_t_rule, mx_scaled_gemm,
+               mx_scaled_gemm_packed)
 
 RECIPES = ("current", "delayed", "mx", "constant")
+
+
+def _packable(m: int, n: int, k: int) -> bool:
+    """Whether an MX product of these sizes runs on packed scales: the casts
+    then write the layout the GEMM copies whole cache lines of (same result,
+    bit for bit)."""
+    return k % 128 == 0 and k >= 512 and m > 0 and n > 0
 
 
 class _History:
@@ -101,10 +109,7 @@ class Fp8LinearFunction(torch.autograd.Function):
         recipe = layer.recipe
         if recipe == "mx":
             rule = layer.mx_rule
-            K = x2.shape[1]
-            if K % 128 == 0 and K >= 512 and x2.shape[0] > 0 and w.shape[0] > 0:
-                # the casts write the scales in the layout the GEMM copies
-                # whole cache lines of (same product, bit for bit)
+            if _packable(x2.shape[0], w.shape[0], x2.shape[1]):
                 qx, px = mx_quantize_packed(x2, E4M3, rule)
                 qw, pw = mx_quantize_packed(w, E4M3, rule)
                 y, amax = mx_scaled_gemm_packed(qx, E4M3, px, qw, E4M3, pw, out_dtype=x.dtype, want_amax=True)
@@ -113,9 +118,13 @@ class Fp8LinearFunction(torch.autograd.Function):
                 qw, sw = mx_quantize_rule(w, E4M3, rule)
                 y, amax = mx_scaled_gemm(qx, E4M3, sx, qw, E4M3, sw, out_dtype=x.dtype, want_amax=True)
             if ctx.needs_input_grad[0] or ctx.needs_input_grad[1]:
-                # backward operands: blocks along out (W^T) and along tokens (X^T)
-                qwT, swT = mx_quantize_t_rule(w, E4M3, rule)
-                qxT, sxT = mx_quantize_t_rule(x2, E4M3, rule)
+                # backward operands: blocks along out (W^T, the K of dX) and
+                # along tokens (X^T, the K of dW)
+                T, N = x2.shape[0], w.shape[0]
+                ctx.pk_dx = _packable(T, w.shape[1], N)
+                ctx.pk_dw = _packable(N, w.shape[1], T)
+                qwT, swT = (mx_quantize_t_packed if ctx.pk_dx else mx_quantize_t_rule)(w, E4M3, rule)
+                qxT, sxT = (mx_quantize_t_packed if ctx.pk_dw else mx_quantize_t_rule)(x2, E4M3, rule)
                 ctx.save_for_backward(qwT, swT, qxT, sxT)
         else:
             bx, qx, qxT = _per_tensor_cast(x2, E4M3, recipe, layer.margin, layer._hx, True, layer._bias,
@@ -142,11 +151,19 @@ class Fp8LinearFunction(torch.autograd.Function):
         if layer.recipe == "mx":
             qwT, swT, qxT, sxT = ctx.saved_tensors
             if ctx.needs_input_grad[0]:
-                qdy, sdy = mx_quantize_rule(dy2, E5M2, layer.mx_rule)
-                dx, _ = mx_scaled_gemm(qdy, E5M2, sdy, qwT, E4M3, swT, out_dtype=ctx.dtype)
+                if ctx.pk_dx:
+                    qdy, pdy = mx_quantize_packed(dy2, E5M2, layer.mx_rule)
+                    dx, _ = mx_scaled_gemm_packed(qdy, E5M2, pdy, qwT, E4M3, swT, out_dtype=ctx.dtype)
+                else:
+                    qdy, sdy = mx_quantize_rule(dy2, E5M2, layer.mx_rule)
+                    dx, _ = mx_scaled_gemm(qdy, E5M2, sdy, qwT, E4M3, swT, out_dtype=ctx.dtype)
             if ctx.needs_input_grad[1]:
-                qdyT, sdyT = mx_quantize_t_rule(dy2, E5M2, layer.mx_rule)
-                dw, _ = mx_scaled_gemm(qdyT, E5M2, sdyT, qxT, E4M3, sxT, out_dtype=ctx.dtype)
+                if ctx.pk_dw:
+                    qdyT, pdyT = mx_quantize_t_packed(dy2, E5M2, layer.mx_rule)
+                    dw, _ = mx_scaled_gemm_packed(qdyT, E5M2, pdyT, qxT, E4M3, sxT, out_dtype=ctx.dtype)
+                else:
+                    qdyT, sdyT = mx_quantize_t_rule(dy2, E5M2, layer.mx_rule)
+                    dw, _ = mx_scaled_gemm(qdyT, E5M2, sdyT, qxT, E4M3, sxT, out_dtype=ctx.dtype)
         else:
             qwT, bw, qxT, bx = ctx.saved_tensors
             bdy, qdy, qdyT = _per_tensor_cast(dy2, E5M2, layer.recipe, layer.margin, layer._hdy,

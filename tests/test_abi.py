@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
                  "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize", "mx_quantize_t",
                  "mx_quantize_rule", "mx_quantize_t_rule", "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string",
                  "fp8_abi_version", "mx_packed_scales_bytes", "mx_pack_scales", "mx_quantize_packed",
-                 "mx_scaled_gemm_packed"]:
+                 "mx_quantize_t_packed", "mx_scaled_gemm_packed"]:
         assert want in names
 
 
@@ -182,6 +182,13 @@ def test_packed_scales_size_and_validation(lib):
     assert c(FAKE, 0, 4, 64, 64, 3, 0, FAKE, 64, FAKE, S) == FORMAT
     assert c(FAKE, 0, 4, 64, 64, 0, 9, FAKE, 64, FAKE, S) == FORMAT
     assert c(None, 0, 4, 64, 64, 0, 0, FAKE, 64, FAKE, S) == NULL
+    t = lib.mx_quantize_t_packed
+    # x, dt, rows, cols, ld, fmt, rule, qT, ldqT, packed, s
+    assert t(FAKE, 0, 64, 16, 16, 0, 0, None, 64, FAKE, S) == NULL
+    assert t(FAKE, 0, 48, 16, 16, 0, 0, FAKE, 48, FAKE, S) == SHAPE
+    assert t(FAKE, 0, 64, 16, 16, 0, 0, FAKE, 32, FAKE, S) == SHAPE
+    assert t(FAKE, 0, 64, 16, 16, 0, 0, FAKE, 64, FAKE + 4, S) == ALIGN
+    assert t(FAKE, 0, 64, 16, 16, 0, 7, FAKE, 64, FAKE, S) == FORMAT
     g = lib.mx_scaled_gemm_packed
     # M, N, K, A, fa, lda, Ap, B, fb, ldb, Bp, C, dt, ldc, amax, s
     assert g(64, 64, 256, FAKE, 0, 256, FAKE, FAKE, 0, 256, FAKE, FAKE, 0, 64, None, S) == UNSUP

@@ -19,11 +19,12 @@ from gpu_helpers import DEV, assert_gemm_close, bf16_dev, host, host_f64, mfma_g
 T, IN, OUT = 256, 512, 384
 
 
-def _tensors(step=0, x_scale=1.0):
-    xb = make("c1", "X", step=step, shape=(T, IN))
+def _tensors(step=0, x_scale=1.0, shape=(T, IN, OUT)):
+    t, i, o = shape
+    xb = make("c1", "X", step=step, shape=(t, i))
     x = oracle.bf16_bits_to_f64(xb) * x_scale                 # exact: power-of-two scales only
-    wb = make("c1", "W", shape=(OUT, IN))
-    dyb = make("c3", "dY", step=step, shape=(T, OUT))
+    wb = make("c1", "W", shape=(o, i))
+    dyb = make("c3", "dY", step=step, shape=(t, o))
     return x, oracle.bf16_bits_to_f64(wb), oracle.bf16_bits_to_f64(dyb)
 
 
@@ -109,14 +110,18 @@ def test_linear_constant_bias_matches_oracle():
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("shape", [(T, IN, OUT), (512, 512, 640)], ids=["256x512x384", "512x512x640"])
 @pytest.mark.parametrize("rule", ["fmax", "ocp"])
-def test_linear_mx_matches_oracle(rule):
+def test_linear_mx_matches_oracle(rule, shape):
+    """The MX recipe's three products against the oracle's.  At 256 x 512 x 384
+    only the forward product (K = 512) runs on packed scales; at 512 x 512 x
+    640 all three do (K = 512, 640, 512)."""
     need_gpu()
-    x, w, dy = _tensors()
-    layer = Fp8Linear(IN, OUT, recipe="mx", mx_rule=rule, device=DEV)
+    x, w, dy = _tensors(shape=shape)
+    layer = Fp8Linear(shape[1], shape[2], recipe="mx", mx_rule=rule, device=DEV)
     with torch.no_grad():
         layer.weight.copy_(_dev(w))
-    say(f"fp8 linear, MX, rule {rule}")
+    say(f"fp8 linear, MX, rule {rule}, T x in x out {shape}")
     y, dx, dw, amax = _run(layer, x, dy)
     qx, sx = oracle.mx_quantize(x, E4M3, rule)
     qw, sw = oracle.mx_quantize(w, E4M3, rule)

@@ -379,3 +379,22 @@ def test_mx_quantize_packed(rows, cols, dtype, fmt, rule):
         rq2, rs2 = oracle.mx_quantize(xv[:, 32:], fmt, rule=rule)
         assert np.array_equal(host(q2), rq2)
         assert np.array_equal(host(ps2), pack_scales_host(rs2))
+
+
+@pytest.mark.parametrize("rows,cols,dtype,fmt,rule", [
+    (320, 300, "bf16", E4M3, "fmax"), (512, 256, "bf16", E4M3, "fmax"), (1056, 70, "f32", E5M2, "fmax"),
+    (2048, 130, "bf16", E5M2, "ocp"), (32, 1, "bf16", E4M3, "fmax")],
+    ids=["320x300", "512x256", "1056x70_f32_e5", "2048x130_e5_ocp", "32x1"])
+def test_mx_quantize_t_packed(rows, cols, dtype, fmt, rule):
+    """mx_quantize_t_packed: qT equal to the oracle's MX cast of x^T, and its
+    E8M0 codes ([cols x rows/32]) in the packed layout with 127 padding
+    (ragged and whole tiles and groups, bf16 / fp32, both rules)."""
+    rng = np.random.default_rng(rows * 3 + cols)
+    vals = rng.standard_normal((rows, cols)) * np.exp(rng.normal(0.0, 2.0, (rows, 1)))
+    bits = f32_to_bf16_bits(vals.astype(np.float32))
+    xv = oracle.bf16_bits_to_f64(bits) if dtype == "bf16" else vals.astype(np.float32).astype(np.float64)
+    x = bf16_dev(bits) if dtype == "bf16" else f32_dev(vals.astype(np.float32))
+    rq, rs = oracle.mx_quantize(np.ascontiguousarray(xv.T), fmt, rule=rule)
+    qT, ps = sq.mx_quantize_t_packed(x, fmt.code, rule=rule)
+    assert np.array_equal(host(qT), rq)
+    assert np.array_equal(host(ps), pack_scales_host(rs))
