@@ -151,6 +151,47 @@ def rmse_c4(dev):
     return out
 
 
+def gemm_configs(dev, reps: int = 10):
+    """GEMM throughput on the other forward workload shapes (outside the
+    headline step, device-drawn N(0, s) inputs cast by the library): the
+    Llama-2-7B attention projection of the delayed-scaling workload (per
+    tensor, 2048 x 4096 x 4096: 128 output tiles for 256 compute units) and
+    the 13B-MLP up-projection of the MXFP8 workload (8192 x 13824 x 5120 on
+    packed scales)."""
+    import torch
+    import scaled_quantize_fp8_amd as sq
+    out = {}
+    for name, (M, N, K), mx in (("attn_7b_2048x4096x4096_per_tensor", (2048, 4096, 4096), False),
+                                ("mlp_up_13b_8192x13824x5120_mx", (8192, 13824, 5120), True)):
+        x = torch.randn(M, K, device=dev).to(torch.bfloat16)
+        w = (torch.randn(N, K, device=dev) * 0.02).to(torch.bfloat16)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        if mx:
+            qx, sx = sq.mx_quantize_packed(x, sq.E4M3)
+            qw, sw = sq.mx_quantize_packed(w, sq.E4M3)
+            fn = lambda: sq.mx_scaled_gemm_packed(qx, sq.E4M3, sx, qw, sq.E4M3, sw, out=y)
+        else:
+            bx, _, _ = sq.fp8_compute_scale(sq.fp8_amax(x), sq.E4M3, 0)
+            bw, _, _ = sq.fp8_compute_scale(sq.fp8_amax(w), sq.E4M3, 0)
+            qx, _, _ = sq.fp8_quantize(x, sq.E4M3, bx)
+            qw, _, _ = sq.fp8_quantize(w, sq.E4M3, bw)
+            fn = lambda: sq.fp8_scaled_gemm(qx, sq.E4M3, bx, qw, sq.E4M3, bw, out=y)
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = 2.0 * M * N * K / ms / 1e9
+        out[name] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1), "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+        del x, w, y, qx, qw
+    torch.cuda.empty_cache()
+    return out
+
+
 def backward_extras(dev, reps: int = 5):
     """The 7B-MLP down-projection backward (dY [4096 x 11008], W [11008 x
     4096], X [4096 x 4096]) as the linear layer runs it: transposed casts,
@@ -378,7 +419,8 @@ def main():
         stream[k] = {"achieved": round(v, 1), "frac": round(v / PEAK_HBM_GBS, 4),
                      "frac_of_copy": round(v / copy_GBps, 4)}
 
-    extras = {"backward_7b_mlp": backward_extras(dev), "rmse_13b_mlp_up": rmse_c4(dev)}
+    extras = {"backward_7b_mlp": backward_extras(dev), "gemm_configs": gemm_configs(dev),
+              "rmse_13b_mlp_up": rmse_c4(dev)}
 
     cpu = None
     if not args.no_cpu_baseline:
