@@ -583,8 +583,17 @@ struct TileSrd {
   v4i a, b, sa, sb;
 };
 
-template <int FA, int FB, bool MX>
+template <int FA, int FB, bool MX, int BMX>
 __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
+  // BMX: tile rows (256, or 128 for grids with fewer 256 x 256 tiles than
+  // compute units).  A 256-row tile puts the 4 waves in 2 x 2, each 128 x
+  // 128 of C; a 128-row tile in 1 x 4, each 128 x 64 (4 op(A) and 2 op(B)
+  // fragments, 8 MFMAs per sub-step, 12 copies per stage).
+  static_assert(BMX == 256 || BMX == 128, "tile rows");
+  constexpr int NI = BMX == 256 ? 4 : 2;            // op(B) fragments per wave
+  constexpr int WN = NI * 32;                       // C columns per wave
+  constexpr int NA = BMX / 32;                      // op(A) copies per stage per wave
+  constexpr int NT = NI * 4;                        // MFMAs per sub-step
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];
   // MX scales, 4 stages per copy: [group slot][operand][tile row][4 dwords]
   __shared__ __attribute__((aligned(16))) uint32_t s_scale[MX ? 2 * 2 * BM * 4 : 1];
@@ -599,7 +608,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   constexpr int kSlot = kTileBytes;                 // 32 KiB per slot per operand
   constexpr int kFrag = 32 * BK;                    // 4 KiB between 32-row fragments
   constexpr int U = MX ? 4 : 2;                     // stages per loop iteration
-  constexpr int LPS = 16;                           // data copies per stage per wave
+  constexpr int LPS = NA + 8;                       // data copies per stage per wave
   // Launch shape (kFwdPersistent): one tile per workgroup, the dispatcher
   // refilling each compute unit as a workgroup ends.  The persistent form
   // (one workgroup per compute unit walking tiles, the last two stages of a
@@ -608,12 +617,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // stores in flight it measures slower (70B-MLP shape: -2.1% at K = 8192,
   // -2.3% at K = 4096).  MX never runs persistent: its scale descriptors
   // leave no SGPRs for a second tile's.
-  constexpr bool PERSIST = kFwdPersistent && !MX;
+  constexpr bool PERSIST = kFwdPersistent && !MX && BMX == 256;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: SGPR
-  const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_m = (int)((g.M + BM - 1) / BM);
+  const int wm = BMX == 256 ? wave >> 1 : 0, wn = BMX == 256 ? wave & 1 : wave;
+  const int tiles_m = (int)((g.M + BMX - 1) / BMX);
   const int tiles_n = (int)((g.N + BN - 1) / BN);
   const int tiles = tiles_m * tiles_n;
   const int P = gridDim.x;                          // persistent: tiles vb, vb + P, ...
@@ -628,8 +637,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     if (vb < tiles && (PERSIST || vb == (int)blockIdx.x)) {
       int tm, tn;
       tile_coords_vb(vb, tiles_m, tiles_n, tm, tn);
-      const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
-      const int64_t ra = g.M - m0 < BM ? g.M - m0 : BM, rb = g.N - n0 < BN ? g.N - n0 : BN;
+      const int64_t m0 = (int64_t)tm * BMX, n0 = (int64_t)tn * BN;
+      const int64_t ra = g.M - m0 < BMX ? g.M - m0 : BMX, rb = g.N - n0 < BN ? g.N - n0 : BN;
       T.a = make_srd(g.A + m0 * g.lda, (ra - 1) * g.lda + g.K);
       T.b = make_srd(g.B + n0 * g.ldb, (rb - 1) * g.ldb + g.K);
       if constexpr (MX) {
@@ -637,7 +646,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
           // one 256-row tile of the packed layout: sgroups x 4 KiB, rows past
           // the matrix padded with code 127 by mx_pack_scales
           const int64_t tb = g.sgroups * (int64_t)kPackTile;
-          T.sa = make_srd(g.sa + (int64_t)tm * tb, tb);
+          // a 128-row tile is one half of a packed 256-row tile: its rows
+          // start 128 rows (2 KiB) into each 4 KiB group block
+          const int64_t ah = BMX == 256 ? 0 : (int64_t)(tm & 1) * 128 * kPackBlocks;
+          T.sa = make_srd(g.sa + (int64_t)(tm / (256 / BMX)) * tb + ah, tb - ah);
           T.sb = make_srd(g.sb + (int64_t)tn * tb, tb);
         } else {
           T.sa = make_srd(g.sa + m0 * g.lds_a, (ra - 1) * g.lds_a + nkb);
@@ -665,7 +677,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = (wave * 8 + i) * 8 + (lane >> 3);
-    offa[i] = (uint32_t)(row * g.lda + 16 * (cl ^ (i & 1)));
+    const int rowa_c = (wave * NA + (i % NA)) * 8 + (lane >> 3);
+    offa[i] = (uint32_t)(rowa_c * g.lda + 16 * (cl ^ (i & 1)));
     offb[i] = (uint32_t)(row * g.ldb + 16 * (cl ^ (i & 1)));
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
@@ -712,14 +725,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     const bool nx = PERSIST && s >= nkU;
     const bool live = s < nk || nx;
     const uint32_t k0 = (uint32_t)((nx ? s - nkU : s) * BK);
-    const int i = t & 7;
-    const bool isb = t >= 8;
+    const bool isb = t >= NA;
+    const int i = isb ? t - NA : t;
     const uint32_t off = isb ? offb[i] : offa[i];
-    const uint32_t la = lds0 + (uint32_t)((isb ? kRegB : 0) + slot * kSlot + (wave * 8 + i) * 1024);
+    const uint32_t la = lds0 + (uint32_t)((isb ? kRegB + (wave * 8 + i) * 1024 : (wave * NA + i) * 1024) +
+                                          slot * kSlot);
     v4i srd = isb ? cur.b : cur.a;
     if constexpr (PERSIST) srd = nx ? (isb ? nxt.b : nxt.a) : srd;
     srd[2] = live ? srd[2] : 0;
-    if ((t & 7) == 0)
+    if (t == 0 || t == NA)
       dma_b128_so<5>(uniform_srd(srd), __builtin_amdgcn_readfirstlane(la), off, __builtin_amdgcn_readfirstlane(k0));
     else
       dma_b128_so<1>(uniform_srd(srd), __builtin_amdgcn_readfirstlane(la), off, __builtin_amdgcn_readfirstlane(k0));
@@ -778,7 +792,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         sc[j] = (int)s_scale[((gs * 2 * BM) + wm * 128 + j * 32 + (lane & 31)) * 4 + d];
-        sc[4 + j] = (int)s_scale[((gs * 2 + 1) * BM + wn * 128 + j * 32 + (lane & 31)) * 4 + d];
+        sc[4 + j] = (int)s_scale[((gs * 2 + 1) * BM + wn * WN + (j % NI) * 32 + (lane & 31)) * 4 + d];
       }
     }
   };
@@ -786,7 +800,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // per-lane fragment bases (slot 0, fragment 0) for sub-steps 0 and 1
   const int s7 = (lane & 7) ^ ((lane >> 3) & 1), gq = lane >> 5;   // fswz of the lane's rows
   const uint32_t rowa = (uint32_t)((wm * 128 + (lane & 31)) * BK);
-  const uint32_t rowb = (uint32_t)(kRegB + (wn * 128 + (lane & 31)) * BK);
+  const uint32_t rowb = (uint32_t)(kRegB + (wn * WN + (lane & 31)) * BK);
   const uint32_t a0lo = rowa + (((0 + gq) ^ s7) << 4), a0hi = rowa + (((2 + gq) ^ s7) << 4);
   const uint32_t a1lo = rowa + (((4 + gq) ^ s7) << 4), a1hi = rowa + (((6 + gq) ^ s7) << 4);
   const uint32_t b0lo = rowb + (((0 + gq) ^ s7) << 4), b0hi = rowb + (((2 + gq) ^ s7) << 4);
@@ -813,10 +827,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   x0[0] = frag_at<0 * kFrag>(smem, a0lo, a0hi); x0[1] = frag_at<1 * kFrag>(smem, a0lo, a0hi);
   x0[2] = frag_at<2 * kFrag>(smem, a0lo, a0hi); x0[3] = frag_at<3 * kFrag>(smem, a0lo, a0hi);
   w0[0] = frag_at<0 * kFrag>(smem, b0lo, b0hi); w0[1] = frag_at<1 * kFrag>(smem, b0lo, b0hi);
-  w0[2] = frag_at<2 * kFrag>(smem, b0lo, b0hi); w0[3] = frag_at<3 * kFrag>(smem, b0lo, b0hi);
+  if constexpr (NI == 4) {
+    w0[2] = frag_at<2 * kFrag>(smem, b0lo, b0hi); w0[3] = frag_at<3 * kFrag>(smem, b0lo, b0hi);
+  }
   read_scales(0, sc[0]);
 
-  v16f acc[4][4];
+  v16f acc[NI][4];
   // One stage in slot SLOT: phase A = sub-step 0 MFMAs (set 0) while reading
   // sub-step 1 (set 1); publish stage kt+1 (wait own DMA, barrier); phase B =
   // sub-step 1 MFMAs while reading stage kt+1's sub-step 0 (set 0) and
@@ -833,7 +849,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const int i = t >> 2, j = t & 3;
       switch (t) {
         case 0: x1[0] = frag_at<SLOT * kSlot + 0 * kFrag>(smem, a1lo, a1hi); break;
@@ -842,8 +858,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
         case 3: x1[3] = frag_at<SLOT * kSlot + 3 * kFrag>(smem, a1lo, a1hi); break;
         case 4: w1[0] = frag_at<SLOT * kSlot + 0 * kFrag>(smem, b1lo, b1hi); break;
         case 5: w1[1] = frag_at<SLOT * kSlot + 1 * kFrag>(smem, b1lo, b1hi); break;
-        case 6: w1[2] = frag_at<SLOT * kSlot + 2 * kFrag>(smem, b1lo, b1hi); break;
-        case 7: w1[3] = frag_at<SLOT * kSlot + 3 * kFrag>(smem, b1lo, b1hi); break;
+        case 6: if constexpr (NI == 4) w1[2] = frag_at<SLOT * kSlot + 2 * kFrag>(smem, b1lo, b1hi); break;
+        case 7: if constexpr (NI == 4) w1[3] = frag_at<SLOT * kSlot + 3 * kFrag>(smem, b1lo, b1hi); break;
         default: break;
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -857,9 +873,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const int i = t >> 2, j = t & 3;
       {
+        if (t == (NT == 16 ? 8 : 6)) read_scales(kt + 1, sc[NSL]);
         switch (t) {
           case 0: x0[0] = frag_at<NSL * kSlot + 0 * kFrag>(smem, a0lo, a0hi); break;
           case 1: x0[1] = frag_at<NSL * kSlot + 1 * kFrag>(smem, a0lo, a0hi); break;
@@ -867,9 +884,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
           case 3: x0[3] = frag_at<NSL * kSlot + 3 * kFrag>(smem, a0lo, a0hi); break;
           case 4: w0[0] = frag_at<NSL * kSlot + 0 * kFrag>(smem, b0lo, b0hi); break;
           case 5: w0[1] = frag_at<NSL * kSlot + 1 * kFrag>(smem, b0lo, b0hi); break;
-          case 6: w0[2] = frag_at<NSL * kSlot + 2 * kFrag>(smem, b0lo, b0hi); break;
-          case 7: w0[3] = frag_at<NSL * kSlot + 3 * kFrag>(smem, b0lo, b0hi); break;
-          case 8: read_scales(kt + 1, sc[NSL]); break;
+          case 6: if constexpr (NI == 4) w0[2] = frag_at<NSL * kSlot + 2 * kFrag>(smem, b0lo, b0hi); break;
+          case 7: if constexpr (NI == 4) w0[3] = frag_at<NSL * kSlot + 3 * kFrag>(smem, b0lo, b0hi); break;
           default: break;
         }
       }
@@ -879,25 +895,28 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
       else
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w1[i], x1[j], acc[i][j], FB, FA, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      dma(kt + 2, t);
+      // the stage's LPS copies spread over its NT MFMA slots
+#pragma unroll
+      for (int c = 0; c < LPS; ++c)
+        if (c * NT / LPS == t) dma(kt + 2, c);
       if constexpr (SCALES)
-        if (t == 15) scale_dma((kt >> 2) + 1);
-      if (t == 15) prefetch_b(kt + 8, pf_owner);
+        if (t == NT - 1) scale_dma((kt >> 2) + 1);
+      if (t == NT - 1) prefetch_b(kt + 8, pf_owner);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  // Global stores of an interior epilogue per wave (bf16: 4 block rows x 2
-  // halves x 4 row groups; fp32: 4 x 4 x 4), the ops issued after the last
+  // Global stores of an interior epilogue per wave (bf16: 4 block rows x NI/2
+  // halves x 4 row groups; fp32: 4 x NI x 4), the ops issued after the last
   // copy of a workgroup's last tile; the final wait leaves them in flight.
-  constexpr int kEpiStores = 32;
+  constexpr int kEpiStores = 4 * (NI / 2) * 4;
   const int e = MX ? 0 : -(*g.bias_a + *g.bias_b);
   uint32_t amax_bits = 0;
   for (;;) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -917,13 +936,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
 
     int tm, tn;
     tile_coords_vb(vb, tiles_m, tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int64_t m0 = (int64_t)tm * BMX, n0 = (int64_t)tn * BN;
     // Epilogue.  Lane l of block (i, j) holds n = 8q + 4(l/32) + 0..3 of row
     // m = l%32.  An interior tile (all of it inside C, rows allowing vector
     // stores) takes a straight-line path: one row pointer per block row,
     // immediate column offsets, bf16 maxima as packed 16-bit maxima of |h|;
     // edge tiles check every element.
-    const bool interior = m0 + BM <= g.M && n0 + BN <= g.N && (g.out_f32 ? g.vec_store : g.row16);
+    const bool interior = m0 + BMX <= g.M && n0 + BN <= g.N && (g.out_f32 ? g.vec_store : g.row16);
     if (interior) {
       us2v pmax = {0, 0};
       uint8_t* stg = cstage + (MX ? 0 : wave * kStage);
@@ -935,11 +954,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t m = m0 + wm * 128 + j * 32 + (lane & 31);
-        const int64_t nb = n0 + wn * 128 + 4 * (lane >> 5);
+        const int64_t nb = n0 + wn * WN + 4 * (lane >> 5);
         if (g.out_f32) {
           float* crow = reinterpret_cast<float*>(g.C) + m * g.ldc + nb;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < NI; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               float v[4];
@@ -969,13 +988,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
           const uint32_t wsw = (wr >> 1) & 7;
           // stores: the wave's C block base (uniform) plus a 32-bit byte
           // offset (the host admits this path only if 128 rows span < 4 GiB)
-          uint8_t* const cw = reinterpret_cast<uint8_t*>(g.C) + ((m0 + wm * 128) * g.ldc + n0 + wn * 128) * 2;
+          uint8_t* const cw = reinterpret_cast<uint8_t*>(g.C) + ((m0 + wm * 128) * g.ldc + n0 + wn * WN) * 2;
           const uint32_t ldcb = (uint32_t)g.ldc * 2u;
           const uint32_t lr = (uint32_t)(ln >> 3), ch = (uint32_t)(ln & 7);
           const uint32_t goff = lr * ldcb + 16u * ch;
           const uint32_t rsw0 = lr * 128 + 16 * (ch ^ (lr >> 1)), rsw1 = lr * 128 + 16 * (ch ^ (lr >> 1) ^ 4u);
 #pragma unroll
-          for (int p = 0; p < 2; ++p) {
+          for (int p = 0; p < NI / 2; ++p) {
 #pragma unroll
             for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
@@ -1004,14 +1023,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     } else {
       // epilogue: lane l of block (i, j) holds n = 8q + 4(l/32) + 0..3 of column m = l%32
     #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NI; ++i) {
     #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int64_t m = m0 + wm * 128 + j * 32 + (lane & 31);
           if (m >= g.M) continue;
     #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int64_t n = n0 + wn * 128 + i * 32 + 8 * q + 4 * (lane >> 5);
+            const int64_t n = n0 + wn * WN + i * 32 + 8 * q + 4 * (lane >> 5);
             float v[4];
     #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = MX ? acc[i][j][4 * q + r] : __builtin_amdgcn_ldexpf(acc[i][j][4 * q + r], e);
@@ -1103,9 +1122,16 @@ static void launch_gemm(const GemmArgs& g, hipStream_t s) {
   // per workgroup (or, with kFwdPersistent, per-tensor products walk tiles
   // with one workgroup per compute unit)
   if (!TA && !TB && g.K > 0 && (g.K % 128) == 0 && (!MX || g.scales_dma)) {
-    const int64_t cus = (MX || !kFwdPersistent) ? tiles : device_cu_count();
+    const int64_t ncu = device_cu_count();
+    if (tiles < ncu) {
+      // fewer 256 x 256 tiles than compute units: 128 x 256 tiles
+      const int64_t t128 = ((g.M + 127) / 128) * ((g.N + BN - 1) / BN);
+      hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128>), dim3((unsigned)t128), dim3(kGemmThreads), 0, s, g);
+      return;
+    }
+    const int64_t cus = (MX || !kFwdPersistent) ? tiles : ncu;
     const int64_t grid = tiles < cus ? tiles : cus;
-    hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, g);
+    hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 256>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, g);
   } else {
     hipLaunchKernelGGL((gemm_kernel<FA, FB, MX, TA, TB>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, g);
   }
