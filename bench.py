@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the products and casts timed outside the step (backward, other workloads, RMSE)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, run a plain 1 GiB device-to-device copy (known bytes) "
                          "to scale rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -419,8 +421,10 @@ def main():
         stream[k] = {"achieved": round(v, 1), "frac": round(v / PEAK_HBM_GBS, 4),
                      "frac_of_copy": round(v / copy_GBps, 4)}
 
-    extras = {"backward_7b_mlp": backward_extras(dev), "gemm_configs": gemm_configs(dev),
-              "rmse_13b_mlp_up": rmse_c4(dev)}
+    extras = None
+    if not args.no_extras:
+        extras = {"backward_7b_mlp": backward_extras(dev), "gemm_configs": gemm_configs(dev),
+                  "rmse_13b_mlp_up": rmse_c4(dev)}
 
     cpu = None
     if not args.no_cpu_baseline:

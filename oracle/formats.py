@@ -1,8 +1,9 @@
 """FP8 number formats, bit for bit — oracle (test infrastructure only).
 
 The paper review "Training and inference of large language models using 8-bit
-floating point", section "Proposed method", uses FP8_E4 for weights and
-activations and FP8_E5 for gradients but does not give their bit layouts.
+floating point", section "Proposed method", assigns the format with four
+exponent bits to weights and activations and the one with five exponent bits
+to gradients, without giving either format's bit layout.
 The layouts below are those of the OCP 8-bit floating point specification
 (OFP8): E4M3 ("FN": no infinities, one NaN mantissa pattern) and E5M2 (IEEE-
 like, with infinities).  These are the encodings whose largest finite values
@@ -114,11 +115,21 @@ def f64_to_bf16_bits(v) -> np.ndarray:
 
 
 def bf16_ulp(v) -> np.ndarray:
-    """Spacing of the bfloat16 grid at |v| (the quantum of v's binade)."""
+    """Spacing of the bfloat16 grid in the binade of |v|: the distance from the
+    largest bf16 value <= |v| to the next larger one.
+
+    bfloat16 has 7 stored mantissa bits and the float32 exponent range, so the
+    binade [2**e, 2**(e+1)) has spacing 2**(e - 7) for e >= -126; below 2**-126
+    (zero included) the subnormals share the spacing 2**-133.  The largest
+    finite binade is e = 127, which also stands for finite values beyond the
+    largest bf16 (they round to Inf); NaN and Inf give NaN.
+    """
     a = np.abs(np.asarray(v, dtype=np.float64))
-    _, exp = np.frexp(a)
-    e = np.maximum(exp - 1, -126)
-    return np.ldexp(1.0, e - 7)
+    finite = np.isfinite(a)
+    _, exp = np.frexp(np.where(finite, a, 1.0))    # a = mant * 2**exp, mant in [0.5, 1)
+    e = np.where(a >= np.ldexp(1.0, -126), exp - 1, -126)   # zero and subnormals: -126
+    e = np.minimum(e, 127)
+    return np.where(finite, np.ldexp(1.0, e - 7), np.nan)
 
 
 # ---------------------------------------------------------------------------

@@ -189,3 +189,45 @@ def test_bf16_rounding_matches_torch_from_float32():
     v32 = (rng.standard_normal(200000) * np.exp(rng.uniform(-30, 30, 200000))).astype(np.float32)
     ref = torch.from_numpy(v32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(oracle.f64_to_bf16_bits(v32.astype(np.float64)), ref)
+
+
+def test_bf16_ulp_is_distance_to_next_code():
+    """bf16_ulp (which widens every bf16-output GEMM tolerance) against brute
+    force over all 65,536 patterns: for each finite non-negative bf16 value x
+    the spacing is the decoded distance to the next larger code (the largest
+    finite value, which has no finite successor, uses its predecessor: same
+    binade), and negative values share the spacing of their magnitude.  Zero
+    and the subnormals must give the subnormal step 2**-133."""
+    pats = all_bf16_patterns().astype(np.int64)
+    vals = oracle.bf16_bits_to_f64(pats.astype(np.uint16))
+    pos = pats[(pats < 0x7F80)]                       # +0 .. largest finite
+    x = oracle.bf16_bits_to_f64(pos.astype(np.uint16))
+    nxt = oracle.bf16_bits_to_f64(np.minimum(pos + 1, 0x7F7F).astype(np.uint16))
+    prv = oracle.bf16_bits_to_f64(np.maximum(pos - 1, 0).astype(np.uint16))
+    want = np.where(pos == 0x7F7F, x - prv, nxt - x)
+    assert np.array_equal(oracle.bf16_ulp(x), want)
+    assert oracle.bf16_ulp(0.0) == 2.0 ** -133 and oracle.bf16_ulp(-0.0) == 2.0 ** -133
+    assert oracle.bf16_ulp(2.0 ** -130) == 2.0 ** -133       # a subnormal
+    assert oracle.bf16_ulp(2.0 ** -126) == 2.0 ** -133       # smallest normal: same step
+    assert oracle.bf16_ulp(1.0) == 2.0 ** -7 and oracle.bf16_ulp(1.999) == 2.0 ** -7
+    neg = pats[(pats > 0x8000) & (pats < 0xFF80)]
+    assert np.array_equal(oracle.bf16_ulp(oracle.bf16_bits_to_f64(neg.astype(np.uint16))),
+                          oracle.bf16_ulp(-oracle.bf16_bits_to_f64(neg.astype(np.uint16))))
+    assert np.all(np.isnan(oracle.bf16_ulp(vals[np.isnan(vals) | np.isinf(vals)])))
+
+
+def test_bf16_ulp_between_codes():
+    """For values between codes (the float64 GEMM references), the spacing is
+    that of the two bf16 neighbours enclosing |v|, found by searching the
+    sorted table of every finite non-negative bf16 value."""
+    pats = np.arange(0, 0x7F80, dtype=np.int64)
+    table = oracle.bf16_bits_to_f64(pats.astype(np.uint16))        # increasing
+    rng = np.random.default_rng(4)
+    v = np.ldexp(rng.uniform(-1, 1, 200000), rng.integers(-140, 128, 200000))
+    v = np.concatenate([v, [0.0, -0.0, 2.0 ** -140, 3.0e38]])
+    a = np.abs(v)
+    i = np.searchsorted(table, a, side="right") - 1                 # largest code <= |v|
+    hi = np.minimum(i + 1, table.size - 1)
+    lo = np.where(i + 1 > table.size - 1, i - 1, i)
+    want = table[hi] - table[lo]
+    assert np.array_equal(oracle.bf16_ulp(v), want)

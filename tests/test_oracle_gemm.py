@@ -148,3 +148,71 @@ def test_bf16_output_rounding_and_rmse():
     assert bits.tolist()[:3] == [0x3F80, 0x3F80, 0x3F82]   # ties to even
     assert bits[4] == 0x7F80                                # overflow -> Inf
     assert oracle.rmse(np.array([1.0, 2.0]), np.array([1.0, 4.0])) == np.sqrt(2.0)
+
+
+@pytest.mark.parametrize("fa,fb", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2)], ids=lambda f: f.name)
+def test_abs_product_sum_matches_fractions(fa, fb):
+    """abs_product_sum (the scale of every per-tensor GEMM tolerance) against
+    the exact rational sum_k |2**-ba dec(a_k) * 2**-bb dec(b_k)| built from
+    the bit fields.  The two biases differ, so dropping or swapping one fails;
+    E4M3 x E4M3 sums are exact in float64, the others within K * 2**-53."""
+    rng = np.random.default_rng(18)
+    m, n, k = 6, 5, 40
+    qa = _finite_codes(rng, (m, k), fa)
+    qb = _finite_codes(rng, (n, k), fb)
+    ba, bb = 5, -3
+    s = oracle.abs_product_sum(qa, fa, ba, qb, fb, bb)
+    assert s.shape == (m, n)
+    for i in range(m):
+        for j in range(n):
+            exact = sum(abs(_frac_decode(int(qa[i, t]), fa) * _frac_decode(int(qb[j, t]), fb)) for t in range(k))
+            exact *= Fraction(2) ** (-(ba + bb))
+            if fa is E4M3 and fb is E4M3:
+                assert s[i, j] == float(exact)
+            else:
+                assert abs(Fraction(float(s[i, j])) - exact) <= k * Fraction(1, 2 ** 53) * exact
+
+
+def test_mx_abs_product_sum_matches_fractions():
+    """mx_abs_product_sum (the scale of every MX GEMM tolerance) against the
+    exact rational sum_j 2**(sa-127) 2**(sb-127) sum_{k in block j}
+    |dec(a_k) dec(b_k)|; per-row, per-block codes differ, so a block scale
+    taken from the wrong block, row or operand fails."""
+    rng = np.random.default_rng(19)
+    m, n, k = 4, 5, 96
+    qa = _finite_codes(rng, (m, k), E4M3)
+    qb = _finite_codes(rng, (n, k), E5M2)
+    sa = rng.integers(100, 150, size=(m, k // 32)).astype(np.uint8)
+    sb = rng.integers(100, 150, size=(n, k // 32)).astype(np.uint8)
+    s = oracle.mx_abs_product_sum(qa, sa, E4M3, qb, sb, E5M2)
+    for i in range(m):
+        for j in range(n):
+            exact = Fraction(0)
+            for blk in range(k // 32):
+                sc = Fraction(2) ** (int(sa[i, blk]) - 127) * Fraction(2) ** (int(sb[j, blk]) - 127)
+                exact += sc * sum(abs(_frac_decode(int(qa[i, t]), E4M3) * _frac_decode(int(qb[j, t]), E5M2))
+                                  for t in range(32 * blk, 32 * blk + 32))
+            assert abs(Fraction(float(s[i, j])) - exact) <= k * Fraction(1, 2 ** 53) * exact
+
+
+def test_rmse_closed_forms():
+    """rmse against values fixed by its definition sqrt(mean((xhat - x)**2)):
+    an error of +-c everywhere gives c; errors (3, 4, 0, 0) give
+    sqrt(25 / 4) = 2.5; an empty input gives 0; and on small integer arrays
+    the square of the result equals the exact rational mean of squared errors
+    to within a few float64 ulps (a sum instead of a mean, a missing square
+    root or a missing square fails)."""
+    rng = np.random.default_rng(20)
+    x = rng.standard_normal(1000)
+    sgn = rng.choice([-1.0, 1.0], 1000)
+    assert oracle.rmse(x, x + 0.375 * sgn) == pytest.approx(0.375, rel=1e-15)
+    assert oracle.rmse(np.zeros(4), np.array([3.0, 4.0, 0.0, 0.0])) == 2.5
+    assert oracle.rmse(np.array([1.0, 2.0, 3.0, 4.0]), np.array([2.0, 3.0, 4.0, 5.0])) == 1.0
+    assert oracle.rmse(np.zeros(0), np.zeros(0)) == 0.0
+    for _ in range(20):
+        n = int(rng.integers(1, 50))
+        a = rng.integers(-100, 100, n)
+        b = rng.integers(-100, 100, n)
+        ms = Fraction(int(np.sum((b - a) ** 2)), n)
+        r = oracle.rmse(a.astype(np.float64), b.astype(np.float64))
+        assert abs(Fraction(r) ** 2 - ms) <= Fraction(4, 2 ** 52) * max(ms, Fraction(1))
