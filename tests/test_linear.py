@@ -14,7 +14,7 @@ from oracle import E4M3, E5M2
 from scaled_quantize_fp8_amd.linear import Fp8Linear
 from workloads import make
 
-from gpu_helpers import DEV, assert_gemm_close, bf16_dev, host, host_f64, mfma_group_term, need_gpu, say
+from gpu_helpers import DEV, assert_gemm_close, bf16_dev, host, host_f64, mfma_operands_mx, mfma_operands_pt, need_gpu, say
 
 T, IN, OUT = 256, 512, 384
 
@@ -51,7 +51,7 @@ def _check_pt(y, dx, dw, x, w, dy, bx, bw, bdy):
                                             ("dw", dw, qdyT, E5M2, bdy, qxT, E4M3, bx)):
         ref = oracle.scaled_gemm_ref(a, fa, ba, b, fb, bb)
         s = oracle.abs_product_sum(a, fa, ba, b, fb, bb)
-        gt = mfma_group_term(oracle.dequantize(a, fa, ba), oracle.dequantize(b, fb, bb))
+        gt = mfma_operands_pt(a, fa, ba, b, fb, bb)
         _check(what, got, ref, s, gt)
 
 
@@ -134,7 +134,7 @@ def test_linear_mx_matches_oracle(rule, shape):
                                             ("dw", dw, qdyT, sdyT, E5M2, qxT, sxT, E4M3)):
         ref = oracle.mx_gemm_ref(a, sa, fa, b, sb, fb)
         s = oracle.mx_abs_product_sum(a, sa, fa, b, sb, fb)
-        gt = mfma_group_term(oracle.mx_dequantize(a, sa, fa), oracle.mx_dequantize(b, sb, fb))
+        gt = mfma_operands_mx(a, sa, fa, b, sb, fb)
         _check(what, got, ref, s, gt)
     assert host(amax)[0] == np.max(np.abs(y))
 

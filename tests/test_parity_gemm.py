@@ -3,12 +3,13 @@
 Operands are FP8 codes, biases and E8M0 scales produced by the ORACLE from
 the workload generators' bf16 inputs, so expected values never depend on the
 HIP path.  Acceptance: |C - C_ref| <= 1e-5 * sum_k |a_k b_k| (fp32 output),
-plus one bf16 ulp of C_ref (bf16 output); the workload configurations (the
-256x768x768 layer, the 7B-MLP backward products, the 70B-MLP forward) are held
-to exactly that.  Short-K synthetic edge cases add the FP8 MFMA's in-group
-truncation allowance (``mfma_group_term``), a property of the instruction
-measured on gfx950.  The fused output amax must equal max |C| over the
-stored output bit for bit."""
+plus one bf16 ulp of C_ref (bf16 output).  An output beyond that bound passes
+only where the bound is out of the FP8 instruction's reach: the GPU returned
+the value of the pinned model of the instruction's in-group truncation
+(``mfma_model``), up to float32 accumulation, rounded to the output type
+(``assert_gemm_close`` with ``mfma_operands_pt`` / ``mfma_operands_mx``);
+the workload tests report how many outputs that applies to.  The fused
+output amax must equal max |C| over the stored output bit for bit."""
 
 import numpy as np
 import pytest
@@ -20,7 +21,7 @@ from oracle import E4M3, E5M2
 from workloads import f32_to_bf16_bits, make
 
 from gpu_helpers import (DEV, assert_gemm_close, bf16_dev, f32_bits_of, host, host_f64, i32_dev,
-                         mfma_group_term, need_gpu, oracle_mx_chunked, oracle_quantize_chunked, pack_scales_host,
+                         mfma_operands_mx, mfma_operands_pt, need_gpu, oracle_mx_chunked, oracle_quantize_chunked, pack_scales_host,
                          oracle_amax_chunked, say, u8_dev)
 
 pytestmark = pytest.mark.gpu
@@ -65,7 +66,7 @@ def test_gemm_ragged_tiles(fa, fb, out_dtype):
     C, am = _run_pt(qa, fa, ba, qb, fb, bb, False, False, out_dtype)
     ref = oracle.scaled_gemm_ref(qa, fa, ba, qb, fb, bb)
     s = oracle.abs_product_sum(qa, fa, ba, qb, fb, bb)
-    gt = mfma_group_term(oracle.dequantize(qa, fa, ba), oracle.dequantize(qb, fb, bb))
+    gt = mfma_operands_pt(qa, fa, ba, qb, fb, bb)
     assert_gemm_close(host_f64(C), ref, s, out_dtype == torch.bfloat16, "ragged", gt)
     _check_amax(C, am)
 
@@ -85,7 +86,7 @@ def test_gemm_k_multiple_of_128(fa, fb, K):
         C, am = _run_pt(qa, fa, ba, qb, fb, bb, False, False, dt)
         ref = oracle.scaled_gemm_ref(qa, fa, ba, qb, fb, bb)
         s = oracle.abs_product_sum(qa, fa, ba, qb, fb, bb)
-        gt = mfma_group_term(oracle.dequantize(qa, fa, ba), oracle.dequantize(qb, fb, bb))
+        gt = mfma_operands_pt(qa, fa, ba, qb, fb, bb)
         assert_gemm_close(host_f64(C), ref, s, dt == torch.bfloat16, f"K={K}", gt)
         _check_amax(C, am)
     pa = np.zeros((40, K + 48), dtype=np.uint8)
@@ -96,7 +97,7 @@ def test_gemm_k_multiple_of_128(fa, fb, K):
                                want_amax=True)
     ref = oracle.scaled_gemm_ref(qa[:40], fa, ba, qb[:24], fb, bb)
     s = oracle.abs_product_sum(qa[:40], fa, ba, qb[:24], fb, bb)
-    gt = mfma_group_term(oracle.dequantize(qa[:40], fa, ba), oracle.dequantize(qb[:24], fb, bb))
+    gt = mfma_operands_pt(qa[:40], fa, ba, qb[:24], fb, bb)
     assert_gemm_close(host_f64(C), ref, s, False, f"small K={K}", gt)
     _check_amax(C, am)
 
@@ -116,11 +117,11 @@ def test_gemm_bf16_padded_outputs(mx):
         sb = rng.integers(118, 136, (N, K // 32)).astype(np.uint8)
         ref = oracle.mx_gemm_ref(qa, sa, E4M3, qb, sb, E4M3)
         s = oracle.mx_abs_product_sum(qa, sa, E4M3, qb, sb, E4M3)
-        gt = mfma_group_term(oracle.mx_dequantize(qa, sa, E4M3), oracle.mx_dequantize(qb, sb, E4M3))
+        gt = mfma_operands_mx(qa, sa, E4M3, qb, sb, E4M3)
     else:
         ref = oracle.scaled_gemm_ref(qa, E4M3, ba, qb, E4M3, bb)
         s = oracle.abs_product_sum(qa, E4M3, ba, qb, E4M3, bb)
-        gt = mfma_group_term(oracle.dequantize(qa, E4M3, ba), oracle.dequantize(qb, E4M3, bb))
+        gt = mfma_operands_pt(qa, E4M3, ba, qb, E4M3, bb)
     for pad, off in ((8, 0), (4, 4)):
         say(f"gemm bf16 padded out mx={mx} stride N+{pad} offset {off}")
         big = torch.full((M, N + pad + off), -7.0, dtype=torch.bfloat16, device=DEV)
@@ -153,7 +154,7 @@ def test_gemm_transposed_operands(ta, tb):
     C, am = _run_pt(qa, E5M2, ba, qb, E4M3, bb, ta, tb, torch.float32)
     ref = oracle.scaled_gemm_ref(qa, E5M2, ba, qb, E4M3, bb)
     s = oracle.abs_product_sum(qa, E5M2, ba, qb, E4M3, bb)
-    gt = mfma_group_term(oracle.dequantize(qa, E5M2, ba), oracle.dequantize(qb, E4M3, bb))
+    gt = mfma_operands_pt(qa, E5M2, ba, qb, E4M3, bb)
     assert_gemm_close(host_f64(C), ref, s, False, f"trans {ta}{tb}", gt)
     _check_amax(C, am)
 
@@ -177,7 +178,7 @@ def test_gemm_degenerate_shapes():
     C, am = _run_pt(qa1, E4M3, ba1, qb1, E4M3, bb1, False, False, torch.float32)
     assert_gemm_close(host_f64(C), oracle.scaled_gemm_ref(qa1, E4M3, ba1, qb1, E4M3, bb1),
                       oracle.abs_product_sum(qa1, E4M3, ba1, qb1, E4M3, bb1), False, "K=16",
-                      mfma_group_term(oracle.dequantize(qa1, E4M3, ba1), oracle.dequantize(qb1, E4M3, bb1)))
+                      mfma_operands_pt(qa1, E4M3, ba1, qb1, E4M3, bb1))
     # identity B: C = dequantized A exactly (fp32 out)
     one = oracle.encode(np.array([1.0]), E4M3)[0]
     eye = np.where(np.eye(32, dtype=bool), one, 0).astype(np.uint8)
@@ -190,7 +191,7 @@ def test_gemm_degenerate_shapes():
     assert np.all(hb[:, :8] == -7.0) and np.all(hb[:, 56:] == -7.0)
     assert_gemm_close(hb[:, 8:56].astype(np.float64), oracle.scaled_gemm_ref(qa, E4M3, ba, qb, E4M3, bb),
                       oracle.abs_product_sum(qa, E4M3, ba, qb, E4M3, bb), False, "strided out",
-                      mfma_group_term(oracle.dequantize(qa, E4M3, ba), oracle.dequantize(qb, E4M3, bb)))
+                      mfma_operands_pt(qa, E4M3, ba, qb, E4M3, bb))
 
 
 def test_gemm_deterministic():
@@ -211,9 +212,11 @@ def test_gemm_config_c1_full():
     qx, qw = oracle.quantize(xv, E4M3, bx), oracle.quantize(wv, E4M3, bw)
     ref = oracle.scaled_gemm_ref(qx, E4M3, bx, qw, E4M3, bw)
     s = oracle.abs_product_sum(qx, E4M3, bx, qw, E4M3, bw)
+    ops = mfma_operands_pt(qx, E4M3, bx, qw, E4M3, bw)
     for dt in (torch.bfloat16, torch.float32):
         C, am = _run_pt(qx, E4M3, bx, qw, E4M3, bw, False, False, dt)
-        assert_gemm_close(host_f64(C), ref, s, dt == torch.bfloat16, "c1")
+        res = assert_gemm_close(host_f64(C), ref, s, dt == torch.bfloat16, "c1", ops)
+        say(f"c1 {dt}: {res}")
         _check_amax(C, am)
 
 
@@ -230,7 +233,7 @@ def test_mx_gemm_ragged(fa, fb, out_dtype):
                               out_dtype=out_dtype, want_amax=True)
     ref = oracle.mx_gemm_ref(qa, sa, fa, qb, sb, fb)
     s = oracle.mx_abs_product_sum(qa, sa, fa, qb, sb, fb)
-    gt = mfma_group_term(oracle.mx_dequantize(qa, sa, fa), oracle.mx_dequantize(qb, sb, fb))
+    gt = mfma_operands_mx(qa, sa, fa, qb, sb, fb)
     assert_gemm_close(host_f64(C), ref, s, out_dtype == torch.bfloat16, "mx ragged", gt)
     _check_amax(C, am)
 
@@ -250,7 +253,7 @@ def test_mx_gemm_k_multiple_of_128(fa, fb, K):
     qb, sb = oracle.mx_quantize(oracle.bf16_bits_to_f64(wb), fb)
     ref = oracle.mx_gemm_ref(qa, sa, fa, qb, sb, fb)
     s = oracle.mx_abs_product_sum(qa, sa, fa, qb, sb, fb)
-    gt = mfma_group_term(oracle.mx_dequantize(qa, sa, fa), oracle.mx_dequantize(qb, sb, fb))
+    gt = mfma_operands_mx(qa, sa, fa, qb, sb, fb)
     nb = K // 32
     psa = np.zeros((300, nb + 1), dtype=np.uint8)
     psb = np.zeros((260, nb + 1), dtype=np.uint8)
@@ -293,7 +296,7 @@ def test_mx_gemm_packed_scales(fa, fb, M, N, K):
     qb, sb = oracle.mx_quantize(oracle.bf16_bits_to_f64(wb), fb)
     ref = oracle.mx_gemm_ref(qa, sa, fa, qb, sb, fb)
     s = oracle.mx_abs_product_sum(qa, sa, fa, qb, sb, fb)
-    gt = mfma_group_term(oracle.mx_dequantize(qa, sa, fa), oracle.mx_dequantize(qb, sb, fb))
+    gt = mfma_operands_mx(qa, sa, fa, qb, sb, fb)
     A, B, SA, SB = u8_dev(qa), u8_dev(qb), u8_dev(sa), u8_dev(sb)
     PA, PB = sq.mx_pack_scales(SA), sq.mx_pack_scales(SB)
     assert np.array_equal(host(PA), pack_scales_host(sa)) and np.array_equal(host(PB), pack_scales_host(sb))
@@ -321,7 +324,7 @@ def test_mx_gemm_extreme_block_scales():
     C, _ = sq.mx_scaled_gemm(u8_dev(qa), 0, u8_dev(sa), u8_dev(qb), 0, u8_dev(sb), out_dtype=torch.float32)
     ref = oracle.mx_gemm_ref(qa, sa, E4M3, qb, sb, E4M3)
     s = oracle.mx_abs_product_sum(qa, sa, E4M3, qb, sb, E4M3)
-    gt = mfma_group_term(oracle.mx_dequantize(qa, sa, E4M3), oracle.mx_dequantize(qb, sb, E4M3))
+    gt = mfma_operands_mx(qa, sa, E4M3, qb, sb, E4M3)
     assert_gemm_close(host_f64(C), ref, s, False, "mx scales", gt)
 
 
@@ -335,7 +338,7 @@ def test_mx_gemm_uniform_scales_match_per_tensor():
     Cp, _ = _run_pt(qa, E4M3, ba, qb, E4M3, bb, False, False, torch.float32)
     ref = oracle.scaled_gemm_ref(qa, E4M3, ba, qb, E4M3, bb)
     s = oracle.abs_product_sum(qa, E4M3, ba, qb, E4M3, bb)
-    gt = mfma_group_term(oracle.dequantize(qa, E4M3, ba), oracle.dequantize(qb, E4M3, bb))
+    gt = mfma_operands_pt(qa, E4M3, ba, qb, E4M3, bb)
     assert_gemm_close(host_f64(Cm), ref, s, False, "mx uniform", gt)
     assert_gemm_close(host_f64(Cp), ref, s, False, "pt uniform", gt)
     # same codes, same arithmetic: the two kernels agree bit for bit
@@ -358,15 +361,9 @@ def test_mx_weight_gradient_via_transposed_casts():
     assert np.array_equal(host(qx), oqx) and np.array_equal(host(sx), osx)
     ref = oracle.mx_gemm_ref(oqdy, osdy, E5M2, oqx, osx, E4M3)
     s = oracle.mx_abs_product_sum(oqdy, osdy, E5M2, oqx, osx, E4M3)
-    gt = mfma_group_term(oracle.mx_dequantize(oqdy, osdy, E5M2), oracle.mx_dequantize(oqx, osx, E4M3))
+    gt = mfma_operands_mx(oqdy, osdy, E5M2, oqx, osx, E4M3)
     assert_gemm_close(host_f64(C), ref, s, False, "mx dW", gt)
     _check_amax(C, am)
-
-
-def _sample_idx(rng, M, N, n=2048):
-    rows = np.concatenate([rng.integers(0, M, n), [0, M - 1, 0, M - 1]])
-    cols = np.concatenate([rng.integers(0, N, n), [0, N - 1, N - 1, 0]])
-    return rows, cols
 
 
 def _tile_rows(rng, n, extra=64):
@@ -412,7 +409,8 @@ def test_full_size_70b_mlp_end_to_end_sampled():
     oqw = oracle_quantize_chunked(wb, E4M3, rbw, cs)
     y = oracle.scaled_gemm_ref(oqx, E4M3, rbx, oqw, E4M3, rbw)
     sabs = oracle.abs_product_sum(oqx, E4M3, rbx, oqw, E4M3, rbw)
-    assert_gemm_close(got, y, sabs, True, "c5 per-tensor")
+    res = assert_gemm_close(got, y, sabs, True, "c5 per-tensor", mfma_operands_pt(oqx, E4M3, rbx, oqw, E4M3, rbw))
+    say(f"c5 per-tensor: {res}")
     tiles = {(int(r) // 256, int(c) // 256) for r in rs for c in cs}
     assert len(tiles) == (xb.shape[0] // 256) * (wb.shape[0] // 256)
     say("c5 gpu mx path (cast to packed scales)")
@@ -433,23 +431,28 @@ def test_full_size_70b_mlp_end_to_end_sampled():
     oqwm, oswm = oracle_mx_chunked(wb, E4M3, cs)
     y = oracle.mx_gemm_ref(oqxm, osxm, E4M3, oqwm, oswm, E4M3)
     sabs = oracle.mx_abs_product_sum(oqxm, osxm, E4M3, oqwm, oswm, E4M3)
-    assert_gemm_close(got, y, sabs, True, "c5 mx")
+    res = assert_gemm_close(got, y, sabs, True, "c5 mx", mfma_operands_mx(oqxm, osxm, E4M3, oqwm, oswm, E4M3))
+    say(f"c5 mx: {res}")
 
 
 def test_full_size_7b_attn_delayed_gemm_sampled():
     """The delayed-scaling workload's forward product at full size (X_t
-    [2048 x 4096] against W [4096 x 4096], bf16 out) at steps 0 and 1: step 0
-    with the bootstrap bias, step 1 with the window's bias, under which X_1
-    saturates.  Biases come from the oracle's history, codes from the GPU
-    casts (equal to the oracle's), and every output of two sampled rows and
-    columns per 256-wide tile is compared with the oracle's float64 product."""
+    [2048 x 4096] against W [4096 x 4096], bf16 out) at every one of its 16
+    steps: step 0 with the bootstrap bias, step 1 with the window's bias,
+    under which X_1 saturates, then the window's maximum.  Biases come from
+    the oracle's history, codes from the GPU casts (equal to the oracle's),
+    and every output of two sampled rows and columns per 256-wide tile (every
+    output tile) is compared with the oracle's float64 product under the
+    plain bound, outputs beyond it only where they are the FP8 instruction's
+    own result (counted)."""
     h = oracle.DelayedScaling(16)
     wb = make("c2", "W")
     rbw = oracle.compute_bias(oracle.amax(oracle.bf16_bits_to_f64(wb)), E4M3)
     qw = oracle.quantize(oracle.bf16_bits_to_f64(wb), E4M3, rbw)
     Wq = u8_dev(qw)
     rng = np.random.default_rng(41)
-    for t in range(2):
+    total = {"outputs": 0, "beyond_plain": 0}
+    for t in range(16):
         xb = make("c2", "X", step=t)
         xv = oracle.bf16_bits_to_f64(xb)
         if t == 0:
@@ -466,22 +469,29 @@ def test_full_size_7b_attn_delayed_gemm_sampled():
         oqx = oracle.quantize(xv[rs], E4M3, rbx)
         y = oracle.scaled_gemm_ref(oqx, E4M3, rbx, qw[cs], E4M3, rbw)
         sabs = oracle.abs_product_sum(oqx, E4M3, rbx, qw[cs], E4M3, rbw)
-        assert_gemm_close(got, y, sabs, True, f"delayed step {t}")
+        res = assert_gemm_close(got, y, sabs, True, f"delayed step {t}", mfma_operands_pt(oqx, E4M3, rbx, qw[cs], E4M3, rbw))
+        total["outputs"] += res["outputs"]
+        total["beyond_plain"] += res["beyond_plain"]
         assert f32_bits_of(am) == f32_bits_of(sq.fp8_amax(C))
+    say(f"delayed 16 steps: {total}")
 
 
-def test_full_size_13b_mlp_up_mx_gemm_sampled():
-    """The MXFP8 workload at full size: X [8192 x 5120] with log-normal
-    column scales and W [13824 x 5120], MX casts on the GPU (codes and scales
-    equal to the oracle's on the sampled rows), the block-scaled product
-    (bf16 out) on row-major and on packed scales (same bits), and every
-    output of two sampled rows and columns per 256-wide tile against the
-    oracle's float64 product."""
+def test_full_size_13b_mlp_up_mx_gemm_every_output():
+    """The MXFP8 workload at full size, every output: X [8192 x 5120] with
+    log-normal column scales and W [13824 x 5120], MX casts on the GPU (codes
+    and scales equal to the oracle's for every row), the block-scaled product
+    (bf16 out) on row-major and on packed scales (same bits), and all
+    113,246,208 outputs against the oracle's float64 product (512-row
+    panels).
+
+    The column scales (sigma 1.5) make the products inside a group of 8 K
+    very unequal, and the FP8 instruction truncates every product of a group
+    onto the grid of the largest: a small fraction of outputs miss
+    1e-5 sum|ab| + 1 bf16 ulp.  Each of those must be instruction-limited
+    (the pinned model of the instruction is itself that far from the exact
+    sum, and the GPU agrees with the model); the count is reported."""
     xb, wb = make("c4", "X"), make("c4", "W")
     x, w = bf16_dev(xb), bf16_dev(wb)
-    rng = np.random.default_rng(43)
-    rs, cs = _tile_rows(rng, xb.shape[0]), _tile_rows(rng, wb.shape[0])
-    ri, ci = torch.from_numpy(rs).to(DEV), torch.from_numpy(cs).to(DEV)
     say("c4 gpu mx casts and products")
     qx, sx = sq.mx_quantize(x, 0)
     qw, sw = sq.mx_quantize(w, 0)
@@ -492,31 +502,31 @@ def test_full_size_13b_mlp_up_mx_gemm_sampled():
     Cp, amp = sq.mx_scaled_gemm_packed(pqx, 0, psx, pqw, 0, psw, want_amax=True)
     assert torch.equal(Cp.view(torch.int16), C.view(torch.int16)) and f32_bits_of(amp) == f32_bits_of(am)
     assert f32_bits_of(am) == f32_bits_of(sq.fp8_amax(C))
-    got = host_f64(C[ri][:, ci])
-    say(f"c4 oracle, {rs.size} x {cs.size} outputs")
-    oqx, osx = oracle_mx_chunked(xb, E4M3, rs)
-    oqw, osw = oracle_mx_chunked(wb, E4M3, cs)
-    assert np.array_equal(host(qx[ri]), oqx) and np.array_equal(host(sx[ri]), osx)
-    assert np.array_equal(host(qw[ci]), oqw) and np.array_equal(host(sw[ci]), osw)
+    got = host_f64(C)
+    hqx, hsx, hqw, hsw = host(qx), host(sx), host(qw), host(sw)
+    del x, w, C, Cp, qx, sx, qw, sw, pqx, psx, pqw, psw
+    torch.cuda.empty_cache()
+    say("c4 oracle casts, every row")
+    oqx, osx = oracle_mx_chunked(xb, E4M3)
+    oqw, osw = oracle_mx_chunked(wb, E4M3)
+    assert np.array_equal(hqx, oqx) and np.array_equal(hsx, osx)
+    assert np.array_equal(hqw, oqw) and np.array_equal(hsw, osw)
+    say("c4 oracle product, 8192 x 13824 x 5120 in float64")
     y = oracle.mx_gemm_ref(oqx, osx, E4M3, oqw, osw, E4M3)
     sabs = oracle.mx_abs_product_sum(oqx, osx, E4M3, oqw, osw, E4M3)
-    # The column scales (log-normal, sigma 1.5) make the products inside a
-    # group of 8 K very unequal, and the FP8 MFMA truncates every product of
-    # a group onto the grid of the largest: a handful of outputs exceed
-    # 1e-5 sum|ab| (3 of ~22k on the first run) and all stay within the
-    # instruction's in-group allowance.  A wrong block-scale pairing would
-    # miss by factors of two on whole blocks.
-    gt = mfma_group_term(oracle.mx_dequantize(oqx, osx, E4M3), oracle.mx_dequantize(oqw, osw, E4M3))
-    tol = 1e-5 * sabs + oracle.bf16_ulp(y)
-    n_plain = int(np.count_nonzero(np.abs(got - y) > tol))
-    say(f"c4 mx: {n_plain} of {got.size} outputs beyond 1e-5 sum|ab| + 1 bf16 ulp")
-    assert n_plain <= got.size // 1000
-    assert_gemm_close(got, y, sabs, True, "c4 mx", gt)
+    res = assert_gemm_close(got, y, sabs, True, "c4 mx",
+                            mfma_operands_mx(oqx, osx, E4M3, oqw, osw, E4M3))
+    say(f"c4 mx every output: {res['beyond_plain']} of {res['outputs']} beyond 1e-5 sum|ab| + 1 bf16 ulp, "
+        f"all instruction-limited; largest error / allowance {res['max_err_over_tol']:.3f}")
 
 
 def test_backward_shapes_7b_mlp_sampled():
     """dX = dY W (A = dY [4096 x 11008] E5M2, B = W stored [11008 x 4096] ->
-    trans_b) and dW = dY^T X (A = dY^T, B = X^T, both stored transposed)."""
+    trans_b) and dW = dY^T X (A = dY^T, B = X^T, both stored transposed),
+    fp32 out: every output of two sampled rows and columns per 256-wide tile
+    (so every output tile) plus 64 random rows and columns, against the
+    oracle's float64 product; outputs beyond the plain bound only where they
+    are the FP8 instruction's own result (counted)."""
     dyb, wb, xb = make("c3", "dY"), make("c3", "W"), make("c3", "X")
     say("c3 oracle casts")
     bdy = oracle.compute_bias(oracle_amax_chunked(dyb), E5M2)
@@ -529,20 +539,26 @@ def test_backward_shapes_7b_mlp_sampled():
     say("c3 dX")
     dX, _ = sq.fp8_scaled_gemm(u8_dev(qdy), 1, i32_dev(bdy), u8_dev(qw), 0, i32_dev(bw), trans_b=True,
                                out_dtype=torch.float32)
-    rows, cols = _sample_idx(rng, 4096, 4096, 1024)
-    qwT = np.ascontiguousarray(qw.T)
-    y, s = oracle.gemm_sample_ref(qdy, E5M2, bdy, qwT, E4M3, bw, rows, cols)
-    assert_gemm_close(host_f64(dX[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)]), y, s,
-                      False, "dX")
+    rs, cs = _tile_rows(rng, 4096), _tile_rows(rng, 4096)
+    got = host_f64(dX[torch.from_numpy(rs).to(DEV)][:, torch.from_numpy(cs).to(DEV)])
+    a, b = qdy[rs], np.ascontiguousarray(qw[:, cs].T)
+    res = assert_gemm_close(got, oracle.scaled_gemm_ref(a, E5M2, bdy, b, E4M3, bw),
+                            oracle.abs_product_sum(a, E5M2, bdy, b, E4M3, bw), False, "dX",
+                            mfma_operands_pt(a, E5M2, bdy, b, E4M3, bw))
+    say(f"c3 dX: {res}")
     del dX
     say("c3 dW")
     dW, _ = sq.fp8_scaled_gemm(u8_dev(qdy), 1, i32_dev(bdy), u8_dev(qx), 0, i32_dev(bx), trans_a=True,
                                trans_b=True, out_dtype=torch.float32)
-    rows, cols = _sample_idx(rng, 11008, 4096, 1024)
-    y, s = oracle.gemm_sample_ref(np.ascontiguousarray(qdy.T), E5M2, bdy, np.ascontiguousarray(qx.T), E4M3, bx,
-                                  rows, cols)
-    assert_gemm_close(host_f64(dW[torch.from_numpy(rows).to(DEV), torch.from_numpy(cols).to(DEV)]), y, s,
-                      False, "dW")
+    rs, cs = _tile_rows(rng, 11008), _tile_rows(rng, 4096)
+    got = host_f64(dW[torch.from_numpy(rs).to(DEV)][:, torch.from_numpy(cs).to(DEV)])
+    a, b = np.ascontiguousarray(qdy[:, rs].T), np.ascontiguousarray(qx[:, cs].T)
+    res = assert_gemm_close(got, oracle.scaled_gemm_ref(a, E5M2, bdy, b, E4M3, bx),
+                            oracle.abs_product_sum(a, E5M2, bdy, b, E4M3, bx), False, "dW",
+                            mfma_operands_pt(a, E5M2, bdy, b, E4M3, bx))
+    say(f"c3 dW: {res}")
+    tiles = {(int(r) // 256, int(c) // 256) for r in rs for c in cs}
+    assert len(tiles) == 43 * 16
 
 
 def _repeat_identical(fn, reps, what):
