@@ -79,7 +79,8 @@ enum {
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* fp8_status_string(int status);
 
-/* Library ABI version (increases when a signature changes). */
+/* Library ABI version (increases when a signature changes or an entry point
+ * is added): 3. */
 int fp8_abi_version(void);
 
 /*
@@ -147,6 +148,23 @@ int fp8_compute_scale_delayed(const float* hist, const int32_t* state, int windo
 int fp8_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                  int fmt, const int32_t* bias, uint8_t* q, int64_t ldq,
                  uint8_t* qT, int64_t ldqT, float* amax_out, hipStream_t stream);
+
+/*
+ * fp8_quantize_sat — fp8_quantize that also counts the elements the cast
+ * saturates.  "Per-Tensor and Per-Block Scaling Strategies for Effective FP8
+ * Training" (summary page, "Key Questions Answered"): a delayed scale comes
+ * from earlier iterations' maxima, so a step whose amax jumps above them
+ * has values the format cannot hold, which the cast clamps to +-max.
+ *   sat_out  one uint64 (device, required): the number of elements with
+ *            |x * 2^(*bias)| > fmax (+-Inf included, NaN not), exact;
+ *            overwritten.
+ * Every other argument, check and result is that of fp8_quantize (q, qT and
+ * amax_out are bit-identical to its outputs).
+ */
+int fp8_quantize_sat(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                     int fmt, const int32_t* bias, uint8_t* q, int64_t ldq,
+                     uint8_t* qT, int64_t ldqT, float* amax_out, uint64_t* sat_out,
+                     hipStream_t stream);
 
 /*
  * mx_quantize — per-block (MXFP8-style) cast ("Key Questions Answered": a

@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "E4M3", "E5M2", "load_library", "library_path", "Fp8Error",
     "fp8_amax", "fp8_compute_scale", "fp8_history_init", "fp8_history_push",
-    "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize", "mx_quantize_t",
+    "fp8_compute_scale_delayed", "fp8_quantize", "fp8_quantize_sat", "mx_quantize", "mx_quantize_t",
     "mx_quantize_rule", "mx_quantize_t_rule", "MX_RULE_FMAX", "MX_RULE_OCP",
     "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string", "fp8_abi_version",
     "mx_packed_scales_bytes", "mx_pack_scales", "mx_quantize_packed", "mx_quantize_t_packed",
@@ -56,6 +56,7 @@ _SIGNATURES = {
     "fp8_history_push": ([_p, _p, _i, _p, _p], _i),
     "fp8_compute_scale_delayed": ([_p, _p, _i, _i, _i, _p, _p, _p, _p], _i),
     "fp8_quantize": ([_p, _i, _i64, _i64, _i64, _i, _p, _p, _i64, _p, _i64, _p, _p], _i),
+    "fp8_quantize_sat": ([_p, _i, _i64, _i64, _i64, _i, _p, _p, _i64, _p, _i64, _p, _p, _p], _i),
     "mx_quantize": ([_p, _i, _i64, _i64, _i64, _i, _p, _i64, _p, _i64, _p], _i),
     "mx_quantize_t": ([_p, _i, _i64, _i64, _i64, _i, _p, _i64, _p, _i64, _p], _i),
     "mx_quantize_rule": ([_p, _i, _i64, _i64, _i64, _i, _i, _p, _i64, _p, _i64, _p], _i),
@@ -236,12 +237,7 @@ def fp8_compute_scale_delayed(hist: torch.Tensor, state: torch.Tensor, fmt, marg
     return bias_out, scale_out, scale_inv_out
 
 
-def fp8_quantize(x: torch.Tensor, fmt, bias: torch.Tensor, q: torch.Tensor | None = None,
-                 transpose: bool = False, qT: torch.Tensor | None = None,
-                 want_amax: bool = False, amax_out: torch.Tensor | None = None):
-    """Per-tensor cast q = sat_RNE(x * 2**bias).  Returns (q, qT or None,
-    amax of x or None); ``transpose`` also writes qT = q^T, ``want_amax`` fuses
-    the input amax into the same pass."""
+def _quantize_outputs(x, bias, q, transpose, qT, want_amax, amax_out):
     rows, cols, ld = _mat(x, "x")
     _scalar(bias, torch.int32, "bias")
     if q is None:
@@ -262,10 +258,38 @@ def fp8_quantize(x: torch.Tensor, fmt, bias: torch.Tensor, q: torch.Tensor | Non
         if amax_out is None:
             amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
         _scalar(amax_out, torch.float32, "amax_out")
+    return rows, cols, ld, q, ldq, qT, ldqT, amax_out
+
+
+def fp8_quantize(x: torch.Tensor, fmt, bias: torch.Tensor, q: torch.Tensor | None = None,
+                 transpose: bool = False, qT: torch.Tensor | None = None,
+                 want_amax: bool = False, amax_out: torch.Tensor | None = None):
+    """Per-tensor cast q = sat_RNE(x * 2**bias).  Returns (q, qT or None,
+    amax of x or None); ``transpose`` also writes qT = q^T, ``want_amax`` fuses
+    the input amax into the same pass."""
+    rows, cols, ld, q, ldq, qT, ldqT, amax_out = _quantize_outputs(x, bias, q, transpose, qT, want_amax, amax_out)
     _check("fp8_quantize", load_library().fp8_quantize(
         _ptr(x), _dtype_code(x, "x"), rows, cols, ld, _fmt(fmt), _ptr(bias), _ptr(q), ldq,
         _ptr(qT), ldqT, _ptr(amax_out), _stream(x)))
     return q, qT, amax_out
+
+
+def fp8_quantize_sat(x: torch.Tensor, fmt, bias: torch.Tensor, q: torch.Tensor | None = None,
+                     transpose: bool = False, qT: torch.Tensor | None = None,
+                     want_amax: bool = False, amax_out: torch.Tensor | None = None,
+                     sat_out: torch.Tensor | None = None):
+    """fp8_quantize plus the number of elements the cast saturates
+    (|x * 2**bias| > fmax, NaN excluded), counted on the device into a
+    one-element int64 tensor (the C call's uint64).  Returns (q, qT or None,
+    amax or None, sat)."""
+    rows, cols, ld, q, ldq, qT, ldqT, amax_out = _quantize_outputs(x, bias, q, transpose, qT, want_amax, amax_out)
+    if sat_out is None:
+        sat_out = torch.empty(1, dtype=torch.int64, device=x.device)
+    _scalar(sat_out, torch.int64, "sat_out")
+    _check("fp8_quantize_sat", load_library().fp8_quantize_sat(
+        _ptr(x), _dtype_code(x, "x"), rows, cols, ld, _fmt(fmt), _ptr(bias), _ptr(q), ldq,
+        _ptr(qT), ldqT, _ptr(amax_out), _ptr(sat_out), _stream(x)))
+    return q, qT, amax_out, sat_out
 
 
 def _rule(rule) -> int:

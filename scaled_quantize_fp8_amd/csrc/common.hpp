@@ -143,6 +143,34 @@ __device__ __forceinline__ void block_max_to_global(uint32_t v, uint32_t* red, f
   }
 }
 
+// One 64-bit atomicAdd per workgroup of the lanes' counts into *out, skipped
+// when the workgroup's count is zero.  All threads of the block must call it;
+// `red` is __shared__ scratch of blockDim/64 words (not shared with another
+// reduction running in the same block).
+__device__ __forceinline__ void block_sum_to_global(uint32_t v, uint32_t* red, unsigned long long* out) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += (uint32_t)__shfl_xor((int)v, off, kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long s = 0;
+    const int nw = (blockDim.x + kWave - 1) / kWave;
+    for (int i = 0; i < nw; ++i) s += red[i];
+    if (s != 0) atomicAdd(out, s);
+  }
+}
+
+// Saturation count of four scaled values: those whose magnitude exceeds the
+// format maximum (the cast clamps them to +-max; NaN compares false).
+template <int FMT>
+__device__ __forceinline__ uint32_t sat4(float a, float b, float c, float d) {
+  constexpr float M = Fmt<FMT>::kMax;
+  return (uint32_t)(__builtin_fabsf(a) > M) + (uint32_t)(__builtin_fabsf(b) > M) +
+         (uint32_t)(__builtin_fabsf(c) > M) + (uint32_t)(__builtin_fabsf(d) > M);
+}
+
 // Max across aligned groups of 4 / 8 lanes (DPP quad permutes, half-row mirror).
 __device__ __forceinline__ uint32_t group4_max(uint32_t v) {
   uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // lane ^ 1

@@ -49,5 +49,7 @@ inline int64_t packed_bytes(int64_t rows, int64_t kb) {
 // Zero one float on `stream` with a tiny fill kernel (not hipMemsetAsync, so
 // that the call sequence can be captured into a HIP graph safely).
 void zero_float_async(float* p, hipStream_t stream);
+// Zero an optional float and an optional 64-bit count with one fill kernel.
+void zero_outputs_async(float* f, unsigned long long* n, hipStream_t stream);
 
 }  // namespace sfp8

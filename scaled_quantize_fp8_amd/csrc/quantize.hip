@@ -68,17 +68,23 @@ __device__ __forceinline__ uint32_t load_elem(const void* row, int64_t i, float*
   }
 }
 
-// Cast of one element given its float32-layout bits (NaN handled here).
+// Cast of one element given its float32-layout bits (NaN handled here);
+// *sat (when given) gains 1 if the scaled magnitude exceeds the format max.
 template <int FMT>
-__device__ __forceinline__ uint32_t cast_elem(uint32_t bits, int e) {
+__device__ __forceinline__ uint32_t cast_elem(uint32_t bits, int e, uint32_t* sat = nullptr) {
   if ((bits & 0x7fffffffu) > 0x7f800000u) return nan_code_f32(bits);
-  return cvt1<FMT>(__builtin_amdgcn_ldexpf(__uint_as_float(bits), e));
+  const float v = __builtin_amdgcn_ldexpf(__uint_as_float(bits), e);
+  if (sat) *sat += (uint32_t)(__builtin_fabsf(v) > Fmt<FMT>::kMax);
+  return cvt1<FMT>(v);
 }
 
 // Cast of one 16-byte chunk; returns the packed codes (8 bytes for bf16, 4
 // for f32) and the chunk's max |x| bits (float32 layout) in *amax_bits.
-template <int DT, int FMT>
-__device__ __forceinline__ uint2 cast_chunk(uint4 v, int e, uint32_t* amax_bits, bool want_codes) {
+// With SAT, *nsat gains the number of the chunk's elements whose scaled
+// magnitude exceeds the format maximum (NaN excluded).
+template <int DT, int FMT, bool SAT = false>
+__device__ __forceinline__ uint2 cast_chunk(uint4 v, int e, uint32_t* amax_bits, bool want_codes,
+                                            uint32_t* nsat = nullptr) {
   uint2 o = make_uint2(0u, 0u);
   if constexpr (DT == FP8_DT_BF16) {
     const us2 m2 = max_us2(max_us2(abs_bf16x2(v.x), abs_bf16x2(v.y)),
@@ -86,10 +92,13 @@ __device__ __forceinline__ uint2 cast_chunk(uint4 v, int e, uint32_t* amax_bits,
     const uint32_t m = hmax_us2(m2);
     *amax_bits = m << 16;
     if (want_codes) {
-      o.x = cvt4<FMT>(__builtin_amdgcn_ldexpf(bf16_lo(v.x), e), __builtin_amdgcn_ldexpf(bf16_hi(v.x), e),
-                      __builtin_amdgcn_ldexpf(bf16_lo(v.y), e), __builtin_amdgcn_ldexpf(bf16_hi(v.y), e));
-      o.y = cvt4<FMT>(__builtin_amdgcn_ldexpf(bf16_lo(v.z), e), __builtin_amdgcn_ldexpf(bf16_hi(v.z), e),
-                      __builtin_amdgcn_ldexpf(bf16_lo(v.w), e), __builtin_amdgcn_ldexpf(bf16_hi(v.w), e));
+      const float f0 = __builtin_amdgcn_ldexpf(bf16_lo(v.x), e), f1 = __builtin_amdgcn_ldexpf(bf16_hi(v.x), e);
+      const float f2 = __builtin_amdgcn_ldexpf(bf16_lo(v.y), e), f3 = __builtin_amdgcn_ldexpf(bf16_hi(v.y), e);
+      const float f4 = __builtin_amdgcn_ldexpf(bf16_lo(v.z), e), f5 = __builtin_amdgcn_ldexpf(bf16_hi(v.z), e);
+      const float f6 = __builtin_amdgcn_ldexpf(bf16_lo(v.w), e), f7 = __builtin_amdgcn_ldexpf(bf16_hi(v.w), e);
+      o.x = cvt4<FMT>(f0, f1, f2, f3);
+      o.y = cvt4<FMT>(f4, f5, f6, f7);
+      if constexpr (SAT) *nsat += sat4<FMT>(f0, f1, f2, f3) + sat4<FMT>(f4, f5, f6, f7);
       if (__builtin_expect(m > 0x7f80u, 0)) {      // a NaN in the chunk: patch its bytes
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -110,10 +119,12 @@ __device__ __forceinline__ uint2 cast_chunk(uint4 v, int e, uint32_t* amax_bits,
     const uint32_t m = m01 > m23 ? m01 : m23;
     *amax_bits = m;
     if (want_codes) {
-      o.x = cvt4<FMT>(__builtin_amdgcn_ldexpf(__uint_as_float(v.x), e),
-                      __builtin_amdgcn_ldexpf(__uint_as_float(v.y), e),
-                      __builtin_amdgcn_ldexpf(__uint_as_float(v.z), e),
-                      __builtin_amdgcn_ldexpf(__uint_as_float(v.w), e));
+      const float f0 = __builtin_amdgcn_ldexpf(__uint_as_float(v.x), e);
+      const float f1 = __builtin_amdgcn_ldexpf(__uint_as_float(v.y), e);
+      const float f2 = __builtin_amdgcn_ldexpf(__uint_as_float(v.z), e);
+      const float f3 = __builtin_amdgcn_ldexpf(__uint_as_float(v.w), e);
+      o.x = cvt4<FMT>(f0, f1, f2, f3);
+      if constexpr (SAT) *nsat += sat4<FMT>(f0, f1, f2, f3);
       if (__builtin_expect(m > 0x7f800000u, 0)) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -142,9 +153,11 @@ __device__ __forceinline__ void store_codes(uint8_t* qrow, int64_t chunk, uint2 
 // Streaming pass: rows are walked by gridDim.y, 16-byte chunks of a row by a
 // grid-stride loop over x with U (kUnroll, or kUnrollRead for the amax-only
 // pass) non-temporal loads in flight per lane.
-template <int DT, int FMT, bool VEC, bool WQ, bool AMAX>
+template <int DT, int FMT, bool VEC, bool WQ, bool AMAX, bool SAT>
 __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
   __shared__ uint32_t red[kThreads / kWave];
+  __shared__ uint32_t red_sat[SAT ? kThreads / kWave : 1];
+  uint32_t nsat = 0;
   constexpr int ESZ = In<DT>::kEsz;
   constexpr int EPC = In<DT>::kEpc;
   constexpr int U = WQ ? kUnroll : kUnrollRead;
@@ -167,14 +180,14 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           uint32_t m;
-          const uint2 o = cast_chunk<DT, FMT>(v[u], e, &m, WQ);
+          const uint2 o = cast_chunk<DT, FMT, SAT>(v[u], e, &m, WQ, &nsat);
           if (AMAX) amax_bits = amax_bits > m ? amax_bits : m;
           if (WQ) store_codes<DT>(qr, c + u * stride, o);
         }
       }
       for (; c < cpr; c += stride) {
         uint32_t m;
-        const uint2 o = cast_chunk<DT, FMT>(load_nt(x4 + c), e, &m, WQ);
+        const uint2 o = cast_chunk<DT, FMT, SAT>(load_nt(x4 + c), e, &m, WQ, &nsat);
         if (AMAX) amax_bits = amax_bits > m ? amax_bits : m;
         if (WQ) store_codes<DT>(qr, c, o);
       }
@@ -185,28 +198,32 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
       const uint32_t bits = load_elem<DT>(xr, i, &f);
       const uint32_t ab = bits & 0x7fffffffu;
       if (AMAX) amax_bits = amax_bits > ab ? amax_bits : ab;
-      if (WQ) qr[i] = (uint8_t)cast_elem<FMT>(bits, e);
+      if (WQ) qr[i] = (uint8_t)cast_elem<FMT>(bits, e, SAT ? &nsat : nullptr);
     }
   }
   if (AMAX) block_max_to_global(amax_bits, red, a.amax);
+  if (SAT) block_sum_to_global(nsat, red_sat, a.sat);
 }
 
-template <int DT, int FMT, bool VEC, bool WQ, bool AMAX>
+template <int DT, int FMT, bool VEC, bool WQ, bool AMAX, bool SAT>
 static void launch_t(const StreamArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((stream_kernel<DT, FMT, VEC, WQ, AMAX>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((stream_kernel<DT, FMT, VEC, WQ, AMAX, SAT>), grid, dim3(kThreads), 0, s, a);
+}
+
+template <int DT, int FMT, bool VEC>
+static void launch_mode(const StreamArgs& a, bool wq, bool am, bool sat, dim3 grid, hipStream_t s) {
+  if (!wq) launch_t<DT, FMT, VEC, false, true, false>(a, grid, s);
+  else if (sat && am) launch_t<DT, FMT, VEC, true, true, true>(a, grid, s);
+  else if (sat) launch_t<DT, FMT, VEC, true, false, true>(a, grid, s);
+  else if (am) launch_t<DT, FMT, VEC, true, true, false>(a, grid, s);
+  else launch_t<DT, FMT, VEC, true, false, false>(a, grid, s);
 }
 
 template <int DT, int FMT>
 static void launch_vec_mode(const StreamArgs& a, bool vec, bool wq, bool am, dim3 grid, hipStream_t s) {
-  if (vec) {
-    if (wq && am) launch_t<DT, FMT, true, true, true>(a, grid, s);
-    else if (wq) launch_t<DT, FMT, true, true, false>(a, grid, s);
-    else launch_t<DT, FMT, true, false, true>(a, grid, s);
-  } else {
-    if (wq && am) launch_t<DT, FMT, false, true, true>(a, grid, s);
-    else if (wq) launch_t<DT, FMT, false, true, false>(a, grid, s);
-    else launch_t<DT, FMT, false, false, true>(a, grid, s);
-  }
+  const bool sat = wq && a.sat != nullptr;
+  if (vec) launch_mode<DT, FMT, true>(a, wq, am, sat, grid, s);
+  else launch_mode<DT, FMT, false>(a, wq, am, sat, grid, s);
 }
 
 void launch_stream_pass(StreamArgs a, int dtype, int fmt, bool write_q, bool amax, hipStream_t stream) {
@@ -248,12 +265,15 @@ void launch_stream_pass(StreamArgs a, int dtype, int fmt, bool write_q, bool ama
 // ---------------------------------------------------------------------------
 constexpr int kTT = 64;
 
-template <int DT, int FMT, bool AMAX>
+template <int DT, int FMT, bool AMAX, bool SAT>
 __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, const int32_t* __restrict__ bias,
-    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ amax) {
+    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ amax,
+    unsigned long long* __restrict__ sat) {
   __shared__ uint32_t tile[kTT][kTT / 4 + 1];     // 64 rows x 64 bytes, padded by one dword
   __shared__ uint32_t red[kThreads / kWave];
+  __shared__ uint32_t red_sat[SAT ? kThreads / kWave : 1];
+  uint32_t nsat = 0;
   constexpr int ESZ = In<DT>::kEsz;
   const int e = *bias;
   const int64_t r0 = (int64_t)blockIdx.y * kTT;
@@ -274,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
         const uint32_t bits = load_elem<DT>(xr, c, &f);
         const uint32_t ab = bits & 0x7fffffffu;
         if (AMAX) amax_bits = amax_bits > ab ? amax_bits : ab;
-        code = cast_elem<FMT>(bits, e);
+        code = cast_elem<FMT>(bits, e, SAT ? &nsat : nullptr);
         q[r * ldq + c] = (uint8_t)code;
       }
       packed[j / 4] |= code << (8 * (j % 4));
@@ -296,6 +316,7 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
     }
   }
   if (AMAX) block_max_to_global(amax_bits, red, amax);
+  if (SAT) block_sum_to_global(nsat, red_sat, sat);
 }
 
 // ---------------------------------------------------------------------------
@@ -329,12 +350,15 @@ __device__ __forceinline__ void bytes_transpose4(uint32_t a0, uint32_t a1, uint3
 // dY and W, 45M elements, +9% / +11%) and slower on small ones (X, 16.7M
 // elements, -11%: the dirty lines are still being written back when the
 // kernel ends), so the host picks the kind by size.
-template <int FMT, bool AMAX, bool NTQT>
+template <int FMT, bool AMAX, bool NTQT, bool SAT>
 __global__ __launch_bounds__(kThreads) void cast_transpose_vec_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, const int32_t* __restrict__ bias,
-    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ amax) {
+    uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ amax,
+    unsigned long long* __restrict__ sat) {
   __shared__ uint32_t T[kCtC][kCtR / 4 + 1];       // codes, column-major, 4 rows per dword
   __shared__ uint32_t red[kThreads / kWave];
+  __shared__ uint32_t red_sat[SAT ? kThreads / kWave : 1];
+  uint32_t nsat = 0;
   const int e = *bias;
   const int64_t r0 = (int64_t)blockIdx.y * kCtR, c0 = (int64_t)blockIdx.x * kCtC;
   const int cg = threadIdx.x & 7, rg = threadIdx.x >> 3;
@@ -347,7 +371,7 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_vec_kernel(
       const int64_t r = r0 + 4 * rg + i;
       const uint4 v = load_nt(reinterpret_cast<const uint4*>(x + r * ld + c0 + 8 * cg));
       uint32_t m;
-      o[i] = cast_chunk<FP8_DT_BF16, FMT>(v, e, &m, true);
+      o[i] = cast_chunk<FP8_DT_BF16, FMT, SAT>(v, e, &m, true, &nsat);
       if (AMAX) amax_bits = amax_bits > m ? amax_bits : m;
       const v2u_t ov = {o[i].x, o[i].y};
       __builtin_nontemporal_store(ov, reinterpret_cast<v2u_t*>(q + r * ldq + c0 + 8 * cg));
@@ -367,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_vec_kernel(
             const uint32_t bits = load_elem<FP8_DT_BF16>(xr, c, &f);
             const uint32_t ab = bits & 0x7fffffffu;
             if (AMAX) amax_bits = amax_bits > ab ? amax_bits : ab;
-            const uint32_t code = cast_elem<FMT>(bits, e);
+            const uint32_t code = cast_elem<FMT>(bits, e, SAT ? &nsat : nullptr);
             q[r * ldq + c] = (uint8_t)code;
             w[k / 4] |= code << (8 * (k % 4));
           }
@@ -410,6 +434,7 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_vec_kernel(
     }
   }
   if (AMAX) block_max_to_global(amax_bits, red, amax);
+  if (SAT) block_sum_to_global(nsat, red_sat, sat);
 }
 
 // ---------------------------------------------------------------------------
@@ -665,11 +690,11 @@ __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
 
 using namespace sfp8;
 
-extern "C" {
-
-int fp8_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt,
-                 const int32_t* bias, uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT, float* amax_out,
-                 hipStream_t stream) {
+// Per-tensor cast behind fp8_quantize and fp8_quantize_sat (sat_out: count
+// of saturated elements, or null).
+static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                         const int32_t* bias, uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT, float* amax_out,
+                         unsigned long long* sat_out, hipStream_t stream) {
   if (!bias || !q) return FP8_ERR_NULL;
   if (!valid_dtype(dtype)) return FP8_ERR_DTYPE;
   if (!valid_fmt(fmt)) return FP8_ERR_FORMAT;
@@ -680,43 +705,51 @@ int fp8_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
   if (qT && check_matrix(cols, rows, ldqT)) return FP8_ERR_SHAPE;
   const int64_t n = rows * cols;
   if (n > 0 && !x) return FP8_ERR_NULL;
-  if (amax_out) zero_float_async(amax_out, stream);
+  zero_outputs_async(amax_out, sat_out, stream);
   if (n == 0) return launch_status();
+  const bool am = amax_out != nullptr, sc = sat_out != nullptr;
   if (qT && dtype == FP8_DT_BF16 && aligned(x, 16) && ld % 8 == 0 && aligned(q, 8) && ldq % 8 == 0 &&
       aligned(qT, 16) && ldqT % 16 == 0 && (rows + kCtR - 1) / kCtR <= 65535) {
     const dim3 grid((unsigned)((cols + kCtC - 1) / kCtC), (unsigned)((rows + kCtR - 1) / kCtR));
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const bool nt = n < kCtCachedMin;
-#define SFP8_CTV3(FMT, AM, NT)                                                                                \
-  hipLaunchKernelGGL((cast_transpose_vec_kernel<FMT, AM, NT>), grid, dim3(kThreads), 0, stream, xb, rows, cols, \
-                     ld, bias, q, ldq, qT, ldqT, amax_out)
-#define SFP8_CTV(FMT)                                                                                         \
-  do {                                                                                                        \
-    if (amax_out) {                                                                                           \
-      if (nt) SFP8_CTV3(FMT, true, true);                                                                     \
-      else SFP8_CTV3(FMT, true, false);                                                                       \
-    } else {                                                                                                  \
-      if (nt) SFP8_CTV3(FMT, false, true);                                                                    \
-      else SFP8_CTV3(FMT, false, false);                                                                      \
-    }                                                                                                         \
+#define SFP8_CTV4(FMT, AM, NT, SC)                                                                              \
+  hipLaunchKernelGGL((cast_transpose_vec_kernel<FMT, AM, NT, SC>), grid, dim3(kThreads), 0, stream, xb, rows,   \
+                     cols, ld, bias, q, ldq, qT, ldqT, amax_out, sat_out)
+#define SFP8_CTV3(FMT, AM, NT)                                                                                  \
+  do {                                                                                                          \
+    if (sc) SFP8_CTV4(FMT, AM, NT, true);                                                                       \
+    else SFP8_CTV4(FMT, AM, NT, false);                                                                         \
+  } while (0)
+#define SFP8_CTV(FMT)                                                                                           \
+  do {                                                                                                          \
+    if (am) {                                                                                                   \
+      if (nt) SFP8_CTV3(FMT, true, true);                                                                       \
+      else SFP8_CTV3(FMT, true, false);                                                                         \
+    } else {                                                                                                    \
+      if (nt) SFP8_CTV3(FMT, false, true);                                                                      \
+      else SFP8_CTV3(FMT, false, false);                                                                        \
+    }                                                                                                           \
   } while (0)
     if (fmt == FP8_E4M3) SFP8_CTV(FP8_E4M3);
     else SFP8_CTV(FP8_E5M2);
 #undef SFP8_CTV
 #undef SFP8_CTV3
+#undef SFP8_CTV4
     return launch_status();
   }
   if (qT) {
     const dim3 grid((unsigned)((cols + kTT - 1) / kTT), (unsigned)((rows + kTT - 1) / kTT));
     if (grid.y > 65535) return FP8_ERR_SHAPE;
-#define SFP8_CT(DT, FMT)                                                                                   \
-  do {                                                                                                     \
-    if (amax_out)                                                                                          \
-      hipLaunchKernelGGL((cast_transpose_kernel<DT, FMT, true>), grid, dim3(kThreads), 0, stream, x, rows, \
-                         cols, ld, bias, q, ldq, qT, ldqT, amax_out);                                      \
-    else                                                                                                   \
-      hipLaunchKernelGGL((cast_transpose_kernel<DT, FMT, false>), grid, dim3(kThreads), 0, stream, x,      \
-                         rows, cols, ld, bias, q, ldq, qT, ldqT, amax_out);                                \
+#define SFP8_CT2(DT, FMT, AM, SC)                                                                                  \
+  hipLaunchKernelGGL((cast_transpose_kernel<DT, FMT, AM, SC>), grid, dim3(kThreads), 0, stream, x, rows, cols, ld, \
+                     bias, q, ldq, qT, ldqT, amax_out, sat_out)
+#define SFP8_CT(DT, FMT)                                                                                           \
+  do {                                                                                                             \
+    if (am && sc) SFP8_CT2(DT, FMT, true, true);                                                                   \
+    else if (am) SFP8_CT2(DT, FMT, true, false);                                                                   \
+    else if (sc) SFP8_CT2(DT, FMT, false, true);                                                                   \
+    else SFP8_CT2(DT, FMT, false, false);                                                                          \
   } while (0)
     if (dtype == FP8_DT_BF16) {
       if (fmt == FP8_E4M3) SFP8_CT(FP8_DT_BF16, FP8_E4M3);
@@ -726,6 +759,7 @@ int fp8_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
       else SFP8_CT(FP8_DT_F32, FP8_E5M2);
     }
 #undef SFP8_CT
+#undef SFP8_CT2
     return launch_status();
   }
   StreamArgs a;
@@ -737,8 +771,26 @@ int fp8_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t l
   a.q = q;
   a.ldq = ldq;
   a.amax = amax_out;
-  launch_stream_pass(a, dtype, fmt, /*write_q=*/true, /*amax=*/amax_out != nullptr, stream);
+  a.sat = sat_out;
+  launch_stream_pass(a, dtype, fmt, /*write_q=*/true, /*amax=*/am, stream);
   return launch_status();
+}
+
+extern "C" {
+
+int fp8_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                 const int32_t* bias, uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT, float* amax_out,
+                 hipStream_t stream) {
+  return quantize_impl(x, dtype, rows, cols, ld, fmt, bias, q, ldq, qT, ldqT, amax_out, nullptr, stream);
+}
+
+int fp8_quantize_sat(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                     const int32_t* bias, uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT, float* amax_out,
+                     uint64_t* sat_out, hipStream_t stream) {
+  if (!sat_out) return FP8_ERR_NULL;
+  static_assert(sizeof(unsigned long long) == sizeof(uint64_t), "64-bit count");
+  return quantize_impl(x, dtype, rows, cols, ld, fmt, bias, q, ldq, qT, ldqT, amax_out,
+                       reinterpret_cast<unsigned long long*>(sat_out), stream);
 }
 
 // Row-wise MX cast behind mx_quantize_rule (scales row-major, ld_scales) and

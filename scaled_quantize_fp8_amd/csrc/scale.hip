@@ -22,6 +22,15 @@ void zero_float_async(float* p, hipStream_t stream) {
   hipLaunchKernelGGL(zero_float_kernel, dim3(1), dim3(1), 0, stream, p);
 }
 
+__global__ void zero_outputs_kernel(float* f, unsigned long long* n) {
+  if (f) *f = 0.0f;
+  if (n) *n = 0ull;
+}
+
+void zero_outputs_async(float* f, unsigned long long* n, hipStream_t stream) {
+  if (f || n) hipLaunchKernelGGL(zero_outputs_kernel, dim3(1), dim3(1), 0, stream, f, n);
+}
+
 // One thread: bias and optional scales from one amax.
 __global__ void compute_scale_kernel(const float* __restrict__ amax, int emax, int margin,
                                      int32_t* __restrict__ bias_out, float* __restrict__ scale_out,
@@ -99,7 +108,7 @@ const char* fp8_status_string(int status) {
   }
 }
 
-int fp8_abi_version(void) { return 2; }
+int fp8_abi_version(void) { return 3; }
 
 int fp8_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, float* amax_out,
              hipStream_t stream) {
@@ -119,6 +128,7 @@ int fp8_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, f
     a.q = nullptr;
     a.ldq = 0;
     a.amax = amax_out;
+    a.sat = nullptr;
     launch_stream_pass(a, dtype, FP8_E4M3, /*write_q=*/false, /*amax=*/true, stream);
   }
   return launch_status();

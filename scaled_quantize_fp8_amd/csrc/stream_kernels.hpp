@@ -14,10 +14,12 @@ struct StreamArgs {
   uint8_t* q;              // [rows x cols] FP8 codes, leading dimension ldq (quantize only)
   int64_t ldq;
   float* amax;             // device float, already zeroed (amax only)
+  unsigned long long* sat; // device count of saturated elements, already zeroed (quantize; may be null)
 };
 
 // Enqueue one pass over x: cast to FP8 into q when write_q, max-reduce |x|
-// into *amax when amax.  Picks the 16-byte vector kernel when the operands
+// into *amax when amax, count the elements the cast saturates into *a.sat
+// when that pointer is set (casts only).  Picks the 16-byte vector kernel when the operands
 // allow it and collapses contiguous matrices into one long row.
 void launch_stream_pass(StreamArgs a, int dtype, int fmt, bool write_q, bool amax, hipStream_t stream);
 

@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
                  "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize", "mx_quantize_t",
                  "mx_quantize_rule", "mx_quantize_t_rule", "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string",
                  "fp8_abi_version", "mx_packed_scales_bytes", "mx_pack_scales", "mx_quantize_packed",
-                 "mx_quantize_t_packed", "mx_scaled_gemm_packed"]:
+                 "mx_quantize_t_packed", "mx_scaled_gemm_packed", "fp8_quantize_sat"]:
         assert want in names
 
 
@@ -52,7 +52,7 @@ def test_status_strings(lib):
     for code in (NULL, SHAPE, ALIGN, DTYPE, FORMAT, LAUNCH, UNSUP):
         assert sq.fp8_status_string(code) not in ("ok", "unknown status")
     assert sq.fp8_status_string(-99) == "unknown status"
-    assert sq.fp8_abi_version() >= 2
+    assert sq.fp8_abi_version() >= 3
 
 
 def test_amax_validation(lib):
@@ -87,6 +87,13 @@ def test_quantize_validation(lib):
     assert q(FAKE, 0, 4, 4, 4, 0, FAKE, FAKE, 3, None, 0, None, S) == SHAPE     # ldq
     assert q(FAKE, 0, 4, 8, 8, 0, FAKE, FAKE, 8, FAKE, 2, None, S) == SHAPE     # ldqT < rows
     assert q(None, 0, 4, 4, 4, 0, FAKE, FAKE, 4, None, 0, None, S) == NULL
+    qs = lib.fp8_quantize_sat
+    assert qs(FAKE, 0, 4, 4, 4, 0, FAKE, FAKE, 4, None, 0, None, None, S) == NULL  # sat_out required
+    assert qs(FAKE, 0, 4, 4, 4, 0, None, FAKE, 4, None, 0, None, FAKE, S) == NULL  # bias
+    assert qs(FAKE, 3, 4, 4, 4, 0, FAKE, FAKE, 4, None, 0, None, FAKE, S) == DTYPE
+    assert qs(FAKE, 0, 4, 4, 4, 5, FAKE, FAKE, 4, None, 0, None, FAKE, S) == FORMAT
+    assert qs(FAKE, 0, 4, 4, 2, 0, FAKE, FAKE, 4, None, 0, None, FAKE, S) == SHAPE
+    assert qs(FAKE, 0, 4, 8, 8, 0, FAKE, FAKE, 8, FAKE, 2, None, FAKE, S) == SHAPE
     m = lib.mx_quantize
     assert m(FAKE, 0, 4, 48, 48, 0, FAKE, 48, FAKE, 2, S) == SHAPE              # cols % 32
     assert m(FAKE, 0, 4, 64, 64, 0, None, 64, FAKE, 2, S) == NULL

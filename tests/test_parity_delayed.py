@@ -32,15 +32,19 @@ class GpuDelayed:
         sq.fp8_history_init(self.hist, self.state)
         self.step = 0
 
-    def cast(self, x):
+    def cast(self, x, count_saturated=False):
         if self.step == 0:                       # bootstrap: own amax first
             sq.fp8_history_push(self.hist, self.state, sq.fp8_amax(x))
         bias, _, _ = sq.fp8_compute_scale_delayed(self.hist, self.state, E4M3.code, 0)
-        q, _, a = sq.fp8_quantize(x, E4M3.code, bias, want_amax=True)
+        sat = None
+        if count_saturated:
+            q, _, a, sat = sq.fp8_quantize_sat(x, E4M3.code, bias, want_amax=True)
+        else:
+            q, _, a = sq.fp8_quantize(x, E4M3.code, bias, want_amax=True)
         if self.step > 0:
             sq.fp8_history_push(self.hist, self.state, a)
         self.step += 1
-        return q, bias, a
+        return (q, bias, a, sat) if count_saturated else (q, bias, a)
 
 
 def _oracle_steps(xs):
@@ -122,7 +126,7 @@ def test_delayed_full_size_7b_attn_16_steps():
     log = []
     for t in range(16):
         bits = make("c2", "X", step=t)
-        q, bias, a = g.cast(bf16_dev(bits))
+        q, bias, a, gsat = g.cast(bf16_dev(bits), count_saturated=True)
         ra = oracle_amax_chunked(bits)
         if t == 0:
             h.push(ra)
@@ -138,6 +142,7 @@ def test_delayed_full_size_7b_attn_16_steps():
         scaled = np.abs(np.ldexp(oracle.bf16_bits_to_f64(bits), rb))
         sat = scaled > E4M3.max
         assert np.all(at_max[sat])                          # saturated -> the maximum code
+        assert int(host(gsat)[0]) == int(np.count_nonzero(sat))   # the device count, exact
         log.append((t, rb, int(np.count_nonzero(sat))))
         say(f"delayed step {t}: bias {rb}, amax {ra:.4g}, saturated {log[-1][2]}")
     # the window lags a growing amax: some step saturates, step 0 never does

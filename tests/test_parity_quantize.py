@@ -398,3 +398,66 @@ def test_mx_quantize_t_packed(rows, cols, dtype, fmt, rule):
     qT, ps = sq.mx_quantize_t_packed(x, fmt.code, rule=rule)
     assert np.array_equal(host(qT), rq)
     assert np.array_equal(host(ps), pack_scales_host(rs))
+
+
+def _oracle_sat_count(vals, fmt, bias):
+    """Elements the cast clamps: |x * 2**bias| > fmax, NaN excluded (the
+    oracle's encode saturates exactly these)."""
+    s = np.abs(np.ldexp(vals, bias))
+    return int(np.count_nonzero(~np.isnan(s) & (s > fmt.max)))
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=lambda f: f.name)
+def test_saturation_count_every_bf16_pattern(fmt):
+    """fp8_quantize_sat over all 65,536 bf16 patterns (NaN, +-Inf, subnormals,
+    the largest finite values) at biases from -126 to 126 in steps of 7:
+    the device count equals the oracle's count of clamped elements, and the
+    bytes and fused amax equal fp8_quantize's."""
+    bits = all_bf16_patterns().reshape(256, 256)
+    x = bf16_dev(bits)
+    vals = oracle.bf16_bits_to_f64(bits)
+    for b in range(-126, 127, 7):
+        q, _, am, n = sq.fp8_quantize_sat(x, fmt.code, i32_dev(b), want_amax=True)
+        q0, _, am0 = sq.fp8_quantize(x, fmt.code, i32_dev(b), want_amax=True)
+        assert int(host(n)[0]) == _oracle_sat_count(vals, fmt, b), (fmt.name, b)
+        assert torch.equal(q, q0) and f32_bits_of(am) == f32_bits_of(am0)
+
+
+@pytest.mark.parametrize("path", ["rows_vec", "rows_strided", "f32", "transpose_vec", "transpose_generic"])
+def test_saturation_count_every_cast_path(path):
+    """The count on each kernel the per-tensor cast can take: aligned rows
+    (vector loads), a strided unaligned view (element loads), fp32 input, the
+    vector cast-transpose (aligned bf16) and the generic cast-transpose
+    (unaligned leading dimension); ragged shapes, Inf and NaN planted, a bias
+    that clamps the tail of the distribution."""
+    rng = np.random.default_rng(44)
+    full = (rng.standard_normal((301, 264)) * 40).astype(np.float32)
+    full[3, 7], full[100, 200], full[5, 5] = np.inf, -np.inf, np.nan
+    if path == "f32":
+        x = f32_dev(full)[:, :257]
+        vals = full[:, :257].astype(np.float64)
+    else:
+        fb = f32_to_bf16_bits(full)
+        t = bf16_dev(fb)
+        vals_full = oracle.bf16_bits_to_f64(fb)
+        if path in ("rows_strided", "transpose_generic"):
+            x, vals = t[1:, 3:250], vals_full[1:, 3:250]          # unaligned base, ld 264
+        elif path == "transpose_vec":
+            x, vals = t[:288, :256], vals_full[:288, :256]        # qT rows of 288 bytes: vector kernel
+        else:
+            x, vals = t[:, :256], vals_full[:, :256]
+    transpose = path.startswith("transpose")
+    for fmt in FMTS:
+        b = oracle.compute_bias(oracle.amax(vals[np.isfinite(vals)]), fmt) + 2     # clamps the top quarter
+        say(f"saturation count {path} {fmt.name} bias {b}")
+        q, qT, am, n = sq.fp8_quantize_sat(x, fmt.code, i32_dev(b), transpose=transpose, want_amax=True)
+        ref = oracle.quantize(vals, fmt, b)
+        assert np.array_equal(host(q), ref)
+        if transpose:
+            assert np.array_equal(host(qT), ref.T)
+        want = _oracle_sat_count(vals, fmt, b)
+        assert want > 1000 and int(host(n)[0]) == want
+        assert np.isnan(host(am)[0])
+        # without the fused amax, at a bias that clamps only the infinities
+        _, _, _, n0 = sq.fp8_quantize_sat(x, fmt.code, i32_dev(b - 12), transpose=transpose)
+        assert int(host(n0)[0]) == _oracle_sat_count(vals, fmt, b - 12)
