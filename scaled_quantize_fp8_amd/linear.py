@@ -44,7 +44,7 @@ import math
 import torch
 
 from . import (E4M3, E5M2, _rule, fp8_amax, fp8_compute_scale, fp8_compute_scale_delayed,
-               fp8_history_init, fp8_history_push, fp8_quantize, fp8_scaled_gemm, mx_quantize_packed,
+               fp8_history_init, fp8_history_push, fp8_quantize, fp8_quantize_sat, fp8_scaled_gemm, mx_quantize_packed,
                mx_quantize_rule, mx_quantize_t_packed, mx_quantize_t_rule, mx_scaled_gemm,
                mx_scaled_gemm_packed)
 
@@ -70,30 +70,39 @@ class _History:
         self.steps = 0
 
 
+def _cast(x2, fmt, bias, transpose, want_amax, log):
+    """The cast; with a scale log it also counts saturated elements on the
+    device (fp8_quantize_sat: same bytes)."""
+    if log is None:
+        q, qT, amax = fp8_quantize(x2, fmt, bias, transpose=transpose, want_amax=want_amax)
+        return q, qT, amax, None
+    return fp8_quantize_sat(x2, fmt, bias, transpose=transpose, want_amax=want_amax)
+
+
 def _per_tensor_cast(x2: torch.Tensor, fmt, recipe: str, margin: int, hist: _History | None,
                      transpose: bool, const_bias: torch.Tensor | None = None, log=None, name: str = ""):
     """Bias and FP8 codes (plus the transposed copy) of one tensor; with a
-    `log` list, appends (name, bias, amax) as device scalars (amax None for
-    the constant recipe)."""
+    `log` list, appends (name, bias, amax, saturated) as device scalars (amax
+    None for the constant recipe; saturated = elements the cast clamped)."""
     amax = None
     if recipe == "constant":
         bias = const_bias
-        q, qT, _ = fp8_quantize(x2, fmt, bias, transpose=transpose)
+        q, qT, _, sat = _cast(x2, fmt, bias, transpose, False, log)
     elif recipe == "current":
         amax = fp8_amax(x2)
         bias, _, _ = fp8_compute_scale(amax, fmt, margin)
-        q, qT, _ = fp8_quantize(x2, fmt, bias, transpose=transpose)
+        q, qT, _, sat = _cast(x2, fmt, bias, transpose, False, log)
     else:
         # delayed: the first step bootstraps the history with its own amax
         if hist.steps == 0:
             fp8_history_push(hist.hist, hist.state, fp8_amax(x2))
         bias, _, _ = fp8_compute_scale_delayed(hist.hist, hist.state, fmt, margin)
-        q, qT, amax = fp8_quantize(x2, fmt, bias, transpose=transpose, want_amax=True)
+        q, qT, amax, sat = _cast(x2, fmt, bias, transpose, True, log)
         if hist.steps > 0:
             fp8_history_push(hist.hist, hist.state, amax)
         hist.steps += 1
     if log is not None:
-        log.append((name, bias.clone(), None if amax is None else amax.clone()))
+        log.append((name, bias.clone(), None if amax is None else amax.clone(), sat))
     return bias, q, qT
 
 
@@ -230,14 +239,16 @@ class Fp8Linear(torch.nn.Module):
         return Fp8LinearFunction.apply(x, self.weight, self)
 
     def scale_history(self) -> dict:
-        """Per-step (bias, amax) of each tensor ("x", "w", "dy") since the
-        layer was built or the log cleared, in step order; copies the logged
-        device scalars to the host (one synchronization)."""
+        """Per-step (bias, amax, saturated) of each tensor ("x", "w", "dy")
+        since the layer was built or the log cleared, in step order:
+        saturated is the number of elements the cast clamped to +-max (a
+        delayed scale lagging a growing amax).  Copies the logged device
+        scalars to the host."""
         if self._log is None:
             raise RuntimeError("the layer was built without log_scales=True")
         out = {"x": [], "w": [], "dy": []}
-        for name, b, a in self._log:
-            out[name].append((int(b.cpu()[0]), None if a is None else float(a.cpu()[0])))
+        for name, b, a, n in self._log:
+            out[name].append((int(b.cpu()[0]), None if a is None else float(a.cpu()[0]), int(n.cpu()[0])))
         return out
 
     def bias_histogram(self) -> dict:
@@ -246,7 +257,7 @@ class Fp8Linear(torch.nn.Module):
         hist = {}
         for name, rows in self.scale_history().items():
             h = {}
-            for b, _ in rows:
+            for b, *_ in rows:
                 h[b] = h.get(b, 0) + 1
             hist[name] = dict(sorted(h.items()))
         return hist
