@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--rotate", type=int, default=3,
+                    help="copies of X and W the steps rotate through (cold caches for every step's inputs)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the products and casts timed outside the step (backward, other workloads, RMSE)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -53,10 +55,21 @@ def parse():
 def cpu_baseline(xb, wb, target_s: float):
     """Time the oracle (as it stands) on a bounded sample of the workload and
     scale to the metric: TFLOP/s of the full step's GEMM flops over the
-    oracle's extrapolated full-step time."""
+    oracle's extrapolated full-step time.
+
+    Per element (rows 0..R-1 of X and W, NumPy, one thread): amax, bias, E4M3
+    and MX casts, then the reference GEMMs' input preparation (decode and
+    block dequantization).  Per GEMM: the oracle's float64 product engine
+    (BLAS over 512-row panels) on a P-row and a 2P-row panel of X against all
+    N rows of W (values tiled from the sample: the cost does not depend on
+    them); the difference is the cost of P more rows, the rest the per-call
+    cost (the transposed copy of W), so each full product is
+    fixed + (M / P) * per_panel.  Both products (per-tensor, MX) use the same
+    engine, so it is timed once and counted twice."""
     import numpy as np
 
     import oracle
+    from oracle.gemm import _panels
     try:
         from threadpoolctl import threadpool_info
         threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
@@ -64,8 +77,7 @@ def cpu_baseline(xb, wb, target_s: float):
         threads = os.cpu_count() or 1
     M, K = xb.shape
     N = wb.shape[0]
-    # element-wise part: amax, bias, E4M3 cast and MX cast of a row sample
-    rows = 256
+    rows = 512
     t0 = time.perf_counter()
     xs = oracle.bf16_bits_to_f64(xb[:rows])
     ws = oracle.bf16_bits_to_f64(wb[:rows])
@@ -75,41 +87,107 @@ def cpu_baseline(xb, wb, target_s: float):
     qw = oracle.quantize(ws, oracle.E4M3, bw)
     mqx, msx = oracle.mx_quantize(xs, oracle.E4M3)
     mqw, msw = oracle.mx_quantize(ws, oracle.E4M3)
-    t_elem = (time.perf_counter() - t0) / (2 * rows * K)          # seconds per element
-    # GEMM part: float64 reference GEMMs on growing samples until ~target_s
-    m = n = 256
-    t_gemm = 0.0
-    flops = 0.0
-    t_start = time.perf_counter()
-    while time.perf_counter() - t_start < target_s:
-        t0 = time.perf_counter()
-        oracle.scaled_gemm_ref(qx[:m], oracle.E4M3, bx, qw[:n], oracle.E4M3, bw)
-        oracle.mx_gemm_ref(mqx[:m], msx[:m], oracle.E4M3, mqw[:n], msw[:n], oracle.E4M3)
-        t_gemm += time.perf_counter() - t0
-        flops += 2 * 2.0 * m * n * K
-    gemm_rate = flops / t_gemm                                      # flop/s
+    t_cast = (time.perf_counter() - t0) / (2 * rows * K)           # seconds per element
+    t0 = time.perf_counter()
+    ax = oracle.dequantize(qx, oracle.E4M3, bx)
+    aw = oracle.dequantize(qw, oracle.E4M3, bw)
+    oracle.mx_dequantize(mqx, msx, oracle.E4M3)
+    oracle.mx_dequantize(mqw, msw, oracle.E4M3)
+    t_prep = (time.perf_counter() - t0) / (2 * rows * K)
+    wfull = np.tile(aw, (-(-N // rows), 1))[:N]
+    P = 256
+    while True:
+        t = {}
+        for p in (P, 2 * P):
+            a = np.tile(ax, (-(-p // rows), 1))[:p]
+            t0 = time.perf_counter()
+            _panels(a, wfull)
+            t[p] = time.perf_counter() - t0
+        if t[P] + t[2 * P] > target_s / 2 or 2 * P >= 4096:
+            break
+        P *= 2
+    per_panel = max(t[2 * P] - t[P], 1e-9)
+    fixed = max(t[P] - per_panel, 0.0)
+    gemm_time = 2 * (fixed + (M / P) * per_panel)
     full_flops = 2 * 2.0 * M * N * K
-    full_time = t_elem * (M + N) * K * 1.0 + full_flops / gemm_rate
+    full_time = (t_cast + t_prep) * (M + N) * K + gemm_time
     return {
         "value": full_flops / full_time / 1e12, "unit": "TFLOP/s", "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"oracle (NumPy float64) on rows 0..{rows - 1} of X and W for amax/bias/E4M3/MX casts "
-                   f"({t_elem * 1e9:.1f} ns/element, 1 thread) and repeated {m}x{n}x{K} per-tensor + MX "
-                   f"reference GEMMs for {t_gemm:.1f} s ({gemm_rate / 1e9:.1f} GFLOP/s, BLAS threads={threads}); "
-                   f"extrapolated to the full step: {full_time:.0f} s"),
+        "sample": (f"oracle (NumPy float64) on rows 0..{rows - 1} of X and W: amax/bias/E4M3/MX casts "
+                   f"{t_cast * 1e9:.1f} ns/element and GEMM input decoding {t_prep * 1e9:.1f} ns/element "
+                   f"(1 thread); its float64 product engine on {P}- and {2 * P}-row panels of X against all "
+                   f"{N} rows of W ({t[P]:.1f} s, {t[2 * P]:.1f} s: "
+                   f"{2.0 * P * N * K / per_panel / 1e9:.0f} GFLOP/s per added panel, BLAS threads={threads}); "
+                   f"extrapolated to the full step (two products): {full_time:.0f} s"),
     }
 
 
-def gpu_sclk():
-    """Current shader clock as reported by rocm-smi (a child process, after
-    the timed region); None where the tool is missing or prints no sclk."""
-    import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
-    except (OSError, subprocess.SubprocessError):
-        return None
-    lines = [ln.strip() for ln in r.stdout.splitlines() if "sclk" in ln.lower()]
-    return lines[0] if lines else None
+class SclkSampler:
+    """Shader clock sampled in a thread while the timed region runs, through
+    the amdsmi library in this process (the GPU metrics table's current
+    graphics clock, per XCD where it lists one per XCD)."""
+
+    def __init__(self, period_s: float = 0.002):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self._stop = threading.Event()
+        self._t = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception as e:                      # no library or no driver access
+            self._smi = None
+            self.error = f"amdsmi unavailable: {e!r}"[:200]
+
+    def _read(self):
+        smi = self._smi
+        try:
+            m = smi.amdsmi_get_gpu_metrics_info(self._h)
+            v = m.get("current_gfxclks")
+            if isinstance(v, (list, tuple)):
+                v = [c for c in v if isinstance(c, (int, float)) and 0 < c < 10000]
+                if v:
+                    return sum(v) / len(v)
+            v = m.get("current_gfxclk")
+            if isinstance(v, (int, float)) and 0 < v < 10000:
+                return float(v)
+        except Exception as e:
+            self.error = f"gpu metrics: {e!r}"[:200]
+        try:
+            return float(smi.amdsmi_get_clock_info(self._h, smi.AmdSmiClkType.GFX)["clk"])
+        except Exception as e:
+            self.error = f"clock info: {e!r}"[:200]
+            return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            time.sleep(self.period)
+
+    def start(self):
+        import threading
+        if self._smi is not None:
+            self._t = threading.Thread(target=self._run, daemon=True)
+            self._t.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._t is not None:
+            self._t.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"MHz": None, "source": self.error or "no samples"}
+        v = sorted(self.samples)
+        return {"MHz_median": v[len(v) // 2], "MHz_min": v[0], "MHz_max": v[-1], "samples": len(v),
+                "source": "amdsmi gpu metrics during the timed region"}
 
 
 def rmse_c4(dev):
@@ -255,6 +333,96 @@ def backward_extras(dev, reps: int = 5):
     return out
 
 
+def hbm_ceilings(dev, xs, ws, qxs, qws, reps: int = 5):
+    """Plain HBM streams with the casts' access pattern and launch shape (the
+    bench's own kernels in libsfp8_ceiling.so, no arithmetic) over the same
+    tensors: read-only (the amax pass's shape) and 2 bytes read : 1 written
+    (the per-tensor cast's), rotating through the input copies like the
+    step; plus a 1 GiB 1:1 copy.  GB/s per tensor."""
+    import ctypes
+    import torch
+    from scaled_quantize_fp8_amd.build import CEILING_LIB
+    lib = ctypes.CDLL(CEILING_LIB)
+    for fn in (lib.sfp8_ceiling_read, lib.sfp8_ceiling_r2w1, lib.sfp8_ceiling_copy):
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        fn.restype = ctypes.c_int
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn, srcs, dsts):
+        nb = srcs[0].numel() * srcs[0].element_size()
+        for i in range(len(srcs)):                   # warm
+            assert fn(srcs[i].data_ptr(), nb, dsts[i].data_ptr(), stream) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for r in range(reps * len(srcs)):
+            fn(srcs[r % len(srcs)].data_ptr(), nb, dsts[r % len(dsts)].data_ptr(), stream)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * len(srcs))
+
+    out = {}
+    for name, src, dst in (("x", xs, qxs), ("w", ws, qws)):
+        nb = src[0].numel() * src[0].element_size()
+        t_r = timed(lib.sfp8_ceiling_read, src, [sink] * len(src))
+        t_rw = timed(lib.sfp8_ceiling_r2w1, src, dst)
+        out[f"read_{name}_GBps"] = round(nb / t_r / 1e6, 1)
+        out[f"r2w1_{name}_GBps"] = round(1.5 * nb / t_rw / 1e6, 1)
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    t_c = timed(lib.sfp8_ceiling_copy, [a], [b])
+    out["copy_1GiB_GBps"] = round(2 * (1 << 30) / t_c / 1e6, 1)
+    del a, b
+    return out
+
+
+def delayed_leg(dev, steps: int = 16):
+    """The delayed-scaling workload (Llama-2-7B attention projection:
+    X_t [2048 x 4096] with per-step scales and 0.1% outliers x50, W [4096 x
+    4096]) for 16 steps, the way a delayed-scaled layer runs it: bias from
+    the 16-entry window, cast with the step's amax fused, saturation counted
+    on the device (fp8_quantize_sat), amax pushed, per-tensor GEMM.  Per-step
+    bias, amax and saturated elements, and the time of a step (window bias +
+    cast + push + GEMM, HIP events)."""
+    import numpy as np
+    import torch
+    import scaled_quantize_fp8_amd as sq
+    from workloads import make
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    xs = [up(make("c2", "X", step=t)) for t in range(steps)]
+    w = up(make("c2", "W"))
+    bw, _, _ = sq.fp8_compute_scale(sq.fp8_amax(w), sq.E4M3, 0)
+    qw, _, _ = sq.fp8_quantize(w, sq.E4M3, bw)
+    hist = torch.empty(16, dtype=torch.float32, device=dev)
+    state = torch.empty(2, dtype=torch.int32, device=dev)
+    sq.fp8_history_init(hist, state)
+    sq.fp8_history_push(hist, state, sq.fp8_amax(xs[0]))       # step 0 bootstraps with its own amax
+    M, K = xs[0].shape
+    qx = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    y = torch.empty((M, w.shape[0]), dtype=torch.bfloat16, device=dev)
+    log = []
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for t in range(steps):
+        evs[t][0].record()
+        b, _, _ = sq.fp8_compute_scale_delayed(hist, state, sq.E4M3, 0)
+        _, _, a, n = sq.fp8_quantize_sat(xs[t], sq.E4M3, b, q=qx, want_amax=True)
+        if t > 0:
+            sq.fp8_history_push(hist, state, a)
+        sq.fp8_scaled_gemm(qx, sq.E4M3, b, qw, sq.E4M3, bw, out=y)
+        evs[t][1].record()
+        log.append((b, a, n))
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    return {"workload": "delayed_scaling_llama2_7b_attn_2048x4096x4096, window 16",
+            "bias": [int(b.item()) for b, _, _ in log],
+            "amax": [round(float(a.item()), 3) for _, a, _ in log],
+            "saturated": [int(n.item()) for _, _, n in log],
+            "ms_per_step_median": round(ms[len(ms) // 2], 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -276,9 +444,14 @@ def main():
     def up(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    x, w = up(xb), up(wb)
-    M, K = x.shape
-    N = w.shape[0]
+    # R copies of the inputs: step s reads copy s % R, so no step finds its
+    # input in the caches (R * 738 MB rotated, far past the 256 MB Infinity
+    # Cache and the 4 MB L2s)
+    R = max(1, args.rotate)
+    xs = [up(xb) for _ in range(R)]
+    ws = [up(wb) for _ in range(R)]
+    M, K = xs[0].shape
+    N = ws[0].shape[0]
     gen_s = time.perf_counter() - t_gen
 
     # device buffers (allocated once, outside the timed region)
@@ -302,10 +475,12 @@ def main():
     names = ["amax_x", "amax_w", "scale", "quant_x", "quant_w", "gemm_pt", "delayed",
              "mxq_x", "mxq_w", "gemm_mx"]
 
-    def step(ev=None):
-        def mark(i):
+    def step(i, ev=None):
+        x, w = xs[i % R], ws[i % R]
+
+        def mark(j):
             if ev is not None:
-                ev[i].record()
+                ev[j].record()
         mark(0)
         sq.fp8_amax(x, out=ax)
         mark(1)
@@ -338,41 +513,35 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
-    # timed region: K steps bracketed by events; per-kernel events inside
+    # timed region: K steps bracketed by events; per-kernel events inside;
+    # the shader clock sampled meanwhile
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(11)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    sclk = SclkSampler()
     torch.cuda.synchronize()
+    sclk.start()
     start.record()
-    for s in range(args.steps):
-        step(evs[s])
+    for s_ in range(args.steps):
+        step(args.warmup + s_, evs[s_])
     end.record()
     torch.cuda.synchronize()
+    sclk.stop()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
-    samples = {nm: sorted(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps))
+    samples = {nm: sorted(evs[s_][i].elapsed_time(evs[s_][i + 1]) for s_ in range(args.steps))
                for i, nm in enumerate(names)}
     per = {nm: sum(v) / len(v) for nm, v in samples.items()}
     per_median = {nm: v[len(v) // 2] for nm, v in samples.items()}
     per_min = {nm: v[0] for nm, v in samples.items()}
 
-    # empirically achievable HBM rate: a plain 1 GiB device-to-device copy,
-    # timed after (outside) the timed region
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(5):
-        dst.copy_(src)
-    c1.record()
-    torch.cuda.synchronize()
-    copy_GBps = 2 * (1 << 30) * 5 / c0.elapsed_time(c1) / 1e6
-    del src, dst
+    # what the memory system delivers for each cast's mix, on the same tensors
+    ceil = hbm_ceilings(dev, xs, ws, [qx] * R, [qw] * R)
+    copy_GBps = ceil["copy_1GiB_GBps"]
 
     gemm_flops = 2.0 * M * N * K
     step_flops = 2 * gemm_flops
@@ -414,22 +583,23 @@ def main():
                 "traffic_unit": "GB per launch (HBM-side read+write, copy-calibrated rocprofv3 counters)",
                 "algorithmic_GB": round((M * K + N * K + 2 * M * N) / 1e9, 3)}
 
-    # the HBM-bound kernels against the datasheet 8 TB/s and the copy ceiling
-    stream = {"bound": "hbm", "peak": PEAK_HBM_GBS, "copy_ceiling": round(copy_GBps, 1), "unit": "GB/s"}
-    for k in ("amax_w", "quant_w", "mxq_w", "amax_x", "quant_x", "mxq_x"):
+    # the HBM-bound kernels against the datasheet 8 TB/s and against the
+    # measured stream of the same mix over the same tensor
+    stream = {"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s", "ceilings": ceil}
+    for k, c in (("amax_w", "read_w"), ("quant_w", "r2w1_w"), ("mxq_w", "r2w1_w"),
+                 ("amax_x", "read_x"), ("quant_x", "r2w1_x"), ("mxq_x", "r2w1_x")):
         v = breakdown[k + "_GBps"]
         stream[k] = {"achieved": round(v, 1), "frac": round(v / PEAK_HBM_GBS, 4),
-                     "frac_of_copy": round(v / copy_GBps, 4)}
+                     "frac_of_ceiling": round(v / ceil[c + "_GBps"], 4), "ceiling": c}
 
     extras = None
     if not args.no_extras:
         extras = {"backward_7b_mlp": backward_extras(dev), "gemm_configs": gemm_configs(dev),
-                  "rmse_13b_mlp_up": rmse_c4(dev)}
+                  "delayed_7b_attn_16_steps": delayed_leg(dev), "rmse_13b_mlp_up": rmse_c4(dev)}
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(xb, wb, args.cpu_seconds)
-    sclk = gpu_sclk()
 
     out = {
         "metric": "scaled FP8 GEMM TFLOP/s + amax/quantize GB/s (per-tensor, MXFP8), 1 GPU",
@@ -445,7 +615,7 @@ def main():
         "dtype": "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "M": M, "N": N, "K": K, "x_dist": "N(0,1), 0.05% x100",
-                   "w_dist": "0.015 N(0,1)", "out": "bf16", "history_window": 16,
+                   "w_dist": "0.015 N(0,1)", "out": "bf16", "history_window": 16, "input_copies_rotated": R,
                    "step": "amax+bias+E4M3 cast (X,W), per-tensor GEMM+out amax, delayed-history push, "
                            "MX cast (X,W) to packed scales, MX GEMM (packed scales)+out amax"},
         "breakdown": {k: (round(v, 1) if isinstance(v, float) else v) for k, v in breakdown.items()},
@@ -454,7 +624,7 @@ def main():
         "cpu_baseline": cpu,
         "extras": extras,
         "input_generation_s": round(gen_s, 1),
-        "gpu_sclk": sclk,
+        "gpu_sclk": sclk.summary(),
     }
     print(json.dumps(out), flush=True)
 
