@@ -630,7 +630,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   const int nkb = 4 * nk;                           // 32-wide K blocks
   const int nkU = (nk + U - 1) / U * U;             // stages run per tile (zero stages past nk)
   const int ngroups = nkU / 4;                      // MX scale copies per tile
-  const int last_g = (nk - 1) >> 2;                 // last group holding real stages
   const bool pk = MX && g.scales_packed;            // tiled scale layout (uniform)
 
   auto make_tile = [&](int vb, TileSrd& T) {
@@ -683,9 +682,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
   // MX scales: lane L of wave w copies 16 bytes (the codes of 4 stages) of
-  // tile row 64 w + L of each operand.  Group G covers stages 4G .. 4G+3 and
-  // is read from byte min(16 G, nkb - 16) of the row, so the last, partial
-  // group never reads past the row's end (nkb >= 16 is required).
+  // tile row 64 w + L of each operand.  Group G covers stages 4G .. 4G+3:
+  // bytes 16 G .. 16 G + 15 of a row-major scale row (K % 512 == 0 there,
+  // so every group is whole) or the 4 KiB block G of the packed layout
+  // (padded with code 127 past the last block).
   // L2 prefetch of op(B) (the weight panel): every stage of a tile touches a
   // new K slice of it, and all XCDs walk the same panels in step, so its
   // copies are the ones that wait on HBM.  One workgroup per group of kGroupM
@@ -754,9 +754,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     if constexpr (MX) {
       const bool nx = G >= ngroups;
       // packed: group G is the 4 KiB block G of the tile (whole lines);
-      // row-major: bytes 16 G.. of each row, the last group clamped to end at
-      // the row's end
-      const uint32_t so = (uint32_t)(nx ? 0 : (pk ? G * kPackTile : (G < last_g ? 16 * G : nkb - 16)));
+      // row-major: bytes 16 G .. 16 G + 15 of each row
+      const uint32_t so = (uint32_t)(nx ? 0 : (pk ? G * kPackTile : 16 * G));
       const uint32_t la = ldss + (uint32_t)((((gbase + G) & 1) * 2 * BM + wave * 64) * 16);
       v4i sa = cur.sa, sb = cur.sb;
       if constexpr (PERSIST) {
@@ -771,28 +770,28 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
                   __builtin_amdgcn_readfirstlane(so));
     }
   };
-  // E8M0 codes of stage s (0 <= s <= nkU; nkU: the next tile's stage 0) for
-  // this lane: one dword per 32-row fragment holding the row's four block
-  // codes (sc[0..3]: op(A) fragments j, sc[4..7]: op(B) fragments i).
-  // Shifted right by 8 * (lane / 32) when the stage starts, byte 2h is the
-  // code of the block this lane's group scales in sub-step h (op_sel = 2h
-  // picks it); the shift is left until then so that no wait for these reads
-  // lands between the MFMAs.  Zero stages reuse stage nk-1's codes (finite
-  // codes times zero data, or a NaN code the row already carries).
-  auto read_scales = [&](int s, int (&sc)[8]) {
+  // E8M0 codes of one 4-stage group (16 per row) for this lane, two
+  // registers per 32-row fragment (sc[0..3]: op(A) fragments j, sc[4..7]:
+  // op(B) fragments i).  A 16-byte LDS read returns the row's 16 codes
+  // (dword d = stage d of the group, byte b = its 32-wide K block b); lane
+  // group g = lane / 32 scales K block 2h + g of sub-step h, so
+  // v_perm packs bytes g, 2 + g of dwords (0, 1) into the register of stages
+  // 0 and 1 and of dwords (2, 3) into that of stages 2 and 3: stage p,
+  // sub-step h takes byte 2 (p & 1) + h (op_sel) of register p >> 1.  Rows
+  // 16 bytes apart read as one contiguous span: no bank conflicts.
+  const uint32_t psel = (lane >> 5) ? 0x07050301u : 0x06040200u;
+  auto read_group = [&](int G, int (&lo)[8], int (&hi)[8], int j0, int j1) {
     if constexpr (MX) {
-      // selects only: a branch here would split the stage's basic block
-      const bool nx = s >= nkU;
-      const int kc = s < nk ? s : nk - 1;
-      const int G0 = kc >> 2;
-      const int d0 = (pk || G0 < last_g) ? (kc & 3) : kc - (nk - 4);  // dword of stage kc in its copy
-      const int G = nx ? ngroups : G0;
-      const int d = nx ? 0 : d0;
       const int gs = (gbase + G) & 1;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sc[j] = (int)s_scale[((gs * 2 * BM) + wm * 128 + j * 32 + (lane & 31)) * 4 + d];
-        sc[4 + j] = (int)s_scale[((gs * 2 + 1) * BM + wn * WN + (j % NI) * 32 + (lane & 31)) * 4 + d];
+      for (int j = j0; j < j1; ++j) {
+        const uint4 da = *reinterpret_cast<const uint4*>(&s_scale[((gs * 2) * BM + wm * 128 + j * 32 + (lane & 31)) * 4]);
+        const uint4 db = *reinterpret_cast<const uint4*>(
+            &s_scale[((gs * 2 + 1) * BM + wn * WN + (j % NI) * 32 + (lane & 31)) * 4]);
+        lo[j] = (int)__builtin_amdgcn_perm(da.y, da.x, psel);
+        hi[j] = (int)__builtin_amdgcn_perm(da.w, da.z, psel);
+        lo[4 + j] = (int)__builtin_amdgcn_perm(db.y, db.x, psel);
+        hi[4 + j] = (int)__builtin_amdgcn_perm(db.w, db.z, psel);
       }
     }
   };
@@ -823,30 +822,28 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   wait_vm<LPS + 1>();
   __syncthreads();
   v8i x0[4], w0[4], x1[4], w1[4];
-  int sc[2][8] = {};                                 // scales of the stages in slots 0 and 1
+  int sc[2][8] = {};                                 // scale registers of stages 0-1 and 2-3 of the group
+  int sc_next[8] = {};                               // the next group's stages 2-3, read with its 0-1
   x0[0] = frag_at<0 * kFrag>(smem, a0lo, a0hi); x0[1] = frag_at<1 * kFrag>(smem, a0lo, a0hi);
   x0[2] = frag_at<2 * kFrag>(smem, a0lo, a0hi); x0[3] = frag_at<3 * kFrag>(smem, a0lo, a0hi);
   w0[0] = frag_at<0 * kFrag>(smem, b0lo, b0hi); w0[1] = frag_at<1 * kFrag>(smem, b0lo, b0hi);
   if constexpr (NI == 4) {
     w0[2] = frag_at<2 * kFrag>(smem, b0lo, b0hi); w0[3] = frag_at<3 * kFrag>(smem, b0lo, b0hi);
   }
-  read_scales(0, sc[0]);
+  read_group(0, sc[0], sc[1], 0, 4);
 
   v16f acc[NI][4];
   // One stage in slot SLOT: phase A = sub-step 0 MFMAs (set 0) while reading
   // sub-step 1 (set 1); publish stage kt+1 (wait own DMA, barrier); phase B =
   // sub-step 1 MFMAs while reading stage kt+1's sub-step 0 (set 0) and
   // issuing stage kt+2's DMA into the slot stage kt released.
-  auto stage = [&](int kt, auto slot_c, auto scales_c) {
+  auto stage = [&](int kt, auto slot_c, auto scales_c, auto pos_c) {
     constexpr int SLOT = decltype(slot_c)::value;
     constexpr int NSL = 1 - SLOT;
     constexpr bool SCALES = decltype(scales_c)::value;  // issue the next scale group
-    int cs[8];
-    if constexpr (MX) {
-      const int sh = 8 * (lane >> 5);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) cs[k] = (int)((uint32_t)sc[SLOT][k] >> sh);
-    }
+    constexpr int POS = decltype(pos_c)::value;         // stage within the 4-stage scale group (MX)
+    constexpr int HB = POS >> 1;                        // scale register of this stage
+    constexpr int OS = 2 * (POS & 1);                   // op_sel of sub-step 0
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -864,7 +861,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (MX)
-        acc[i][j] = mfma32<FB, FA>(w0[i], x0[j], acc[i][j], cs[4 + i], 0, cs[j], 0);
+        acc[i][j] = mfma32<FB, FA>(w0[i], x0[j], acc[i][j], sc[HB][4 + i], OS, sc[HB][j], OS);
       else
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w0[i], x0[j], acc[i][j], FB, FA, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -876,7 +873,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     for (int t = 0; t < NT; ++t) {
       const int i = t >> 2, j = t & 3;
       {
-        if (t == (NT == 16 ? 8 : 6)) read_scales(kt + 1, sc[NSL]);
+        // the next group's codes at the group's third stage, after the last
+        // use of its first registers: stages 0-1 straight into them, stages
+        // 2-3 held until this group's last stage is done; one op(A) and one
+        // op(B) fragment per MFMA slot
+        constexpr int T0 = NT == 16 ? 8 : 4;
+        if constexpr (MX && POS == 2)
+          if (t >= T0 && t < T0 + 4) read_group((kt >> 2) + 1, sc[0], sc_next, t - T0, t - T0 + 1);
         switch (t) {
           case 0: x0[0] = frag_at<NSL * kSlot + 0 * kFrag>(smem, a0lo, a0hi); break;
           case 1: x0[1] = frag_at<NSL * kSlot + 1 * kFrag>(smem, a0lo, a0hi); break;
@@ -891,7 +894,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
       }
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (MX)
-        acc[i][j] = mfma32<FB, FA>(w1[i], x1[j], acc[i][j], cs[4 + i], 2, cs[j], 2);
+        acc[i][j] = mfma32<FB, FA>(w1[i], x1[j], acc[i][j], sc[HB][4 + i], OS + 1, sc[HB][j], OS + 1);
       else
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w1[i], x1[j], acc[i][j], FB, FA, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -926,11 +929,17 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     // group copy lands in a fixed stage).  The last two stages prefetch the
     // next tile's first two.
     for (int kt = 0; kt < nkU; kt += U) {
-      stage(kt, S0{}, std::bool_constant<MX>{});
-      stage(kt + 1, S1{}, std::false_type{});
+      using P0 = std::integral_constant<int, 0>;
+      using P1 = std::integral_constant<int, 1>;
+      using P2 = std::integral_constant<int, 2>;
+      using P3 = std::integral_constant<int, 3>;
+      stage(kt, S0{}, std::bool_constant<MX>{}, P0{});
+      stage(kt + 1, S1{}, std::false_type{}, P1{});
       if constexpr (MX) {
-        stage(kt + 2, S0{}, std::false_type{});
-        stage(kt + 3, S1{}, std::false_type{});
+        stage(kt + 2, S0{}, std::false_type{}, P2{});
+        stage(kt + 3, S1{}, std::false_type{}, P3{});
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sc[1][k] = sc_next[k];
       }
     }
 
@@ -1117,8 +1126,9 @@ static int device_cu_count() {
 template <int FA, int FB, bool MX, bool TA, bool TB>
 static void launch_gemm(const GemmArgs& g, hipStream_t s) {
   const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  // the forward kernel stages MX scales with dword copies: scale rows must be
-  // 4-byte aligned (always true for packed rows once K % 128 == 0); one tile
+  // the forward kernel copies MX scales 16 codes (4 stages) per row at a
+  // time: row-major scale rows must be 4-byte aligned with K % 512 == 0
+  // (whole groups; packed scales are padded to whole groups); one tile
   // per workgroup (or, with kFwdPersistent, per-tensor products walk tiles
   // with one workgroup per compute unit)
   if (!TA && !TB && g.K > 0 && (g.K % 128) == 0 && (!MX || g.scales_dma)) {
@@ -1263,7 +1273,7 @@ int mx_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int fmt_a,
   g.sa = A_scales; g.lds_a = lds_a; g.sb = B_scales; g.lds_b = lds_b;
   g.sa_dword = aligned(A_scales, 4) && (lds_a % 4) == 0;
   g.sb_dword = aligned(B_scales, 4) && (lds_b % 4) == 0;
-  g.scales_dma = g.sa_dword && g.sb_dword && (K % 128) == 0 && K >= 512 && lds_a < (1LL << 23) && lds_b < (1LL << 23);
+  g.scales_dma = g.sa_dword && g.sb_dword && (K % 512) == 0 && lds_a < (1LL << 23) && lds_b < (1LL << 23);
   g.scales_packed = 0; g.sgroups = 0;
   g.C = C; g.ldc = ldc; g.out_amax = out_amax;
   g.out_f32 = out_dtype == FP8_DT_F32;

@@ -242,9 +242,10 @@ def test_mx_gemm_ragged(fa, fb, out_dtype):
 @pytest.mark.parametrize("fa,fb", [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2), (E5M2, E5M2)],
                          ids=["e4e4", "e5e4", "e4e5", "e5e5"])
 def test_mx_gemm_k_multiple_of_128(fa, fb, K):
-    """K a multiple of 128 (stage counts 3, 5, 8, 9: below the 16-block
-    minimum of the grouped scale copies, a partial last group, whole groups)
-    with ragged M = 300, N = 260; scales passed twice:
+    """K a multiple of 128 (stage counts 3, 5, 8, 9) with ragged M = 300,
+    N = 260: on row-major scales K = 1024 runs the 32x32x64 kernel (whole
+    4-stage scale groups) and the others the 16x16x128 kernel; scales passed
+    twice:
     packed rows (K/32 bytes each, dword-aligned) and rows padded to an odd
     stride (K/32 + 1 bytes), which the kernel must read byte by byte."""
     xb = make("c4", "X", shape=(300, K))
