@@ -1215,6 +1215,9 @@ int fp8_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int fmt_a
   if (trans_a ? (lda < M || (M % 16) != 0) : (lda < K)) return FP8_ERR_SHAPE;
   if (trans_b ? (ldb < N || (N % 16) != 0) : (ldb < K)) return FP8_ERR_SHAPE;
   if (ldc < N) return FP8_ERR_SHAPE;
+  if (check_matrix(M, N, ldc) || (trans_a ? check_matrix(K, M, lda) : check_matrix(M, K, lda)) ||
+      (trans_b ? check_matrix(K, N, ldb) : check_matrix(N, K, ldb)))
+    return FP8_ERR_SHAPE;
   if (M > 0 && N > 0 && !C) return FP8_ERR_NULL;
   if (M > 0 && N > 0 && K > 0 && (!A || !B)) return FP8_ERR_NULL;
   if (M > 0 && N > 0 && K > 0) {
@@ -1254,6 +1257,9 @@ int mx_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int fmt_a,
   if (!valid_dtype(out_dtype)) return FP8_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0 || (K % 32) != 0) return FP8_ERR_SHAPE;
   if (lda < K || ldb < K || ldc < N || lds_a < K / 32 || lds_b < K / 32) return FP8_ERR_SHAPE;
+  if (check_matrix(M, N, ldc) || check_matrix(M, K, lda) || check_matrix(N, K, ldb) ||
+      check_matrix(M, K / 32, lds_a) || check_matrix(N, K / 32, lds_b))
+    return FP8_ERR_SHAPE;
   if (M > 0 && N > 0 && !C) return FP8_ERR_NULL;
   if (M > 0 && N > 0 && K > 0) {
     if (!A || !B || !A_scales || !B_scales) return FP8_ERR_NULL;
@@ -1287,8 +1293,8 @@ int mx_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int fmt_a,
 }
 
 int64_t mx_packed_scales_bytes(int64_t rows, int64_t kblocks) {
-  if (rows < 0 || kblocks < 0) return FP8_ERR_SHAPE;
-  return packed_bytes(rows, kblocks);
+  const int64_t b = packed_bytes_checked(rows, kblocks);
+  return b < 0 ? FP8_ERR_SHAPE : b;
 }
 
 int mx_pack_scales(const uint8_t* scales, int64_t rows, int64_t kblocks, int64_t ld_scales, uint8_t* packed,
@@ -1314,6 +1320,7 @@ int mx_scaled_gemm_packed(int64_t M, int64_t N, int64_t K, const uint8_t* A, int
   if (!valid_dtype(out_dtype)) return FP8_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0 || (K % 32) != 0) return FP8_ERR_SHAPE;
   if (lda < K || ldb < K || ldc < N) return FP8_ERR_SHAPE;
+  if (check_matrix(M, N, ldc) || check_matrix(M, K, lda) || check_matrix(N, K, ldb)) return FP8_ERR_SHAPE;
   if (M > 0 && N > 0 && !C) return FP8_ERR_NULL;
   if (M > 0 && N > 0) {
     if ((K % 128) != 0 || K < 512) return FP8_ERR_UNSUPPORTED;

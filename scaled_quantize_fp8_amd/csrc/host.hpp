@@ -15,11 +15,21 @@ inline bool valid_dtype(int d) { return d == FP8_DT_BF16 || d == FP8_DT_F32; }
 inline int dtype_size(int d) { return d == FP8_DT_BF16 ? 2 : 4; }
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// rows x cols matrix with leading dimension ld: sizes non-negative, ld >= cols
-// (ld is irrelevant when rows <= 1 but must still be >= cols if rows > 1).
+// Largest extent of one dimension or leading dimension, and largest element
+// span of one matrix: every size product the host code forms afterwards
+// (elements, bytes, tiles, scale blocks) then stays far inside int64.
+constexpr int64_t kMaxExtent = int64_t(1) << 40;
+constexpr int64_t kMaxSpan = int64_t(1) << 56;
+inline bool extent_ok(int64_t v) { return v >= 0 && v <= kMaxExtent; }
+
+// rows x cols matrix with leading dimension ld: sizes non-negative and within
+// kMaxExtent, ld >= cols (ld is irrelevant when rows <= 1 but must still be
+// >= cols if rows > 1), rows * max(ld, cols) within kMaxSpan.
 inline int check_matrix(int64_t rows, int64_t cols, int64_t ld) {
-  if (rows < 0 || cols < 0 || ld < 0) return FP8_ERR_SHAPE;
+  if (!extent_ok(rows) || !extent_ok(cols) || !extent_ok(ld)) return FP8_ERR_SHAPE;
   if (rows > 1 && ld < cols) return FP8_ERR_SHAPE;
+  int64_t span;
+  if (__builtin_mul_overflow(rows, ld > cols ? ld : cols, &span) || span > kMaxSpan) return FP8_ERR_SHAPE;
   return FP8_OK;
 }
 
@@ -44,6 +54,14 @@ constexpr int kPackRows = 256, kPackBlocks = 16, kPackTile = kPackRows * kPackBl
 inline int64_t packed_scale_groups(int64_t kb) { return (kb + kPackBlocks - 1) / kPackBlocks; }
 inline int64_t packed_bytes(int64_t rows, int64_t kb) {
   return ((rows + kPackRows - 1) / kPackRows) * packed_scale_groups(kb) * (int64_t)kPackTile;
+}
+// packed_bytes for caller-supplied sizes: -1 when they are out of range.
+inline int64_t packed_bytes_checked(int64_t rows, int64_t kb) {
+  if (!extent_ok(rows) || !extent_ok(kb)) return -1;
+  int64_t t;
+  if (__builtin_mul_overflow((rows + kPackRows - 1) / kPackRows, packed_scale_groups(kb), &t)) return -1;
+  if (__builtin_mul_overflow(t, (int64_t)kPackTile, &t) || t > kMaxSpan) return -1;
+  return t;
 }
 
 // Zero one float on `stream` with a tiny fill kernel (not hipMemsetAsync, so
