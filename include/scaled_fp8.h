@@ -80,7 +80,7 @@ enum {
 const char* fp8_status_string(int status);
 
 /* Library ABI version (increases when a signature changes or an entry point
- * is added): 3. */
+ * is added): 4. */
 int fp8_abi_version(void);
 
 /*
@@ -94,6 +94,33 @@ int fp8_abi_version(void);
  */
 int fp8_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
              float* amax_out, hipStream_t stream);
+
+/*
+ * fp8_amax_scale — current scaling in one launch: fp8_amax followed by
+ * fp8_compute_scale ("Proposed method": the bias comes from log2 of the ratio
+ * of the format maximum to the tensor's largest magnitude, with a margin),
+ * fused so that the scale is ready after a single pass over x.
+ *   x, dtype, rows, cols, ld   as fp8_amax;
+ *   fmt, margin                as fp8_compute_scale;
+ *   amax_out, bias_out         required, overwritten: exactly fp8_amax's amax
+ *                              and fp8_compute_scale's bias of it;
+ *   scale_out, scale_inv_out   optional (NULL = skip);
+ *   workspace                  FP8_AMAX_SCALE_WORKSPACE_BYTES of caller-owned
+ *                              device memory, 4-byte aligned.  Its first 4
+ *                              bytes (a ticket) must be ZERO before the first
+ *                              use and every call leaves them zero; the rest
+ *                              is overwritten by each call.  Calls sharing a
+ *                              workspace must not overlap (order them on one
+ *                              stream).
+ * One kernel: each workgroup reduces its share and stores a partial maximum
+ * in the workspace; the last workgroup reduces the partials and writes the
+ * outputs.  No zero-fill launch and no separate scale launch.
+ */
+#define FP8_AMAX_SCALE_WORKSPACE_BYTES 16384
+int fp8_amax_scale(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                   int fmt, int margin, float* amax_out, int32_t* bias_out,
+                   float* scale_out, float* scale_inv_out, void* workspace,
+                   hipStream_t stream);
 
 /*
  * fp8_compute_scale — exponent bias from an amax ("Proposed method": log2 of

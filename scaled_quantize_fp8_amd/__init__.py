@@ -22,7 +22,8 @@ import torch
 
 __all__ = [
     "E4M3", "E5M2", "load_library", "library_path", "Fp8Error",
-    "fp8_amax", "fp8_compute_scale", "fp8_history_init", "fp8_history_push",
+    "fp8_amax", "fp8_amax_scale", "amax_scale_workspace", "AMAX_SCALE_WORKSPACE_BYTES",
+    "fp8_compute_scale", "fp8_history_init", "fp8_history_push",
     "fp8_compute_scale_delayed", "fp8_quantize", "fp8_quantize_sat", "mx_quantize", "mx_quantize_t",
     "mx_quantize_rule", "mx_quantize_t_rule", "MX_RULE_FMAX", "MX_RULE_OCP",
     "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string", "fp8_abi_version",
@@ -37,6 +38,7 @@ _DT_F32 = 1
 _FMT_NAMES = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
 MX_RULE_FMAX = 0
 MX_RULE_OCP = 1
+AMAX_SCALE_WORKSPACE_BYTES = 16384     # FP8_AMAX_SCALE_WORKSPACE_BYTES
 _RULE_NAMES = {"fmax": MX_RULE_FMAX, "ocp": MX_RULE_OCP, MX_RULE_FMAX: MX_RULE_FMAX,
                MX_RULE_OCP: MX_RULE_OCP}
 
@@ -51,6 +53,7 @@ _SIGNATURES = {
     "fp8_status_string": ([_i], ctypes.c_char_p),
     "fp8_abi_version": ([], _i),
     "fp8_amax": ([_p, _i, _i64, _i64, _i64, _p, _p], _i),
+    "fp8_amax_scale": ([_p, _i, _i64, _i64, _i64, _i, _i, _p, _p, _p, _p, _p, _p], _i),
     "fp8_compute_scale": ([_p, _i, _i, _p, _p, _p, _p], _i),
     "fp8_history_init": ([_p, _p, _i, _p], _i),
     "fp8_history_push": ([_p, _p, _i, _p, _p], _i),
@@ -188,6 +191,50 @@ def fp8_amax(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
     _check("fp8_amax", load_library().fp8_amax(
         _ptr(x), _dtype_code(x, "x"), rows, cols, ld, _ptr(out), _stream(x)))
     return out
+
+
+def amax_scale_workspace(device) -> torch.Tensor:
+    """A zeroed workspace for fp8_amax_scale (FP8_AMAX_SCALE_WORKSPACE_BYTES);
+    each call leaves its ticket word zero again, so one per stream of calls
+    suffices."""
+    return torch.zeros(AMAX_SCALE_WORKSPACE_BYTES // 4, dtype=torch.int32, device=device)
+
+
+def _amax_scale_outputs(x, amax_out, bias_out, scale_out, scale_inv_out, want_scales):
+    if amax_out is None:
+        amax_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    if bias_out is None:
+        bias_out = torch.empty(1, dtype=torch.int32, device=x.device)
+    _scalar(amax_out, torch.float32, "amax_out")
+    _scalar(bias_out, torch.int32, "bias_out")
+    if want_scales:
+        if scale_out is None:
+            scale_out = torch.empty(1, dtype=torch.float32, device=x.device)
+        if scale_inv_out is None:
+            scale_inv_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    for t, n in ((scale_out, "scale_out"), (scale_inv_out, "scale_inv_out")):
+        if t is not None:
+            _scalar(t, torch.float32, n)
+    return amax_out, bias_out, scale_out, scale_inv_out
+
+
+def fp8_amax_scale(x: torch.Tensor, fmt, workspace: torch.Tensor, margin: int = 0, amax_out=None, bias_out=None,
+                   scale_out=None, scale_inv_out=None, want_scales: bool = False):
+    """Current scaling in one launch: amax of x and its bias (and optionally
+    2**bias, 2**-bias).  ``workspace``: a device tensor of at least
+    AMAX_SCALE_WORKSPACE_BYTES whose first word is zero (amax_scale_workspace);
+    each call leaves that word zero.  Returns
+    (amax, bias, scale or None, scale_inv or None)."""
+    rows, cols, ld = _mat(x, "x")
+    _dev(workspace, "workspace")
+    if workspace.numel() * workspace.element_size() < AMAX_SCALE_WORKSPACE_BYTES or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor of AMAX_SCALE_WORKSPACE_BYTES")
+    amax_out, bias_out, scale_out, scale_inv_out = _amax_scale_outputs(x, amax_out, bias_out, scale_out,
+                                                                       scale_inv_out, want_scales)
+    _check("fp8_amax_scale", load_library().fp8_amax_scale(
+        _ptr(x), _dtype_code(x, "x"), rows, cols, ld, _fmt(fmt), int(margin), _ptr(amax_out), _ptr(bias_out),
+        _ptr(scale_out), _ptr(scale_inv_out), _ptr(workspace), _stream(x)))
+    return amax_out, bias_out, scale_out, scale_inv_out
 
 
 def fp8_compute_scale(amax: torch.Tensor, fmt, margin: int = 0, bias_out=None,

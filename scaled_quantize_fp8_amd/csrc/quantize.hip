@@ -153,7 +153,52 @@ __device__ __forceinline__ void store_codes(uint8_t* qrow, int64_t chunk, uint2 
 // Streaming pass: rows are walked by gridDim.y, 16-byte chunks of a row by a
 // grid-stride loop over x with U (kUnroll, or kUnrollRead for the amax-only
 // pass) non-temporal loads in flight per lane.
-template <int DT, int FMT, bool VEC, bool WQ, bool AMAX, bool SAT>
+// End of the one-launch amax + scale pass: the workgroup's maximum becomes
+// its partial; the last workgroup to take a ticket reduces every partial and
+// writes amax, bias and scales (the bias rule of fp8_compute_scale), then
+// resets the ticket for the next launch.  Partials and ticket are accessed
+// with agent-scope atomics: workgroups on different XCDs see them coherently.
+__device__ __forceinline__ void amax_scale_finish(uint32_t v, uint32_t* red, const StreamArgs& a) {
+  __shared__ uint32_t s_last;
+  v = wave_max_u32(v);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int nw = (blockDim.x + kWave - 1) / kWave;
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  const uint32_t nblk = gridDim.x * gridDim.y;
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+    for (int i = 0; i < nw; ++i) m = m > red[i] ? m : red[i];
+    const uint32_t b = blockIdx.y * gridDim.x + blockIdx.x;
+    __hip_atomic_store(a.ws + 1 + b, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t t = __hip_atomic_fetch_add(a.ws, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = t == nblk - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  uint32_t m = 0;
+  for (uint32_t i = threadIdx.x; i < nblk; i += blockDim.x) {
+    const uint32_t p = __hip_atomic_load(a.ws + 1 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    m = m > p ? m : p;
+  }
+  m = wave_max_u32(m);
+  __syncthreads();                                  // red is reused
+  if (lane == 0) red[wid] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 0; i < nw; ++i) m = m > red[i] ? m : red[i];
+    *a.amax = __uint_as_float(m);
+    const int bias = bias_from_amax_bits(m, a.emax, a.margin, -126, 126);
+    *a.bias_out = bias;
+    if (a.scale_out) *a.scale_out = pow2f(bias);
+    if (a.scale_inv_out) *a.scale_inv_out = pow2f(-bias);
+    __hip_atomic_store(a.ws, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int DT, int FMT, bool VEC, bool WQ, bool AMAX, bool SAT, bool SCALE = false>
 __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
   __shared__ uint32_t red[kThreads / kWave];
   __shared__ uint32_t red_sat[SAT ? kThreads / kWave : 1];
@@ -201,7 +246,8 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
       if (WQ) qr[i] = (uint8_t)cast_elem<FMT>(bits, e, SAT ? &nsat : nullptr);
     }
   }
-  if (AMAX) block_max_to_global(amax_bits, red, a.amax);
+  if (AMAX && !SCALE) block_max_to_global(amax_bits, red, a.amax);
+  if (SCALE) amax_scale_finish(amax_bits, red, a);
   if (SAT) block_sum_to_global(nsat, red_sat, a.sat);
 }
 
@@ -254,6 +300,34 @@ void launch_stream_pass(StreamArgs a, int dtype, int fmt, bool write_q, bool ama
     if (fmt == FP8_E4M3) launch_vec_mode<FP8_DT_F32, FP8_E4M3>(a, vec, write_q, amax, grid, stream);
     else launch_vec_mode<FP8_DT_F32, FP8_E5M2>(a, vec, write_q, amax, grid, stream);
   }
+}
+
+void launch_amax_scale(StreamArgs a, int dtype, hipStream_t stream) {
+  const int esz = dtype_size(dtype);
+  const int epc = 16 / esz;
+  if (a.rows > 1 && a.ld == a.cols) {              // contiguous matrix -> one long row
+    a.cols *= a.rows;
+    a.rows = 1;
+    a.ld = a.cols;
+  }
+  const bool vec = aligned(a.x, 16) && (a.rows == 1 || (a.ld * esz) % 16 == 0);
+  const int64_t units = vec ? (a.cols / epc) : a.cols;
+  unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? kUnrollRead * kItersRead : kItersRead));
+  if (gx > (unsigned)kAmaxScaleMaxBlocks) gx = kAmaxScaleMaxBlocks;
+  int64_t gy = a.rows < 1 ? 1 : a.rows;
+  if (gy > kAmaxScaleMaxBlocks / gx) gy = kAmaxScaleMaxBlocks / gx;
+  if (gy < 1) gy = 1;
+  const dim3 grid(gx, (unsigned)gy);
+#define SFP8_AS(DT, V) \
+  hipLaunchKernelGGL((stream_kernel<DT, FP8_E4M3, V, false, true, false, true>), grid, dim3(kThreads), 0, stream, a)
+  if (dtype == FP8_DT_BF16) {
+    if (vec) SFP8_AS(FP8_DT_BF16, true);
+    else SFP8_AS(FP8_DT_BF16, false);
+  } else {
+    if (vec) SFP8_AS(FP8_DT_F32, true);
+    else SFP8_AS(FP8_DT_F32, false);
+  }
+#undef SFP8_AS
 }
 
 // ---------------------------------------------------------------------------

@@ -9,12 +9,14 @@
 //
 // The amax reduction itself shares the streaming kernel of quantize.hip
 // (a pass that only reads); this file holds the scalar kernels and the
-// entry points fp8_amax, fp8_compute_scale, fp8_history_*.
+// entry points fp8_amax, fp8_amax_scale, fp8_compute_scale, fp8_history_*.
 #include "common.hpp"
 #include "host.hpp"
 #include "stream_kernels.hpp"
 
 namespace sfp8 {
+
+static_assert(kAmaxScaleStateBytes <= FP8_AMAX_SCALE_WORKSPACE_BYTES, "workspace holds the reduction state");
 
 __global__ void zero_float_kernel(float* p) { *p = 0.0f; }
 
@@ -108,7 +110,7 @@ const char* fp8_status_string(int status) {
   }
 }
 
-int fp8_abi_version(void) { return 3; }
+int fp8_abi_version(void) { return 4; }
 
 int fp8_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, float* amax_out,
              hipStream_t stream) {
@@ -132,6 +134,50 @@ int fp8_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, f
     launch_stream_pass(a, dtype, FP8_E4M3, /*write_q=*/false, /*amax=*/true, stream);
   }
   return launch_status();
+}
+
+// Checks and launch of fp8_amax_scale.
+static int amax_scale_impl(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, int margin,
+                           float* amax_out, int32_t* bias_out, float* scale_out, float* scale_inv_out,
+                           uint32_t* state, hipStream_t stream) {
+  StreamArgs a;
+  a.x = x;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.bias = nullptr;
+  a.q = nullptr;
+  a.ldq = 0;
+  a.amax = amax_out;
+  a.sat = nullptr;
+  a.ws = state;
+  a.emax = fmt == FP8_E4M3 ? 8 : 15;
+  a.margin = margin;
+  a.bias_out = bias_out;
+  a.scale_out = scale_out;
+  a.scale_inv_out = scale_inv_out;
+  launch_amax_scale(a, dtype, stream);
+  return launch_status();
+}
+
+static int amax_scale_check(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt,
+                            const float* amax_out, const int32_t* bias_out) {
+  if (!amax_out || !bias_out) return FP8_ERR_NULL;
+  if (!valid_dtype(dtype)) return FP8_ERR_DTYPE;
+  if (!valid_fmt(fmt)) return FP8_ERR_FORMAT;
+  if (int st = check_matrix(rows, cols, ld)) return st;
+  if (rows * cols > 0 && !x) return FP8_ERR_NULL;
+  return FP8_OK;
+}
+
+int fp8_amax_scale(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, int margin,
+                   float* amax_out, int32_t* bias_out, float* scale_out, float* scale_inv_out, void* workspace,
+                   hipStream_t stream) {
+  if (int st = amax_scale_check(x, dtype, rows, cols, ld, fmt, amax_out, bias_out)) return st;
+  if (!workspace) return FP8_ERR_NULL;
+  if (!aligned(workspace, 4)) return FP8_ERR_ALIGN;
+  return amax_scale_impl(x, dtype, rows, cols, ld, fmt, margin, amax_out, bias_out, scale_out, scale_inv_out,
+                         static_cast<uint32_t*>(workspace), stream);
 }
 
 int fp8_compute_scale(const float* amax, int fmt, int margin, int32_t* bias_out, float* scale_out,

@@ -56,6 +56,16 @@ void amax_and_scale() {
   expect("amax null x", fp8_amax(nullptr, FP8_DT_BF16, 4, 4, 4, F, S), FP8_ERR_NULL);
   expect("amax huge", fp8_amax(A16, FP8_DT_BF16, BIG, BIG, BIG, F, S), FP8_ERR_SHAPE);
   expect("amax huge rows", fp8_amax(A16, FP8_DT_BF16, HUGE_, 2, 2, F, S), FP8_ERR_SHAPE);
+  expect("amax_scale null workspace", fp8_amax_scale(A16, 0, 4, 4, 4, 0, 0, F, I, nullptr, nullptr, nullptr, S),
+         FP8_ERR_NULL);
+  expect("amax_scale null amax", fp8_amax_scale(A16, 0, 4, 4, 4, 0, 0, nullptr, I, nullptr, nullptr, A16, S),
+         FP8_ERR_NULL);
+  expect("amax_scale unaligned workspace", fp8_amax_scale(A16, 0, 4, 4, 4, 0, 0, F, I, nullptr, nullptr, A1, S),
+         FP8_ERR_ALIGN);
+  expect("amax_scale dtype", fp8_amax_scale(A16, 5, 4, 4, 4, 0, 0, F, I, nullptr, nullptr, A16, S), FP8_ERR_DTYPE);
+  expect("amax_scale format", fp8_amax_scale(A16, 0, 4, 4, 4, 7, 0, F, I, nullptr, nullptr, A16, S), FP8_ERR_FORMAT);
+  expect("amax_scale huge", fp8_amax_scale(A16, 0, BIG, BIG, BIG, 0, 0, F, I, nullptr, nullptr, A16, S),
+         FP8_ERR_SHAPE);
   expect("scale null amax", fp8_compute_scale(nullptr, FP8_E4M3, 0, I, nullptr, nullptr, S), FP8_ERR_NULL);
   expect("scale null bias", fp8_compute_scale(F, FP8_E4M3, 0, nullptr, nullptr, nullptr, S), FP8_ERR_NULL);
   expect("scale format", fp8_compute_scale(F, 2, 0, I, nullptr, nullptr, S), FP8_ERR_FORMAT);

@@ -38,7 +38,7 @@ def test_header_declares_the_boundary():
                  "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize", "mx_quantize_t",
                  "mx_quantize_rule", "mx_quantize_t_rule", "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string",
                  "fp8_abi_version", "mx_packed_scales_bytes", "mx_pack_scales", "mx_quantize_packed",
-                 "mx_quantize_t_packed", "mx_scaled_gemm_packed", "fp8_quantize_sat"]:
+                 "mx_quantize_t_packed", "mx_scaled_gemm_packed", "fp8_quantize_sat", "fp8_amax_scale"]:
         assert want in names
 
 
@@ -52,7 +52,7 @@ def test_status_strings(lib):
     for code in (NULL, SHAPE, ALIGN, DTYPE, FORMAT, LAUNCH, UNSUP):
         assert sq.fp8_status_string(code) not in ("ok", "unknown status")
     assert sq.fp8_status_string(-99) == "unknown status"
-    assert sq.fp8_abi_version() >= 3
+    assert sq.fp8_abi_version() >= 4
 
 
 def test_amax_validation(lib):
@@ -61,6 +61,19 @@ def test_amax_validation(lib):
     assert lib.fp8_amax(FAKE, 0, 4, 8, 4, FAKE, S) == SHAPE          # ld < cols
     assert lib.fp8_amax(FAKE, 0, -1, 8, 8, FAKE, S) == SHAPE
     assert lib.fp8_amax(None, 0, 4, 4, 4, FAKE, S) == NULL
+
+
+def test_amax_scale_validation(lib):
+    a = lib.fp8_amax_scale
+    # x, dtype, rows, cols, ld, fmt, margin, amax, bias, scale, scale_inv, workspace, stream
+    assert a(FAKE, 0, 4, 4, 4, 0, 0, FAKE, FAKE, None, None, None, S) == NULL       # workspace
+    assert a(FAKE, 0, 4, 4, 4, 0, 0, None, FAKE, None, None, FAKE, S) == NULL       # amax
+    assert a(FAKE, 0, 4, 4, 4, 0, 0, FAKE, None, None, None, FAKE, S) == NULL       # bias
+    assert a(FAKE, 0, 4, 4, 4, 0, 0, FAKE, FAKE, None, None, FAKE + 2, S) == ALIGN
+    assert a(FAKE, 9, 4, 4, 4, 0, 0, FAKE, FAKE, None, None, FAKE, S) == DTYPE
+    assert a(FAKE, 0, 4, 4, 4, 3, 0, FAKE, FAKE, None, None, FAKE, S) == FORMAT
+    assert a(FAKE, 0, 4, 8, 4, 0, 0, FAKE, FAKE, None, None, FAKE, S) == SHAPE
+    assert a(None, 0, 4, 4, 4, 0, 0, FAKE, FAKE, None, None, FAKE, S) == NULL
 
 
 def test_scale_and_history_validation(lib):

@@ -461,3 +461,69 @@ def test_saturation_count_every_cast_path(path):
         # without the fused amax, at a bias that clamps only the infinities
         _, _, _, n0 = sq.fp8_quantize_sat(x, fmt.code, i32_dev(b - 12), transpose=transpose)
         assert int(host(n0)[0]) == _oracle_sat_count(vals, fmt, b - 12)
+
+
+def _two_step(x, fmt, margin):
+    a = sq.fp8_amax(x)
+    b, s, si = sq.fp8_compute_scale(a, fmt, margin)
+    return a, b, s, si
+
+
+def _same_outputs(one, two, what):
+    a1, b1, s1, si1 = one
+    a2, b2, s2, si2 = two
+    assert f32_bits_of(a1) == f32_bits_of(a2), what
+    assert int(host(b1)[0]) == int(host(b2)[0]), what
+    assert f32_bits_of(s1) == f32_bits_of(s2) and f32_bits_of(si1) == f32_bits_of(si2), what
+
+
+def test_amax_scale_one_launch_equals_two_step():
+    """fp8_amax_scale (one launch: amax reduced across workgroups through a
+    ticket in the workspace, bias and scales written by the last workgroup)
+    gives exactly fp8_amax + fp8_compute_scale, and the oracle's amax and
+    bias, on: every bf16 pattern (NaN: bias 0), every finite one, fp32 with
+    Inf, a strided unaligned view (element loads), one ragged row, an empty
+    tensor, E5M2 and margins; the workspace's ticket word is back to zero
+    after every call (the partial maxima are overwritten by each call)."""
+    ws = sq.amax_scale_workspace(DEV)
+    rng = np.random.default_rng(51)
+    bits = all_bf16_patterns()
+    finite = bits[np.isfinite(oracle.bf16_bits_to_f64(bits))]
+    f32 = (rng.standard_normal((130, 257)) * 1e3).astype(np.float32)
+    f32[7, 9] = np.inf
+    strided = f32_to_bf16_bits((rng.standard_normal((77, 300)) * 5).astype(np.float32))
+    cases = [("all bf16", bf16_dev(bits.reshape(256, 256)), oracle.bf16_bits_to_f64(bits)),
+             ("finite bf16", bf16_dev(finite.reshape(1, -1)), oracle.bf16_bits_to_f64(finite)),
+             ("f32 with inf", f32_dev(f32), f32.astype(np.float64)),
+             ("strided view", bf16_dev(strided)[1:, 3:291], oracle.bf16_bits_to_f64(strided)[1:, 3:291]),
+             ("one ragged row", bf16_dev(strided[:1, :77]), oracle.bf16_bits_to_f64(strided[:1, :77])),
+             ("empty", torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV), np.zeros((0, 64)))]
+    for name, x, vals in cases:
+        for fmt in FMTS:
+            for margin in (0, 2):
+                one = sq.fp8_amax_scale(x, fmt.code, ws, margin, want_scales=True)
+                _same_outputs(one, _two_step(x, fmt.code, margin), f"{name} {fmt.name} margin {margin}")
+                ra = oracle.amax(vals) if vals.size else 0.0
+                got = host(one[0])[0]
+                assert (np.isnan(got) and np.isnan(ra)) or got == ra
+                assert int(host(one[1])[0]) == oracle.compute_bias(ra, fmt, margin)
+                assert int(host(ws[:1])[0]) == 0, f"ticket not reset after {name}"
+
+
+@pytest.mark.parametrize("shape", [(16384, 8192), (28672, 8192), (24576, 32768)],
+                         ids=["70b_mlp_x", "70b_mlp_w", "805M_elements"])
+def test_amax_scale_full_size(shape):
+    """The 70B-MLP X and W (1024 and 1792 workgroups) and a tensor of 805M
+    elements, whose grid is capped at 2048 workgroups striding over it: the
+    one-launch amax and bias equal the two-step ones, repeated calls agree,
+    and the workspace's ticket is back to zero."""
+    g = torch.Generator(device=DEV).manual_seed(shape[0])
+    x = torch.randn(shape, device=DEV, dtype=torch.bfloat16, generator=g)
+    x.view(-1)[shape[0] * 77] = 99.5                    # one outlier far into the tensor
+    ws = sq.amax_scale_workspace(DEV)
+    say(f"amax_scale full size {shape}")
+    ref = _two_step(x, E4M3.code, 0)
+    for _ in range(3):
+        _same_outputs(sq.fp8_amax_scale(x, E4M3.code, ws, want_scales=True), ref, f"{shape}")
+    assert host(ref[0])[0] == 99.5
+    assert int(host(ws[:1])[0]) == 0
