@@ -123,6 +123,24 @@ int fp8_amax_scale(const void* x, int dtype, int64_t rows, int64_t cols, int64_t
                    hipStream_t stream);
 
 /*
+ * fp8_amax_scale_noalloc — fp8_amax_scale without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops).  The reduction state lives in a static array of
+ * FP8_AMAX_SCALE_WORKSPACE_BYTES inside the library, one copy per GPU, held
+ * until the process ends; it is cleared the first time a GPU uses it (a small
+ * kernel on `stream`) and every call leaves its ticket word zero again.  Every call on one GPU
+ * shares that array: calls that overlap on the same GPU (different streams,
+ * host threads) race and give wrong results; order them.  The state does not
+ * grow with the tensor (at most 2048 workgroups stride over any size), so no
+ * input is too large for it; arguments and results are those of
+ * fp8_amax_scale.  Allocates nothing (no hipMalloc, no library allocation);
+ * FP8_ERR_LAUNCH if the array's device address cannot be obtained.
+ */
+int fp8_amax_scale_noalloc(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                           int fmt, int margin, float* amax_out, int32_t* bias_out,
+                           float* scale_out, float* scale_inv_out, hipStream_t stream);
+
+/*
  * fp8_compute_scale — exponent bias from an amax ("Proposed method": log2 of
  * the ratio of the format maximum to the tensor amplitude, with a margin).
  *   amax      one float (device), e.g. from fp8_amax.

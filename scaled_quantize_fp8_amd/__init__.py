@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "E4M3", "E5M2", "load_library", "library_path", "Fp8Error",
-    "fp8_amax", "fp8_amax_scale", "amax_scale_workspace", "AMAX_SCALE_WORKSPACE_BYTES",
+    "fp8_amax", "fp8_amax_scale", "fp8_amax_scale_noalloc", "amax_scale_workspace", "AMAX_SCALE_WORKSPACE_BYTES",
     "fp8_compute_scale", "fp8_history_init", "fp8_history_push",
     "fp8_compute_scale_delayed", "fp8_quantize", "fp8_quantize_sat", "mx_quantize", "mx_quantize_t",
     "mx_quantize_rule", "mx_quantize_t_rule", "MX_RULE_FMAX", "MX_RULE_OCP",
@@ -54,6 +54,7 @@ _SIGNATURES = {
     "fp8_abi_version": ([], _i),
     "fp8_amax": ([_p, _i, _i64, _i64, _i64, _p, _p], _i),
     "fp8_amax_scale": ([_p, _i, _i64, _i64, _i64, _i, _i, _p, _p, _p, _p, _p, _p], _i),
+    "fp8_amax_scale_noalloc": ([_p, _i, _i64, _i64, _i64, _i, _i, _p, _p, _p, _p, _p], _i),
     "fp8_compute_scale": ([_p, _i, _i, _p, _p, _p, _p], _i),
     "fp8_history_init": ([_p, _p, _i, _p], _i),
     "fp8_history_push": ([_p, _p, _i, _p, _p], _i),
@@ -234,6 +235,20 @@ def fp8_amax_scale(x: torch.Tensor, fmt, workspace: torch.Tensor, margin: int = 
     _check("fp8_amax_scale", load_library().fp8_amax_scale(
         _ptr(x), _dtype_code(x, "x"), rows, cols, ld, _fmt(fmt), int(margin), _ptr(amax_out), _ptr(bias_out),
         _ptr(scale_out), _ptr(scale_inv_out), _ptr(workspace), _stream(x)))
+    return amax_out, bias_out, scale_out, scale_inv_out
+
+
+def fp8_amax_scale_noalloc(x: torch.Tensor, fmt, margin: int = 0, amax_out=None, bias_out=None, scale_out=None,
+                           scale_inv_out=None, want_scales: bool = False):
+    """fp8_amax_scale with the reduction state in the library's own per-GPU
+    array (the C entry point allocates nothing; calls that overlap on one GPU
+    race).  Returns (amax, bias, scale or None, scale_inv or None)."""
+    rows, cols, ld = _mat(x, "x")
+    amax_out, bias_out, scale_out, scale_inv_out = _amax_scale_outputs(x, amax_out, bias_out, scale_out,
+                                                                       scale_inv_out, want_scales)
+    _check("fp8_amax_scale_noalloc", load_library().fp8_amax_scale_noalloc(
+        _ptr(x), _dtype_code(x, "x"), rows, cols, ld, _fmt(fmt), int(margin), _ptr(amax_out), _ptr(bias_out),
+        _ptr(scale_out), _ptr(scale_inv_out), _stream(x)))
     return amax_out, bias_out, scale_out, scale_inv_out
 
 

@@ -9,7 +9,10 @@
 //
 // The amax reduction itself shares the streaming kernel of quantize.hip
 // (a pass that only reads); this file holds the scalar kernels and the
-// entry points fp8_amax, fp8_amax_scale, fp8_compute_scale, fp8_history_*.
+// entry points fp8_amax, fp8_amax_scale(_noalloc), fp8_compute_scale,
+// fp8_history_*.
+#include <mutex>
+
 #include "common.hpp"
 #include "host.hpp"
 #include "stream_kernels.hpp"
@@ -17,6 +20,35 @@
 namespace sfp8 {
 
 static_assert(kAmaxScaleStateBytes <= FP8_AMAX_SCALE_WORKSPACE_BYTES, "workspace holds the reduction state");
+
+// Reduction state of fp8_amax_scale_noalloc: one copy per GPU, zeroed once
+// when the library first uses it on that GPU; every call leaves its ticket
+// word (the only one that must start at zero) zero again.
+constexpr int kScratchWords = FP8_AMAX_SCALE_WORKSPACE_BYTES / 4;
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+__global__ void zero_u32_kernel(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+// Device address of `scratch` on the current GPU (the host-side name is only
+// a stand-in): looked up once per device with hipGetSymbolAddress, the array
+// cleared on `stream` the first time; nullptr when the lookup fails.
+static uint32_t* scratch_on_current_device(hipStream_t stream) {
+  static std::mutex mu;
+  static uint32_t* ptr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(256), 0, stream, static_cast<uint32_t*>(p), kScratchWords);
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    ptr[dev] = static_cast<uint32_t*>(p);
+  }
+  return ptr[dev];
+}
 
 __global__ void zero_float_kernel(float* p) { *p = 0.0f; }
 
@@ -136,7 +168,7 @@ int fp8_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, f
   return launch_status();
 }
 
-// Checks and launch of fp8_amax_scale.
+// Checks and launch of fp8_amax_scale and fp8_amax_scale_noalloc.
 static int amax_scale_impl(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, int margin,
                            float* amax_out, int32_t* bias_out, float* scale_out, float* scale_inv_out,
                            uint32_t* state, hipStream_t stream) {
@@ -178,6 +210,16 @@ int fp8_amax_scale(const void* x, int dtype, int64_t rows, int64_t cols, int64_t
   if (!aligned(workspace, 4)) return FP8_ERR_ALIGN;
   return amax_scale_impl(x, dtype, rows, cols, ld, fmt, margin, amax_out, bias_out, scale_out, scale_inv_out,
                          static_cast<uint32_t*>(workspace), stream);
+}
+
+int fp8_amax_scale_noalloc(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, int margin,
+                           float* amax_out, int32_t* bias_out, float* scale_out, float* scale_inv_out,
+                           hipStream_t stream) {
+  if (int st = amax_scale_check(x, dtype, rows, cols, ld, fmt, amax_out, bias_out)) return st;
+  uint32_t* state = scratch_on_current_device(stream);
+  if (!state) return FP8_ERR_LAUNCH;
+  return amax_scale_impl(x, dtype, rows, cols, ld, fmt, margin, amax_out, bias_out, scale_out, scale_inv_out, state,
+                         stream);
 }
 
 int fp8_compute_scale(const float* amax, int fmt, int margin, int32_t* bias_out, float* scale_out,

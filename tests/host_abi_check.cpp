@@ -66,6 +66,12 @@ void amax_and_scale() {
   expect("amax_scale format", fp8_amax_scale(A16, 0, 4, 4, 4, 7, 0, F, I, nullptr, nullptr, A16, S), FP8_ERR_FORMAT);
   expect("amax_scale huge", fp8_amax_scale(A16, 0, BIG, BIG, BIG, 0, 0, F, I, nullptr, nullptr, A16, S),
          FP8_ERR_SHAPE);
+  expect("amax_scale_noalloc null bias", fp8_amax_scale_noalloc(A16, 0, 4, 4, 4, 0, 0, F, nullptr, nullptr, nullptr, S),
+         FP8_ERR_NULL);
+  expect("amax_scale_noalloc dtype", fp8_amax_scale_noalloc(A16, 4, 4, 4, 4, 0, 0, F, I, nullptr, nullptr, S),
+         FP8_ERR_DTYPE);
+  expect("amax_scale_noalloc huge", fp8_amax_scale_noalloc(A16, 0, BIG, BIG, BIG, 0, 0, F, I, nullptr, nullptr, S),
+         FP8_ERR_SHAPE);
   expect("scale null amax", fp8_compute_scale(nullptr, FP8_E4M3, 0, I, nullptr, nullptr, S), FP8_ERR_NULL);
   expect("scale null bias", fp8_compute_scale(F, FP8_E4M3, 0, nullptr, nullptr, nullptr, S), FP8_ERR_NULL);
   expect("scale format", fp8_compute_scale(F, 2, 0, I, nullptr, nullptr, S), FP8_ERR_FORMAT);

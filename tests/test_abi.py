@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
                  "fp8_compute_scale_delayed", "fp8_quantize", "mx_quantize", "mx_quantize_t",
                  "mx_quantize_rule", "mx_quantize_t_rule", "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string",
                  "fp8_abi_version", "mx_packed_scales_bytes", "mx_pack_scales", "mx_quantize_packed",
-                 "mx_quantize_t_packed", "mx_scaled_gemm_packed", "fp8_quantize_sat", "fp8_amax_scale"]:
+                 "mx_quantize_t_packed", "mx_scaled_gemm_packed", "fp8_quantize_sat", "fp8_amax_scale",
+                 "fp8_amax_scale_noalloc"]:
         assert want in names
 
 
@@ -74,6 +75,13 @@ def test_amax_scale_validation(lib):
     assert a(FAKE, 0, 4, 4, 4, 3, 0, FAKE, FAKE, None, None, FAKE, S) == FORMAT
     assert a(FAKE, 0, 4, 8, 4, 0, 0, FAKE, FAKE, None, None, FAKE, S) == SHAPE
     assert a(None, 0, 4, 4, 4, 0, 0, FAKE, FAKE, None, None, FAKE, S) == NULL
+    n = lib.fp8_amax_scale_noalloc          # rejected before the scratch lookup (no HIP call)
+    assert n(FAKE, 0, 4, 4, 4, 0, 0, None, FAKE, None, None, S) == NULL
+    assert n(FAKE, 0, 4, 4, 4, 0, 0, FAKE, None, None, None, S) == NULL
+    assert n(FAKE, 9, 4, 4, 4, 0, 0, FAKE, FAKE, None, None, S) == DTYPE
+    assert n(FAKE, 0, 4, 4, 4, 3, 0, FAKE, FAKE, None, None, S) == FORMAT
+    assert n(FAKE, 0, 4, 8, 4, 0, 0, FAKE, FAKE, None, None, S) == SHAPE
+    assert n(None, 0, 4, 4, 4, 0, 0, FAKE, FAKE, None, None, S) == NULL
 
 
 def test_scale_and_history_validation(lib):
