@@ -106,17 +106,18 @@ int fp8_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
  *                              and fp8_compute_scale's bias of it;
  *   scale_out, scale_inv_out   optional (NULL = skip);
  *   workspace                  FP8_AMAX_SCALE_WORKSPACE_BYTES of caller-owned
- *                              device memory, 4-byte aligned.  Its first 4
- *                              bytes (a ticket) must be ZERO before the first
- *                              use and every call leaves them zero; the rest
- *                              is overwritten by each call.  Calls sharing a
+ *                              device memory, 4-byte aligned, ZERO before the
+ *                              first use; every call leaves it zero again (its
+ *                              first 8 bytes hold a ticket and a running
+ *                              maximum during the call).  Calls sharing a
  *                              workspace must not overlap (order them on one
  *                              stream).
- * One kernel: each workgroup reduces its share and stores a partial maximum
- * in the workspace; the last workgroup reduces the partials and writes the
- * outputs.  No zero-fill launch and no separate scale launch.
+ * One kernel: each workgroup reduces its share, folds it into the running
+ * maximum with an atomic max and takes a ticket; the workgroup that takes the
+ * last ticket writes the outputs and clears the workspace.  No zero-fill
+ * launch and no separate scale launch; the state is the same for any size.
  */
-#define FP8_AMAX_SCALE_WORKSPACE_BYTES 16384
+#define FP8_AMAX_SCALE_WORKSPACE_BYTES 256
 int fp8_amax_scale(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
                    int fmt, int margin, float* amax_out, int32_t* bias_out,
                    float* scale_out, float* scale_inv_out, void* workspace,
@@ -128,10 +129,10 @@ int fp8_amax_scale(const void* x, int dtype, int64_t rows, int64_t cols, int64_t
  * tight serving loops).  The reduction state lives in a static array of
  * FP8_AMAX_SCALE_WORKSPACE_BYTES inside the library, one copy per GPU, held
  * until the process ends; it is cleared the first time a GPU uses it (a small
- * kernel on `stream`) and every call leaves its ticket word zero again.  Every call on one GPU
- * shares that array: calls that overlap on the same GPU (different streams,
- * host threads) race and give wrong results; order them.  The state does not
- * grow with the tensor (at most 2048 workgroups stride over any size), so no
+ * kernel on `stream`) and every call leaves it zero again.  Every call on one
+ * GPU shares that array: calls that overlap on the same GPU (different
+ * streams, host threads) race and give wrong results; order them.  The state
+ * does not grow with the tensor (a ticket and a running maximum), so no
  * input is too large for it; arguments and results are those of
  * fp8_amax_scale.  Allocates nothing (no hipMalloc, no library allocation);
  * FP8_ERR_LAUNCH if the array's device address cannot be obtained.

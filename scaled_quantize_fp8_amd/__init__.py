@@ -38,7 +38,7 @@ _DT_F32 = 1
 _FMT_NAMES = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
 MX_RULE_FMAX = 0
 MX_RULE_OCP = 1
-AMAX_SCALE_WORKSPACE_BYTES = 16384     # FP8_AMAX_SCALE_WORKSPACE_BYTES
+AMAX_SCALE_WORKSPACE_BYTES = 256       # FP8_AMAX_SCALE_WORKSPACE_BYTES
 _RULE_NAMES = {"fmax": MX_RULE_FMAX, "ocp": MX_RULE_OCP, MX_RULE_FMAX: MX_RULE_FMAX,
                MX_RULE_OCP: MX_RULE_OCP}
 
@@ -196,8 +196,7 @@ def fp8_amax(x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
 
 def amax_scale_workspace(device) -> torch.Tensor:
     """A zeroed workspace for fp8_amax_scale (FP8_AMAX_SCALE_WORKSPACE_BYTES);
-    each call leaves its ticket word zero again, so one per stream of calls
-    suffices."""
+    each call leaves it zero again, so one per stream of calls suffices."""
     return torch.zeros(AMAX_SCALE_WORKSPACE_BYTES // 4, dtype=torch.int32, device=device)
 
 
@@ -223,8 +222,8 @@ def fp8_amax_scale(x: torch.Tensor, fmt, workspace: torch.Tensor, margin: int = 
                    scale_out=None, scale_inv_out=None, want_scales: bool = False):
     """Current scaling in one launch: amax of x and its bias (and optionally
     2**bias, 2**-bias).  ``workspace``: a device tensor of at least
-    AMAX_SCALE_WORKSPACE_BYTES whose first word is zero (amax_scale_workspace);
-    each call leaves that word zero.  Returns
+    AMAX_SCALE_WORKSPACE_BYTES, zero before the first use
+    (amax_scale_workspace); each call leaves it zero.  Returns
     (amax, bias, scale or None, scale_inv or None)."""
     rows, cols, ld = _mat(x, "x")
     _dev(workspace, "workspace")

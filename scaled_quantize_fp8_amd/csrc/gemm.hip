@@ -356,7 +356,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
   }
 
   // ---- epilogue: unscale, round, store, fused |C| max ----------------------
-  const int e = MX ? 0 : -(*g.bias_a + *g.bias_b);
+  // (for MX the exponent is 0, hidden from the compiler as in gemm_fwd_kernel)
+  int e = MX ? 0 : -(*g.bias_a + *g.bias_b);
+  if constexpr (MX) asm volatile("" : "+s"(e));
   uint32_t amax_bits = 0;
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) {
@@ -367,7 +369,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
       if (m >= g.M) continue;
       float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = MX ? acc[nb][mb][r] : __builtin_amdgcn_ldexpf(acc[nb][mb][r], e);
+      for (int r = 0; r < 4; ++r) v[r] = __builtin_amdgcn_ldexpf(acc[nb][mb][r], e);
       if (g.out_f32) {
         float* crow = reinterpret_cast<float*>(g.C) + m * g.ldc;
         if (g.vec_store && n + 3 < g.N) {
@@ -915,7 +917,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // halves x 4 row groups; fp32: 4 x NI x 4), the ops issued after the last
   // copy of a workgroup's last tile; the final wait leaves them in flight.
   constexpr int kEpiStores = 4 * (NI / 2) * 4;
-  const int e = MX ? 0 : -(*g.bias_a + *g.bias_b);
+  // Output exponent: -(bias_a + bias_b), or 0 for MX (block scales are
+  // applied inside the MFMA), applied to every accumulator by ldexp (exact at
+  // 0).  For MX the 0 is hidden from the compiler: with the plain
+  // accumulators as epilogue values it copied all 256 of them out of the
+  // accumulation registers ahead of the interior/edge branch and spilled.
+  int e = MX ? 0 : -(*g.bias_a + *g.bias_b);
+  if constexpr (MX) asm volatile("" : "+s"(e));
   uint32_t amax_bits = 0;
   for (;;) {
 #pragma unroll
@@ -973,7 +981,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
               float v[4];
 #pragma unroll
               for (int r = 0; r < 4; ++r)
-                v[r] = MX ? acc[i][j][4 * q + r] : __builtin_amdgcn_ldexpf(acc[i][j][4 * q + r], e);
+                v[r] = __builtin_amdgcn_ldexpf(acc[i][j][4 * q + r], e);
               *reinterpret_cast<float4*>(crow + i * 32 + 8 * q) = make_float4(v[0], v[1], v[2], v[3]);
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
@@ -1012,7 +1020,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
                 float v[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                  v[r] = MX ? acc[i][j][4 * q + r] : __builtin_amdgcn_ldexpf(acc[i][j][4 * q + r], e);
+                  v[r] = __builtin_amdgcn_ldexpf(acc[i][j][4 * q + r], e);
                 const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
                 *reinterpret_cast<uint2*>(stg + wbase + 16 * ((uint32_t)(4 * ii + q) ^ wsw)) = make_uint2(lo, hi);
                 pmax = __builtin_elementwise_max(pmax, __builtin_bit_cast(us2v, lo & 0x7fff7fffu));
@@ -1042,7 +1050,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
             const int64_t n = n0 + wn * WN + i * 32 + 8 * q + 4 * (lane >> 5);
             float v[4];
     #pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = MX ? acc[i][j][4 * q + r] : __builtin_amdgcn_ldexpf(acc[i][j][4 * q + r], e);
+            for (int r = 0; r < 4; ++r) v[r] = __builtin_amdgcn_ldexpf(acc[i][j][4 * q + r], e);
             if (g.out_f32) {
               float* crow = reinterpret_cast<float*>(g.C) + m * g.ldc;
               if (g.vec_store && n + 3 < g.N) {

@@ -153,11 +153,18 @@ __device__ __forceinline__ void store_codes(uint8_t* qrow, int64_t chunk, uint2 
 // Streaming pass: rows are walked by gridDim.y, 16-byte chunks of a row by a
 // grid-stride loop over x with U (kUnroll, or kUnrollRead for the amax-only
 // pass) non-temporal loads in flight per lane.
-// End of the one-launch amax + scale pass: the workgroup's maximum becomes
-// its partial; the last workgroup to take a ticket reduces every partial and
-// writes amax, bias and scales (the bias rule of fp8_compute_scale), then
-// resets the ticket for the next launch.  Partials and ticket are accessed
-// with agent-scope atomics: workgroups on different XCDs see them coherently.
+// End of the one-launch amax + scale pass.  Thread 0 of each workgroup folds
+// the workgroup's maximum into the running maximum ws[1] with a returning
+// agent-scope atomic max, then takes a ticket ws[0]; the workgroup that takes
+// the last ticket swaps the running maximum for zero and writes amax, bias and
+// scales (the bias rule of fp8_compute_scale), then resets the ticket.
+// Ordering without fences: the ticket's increment depends on the value the max
+// returned, so it is issued only after that max has been performed at the
+// word's coherence point; the last ticket thus follows every workgroup's max,
+// and the final swap, issued after it, reads their combined result.  (An
+// agent-scope release/acquire here costs an L2 write-back and invalidate per
+// workgroup, which nearly doubled the pass.)  Increment: old <= 0x7fffffff
+// (sign bits are cleared), so it is always 1.
 __device__ __forceinline__ void amax_scale_finish(uint32_t v, uint32_t* red, const StreamArgs& a) {
   __shared__ uint32_t s_last;
   v = wave_max_u32(v);
@@ -170,25 +177,14 @@ __device__ __forceinline__ void amax_scale_finish(uint32_t v, uint32_t* red, con
   if (threadIdx.x == 0) {
     uint32_t m = 0;
     for (int i = 0; i < nw; ++i) m = m > red[i] ? m : red[i];
-    const uint32_t b = blockIdx.y * gridDim.x + blockIdx.x;
-    __hip_atomic_store(a.ws + 1 + b, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t t = __hip_atomic_fetch_add(a.ws, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_max(a.ws + 1, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t t = __hip_atomic_fetch_add(a.ws, 1u + (old >> 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = t == nblk - 1;
   }
   __syncthreads();
   if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  uint32_t m = 0;
-  for (uint32_t i = threadIdx.x; i < nblk; i += blockDim.x) {
-    const uint32_t p = __hip_atomic_load(a.ws + 1 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    m = m > p ? m : p;
-  }
-  m = wave_max_u32(m);
-  __syncthreads();                                  // red is reused
-  if (lane == 0) red[wid] = m;
-  __syncthreads();
   if (threadIdx.x == 0) {
-    for (int i = 0; i < nw; ++i) m = m > red[i] ? m : red[i];
+    const uint32_t m = __hip_atomic_exchange(a.ws + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *a.amax = __uint_as_float(m);
     const int bias = bias_from_amax_bits(m, a.emax, a.margin, -126, 126);
     *a.bias_out = bias;
@@ -312,12 +308,12 @@ void launch_amax_scale(StreamArgs a, int dtype, hipStream_t stream) {
   }
   const bool vec = aligned(a.x, 16) && (a.rows == 1 || (a.ld * esz) % 16 == 0);
   const int64_t units = vec ? (a.cols / epc) : a.cols;
-  unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? kUnrollRead * kItersRead : kItersRead));
-  if (gx > (unsigned)kAmaxScaleMaxBlocks) gx = kAmaxScaleMaxBlocks;
-  int64_t gy = a.rows < 1 ? 1 : a.rows;
-  if (gy > kAmaxScaleMaxBlocks / gx) gy = kAmaxScaleMaxBlocks / gx;
+  // the amax pass's grid (the reduction state does not depend on it)
+  const unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? kUnrollRead * kItersRead : kItersRead));
+  unsigned gy = (unsigned)(a.rows < 65535 ? a.rows : 65535);
   if (gy < 1) gy = 1;
-  const dim3 grid(gx, (unsigned)gy);
+  while ((uint64_t)gx * gy > 32768 && gy > 1) gy = (gy + 1) / 2;
+  const dim3 grid(gx, gy);
 #define SFP8_AS(DT, V) \
   hipLaunchKernelGGL((stream_kernel<DT, FP8_E4M3, V, false, true, false, true>), grid, dim3(kThreads), 0, stream, a)
   if (dtype == FP8_DT_BF16) {

@@ -16,24 +16,22 @@ struct StreamArgs {
   float* amax;             // device float, already zeroed (amax only; written whole by the one-launch scale)
   unsigned long long* sat; // device count of saturated elements, already zeroed (quantize; may be null)
   // one-launch amax + scale (launch_amax_scale): reduction state and outputs
-  uint32_t* ws;            // [0] ticket (0 on entry, left 0), [1 + b] partial max of workgroup b
+  uint32_t* ws;            // [0] ticket, [1] running max |x| bits (both 0 on entry, left 0)
   int emax, margin;        // bias rule of the format
   int32_t* bias_out;
   float* scale_out;        // optional
   float* scale_inv_out;    // optional
 };
 
-// Workgroups of the one-launch amax + scale pass (a grid-stride loop covers
-// any tensor), hence the size of its reduction state: a ticket and one
-// partial maximum per workgroup.
-constexpr int kAmaxScaleMaxBlocks = 2048;
-constexpr int64_t kAmaxScaleStateBytes = 4 * (1 + kAmaxScaleMaxBlocks);
+// Reduction state of the one-launch amax + scale pass: a ticket and the
+// running maximum, whatever the grid.
+constexpr int64_t kAmaxScaleStateBytes = 8;
 
 // One pass over x that reduces max |x| and derives the bias and scales from
-// it in the same launch: each workgroup stores its partial maximum in a.ws,
-// the last to finish (an agent-scope ticket) reduces them, writes *a.amax,
-// *a.bias_out and the optional scales, and resets the ticket.  a.ws must hold
-// kAmaxScaleStateBytes with ws[0] == 0; launches sharing it must not overlap.
+// it in the same launch: each workgroup folds its maximum into a.ws[1] and
+// takes a ticket in a.ws[0]; the last to finish writes *a.amax, *a.bias_out
+// and the optional scales and resets both words.  a.ws must hold
+// kAmaxScaleStateBytes, both words zero; launches sharing it must not overlap.
 void launch_amax_scale(StreamArgs a, int dtype, hipStream_t stream);
 
 // Enqueue one pass over x: cast to FP8 into q when write_q, max-reduce |x|

@@ -43,7 +43,7 @@ import math
 
 import torch
 
-from . import (E4M3, E5M2, _rule, fp8_amax, fp8_compute_scale, fp8_compute_scale_delayed,
+from . import (E4M3, E5M2, _rule, amax_scale_workspace, fp8_amax, fp8_amax_scale, fp8_compute_scale_delayed,
                fp8_history_init, fp8_history_push, fp8_quantize, fp8_quantize_sat, fp8_scaled_gemm, mx_quantize_packed,
                mx_quantize_rule, mx_quantize_t_packed, mx_quantize_t_rule, mx_scaled_gemm,
                mx_scaled_gemm_packed)
@@ -80,7 +80,8 @@ def _cast(x2, fmt, bias, transpose, want_amax, log):
 
 
 def _per_tensor_cast(x2: torch.Tensor, fmt, recipe: str, margin: int, hist: _History | None,
-                     transpose: bool, const_bias: torch.Tensor | None = None, log=None, name: str = ""):
+                     transpose: bool, const_bias: torch.Tensor | None = None, log=None, name: str = "",
+                     ws: torch.Tensor | None = None):
     """Bias and FP8 codes (plus the transposed copy) of one tensor; with a
     `log` list, appends (name, bias, amax, saturated) as device scalars (amax
     None for the constant recipe; saturated = elements the cast clamped)."""
@@ -89,8 +90,7 @@ def _per_tensor_cast(x2: torch.Tensor, fmt, recipe: str, margin: int, hist: _His
         bias = const_bias
         q, qT, _, sat = _cast(x2, fmt, bias, transpose, False, log)
     elif recipe == "current":
-        amax = fp8_amax(x2)
-        bias, _, _ = fp8_compute_scale(amax, fmt, margin)
+        amax, bias, _, _ = fp8_amax_scale(x2, fmt, ws, margin)       # amax and bias in one launch
         q, qT, _, sat = _cast(x2, fmt, bias, transpose, False, log)
     else:
         # delayed: the first step bootstraps the history with its own amax
@@ -137,9 +137,9 @@ class Fp8LinearFunction(torch.autograd.Function):
                 ctx.save_for_backward(qwT, swT, qxT, sxT)
         else:
             bx, qx, qxT = _per_tensor_cast(x2, E4M3, recipe, layer.margin, layer._hx, True, layer._bias,
-                                           layer._log, "x")
+                                           layer._log, "x", layer._ws)
             bw, qw, qwT = _per_tensor_cast(w, E4M3, recipe, layer.margin, layer._hw, True, layer._bias,
-                                           layer._log, "w")
+                                           layer._log, "w", layer._ws)
             y, amax = fp8_scaled_gemm(qx, E4M3, bx, qw, E4M3, bw, out_dtype=x.dtype, want_amax=True)
             ctx.save_for_backward(qwT, bw, qxT, bx)
         layer.last_output_amax = amax
@@ -176,7 +176,7 @@ class Fp8LinearFunction(torch.autograd.Function):
         else:
             qwT, bw, qxT, bx = ctx.saved_tensors
             bdy, qdy, qdyT = _per_tensor_cast(dy2, E5M2, layer.recipe, layer.margin, layer._hdy,
-                                              ctx.needs_input_grad[1], layer._bias, layer._log, "dy")
+                                              ctx.needs_input_grad[1], layer._bias, layer._log, "dy", layer._ws)
             if ctx.needs_input_grad[0]:
                 dx, _ = fp8_scaled_gemm(qdy, E5M2, bdy, qwT, E4M3, bw, out_dtype=ctx.dtype)
             if ctx.needs_input_grad[1]:
@@ -214,6 +214,13 @@ class Fp8Linear(torch.nn.Module):
         torch.nn.init.kaiming_uniform_(self.weight, a=math.sqrt(5))
         self.last_output_amax = None
         self._hx = self._hw = self._hdy = None
+        # current scaling: one reduction workspace for the layer's one-launch
+        # scales (x, w, dy are scaled one after another on the stream); a
+        # buffer, so that it follows the layer to its device
+        if recipe == "current":
+            self.register_buffer("_ws", amax_scale_workspace(self.weight.device), persistent=False)
+        else:
+            self._ws = None
         if log_scales and recipe == "mx":
             raise ValueError("scale logging covers the per-tensor recipes")
         self._log = [] if log_scales else None

@@ -53,7 +53,7 @@ def test_status_strings(lib):
     for code in (NULL, SHAPE, ALIGN, DTYPE, FORMAT, LAUNCH, UNSUP):
         assert sq.fp8_status_string(code) not in ("ok", "unknown status")
     assert sq.fp8_status_string(-99) == "unknown status"
-    assert sq.fp8_abi_version() >= 4
+    assert sq.fp8_abi_version() >= 5
 
 
 def test_amax_validation(lib):

@@ -478,13 +478,13 @@ def _same_outputs(one, two, what):
 
 
 def test_amax_scale_one_launch_equals_two_step():
-    """fp8_amax_scale (one launch: amax reduced across workgroups through a
-    ticket in the workspace, bias and scales written by the last workgroup)
-    gives exactly fp8_amax + fp8_compute_scale, and the oracle's amax and
-    bias, on: every bf16 pattern (NaN: bias 0), every finite one, fp32 with
-    Inf, a strided unaligned view (element loads), one ragged row, an empty
-    tensor, E5M2 and margins; the workspace's ticket word is back to zero
-    after every call (the partial maxima are overwritten by each call)."""
+    """fp8_amax_scale (one launch: workgroup maxima folded into a running
+    maximum in the workspace, a ticket, bias and scales written by the last
+    workgroup) gives exactly fp8_amax + fp8_compute_scale, and the oracle's
+    amax and bias, on: every bf16 pattern (NaN: bias 0), every finite one,
+    fp32 with Inf, a strided unaligned view (element loads), one ragged row,
+    an empty tensor, E5M2 and margins; the whole workspace is back to zero
+    after every call."""
     ws = sq.amax_scale_workspace(DEV)
     rng = np.random.default_rng(51)
     bits = all_bf16_patterns()
@@ -507,16 +507,15 @@ def test_amax_scale_one_launch_equals_two_step():
                 got = host(one[0])[0]
                 assert (np.isnan(got) and np.isnan(ra)) or got == ra
                 assert int(host(one[1])[0]) == oracle.compute_bias(ra, fmt, margin)
-                assert int(host(ws[:1])[0]) == 0, f"ticket not reset after {name}"
+                assert not host(ws).any(), f"workspace not cleared after {name}"
 
 
 @pytest.mark.parametrize("shape", [(16384, 8192), (28672, 8192), (24576, 32768)],
                          ids=["70b_mlp_x", "70b_mlp_w", "805M_elements"])
 def test_amax_scale_full_size(shape):
     """The 70B-MLP X and W (1024 and 1792 workgroups) and a tensor of 805M
-    elements, whose grid is capped at 2048 workgroups striding over it: the
-    one-launch amax and bias equal the two-step ones, repeated calls agree,
-    and the workspace's ticket is back to zero."""
+    elements (6144 workgroups): the one-launch amax and bias equal the
+    two-step ones, repeated calls agree, and the workspace is back to zero."""
     g = torch.Generator(device=DEV).manual_seed(shape[0])
     x = torch.randn(shape, device=DEV, dtype=torch.bfloat16, generator=g)
     x.view(-1)[shape[0] * 77] = 99.5                    # one outlier far into the tensor
@@ -526,4 +525,4 @@ def test_amax_scale_full_size(shape):
     for _ in range(3):
         _same_outputs(sq.fp8_amax_scale(x, E4M3.code, ws, want_scales=True), ref, f"{shape}")
     assert host(ref[0])[0] == 99.5
-    assert int(host(ws[:1])[0]) == 0
+    assert not host(ws).any()
