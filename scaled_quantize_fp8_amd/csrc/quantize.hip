@@ -394,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
 // loads 16 bytes (8 columns) of 4 consecutive rows, casts them, stores the 4
 // x 8 codes of q directly (8 bytes per row), transposes them 4 x 4 bytes at a
 // time in registers and writes 8 dwords (4 rows each) into a column-major
-// LDS tile; then lane (j, s) writes 32 contiguous bytes of qT row j.  Tiles
+// LDS tile; then 8 lanes write each 128-byte qT row (16 bytes each).  Tiles
 // reaching past the matrix take a per-element path with the same exchange.
 // ---------------------------------------------------------------------------
 constexpr int kCtR = 128, kCtC = 64;
@@ -414,12 +414,12 @@ __device__ __forceinline__ void bytes_transpose4(uint32_t a0, uint32_t a1, uint3
   d[3] = __builtin_amdgcn_perm(hi23, hi01, 0x07060302u);
 }
 
-// NTQT: non-temporal qT stores.  A store instruction writes half of each of
-// 32 qT lines (4 pieces of 16 bytes); cached, the halves merge in L2 before
-// the write-back, which measures faster on large tensors (7B-MLP backward:
-// dY and W, 45M elements, +9% / +11%) and slower on small ones (X, 16.7M
-// elements, -11%: the dirty lines are still being written back when the
-// kernel ends), so the host picks the kind by size.
+// NTQT: non-temporal qT stores.  A store instruction writes 8 whole qT lines
+// (8 lanes of 16 bytes each; 4 pieces 32 bytes apart into 16 lines was
+// 1-6% slower).  Through the cache measures faster on large tensors (7B-MLP
+// backward: dY and W, 45M elements, +9% / +11%) and slower on small ones
+// (X, 16.7M elements, -11%: the dirty lines are still being written back
+// when the kernel ends), so the host picks the kind by size.
 template <int FMT, bool AMAX, bool NTQT, bool SAT>
 __global__ __launch_bounds__(kThreads) void cast_transpose_vec_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, const int32_t* __restrict__ bias,
@@ -481,26 +481,26 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_vec_kernel(
 #pragma unroll
   for (int k = 0; k < 8; ++k) T[8 * cg + k][rg] = d[k];
   __syncthreads();
-  const int j = threadIdx.x >> 2, sgm = threadIdx.x & 3;
-  const int64_t cT = c0 + j;
-  uint32_t w[8];
+  // qT: each of the tile's 64 rows is one 128-byte line, 8 lanes of 16 bytes
 #pragma unroll
-  for (int i = 0; i < 8; ++i) w[i] = T[j][8 * sgm + i];
-  if (interior) {
-    v4u_t* dst = reinterpret_cast<v4u_t*>(qT + cT * ldqT + r0 + 32 * sgm);
-    const v4u_t lo = {w[0], w[1], w[2], w[3]}, hi = {w[4], w[5], w[6], w[7]};
-    if constexpr (NTQT) {
-      __builtin_nontemporal_store(lo, dst);
-      __builtin_nontemporal_store(hi, dst + 1);
-    } else {
-      dst[0] = lo;
-      dst[1] = hi;
-    }
-  } else if (cT < cols) {
+  for (int k = 0; k < 2; ++k) {
+    const int idx = threadIdx.x + k * kThreads;
+    const int j = idx >> 3, p = idx & 7;
+    const int64_t cT = c0 + j;
+    uint32_t w[4];
 #pragma unroll
-    for (int b = 0; b < 32; ++b) {
-      const int64_t r = r0 + 32 * sgm + b;
-      if (r < rows) qT[cT * ldqT + r] = (uint8_t)(w[b / 4] >> (8 * (b % 4)));
+    for (int i = 0; i < 4; ++i) w[i] = T[j][4 * p + i];
+    if (interior) {
+      v4u_t* dst = reinterpret_cast<v4u_t*>(qT + cT * ldqT + r0 + 16 * p);
+      const v4u_t v = {w[0], w[1], w[2], w[3]};
+      if constexpr (NTQT) __builtin_nontemporal_store(v, dst);
+      else dst[0] = v;
+    } else if (cT < cols) {
+#pragma unroll
+      for (int b = 0; b < 16; ++b) {
+        const int64_t r = r0 + 16 * p + b;
+        if (r < rows) qT[cT * ldqT + r] = (uint8_t)(w[b / 4] >> (8 * (b % 4)));
+      }
     }
   }
   if (AMAX) block_max_to_global(amax_bits, red, amax);
@@ -525,6 +525,7 @@ struct MxArgs {
   int64_t kb;          // packed: blocks per row of the code matrix (the last one pads its group)
   int collapsed;       // packed and the rows collapsed into one long row: block j of it is
                        // block j % kb of matrix row j / kb (fewer than 2^32 blocks)
+  int nt;              // transposed cast: qT lines stored non-temporal
 };
 
 // Where the E8M0 code of (row r, block j) goes: row-major (scales + r lds + j)
@@ -664,14 +665,16 @@ static void launch_mx(const MxArgs& a, bool vec, hipStream_t s) {
 // Transposed MX cast: blocks of 32 consecutive ROWS of one column, written as
 // qT [cols x rows] with scalesT [cols x rows/32], i.e. the MX cast of x^T
 // (for a GEMM that contracts over `rows`, such as a weight gradient whose K
-// is the token axis).  128 x 64 tiles: the workgroup stages the tile as fp32
-// bit patterns in LDS (consecutive lanes load consecutive 16-byte chunks of
-// a row), then lane (c, b) owns the whole 32-row block b of tile column c:
-// it reduces the block's maximum, casts its 32 elements and writes them as
-// 32 contiguous bytes of qT row c, so each qT row receives one full 128-byte
-// line per workgroup.
+// is the token axis).  128 x 64 tiles: the workgroup stages the tile in LDS
+// (consecutive lanes load consecutive 16-byte chunks of a row), then lane
+// (c, b) owns the whole 32-row block b of tile column c: it reduces the
+// block's maximum, casts its 32 elements and puts them, as 32 contiguous
+// bytes of qT row c, back into LDS, from where the workgroup writes each of
+// its 64 qT rows as one full 128-byte line.
 // ---------------------------------------------------------------------------
 constexpr int kMtR = 128, kMtC = 64;
+// Elements from which mx_transpose_kernel stores qT through the cache.
+constexpr int64_t kMxtCachedMin = 64LL << 20;
 
 template <int DT, int FMT, bool VEC, bool OCP>
 __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
@@ -715,45 +718,74 @@ __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
   }
   __syncthreads();
   const int c = threadIdx.x % kMtC;
-  const int blk = threadIdx.x / kMtC;              // 0..3: tile rows 32 blk .. 32 blk + 31
+  const int blk = threadIdx.x / kMtC;              // 0..3 (the wave): tile rows 32 blk .. 32 blk + 31
   const int64_t col = c0 + c;                      // qT row
   const int64_t rr = r0 + 32 * blk;                // first qT column of this block
-  if (col >= a.cols || rr >= a.rows) return;       // rows % 32 == 0: a block exists whole or not at all
-  uint32_t v[32];
-  uint32_t bm = 0;
+  const bool live = col < a.cols && rr < a.rows;   // rows % 32 == 0: a block exists whole or not at all
+  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (live) {
+    uint32_t v[32];
+    uint32_t bm = 0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    v[i] = DT == FP8_DT_BF16 ? (uint32_t)tile[32 * blk + i][c] << 16 : (uint32_t)tile[32 * blk + i][c];
-    const uint32_t ab = v[i] & 0x7fffffffu;
-    bm = bm > ab ? bm : ab;
+    for (int i = 0; i < 32; ++i) {
+      v[i] = DT == FP8_DT_BF16 ? (uint32_t)tile[32 * blk + i][c] << 16 : (uint32_t)tile[32 * blk + i][c];
+      const uint32_t ab = v[i] & 0x7fffffffu;
+      bm = bm > ab ? bm : ab;
+    }
+    int e;
+    uint32_t code;
+    block_exponent<FMT, OCP>(bm, &e, &code);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      w[k] = cvt4<FMT>(__builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k]), e),
+                       __builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k + 1]), e),
+                       __builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k + 2]), e),
+                       __builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k + 3]), e));
+    if (__builtin_expect(bm > 0x7f800000u, 0)) {    // a NaN in the block: patch its codes
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if ((v[i] & 0x7fffffffu) > 0x7f800000u)
+          w[i / 4] = (w[i / 4] & ~(0xffu << (8 * (i % 4)))) | (nan_code_f32(v[i]) << (8 * (i % 4)));
+    }
+    store_scale(a, col, rr / 32, code);            // qT row col, block rr / 32
   }
-  int e;
-  uint32_t code;
-  block_exponent<FMT, OCP>(bm, &e, &code);
-  uint32_t w[8];
+  // The codes go out through LDS: the tile's kMtC qT rows of kMtR bytes
+  // (row stride kMtR + 16: the 16-byte writes of 16 lanes hit 64 distinct
+  // banks) are written back as whole 128-byte lines, 8 lanes per line, where
+  // each lane had written 32 bytes into each of 64 rows.  Non-temporal
+  // below kMxtCachedMin elements, through the cache above (the host's
+  // choice, a.nt): measured on the 7B-MLP tensors (16.7M and 45M elements)
+  // and the 70B-MLP X (134M).
+  constexpr int OS = kMtR + 16;
+  static_assert(kMtC * OS <= (int)sizeof(tile), "output staging fits in the tile");
+  uint8_t* ost = reinterpret_cast<uint8_t*>(&tile[0][0]);
+  __syncthreads();                                 // every column has been read
+  *reinterpret_cast<uint4*>(ost + c * OS + 32 * blk) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4*>(ost + c * OS + 32 * blk + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+  __syncthreads();
+  constexpr int CH = kMtR / 16;                    // 16-byte chunks per qT row of the tile
 #pragma unroll
-  for (int k = 0; k < 8; ++k)
-    w[k] = cvt4<FMT>(__builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k]), e),
-                     __builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k + 1]), e),
-                     __builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k + 2]), e),
-                     __builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k + 3]), e));
-  if (__builtin_expect(bm > 0x7f800000u, 0)) {      // a NaN in the block: patch its codes
+  for (int k = 0; k < kMtC * CH / kThreads; ++k) {
+    const int idx = threadIdx.x + k * kThreads;
+    const int orow = idx / CH, ch = idx % CH;
+    const int64_t ocol = c0 + orow, orr = r0 + 16 * ch;
+    if (ocol < a.cols && orr < a.rows) {
+      const uint4 d = *reinterpret_cast<const uint4*>(ost + orow * OS + 16 * ch);
+      uint8_t* dst = a.q + ocol * a.ldq + orr;
+      if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        if (a.nt) {
+          const v4u_t dv = {d.x, d.y, d.z, d.w};
+          __builtin_nontemporal_store(dv, reinterpret_cast<v4u_t*>(dst));
+        } else {
+          *reinterpret_cast<uint4*>(dst) = d;
+        }
+      } else {
+        const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
-    for (int i = 0; i < 32; ++i)
-      if ((v[i] & 0x7fffffffu) > 0x7f800000u)
-        w[i / 4] = (w[i / 4] & ~(0xffu << (8 * (i % 4)))) | (nan_code_f32(v[i]) << (8 * (i % 4)));
+        for (int b = 0; b < 16; ++b) dst[b] = (uint8_t)(dw[b / 4] >> (8 * (b % 4)));
+      }
+    }
   }
-  // cached stores: the four blocks of a qT line come from four waves, and L2
-  // merges them into one full line before it is written back
-  uint8_t* dst = a.q + col * a.ldq + rr;
-  if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-    reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 32; ++k) dst[k] = (uint8_t)(w[k / 4] >> (8 * (k % 4)));
-  }
-  store_scale(a, col, rr / 32, code);              // qT row col, block rr / 32
 }
 
 }  // namespace sfp8
@@ -897,6 +929,7 @@ static int mx_cast_rows(const void* x, int dtype, int64_t rows, int64_t cols, in
   a.sgroups = packed_scale_groups(cols / 32);
   a.kb = cols / 32;
   a.collapsed = 0;
+  a.nt = 0;
   if (packed && (rows % kPackRows) != 0) {
     // rows past the matrix hold 127 (scale 1): fill the whole buffer first,
     // then the cast overwrites every code of the matrix (blocks past a row's
@@ -994,6 +1027,7 @@ static int mx_cast_t(const void* x, int dtype, int64_t rows, int64_t cols, int64
   a.sgroups = packed_scale_groups(rows / 32);
   a.kb = rows / 32;
   a.collapsed = 0;
+  a.nt = rows * cols < kMxtCachedMin;
   if (packed && (cols % kPackRows) != 0) {
     const int64_t n16 = packed_bytes(cols, rows / 32) / 16;        // 127 for the rows past the matrix
     hipLaunchKernelGGL(fill_u8_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, stream, scalesT, n16,
