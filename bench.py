@@ -205,6 +205,78 @@ def gemm_configs(dev, reps: int = 10):
     return out
 
 
+def vs_hipblaslt(x, w, rounds: int = 3, reps: int = 5):
+    """For context only (not a baseline of this method): the vendor library's
+    FP8 GEMM (hipBLASLt through torch._scaled_mm) on the step's own operands,
+    timed alternately with the library's products in the same process, so
+    that both see the same clock and temperature.  Per tensor: the E4M3 cast
+    of the step's X and W (current scaling) with dequantization scales
+    2^-bias; MX: their 1x32 E8M0 cast (row-major scales, which both take).
+    Reports the median over rounds and the largest difference between the
+    two outputs relative to max |C|."""
+    import torch
+    import scaled_quantize_fp8_amd as sq
+    M, K = x.shape
+    N = w.shape[0]
+    dev = x.device
+    f8 = torch.float8_e4m3fn
+    ws_ = sq.amax_scale_workspace(dev)
+    _, bx, _, _ = sq.fp8_amax_scale(x, sq.E4M3, ws_)
+    _, bw, _, _ = sq.fp8_amax_scale(w, sq.E4M3, ws_)
+    qx, _, _ = sq.fp8_quantize(x, sq.E4M3, bx)
+    qw, _, _ = sq.fp8_quantize(w, sq.E4M3, bw)
+    sa = torch.pow(2.0, -bx.float()).reshape(())
+    sb = torch.pow(2.0, -bw.float()).reshape(())
+    y0 = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    mqx, msx = sq.mx_quantize(x, sq.E4M3)
+    mqw, msw = sq.mx_quantize(w, sq.E4M3)
+    e8 = getattr(torch, "float8_e8m0fnu", None)
+    legs = {
+        "per_tensor_ours": lambda: sq.fp8_scaled_gemm(qx, sq.E4M3, bx, qw, sq.E4M3, bw, out=y0),
+        "per_tensor_hipblaslt": lambda: torch._scaled_mm(qx.view(f8), qw.view(f8).t(), scale_a=sa, scale_b=sb,
+                                                         out_dtype=torch.bfloat16),
+        "mx_ours": lambda: sq.mx_scaled_gemm(mqx, sq.E4M3, msx, mqw, sq.E4M3, msw, out=y0),
+    }
+    if e8 is not None:
+        legs["mx_hipblaslt"] = lambda: torch._scaled_mm(mqx.view(f8), mqw.view(f8).t(), scale_a=msx.view(e8),
+                                                        scale_b=msw.view(e8), out_dtype=torch.bfloat16)
+    out, diff = {}, {}
+    for pair in (("per_tensor_ours", "per_tensor_hipblaslt"), ("mx_ours", "mx_hipblaslt")):
+        try:
+            legs[pair[0]]()
+            ref = y0.float()
+            other = legs[pair[1]]().float() if pair[1] in legs else None
+            torch.cuda.synchronize()
+            if other is not None:
+                diff[pair[0][:-5]] = float((other - ref).abs().max() / ref.abs().max())
+        except Exception as e:                      # the vendor path may not take this form
+            out[pair[1]] = {"error": repr(e)[:160]}
+            legs.pop(pair[1], None)
+    times = {k: [] for k in legs}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(rounds):
+        for k, fn in legs.items():
+            fn()
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times[k].append(e0.elapsed_time(e1) / reps)
+    for k, v in times.items():
+        ms = sorted(v)[len(v) // 2]
+        out[k] = {"ms": round(ms, 4), "TFLOPs": round(2.0 * M * N * K / ms / 1e9, 1)}
+    for kind in ("per_tensor", "mx"):
+        if f"{kind}_ours" in times and f"{kind}_hipblaslt" in times:
+            out[f"{kind}_ours_over_hipblaslt"] = round(out[f"{kind}_ours"]["TFLOPs"] /
+                                                       out[f"{kind}_hipblaslt"]["TFLOPs"], 3)
+    out["max_abs_diff_over_max_abs_C"] = diff
+    out["note"] = "context only: hipBLASLt via torch._scaled_mm, same operands, alternated with ours"
+    del y0, mqx, msx, mqw, msw, qx, qw
+    torch.cuda.empty_cache()
+    return out
+
+
 def backward_extras(dev, reps: int = 5):
     """The 7B-MLP down-projection backward (dY [4096 x 11008], W [11008 x
     4096], X [4096 x 4096]) as the linear layer runs it: transposed casts,
@@ -467,6 +539,7 @@ def main():
     per_min = {nm: v[0] for nm, v in samples.items()}
 
     # what the memory system delivers for each cast's mix, on the same tensors
+    # (the r2w1 streams write into qx / qw: their codes are garbage afterwards)
     ceil = hbm_ceilings(dev, xs, ws, [qx] * R, [qw] * R)
     copy_GBps = ceil["copy_1GiB_GBps"]
 
@@ -521,7 +594,8 @@ def main():
 
     extras = None
     if not args.no_extras:
-        extras = {"backward_7b_mlp": backward_extras(dev), "gemm_configs": gemm_configs(dev),
+        extras = {"vs_hipblaslt_70b_mlp": vs_hipblaslt(xs[0], ws[0]),
+                  "backward_7b_mlp": backward_extras(dev), "gemm_configs": gemm_configs(dev),
                   "delayed_7b_attn_16_steps": delayed_leg(dev), "rmse_13b_mlp_up": rmse_c4(dev)}
 
     cpu = None
