@@ -585,7 +585,7 @@ struct TileSrd {
   v4i a, b, sa, sb;
 };
 
-template <int FA, int FB, bool MX, int BMX>
+template <int FA, int FB, bool MX, int BMX, int NSLOT>
 __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // BMX: tile rows (256, or 128 for grids with fewer 256 x 256 tiles than
   // compute units).  A 256-row tile puts the 4 waves in 2 x 2, each 128 x
@@ -596,20 +596,32 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   constexpr int WN = NI * 32;                       // C columns per wave
   constexpr int NA = BMX / 32;                      // op(A) copies per stage per wave
   constexpr int NT = NI * 4;                        // MFMAs per sub-step
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];
+  // NSLOT: LDS slots (stages resident).  Two, or three for the per-tensor
+  // 128-row tile at K >= 4096: its stages are half as long as a 256-row
+  // tile's, too short to cover a copy's latency with one stage in flight
+  // (2048 x 4096 x 4096: waves wait on copies 30% of their cycles against
+  // 10% on the 70B-MLP shape).  With three, the L2 prefetch is off (no room
+  // for its landing words) and the epilogue stages C in the slots, idle by
+  // then.  Measured: 2048 x 4096 x 4096 +6%, 4096 x 2048 x 4096 +7%,
+  // K = 8192 +17%; below K = 4096 two slots were 2-4% faster.
+  constexpr int NS = NSLOT;
+  static_assert(NS == 2 || (NS == 3 && BMX == 128 && !MX), "slot count");
+  constexpr int kSlotA = NS == 3 ? BMX * BK : kTileBytes;   // op(A) bytes per slot
+  constexpr int kSlotB = kTileBytes;                        // op(B) bytes per slot
+  constexpr bool PF = NS == 2;                              // L2 prefetch of op(B)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * (kSlotA + kSlotB)];
   // MX scales, 4 stages per copy: [group slot][operand][tile row][4 dwords]
   __shared__ __attribute__((aligned(16))) uint32_t s_scale[MX ? 2 * 2 * BM * 4 : 1];
   __shared__ uint32_t red[kGemmThreads / kWave];
-  __shared__ uint32_t pf_sink[64];                  // landing words of the L2 prefetch (never read)
+  __shared__ uint32_t pf_sink[PF ? 64 : 1];         // landing words of the L2 prefetch (never read)
   // bf16 epilogue staging, 4 KiB per wave (32 rows x 128 bytes of C).  MX
   // has room for two waves' areas only: waves 0 and 1 stage in the scale
   // slot the finished tile has released.
   constexpr int kStage = 32 * 128;
-  __shared__ __attribute__((aligned(16))) uint8_t cstage[(MX ? 2 : 4) * kStage];
-  constexpr int kRegB = 2 * kTileBytes;             // op(B) region offset (64 KiB)
-  constexpr int kSlot = kTileBytes;                 // 32 KiB per slot per operand
+  __shared__ __attribute__((aligned(16))) uint8_t cstage[NS == 3 ? 16 : (MX ? 2 : 4) * kStage];
+  constexpr int kRegB = NS * kSlotA;                // op(B) region offset
   constexpr int kFrag = 32 * BK;                    // 4 KiB between 32-row fragments
-  constexpr int U = MX ? 4 : 2;                     // stages per loop iteration
+  constexpr int U = MX ? 4 : NS;                    // stages per loop iteration
   constexpr int LPS = NA + 8;                       // data copies per stage per wave
   // Launch shape (kFwdPersistent): one tile per workgroup, the dispatcher
   // refilling each compute unit as a workgroup ends.  The persistent form
@@ -723,15 +735,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // nk <= s < nkU zeros (size-0 descriptor), s >= nkU the next tile's
   // stage s - nkU.  nkU is even, so slot parity runs on across tiles.
   auto dma = [&](int s, int t) {
-    const int slot = s & 1;
+    const int slot = s % NS;
     const bool nx = PERSIST && s >= nkU;
     const bool live = s < nk || nx;
     const uint32_t k0 = (uint32_t)((nx ? s - nkU : s) * BK);
     const bool isb = t >= NA;
     const int i = isb ? t - NA : t;
     const uint32_t off = isb ? offb[i] : offa[i];
-    const uint32_t la = lds0 + (uint32_t)((isb ? kRegB + (wave * 8 + i) * 1024 : (wave * NA + i) * 1024) +
-                                          slot * kSlot);
+    const uint32_t la = lds0 + (uint32_t)(isb ? kRegB + (wave * 8 + i) * 1024 + slot * kSlotB
+                                              : (wave * NA + i) * 1024 + slot * kSlotA);
     v4i srd = isb ? cur.b : cur.a;
     if constexpr (PERSIST) srd = nx ? (isb ? nxt.b : nxt.a) : srd;
     srd[2] = live ? srd[2] : 0;
@@ -742,6 +754,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   };
   // prefetch of op(B) stage s (descriptor choice as for the copies)
   auto prefetch_b = [&](int s, bool owner) {
+    if constexpr (!PF) return;
     const bool nx = PERSIST && s >= nkU;
     const bool live = owner && (s < nk || nx);
     const uint32_t k0 = (uint32_t)((nx ? s - nkU : s) * BK);
@@ -815,13 +828,19 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   for (int t = 0; t < LPS; ++t) dma(0, t);
 #pragma unroll
   for (int t = 0; t < LPS; ++t) dma(1, t);
+  if constexpr (NS == 3) {
+#pragma unroll
+    for (int t = 0; t < LPS; ++t) dma(2, t);
+  }
   // Every stage's copy wait (wait_vm<1>) leaves one copy in flight: the L2
   // prefetch each stage issues last.  The prologue ends with one too (stage
   // 7's, which no stage prefetches), so that stage 0's wait covers all of
   // stage 1's copies; without it the last copy of stage 1 could still be in
-  // flight when the barrier publishes the stage.
+  // flight when the barrier publishes the stage.  Three slots: no prefetch,
+  // and each wait leaves the next stage's LPS copies in flight.
   prefetch_b(7, pf_owner);
-  wait_vm<LPS + 1>();
+  if constexpr (NS == 3) wait_vm<2 * LPS>();
+  else wait_vm<LPS + 1>();
   __syncthreads();
   v8i x0[4], w0[4], x1[4], w1[4];
   int sc[2][8] = {};                                 // scale registers of stages 0-1 and 2-3 of the group
@@ -841,7 +860,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // issuing stage kt+2's DMA into the slot stage kt released.
   auto stage = [&](int kt, auto slot_c, auto scales_c, auto pos_c) {
     constexpr int SLOT = decltype(slot_c)::value;
-    constexpr int NSL = 1 - SLOT;
+    constexpr int NSL = (SLOT + 1) % NS;
     constexpr bool SCALES = decltype(scales_c)::value;  // issue the next scale group
     constexpr int POS = decltype(pos_c)::value;         // stage within the 4-stage scale group (MX)
     constexpr int HB = POS >> 1;                        // scale register of this stage
@@ -851,14 +870,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     for (int t = 0; t < NT; ++t) {
       const int i = t >> 2, j = t & 3;
       switch (t) {
-        case 0: x1[0] = frag_at<SLOT * kSlot + 0 * kFrag>(smem, a1lo, a1hi); break;
-        case 1: x1[1] = frag_at<SLOT * kSlot + 1 * kFrag>(smem, a1lo, a1hi); break;
-        case 2: x1[2] = frag_at<SLOT * kSlot + 2 * kFrag>(smem, a1lo, a1hi); break;
-        case 3: x1[3] = frag_at<SLOT * kSlot + 3 * kFrag>(smem, a1lo, a1hi); break;
-        case 4: w1[0] = frag_at<SLOT * kSlot + 0 * kFrag>(smem, b1lo, b1hi); break;
-        case 5: w1[1] = frag_at<SLOT * kSlot + 1 * kFrag>(smem, b1lo, b1hi); break;
-        case 6: if constexpr (NI == 4) w1[2] = frag_at<SLOT * kSlot + 2 * kFrag>(smem, b1lo, b1hi); break;
-        case 7: if constexpr (NI == 4) w1[3] = frag_at<SLOT * kSlot + 3 * kFrag>(smem, b1lo, b1hi); break;
+        case 0: x1[0] = frag_at<SLOT * kSlotA + 0 * kFrag>(smem, a1lo, a1hi); break;
+        case 1: x1[1] = frag_at<SLOT * kSlotA + 1 * kFrag>(smem, a1lo, a1hi); break;
+        case 2: x1[2] = frag_at<SLOT * kSlotA + 2 * kFrag>(smem, a1lo, a1hi); break;
+        case 3: x1[3] = frag_at<SLOT * kSlotA + 3 * kFrag>(smem, a1lo, a1hi); break;
+        case 4: w1[0] = frag_at<SLOT * kSlotB + 0 * kFrag>(smem, b1lo, b1hi); break;
+        case 5: w1[1] = frag_at<SLOT * kSlotB + 1 * kFrag>(smem, b1lo, b1hi); break;
+        case 6: if constexpr (NI == 4) w1[2] = frag_at<SLOT * kSlotB + 2 * kFrag>(smem, b1lo, b1hi); break;
+        case 7: if constexpr (NI == 4) w1[3] = frag_at<SLOT * kSlotB + 3 * kFrag>(smem, b1lo, b1hi); break;
         default: break;
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -868,7 +887,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w0[i], x0[j], acc[i][j], FB, FA, 0, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vm<1>();                                     // all but the prefetch, issued last
+    if constexpr (NS == 3) wait_vm<LPS>();            // all but stage kt+2's copies
+    else wait_vm<1>();                                // all but the prefetch, issued last
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -883,14 +903,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
         if constexpr (MX && POS == 2)
           if (t >= T0 && t < T0 + 4) read_group((kt >> 2) + 1, sc[0], sc_next, t - T0, t - T0 + 1);
         switch (t) {
-          case 0: x0[0] = frag_at<NSL * kSlot + 0 * kFrag>(smem, a0lo, a0hi); break;
-          case 1: x0[1] = frag_at<NSL * kSlot + 1 * kFrag>(smem, a0lo, a0hi); break;
-          case 2: x0[2] = frag_at<NSL * kSlot + 2 * kFrag>(smem, a0lo, a0hi); break;
-          case 3: x0[3] = frag_at<NSL * kSlot + 3 * kFrag>(smem, a0lo, a0hi); break;
-          case 4: w0[0] = frag_at<NSL * kSlot + 0 * kFrag>(smem, b0lo, b0hi); break;
-          case 5: w0[1] = frag_at<NSL * kSlot + 1 * kFrag>(smem, b0lo, b0hi); break;
-          case 6: if constexpr (NI == 4) w0[2] = frag_at<NSL * kSlot + 2 * kFrag>(smem, b0lo, b0hi); break;
-          case 7: if constexpr (NI == 4) w0[3] = frag_at<NSL * kSlot + 3 * kFrag>(smem, b0lo, b0hi); break;
+          case 0: x0[0] = frag_at<NSL * kSlotA + 0 * kFrag>(smem, a0lo, a0hi); break;
+          case 1: x0[1] = frag_at<NSL * kSlotA + 1 * kFrag>(smem, a0lo, a0hi); break;
+          case 2: x0[2] = frag_at<NSL * kSlotA + 2 * kFrag>(smem, a0lo, a0hi); break;
+          case 3: x0[3] = frag_at<NSL * kSlotA + 3 * kFrag>(smem, a0lo, a0hi); break;
+          case 4: w0[0] = frag_at<NSL * kSlotB + 0 * kFrag>(smem, b0lo, b0hi); break;
+          case 5: w0[1] = frag_at<NSL * kSlotB + 1 * kFrag>(smem, b0lo, b0hi); break;
+          case 6: if constexpr (NI == 4) w0[2] = frag_at<NSL * kSlotB + 2 * kFrag>(smem, b0lo, b0hi); break;
+          case 7: if constexpr (NI == 4) w0[3] = frag_at<NSL * kSlotB + 3 * kFrag>(smem, b0lo, b0hi); break;
           default: break;
         }
       }
@@ -903,7 +923,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
       // the stage's LPS copies spread over its NT MFMA slots
 #pragma unroll
       for (int c = 0; c < LPS; ++c)
-        if (c * NT / LPS == t) dma(kt + 2, c);
+        if (c * NT / LPS == t) dma(kt + NS, c);
       if constexpr (SCALES)
         if (t == NT - 1) scale_dma((kt >> 2) + 1);
       if (t == NT - 1) prefetch_b(kt + 8, pf_owner);
@@ -943,6 +963,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
       using P3 = std::integral_constant<int, 3>;
       stage(kt, S0{}, std::bool_constant<MX>{}, P0{});
       stage(kt + 1, S1{}, std::false_type{}, P1{});
+      if constexpr (NS == 3) stage(kt + 2, std::integral_constant<int, 2>{}, std::false_type{}, P0{});
       if constexpr (MX) {
         stage(kt + 2, S0{}, std::false_type{}, P2{});
         stage(kt + 3, S1{}, std::false_type{}, P3{});
@@ -951,6 +972,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
       }
     }
 
+    if constexpr (NS == 3) {
+      // the slots take the epilogue's staging: every copy (the zero copies
+      // of stages past the last) has landed, every wave is out of the loop
+      wait_vm<0>();
+      __syncthreads();
+    }
     int tm, tn;
     tile_coords_vb(vb, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * BMX, n0 = (int64_t)tn * BN;
@@ -962,7 +989,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     const bool interior = m0 + BMX <= g.M && n0 + BN <= g.N && (g.out_f32 ? g.vec_store : g.row16);
     if (interior) {
       us2v pmax = {0, 0};
-      uint8_t* stg = cstage + (MX ? 0 : wave * kStage);
+      uint8_t* stg = (NS == 3 ? smem : cstage) + (MX ? 0 : wave * kStage);
       if constexpr (MX) {
         const int fs = (gbase + ngroups - 1) & 1;     // scale slot of the tile's last group: free now
         stg = wave < 2 ? reinterpret_cast<uint8_t*>(s_scale) + fs * (2 * BM * 16) + wave * kStage
@@ -1144,12 +1171,19 @@ static void launch_gemm(const GemmArgs& g, hipStream_t s) {
     if (tiles < ncu) {
       // fewer 256 x 256 tiles than compute units: 128 x 256 tiles
       const int64_t t128 = ((g.M + 127) / 128) * ((g.N + BN - 1) / BN);
-      hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128>), dim3((unsigned)t128), dim3(kGemmThreads), 0, s, g);
+      // three LDS slots for long per-tensor products (see gemm_fwd_kernel)
+      if constexpr (!MX) {
+        if (g.K >= 4096) {
+          hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 3>), dim3((unsigned)t128), dim3(kGemmThreads), 0, s, g);
+          return;
+        }
+      }
+      hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 2>), dim3((unsigned)t128), dim3(kGemmThreads), 0, s, g);
       return;
     }
     const int64_t cus = (MX || !kFwdPersistent) ? tiles : ncu;
     const int64_t grid = tiles < cus ? tiles : cus;
-    hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 256>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, g);
+    hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 256, 2>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, g);
   } else {
     hipLaunchKernelGGL((gemm_kernel<FA, FB, MX, TA, TB>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, g);
   }

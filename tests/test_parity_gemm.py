@@ -102,6 +102,35 @@ def test_gemm_k_multiple_of_128(fa, fb, K):
     _check_amax(C, am)
 
 
+@pytest.mark.parametrize("K", [4096, 4224, 4352], ids=["K4096", "K4224", "K4352"])
+def test_gemm_small_grid_three_slot_pipeline(K):
+    """Per-tensor products with fewer 256 x 256 tiles than compute units and
+    K >= 4096 run 128-row tiles with three LDS stage slots, the epilogue
+    staging C in those slots.  K = 4096, 4224, 4352 (32, 33, 34 stages: every
+    count mod 3, so 1 or 2 zero stages pad the last loop iteration or none).
+    Every output of a ragged 300 x 520 product (bf16 and fp32 out) and of an
+    interior 512 x 768 one (bf16, staged stores) against the oracle; and the
+    first 512 rows bit-identical to the same rows of an 8192-row product,
+    which runs 256-row tiles with two slots."""
+    rng = np.random.default_rng(83 + K)
+    qa, ba = _operand(rng, (512, K), 1.0, E4M3)
+    qb, bb = _operand(rng, (768, K), 0.02, E4M3)
+    say(f"gemm three-slot K={K}")
+    for (m, n, dt) in ((300, 520, torch.bfloat16), (300, 520, torch.float32), (512, 768, torch.bfloat16)):
+        C, am = _run_pt(qa[:m], E4M3, ba, qb[:n], E4M3, bb, False, False, dt)
+        ref = oracle.scaled_gemm_ref(qa[:m], E4M3, ba, qb[:n], E4M3, bb)
+        s_ = oracle.abs_product_sum(qa[:m], E4M3, ba, qb[:n], E4M3, bb)
+        gt = mfma_operands_pt(qa[:m], E4M3, ba, qb[:n], E4M3, bb)
+        assert_gemm_close(host_f64(C), ref, s_, dt == torch.bfloat16, f"three-slot {m}x{n} K={K}", gt)
+        _check_amax(C, am)
+    # the same rows inside a product of 8192 rows x 2048 columns (256 tiles)
+    big = np.concatenate([qa, rng.integers(0, 0x78, size=(8192 - 512, K), dtype=np.uint8)])
+    qb2 = np.concatenate([qb, rng.integers(0, 0x78, size=(2048 - 768, K), dtype=np.uint8)])
+    Cs, _ = _run_pt(qa, E4M3, ba, qb2, E4M3, bb, False, False, torch.bfloat16)     # 4 x 8 tiles: three slots
+    Cb, _ = _run_pt(big, E4M3, ba, qb2, E4M3, bb, False, False, torch.bfloat16)    # 32 x 8 tiles: two slots
+    assert torch.equal(Cs.view(torch.int16), Cb[:512].view(torch.int16))
+
+
 @pytest.mark.parametrize("mx", [False, True], ids=["pt", "mx"])
 def test_gemm_bf16_padded_outputs(mx):
     """bf16 C written into padded views, 2 x 2 interior tiles: row stride
