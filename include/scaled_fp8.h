@@ -213,6 +213,48 @@ int fp8_quantize_sat(const void* x, int dtype, int64_t rows, int64_t cols, int64
                      hipStream_t stream);
 
 /*
+ * fp8_quantize_delayed — one step of delayed scaling in one launch: the bias
+ * from the window of earlier steps' amaxes ("Per-Tensor and Per-Block
+ * Scaling Strategies ...", "Key Questions Answered": the scale follows the
+ * largest amax over past iterations), the cast with it, and the push of this
+ * step's amax into the window.  Results equal, bit for bit, the sequence
+ *   fp8_compute_scale_delayed(hist, state, window, fmt, margin, bias_out)
+ *   fp8_quantize_sat(x, ..., bias_out, q, ldq, qT, ldqT, amax_out, sat)
+ *   fp8_history_push(hist, state, window, amax_out)
+ * including the window and state it leaves behind.
+ *   x, dtype, rows, cols, ld, fmt, q, ldq, qT, ldqT   as fp8_quantize (x and
+ *                                  q may be NULL when rows * cols == 0);
+ *   margin, hist, state, window    as fp8_compute_scale_delayed / the
+ *                                  history calls (the window must not be
+ *                                  empty for a delayed scale: the first step
+ *                                  pushes its own amax beforehand, as in the
+ *                                  sequence; an empty window gives bias 0);
+ *   bias_out, amax_out             required, overwritten: the bias used and
+ *                                  max |x| (the amax pushed);
+ *   sat_out                        optional (NULL = skip): saturated count
+ *                                  as in fp8_quantize_sat;
+ *   workspace                      FP8_AMAX_SCALE_WORKSPACE_BYTES of
+ *                                  caller-owned device memory, 8-byte
+ *                                  aligned, ZERO before the first use and
+ *                                  left zero by every call (its first 16
+ *                                  bytes hold a ticket, a running maximum
+ *                                  and a 64-bit count during the call).
+ *                                  Calls sharing a workspace, or a history,
+ *                                  must not overlap (order them on one
+ *                                  stream).
+ * One kernel: each workgroup takes the bias from the window, casts its
+ * share and folds its maximum and count into the workspace; the last to
+ * finish writes the outputs and pushes the amax.  With a transposed copy of
+ * an input other than 16-byte aligned bf16 rows the step runs as the three
+ * calls above (the workspace is then not touched).
+ */
+int fp8_quantize_delayed(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld,
+                         int fmt, int margin, float* hist, int32_t* state, int window,
+                         uint8_t* q, int64_t ldq, uint8_t* qT, int64_t ldqT,
+                         int32_t* bias_out, float* amax_out, uint64_t* sat_out,
+                         void* workspace, hipStream_t stream);
+
+/*
  * mx_quantize — per-block (MXFP8-style) cast ("Key Questions Answered": a
  * tensor is split into blocks with a scale each).  Blocks are 1 x 32 along
  * cols (the GEMM's K axis); cols % 32 == 0 is required.

@@ -24,7 +24,8 @@ __all__ = [
     "E4M3", "E5M2", "load_library", "library_path", "Fp8Error",
     "fp8_amax", "fp8_amax_scale", "fp8_amax_scale_noalloc", "amax_scale_workspace", "AMAX_SCALE_WORKSPACE_BYTES",
     "fp8_compute_scale", "fp8_history_init", "fp8_history_push",
-    "fp8_compute_scale_delayed", "fp8_quantize", "fp8_quantize_sat", "mx_quantize", "mx_quantize_t",
+    "fp8_compute_scale_delayed", "fp8_quantize", "fp8_quantize_sat", "fp8_quantize_delayed", "mx_quantize",
+    "mx_quantize_t",
     "mx_quantize_rule", "mx_quantize_t_rule", "MX_RULE_FMAX", "MX_RULE_OCP",
     "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string", "fp8_abi_version",
     "mx_packed_scales_bytes", "mx_pack_scales", "mx_quantize_packed", "mx_quantize_t_packed",
@@ -61,6 +62,8 @@ _SIGNATURES = {
     "fp8_compute_scale_delayed": ([_p, _p, _i, _i, _i, _p, _p, _p, _p], _i),
     "fp8_quantize": ([_p, _i, _i64, _i64, _i64, _i, _p, _p, _i64, _p, _i64, _p, _p], _i),
     "fp8_quantize_sat": ([_p, _i, _i64, _i64, _i64, _i, _p, _p, _i64, _p, _i64, _p, _p, _p], _i),
+    "fp8_quantize_delayed": ([_p, _i, _i64, _i64, _i64, _i, _i, _p, _p, _i, _p, _i64, _p, _i64, _p, _p, _p, _p,
+                              _p], _i),
     "mx_quantize": ([_p, _i, _i64, _i64, _i64, _i, _p, _i64, _p, _i64, _p], _i),
     "mx_quantize_t": ([_p, _i, _i64, _i64, _i64, _i, _p, _i64, _p, _i64, _p], _i),
     "mx_quantize_rule": ([_p, _i, _i64, _i64, _i64, _i, _i, _p, _i64, _p, _i64, _p], _i),
@@ -351,6 +354,35 @@ def fp8_quantize_sat(x: torch.Tensor, fmt, bias: torch.Tensor, q: torch.Tensor |
         _ptr(x), _dtype_code(x, "x"), rows, cols, ld, _fmt(fmt), _ptr(bias), _ptr(q), ldq,
         _ptr(qT), ldqT, _ptr(amax_out), _ptr(sat_out), _stream(x)))
     return q, qT, amax_out, sat_out
+
+
+def fp8_quantize_delayed(x: torch.Tensor, fmt, hist: torch.Tensor, state: torch.Tensor, workspace: torch.Tensor,
+                         margin: int = 0, q: torch.Tensor | None = None, transpose: bool = False,
+                         qT: torch.Tensor | None = None, want_sat: bool = False, bias_out=None, amax_out=None,
+                         sat_out=None):
+    """One step of delayed scaling in one launch: the bias from the history
+    window, the cast of x with it, and the push of x's amax into the window
+    (bit for bit fp8_compute_scale_delayed + fp8_quantize_sat + fp8_history_push).
+    ``workspace``: as for fp8_amax_scale (amax_scale_workspace), left zero.
+    Returns (q, qT or None, bias, amax, saturated count or None)."""
+    _scalar(hist, torch.float32, "hist")
+    _scalar(state, torch.int32, "state")
+    _dev(workspace, "workspace")
+    if workspace.numel() * workspace.element_size() < AMAX_SCALE_WORKSPACE_BYTES or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor of AMAX_SCALE_WORKSPACE_BYTES")
+    dev = x.device
+    if bias_out is None:
+        bias_out = torch.empty(1, dtype=torch.int32, device=dev)
+    _scalar(bias_out, torch.int32, "bias_out")
+    rows, cols, ld, q, ldq, qT, ldqT, amax_out = _quantize_outputs(x, bias_out, q, transpose, qT, True, amax_out)
+    if want_sat or sat_out is not None:
+        if sat_out is None:
+            sat_out = torch.empty(1, dtype=torch.int64, device=dev)
+        _scalar(sat_out, torch.int64, "sat_out")
+    _check("fp8_quantize_delayed", load_library().fp8_quantize_delayed(
+        _ptr(x), _dtype_code(x, "x"), rows, cols, ld, _fmt(fmt), int(margin), _ptr(hist), _ptr(state), hist.numel(),
+        _ptr(q), ldq, _ptr(qT), ldqT, _ptr(bias_out), _ptr(amax_out), _ptr(sat_out), _ptr(workspace), _stream(x)))
+    return q, qT, bias_out, amax_out, sat_out
 
 
 def _rule(rule) -> int:

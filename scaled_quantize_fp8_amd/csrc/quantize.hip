@@ -194,7 +194,82 @@ __device__ __forceinline__ void amax_scale_finish(uint32_t v, uint32_t* red, con
   }
 }
 
-template <int DT, int FMT, bool VEC, bool WQ, bool AMAX, bool SAT, bool SCALE = false>
+// One step of delayed scaling in one launch.  Start: the bias from the
+// window, the rule of fp8_compute_scale_delayed (largest of the valid
+// entries' magnitudes), computed by wave 0 and shared through LDS; every
+// workgroup reads the window before it takes its ticket, so before the last
+// one pushes.  End: the workgroup's maximum and saturation count fold into
+// the workspace with returning atomics, the ticket's increment depends on
+// both results (they are always 0 in it: the maximum's sign bit is clear,
+// the count is below 2^63), and the workgroup that takes the last ticket
+// swaps the state for zeros, writes bias, amax and count, and pushes the
+// amax as fp8_history_push does.
+__device__ __forceinline__ int window_bias(const DelayedArgs& d) {
+  __shared__ int s_e;
+  if (threadIdx.x < kWave) {
+    int count = d.state[0];
+    count = count < 0 ? 0 : (count > d.window ? d.window : count);
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < count; i += kWave) {
+      const uint32_t v = __float_as_uint(d.hist[i]) & 0x7fffffffu;
+      m = m > v ? m : v;
+    }
+    m = wave_max_u32(m);
+    if (threadIdx.x == 0) s_e = bias_from_amax_bits(m, d.emax, d.margin, -126, 126);
+  }
+  __syncthreads();
+  return s_e;
+}
+
+__device__ __forceinline__ void delayed_finish(uint32_t amax_bits, uint32_t nsat, int e, uint32_t* red,
+                                               const DelayedArgs& d) {
+  __shared__ uint32_t red_s[kThreads / kWave];
+  __shared__ uint32_t s_last;
+  amax_bits = wave_max_u32(amax_bits);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) nsat += (uint32_t)__shfl_xor((int)nsat, off, kWave);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wid = threadIdx.x / kWave;
+  const int nw = (blockDim.x + kWave - 1) / kWave;
+  if (lane == 0) {
+    red[wid] = amax_bits;
+    red_s[wid] = nsat;
+  }
+  __syncthreads();
+  const uint32_t nblk = gridDim.x * gridDim.y;
+  unsigned long long* ws_sat = reinterpret_cast<unsigned long long*>(d.ws + 2);
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+    unsigned long long n = 0;
+    for (int i = 0; i < nw; ++i) {
+      m = m > red[i] ? m : red[i];
+      n += red_s[i];
+    }
+    const uint32_t om = __hip_atomic_fetch_max(d.ws + 1, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long on = __hip_atomic_fetch_add(ws_sat, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t t = __hip_atomic_fetch_add(d.ws, 1u + (om >> 31) + (uint32_t)(on >> 63), __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    s_last = t == nblk - 1;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0 || !s_last) return;
+  const uint32_t m = __hip_atomic_exchange(d.ws + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long n = __hip_atomic_exchange(ws_sat, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float amax = __uint_as_float(m);
+  *d.amax_out = amax;
+  *d.bias_out = e;
+  if (d.sat_out) *d.sat_out = n;
+  int count = d.state[0];
+  int head = d.state[1];
+  head = (head < 0 || head >= d.window) ? 0 : head;
+  count = count < 0 ? 0 : (count > d.window ? d.window : count);
+  d.hist[head] = amax;
+  d.state[1] = (head + 1) % d.window;
+  d.state[0] = count + 1 > d.window ? d.window : count + 1;
+  __hip_atomic_store(d.ws, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int DT, int FMT, bool VEC, bool WQ, bool AMAX, bool SAT, bool SCALE = false, bool DEL = false>
 __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
   __shared__ uint32_t red[kThreads / kWave];
   __shared__ uint32_t red_sat[SAT ? kThreads / kWave : 1];
@@ -202,7 +277,10 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
   constexpr int ESZ = In<DT>::kEsz;
   constexpr int EPC = In<DT>::kEpc;
   constexpr int U = WQ ? kUnroll : kUnrollRead;
-  const int e = WQ ? *a.bias : 0;
+  static_assert(!DEL || (WQ && AMAX && SAT && !SCALE), "the delayed step casts, reduces and counts");
+  int e = 0;
+  if constexpr (DEL) e = window_bias(a.del);
+  else if constexpr (WQ) e = *a.bias;
   uint32_t amax_bits = 0;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -242,9 +320,13 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
       if (WQ) qr[i] = (uint8_t)cast_elem<FMT>(bits, e, SAT ? &nsat : nullptr);
     }
   }
-  if (AMAX && !SCALE) block_max_to_global(amax_bits, red, a.amax);
-  if (SCALE) amax_scale_finish(amax_bits, red, a);
-  if (SAT) block_sum_to_global(nsat, red_sat, a.sat);
+  if constexpr (DEL) {
+    delayed_finish(amax_bits, nsat, e, red, a.del);
+  } else {
+    if (AMAX && !SCALE) block_max_to_global(amax_bits, red, a.amax);
+    if (SCALE) amax_scale_finish(amax_bits, red, a);
+    if (SAT) block_sum_to_global(nsat, red_sat, a.sat);
+  }
 }
 
 template <int DT, int FMT, bool VEC, bool WQ, bool AMAX, bool SAT>
@@ -324,6 +406,45 @@ void launch_amax_scale(StreamArgs a, int dtype, hipStream_t stream) {
     else SFP8_AS(FP8_DT_F32, false);
   }
 #undef SFP8_AS
+}
+
+void launch_quantize_delayed(StreamArgs a, int dtype, int fmt, hipStream_t stream) {
+  const int esz = dtype_size(dtype);
+  const int epc = 16 / esz;
+  if (a.rows > 1 && a.ld == a.cols && a.ldq == a.cols) {   // contiguous matrices -> one long row
+    a.cols *= a.rows;
+    a.rows = 1;
+    a.ld = a.cols;
+    a.ldq = a.cols;
+  }
+  bool vec = aligned(a.x, 16) && (a.rows == 1 || (a.ld * esz) % 16 == 0);
+  vec = vec && aligned(a.q, epc) && (a.rows == 1 || a.ldq % epc == 0);
+  const int64_t units = vec ? (a.cols / epc) : a.cols;
+  // the cast-with-amax grid of launch_stream_pass; one workgroup for an
+  // empty tensor (it still takes the bias and pushes amax 0)
+  unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? kUnroll * kItersCastAmax : kItersCastAmax));
+  unsigned gy = (unsigned)(a.rows < 65535 ? a.rows : 65535);
+  if (gy < 1) gy = 1;
+  while ((uint64_t)gx * gy > 32768 && gy > 1) gy = (gy + 1) / 2;
+  if (a.rows * a.cols == 0) gx = gy = 1;
+  const dim3 grid(gx, gy);
+#define SFP8_QD(DT, FMT, V)                                                                                  \
+  hipLaunchKernelGGL((stream_kernel<DT, FMT, V, true, true, true, false, true>), grid, dim3(kThreads), 0, \
+                     stream, a)
+#define SFP8_QD2(DT, FMT)       \
+  do {                          \
+    if (vec) SFP8_QD(DT, FMT, true); \
+    else SFP8_QD(DT, FMT, false);    \
+  } while (0)
+  if (dtype == FP8_DT_BF16) {
+    if (fmt == FP8_E4M3) SFP8_QD2(FP8_DT_BF16, FP8_E4M3);
+    else SFP8_QD2(FP8_DT_BF16, FP8_E5M2);
+  } else {
+    if (fmt == FP8_E4M3) SFP8_QD2(FP8_DT_F32, FP8_E4M3);
+    else SFP8_QD2(FP8_DT_F32, FP8_E5M2);
+  }
+#undef SFP8_QD2
+#undef SFP8_QD
 }
 
 // ---------------------------------------------------------------------------
@@ -420,16 +541,22 @@ __device__ __forceinline__ void bytes_transpose4(uint32_t a0, uint32_t a1, uint3
 // backward: dY and W, 45M elements, +9% / +11%) and slower on small ones
 // (X, 16.7M elements, -11%: the dirty lines are still being written back
 // when the kernel ends), so the host picks the kind by size.
-template <int FMT, bool AMAX, bool NTQT, bool SAT>
+// DEL: one step of delayed scaling (fp8_quantize_delayed): the bias from the
+// window in del, the outputs and the push by the last workgroup, as in
+// stream_kernel.
+template <int FMT, bool AMAX, bool NTQT, bool SAT, bool DEL = false>
 __global__ __launch_bounds__(kThreads) void cast_transpose_vec_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, const int32_t* __restrict__ bias,
     uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ amax,
-    unsigned long long* __restrict__ sat) {
+    unsigned long long* __restrict__ sat, DelayedArgs del) {
+  static_assert(!DEL || (AMAX && SAT), "the delayed step reduces and counts");
   __shared__ uint32_t T[kCtC][kCtR / 4 + 1];       // codes, column-major, 4 rows per dword
   __shared__ uint32_t red[kThreads / kWave];
   __shared__ uint32_t red_sat[SAT ? kThreads / kWave : 1];
   uint32_t nsat = 0;
-  const int e = *bias;
+  int e;
+  if constexpr (DEL) e = window_bias(del);
+  else e = *bias;
   const int64_t r0 = (int64_t)blockIdx.y * kCtR, c0 = (int64_t)blockIdx.x * kCtC;
   const int cg = threadIdx.x & 7, rg = threadIdx.x >> 3;
   const bool interior = r0 + kCtR <= rows && c0 + kCtC <= cols;
@@ -503,8 +630,12 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_vec_kernel(
       }
     }
   }
-  if (AMAX) block_max_to_global(amax_bits, red, amax);
-  if (SAT) block_sum_to_global(nsat, red_sat, sat);
+  if constexpr (DEL) {
+    delayed_finish(amax_bits, nsat, e, red, del);
+  } else {
+    if (AMAX) block_max_to_global(amax_bits, red, amax);
+    if (SAT) block_sum_to_global(nsat, red_sat, sat);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -817,7 +948,7 @@ static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, i
     const bool nt = n < kCtCachedMin;
 #define SFP8_CTV4(FMT, AM, NT, SC)                                                                              \
   hipLaunchKernelGGL((cast_transpose_vec_kernel<FMT, AM, NT, SC>), grid, dim3(kThreads), 0, stream, xb, rows,   \
-                     cols, ld, bias, q, ldq, qT, ldqT, amax_out, sat_out)
+                     cols, ld, bias, q, ldq, qT, ldqT, amax_out, sat_out, DelayedArgs{})
 #define SFP8_CTV3(FMT, AM, NT)                                                                                  \
   do {                                                                                                          \
     if (sc) SFP8_CTV4(FMT, AM, NT, true);                                                                       \
@@ -893,6 +1024,70 @@ int fp8_quantize_sat(const void* x, int dtype, int64_t rows, int64_t cols, int64
   static_assert(sizeof(unsigned long long) == sizeof(uint64_t), "64-bit count");
   return quantize_impl(x, dtype, rows, cols, ld, fmt, bias, q, ldq, qT, ldqT, amax_out,
                        reinterpret_cast<unsigned long long*>(sat_out), stream);
+}
+
+int fp8_quantize_delayed(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, int fmt, int margin,
+                         float* hist, int32_t* state, int window, uint8_t* q, int64_t ldq, uint8_t* qT,
+                         int64_t ldqT, int32_t* bias_out, float* amax_out, uint64_t* sat_out, void* workspace,
+                         hipStream_t stream) {
+  if (!hist || !state || !bias_out || !amax_out || !workspace) return FP8_ERR_NULL;
+  if (window < 1 || window > 4096) return FP8_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return FP8_ERR_DTYPE;
+  if (!valid_fmt(fmt)) return FP8_ERR_FORMAT;
+  if (int st = check_matrix(rows, cols, ld)) return st;
+  if (int st = check_matrix(rows, cols, ldq)) return st;
+  if (qT && check_matrix(cols, rows, ldqT)) return FP8_ERR_SHAPE;
+  const int64_t n = rows * cols;
+  if (n > 0 && (!x || !q)) return FP8_ERR_NULL;     // an empty step writes no codes
+  if (!aligned(workspace, 8)) return FP8_ERR_ALIGN;
+  unsigned long long* sat = reinterpret_cast<unsigned long long*>(sat_out);
+  DelayedArgs d;
+  d.hist = hist;
+  d.state = state;
+  d.window = window;
+  d.emax = fmt == FP8_E4M3 ? 8 : 15;
+  d.margin = margin;
+  d.ws = static_cast<uint32_t*>(workspace);
+  d.bias_out = bias_out;
+  d.amax_out = amax_out;
+  d.sat_out = sat;
+  if (qT && n > 0) {
+    if (dtype == FP8_DT_BF16 && aligned(x, 16) && ld % 8 == 0 && aligned(q, 8) && ldq % 8 == 0 &&
+        aligned(qT, 16) && ldqT % 16 == 0 && (rows + kCtR - 1) / kCtR <= 65535) {
+      const dim3 grid((unsigned)((cols + kCtC - 1) / kCtC), (unsigned)((rows + kCtR - 1) / kCtR));
+      const uint16_t* xb = static_cast<const uint16_t*>(x);
+      const bool nt = n < kCtCachedMin;
+#define SFP8_CTD(FMT, NT)                                                                                     \
+  hipLaunchKernelGGL((cast_transpose_vec_kernel<FMT, true, NT, true, true>), grid, dim3(kThreads), 0, stream, \
+                     xb, rows, cols, ld, nullptr, q, ldq, qT, ldqT, nullptr, nullptr, d)
+      if (fmt == FP8_E4M3) {
+        if (nt) SFP8_CTD(FP8_E4M3, true);
+        else SFP8_CTD(FP8_E4M3, false);
+      } else {
+        if (nt) SFP8_CTD(FP8_E5M2, true);
+        else SFP8_CTD(FP8_E5M2, false);
+      }
+#undef SFP8_CTD
+      return launch_status();
+    }
+    // other layouts with a transposed copy: the same step as three launches
+    // (the workspace is not used and stays zero)
+    if (int st = fp8_compute_scale_delayed(hist, state, window, fmt, margin, bias_out, nullptr, nullptr, stream))
+      return st;
+    if (int st = quantize_impl(x, dtype, rows, cols, ld, fmt, bias_out, q, ldq, qT, ldqT, amax_out, sat, stream))
+      return st;
+    return fp8_history_push(hist, state, window, amax_out, stream);
+  }
+  StreamArgs a{};
+  a.x = x;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.q = q;
+  a.ldq = ldq;
+  a.del = d;
+  launch_quantize_delayed(a, dtype, fmt, stream);
+  return launch_status();
 }
 
 // Row-wise MX cast behind mx_quantize_rule (scales row-major, ld_scales) and

@@ -19,7 +19,8 @@
 
 namespace sfp8 {
 
-static_assert(kAmaxScaleStateBytes <= FP8_AMAX_SCALE_WORKSPACE_BYTES, "workspace holds the reduction state");
+static_assert(kAmaxScaleStateBytes <= FP8_AMAX_SCALE_WORKSPACE_BYTES && kDelayedStateBytes <= FP8_AMAX_SCALE_WORKSPACE_BYTES,
+              "workspace holds the reduction state");
 
 // Reduction state of fp8_amax_scale_noalloc: one copy per GPU, zeroed once
 // when the library first uses it on that GPU; every call leaves its state
@@ -142,7 +143,7 @@ const char* fp8_status_string(int status) {
   }
 }
 
-int fp8_abi_version(void) { return 5; }
+int fp8_abi_version(void) { return 6; }
 
 int fp8_amax(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ld, float* amax_out,
              hipStream_t stream) {

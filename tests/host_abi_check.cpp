@@ -107,6 +107,29 @@ void quantize() {
          fp8_quantize_sat(A16, 0, 4, 4, 4, 0, I, U16, 4, nullptr, 0, nullptr, nullptr, S), FP8_ERR_NULL);
 }
 
+void quantize_delayed() {
+  auto d = [](const void* x, int dt, int64_t r, int64_t c, int64_t ld, int fmt, int win, int64_t ldq, uint8_t* qt,
+              int64_t ldqt, void* ws) {
+    return fp8_quantize_delayed(x, dt, r, c, ld, fmt, 0, F, I, win, U16, ldq, qt, ldqt, I, F, Q, ws, S);
+  };
+  expect("delayed null workspace", d(A16, 0, 4, 4, 4, 0, 16, 4, nullptr, 0, nullptr), FP8_ERR_NULL);
+  expect("delayed window 0", d(A16, 0, 4, 4, 4, 0, 0, 4, nullptr, 0, A16), FP8_ERR_SHAPE);
+  expect("delayed window 4097", d(A16, 0, 4, 4, 4, 0, 4097, 4, nullptr, 0, A16), FP8_ERR_SHAPE);
+  expect("delayed dtype", d(A16, 4, 4, 4, 4, 0, 16, 4, nullptr, 0, A16), FP8_ERR_DTYPE);
+  expect("delayed format", d(A16, 0, 4, 4, 4, 2, 16, 4, nullptr, 0, A16), FP8_ERR_FORMAT);
+  expect("delayed ld", d(A16, 0, 4, 4, 2, 0, 16, 4, nullptr, 0, A16), FP8_ERR_SHAPE);
+  expect("delayed ldq", d(A16, 0, 4, 4, 4, 0, 16, 3, nullptr, 0, A16), FP8_ERR_SHAPE);
+  expect("delayed ldqT", d(A16, 0, 4, 8, 8, 0, 16, 8, U16, 2, A16), FP8_ERR_SHAPE);
+  expect("delayed null x", d(nullptr, 0, 4, 4, 4, 0, 16, 4, nullptr, 0, A16), FP8_ERR_NULL);
+  expect("delayed workspace align", d(A16, 0, 4, 4, 4, 0, 16, 4, nullptr, 0, static_cast<char*>(A16) + 4),
+         FP8_ERR_ALIGN);
+  expect("delayed huge", d(A16, 0, BIG, BIG, BIG, 0, 16, BIG, nullptr, 0, A16), FP8_ERR_SHAPE);
+  expect("delayed huge qT", d(A16, 0, BIG, BIG, BIG, 0, 16, BIG, U16, BIG, A16), FP8_ERR_SHAPE);
+  expect("delayed null hist",
+         fp8_quantize_delayed(A16, 0, 4, 4, 4, 0, 0, nullptr, I, 16, U16, 4, nullptr, 0, I, F, Q, A16, S),
+         FP8_ERR_NULL);
+}
+
 void mx_casts() {
   for (int variant = 0; variant < 3; ++variant) {   // row-major, explicit rule, packed
     auto m = [&](const void* x, int dt, int64_t r, int64_t c, int64_t ld, int fmt, int rule, uint8_t* qq, int64_t ldq,
@@ -219,6 +242,7 @@ int main() {
   status_strings();
   amax_and_scale();
   quantize();
+  quantize_delayed();
   mx_casts();
   packed_scales();
   gemms();

@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
                  "mx_quantize_rule", "mx_quantize_t_rule", "fp8_scaled_gemm", "mx_scaled_gemm", "fp8_status_string",
                  "fp8_abi_version", "mx_packed_scales_bytes", "mx_pack_scales", "mx_quantize_packed",
                  "mx_quantize_t_packed", "mx_scaled_gemm_packed", "fp8_quantize_sat", "fp8_amax_scale",
-                 "fp8_amax_scale_noalloc"]:
+                 "fp8_amax_scale_noalloc", "fp8_quantize_delayed"]:
         assert want in names
 
 
@@ -53,7 +53,7 @@ def test_status_strings(lib):
     for code in (NULL, SHAPE, ALIGN, DTYPE, FORMAT, LAUNCH, UNSUP):
         assert sq.fp8_status_string(code) not in ("ok", "unknown status")
     assert sq.fp8_status_string(-99) == "unknown status"
-    assert sq.fp8_abi_version() >= 5
+    assert sq.fp8_abi_version() >= 6
 
 
 def test_amax_validation(lib):
@@ -96,6 +96,31 @@ def test_scale_and_history_validation(lib):
     assert lib.fp8_compute_scale_delayed(FAKE, FAKE, 16, 9, 0, FAKE, None, None, S) == FORMAT
     assert lib.fp8_compute_scale_delayed(FAKE, None, 16, 0, 0, FAKE, None, None, S) == NULL
     assert lib.fp8_compute_scale_delayed(FAKE, FAKE, 0, 0, 0, FAKE, None, None, S) == SHAPE
+
+
+def test_quantize_delayed_validation(lib):
+    d = lib.fp8_quantize_delayed
+    # x, dtype, rows, cols, ld, fmt, margin, hist, state, window, q, ldq, qT, ldqT, bias, amax, sat, ws, stream
+    ok = [FAKE, 0, 4, 4, 4, 0, 0, FAKE, FAKE, 16, FAKE, 4, None, 0, FAKE, FAKE, None, FAKE, S]
+
+    def call(**kw):
+        args = list(ok)
+        names = ["x", "dtype", "rows", "cols", "ld", "fmt", "margin", "hist", "state", "window", "q", "ldq", "qT",
+                 "ldqT", "bias", "amax", "sat", "ws", "stream"]
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return d(*args)
+    for k in ("hist", "state", "q", "bias", "amax", "ws"):
+        assert call(**{k: None}) == NULL, k
+    assert call(window=0) == SHAPE
+    assert call(window=4097) == SHAPE
+    assert call(dtype=5) == DTYPE
+    assert call(fmt=2) == FORMAT
+    assert call(ld=2) == SHAPE
+    assert call(ldq=3) == SHAPE
+    assert call(qT=FAKE, ldqT=2) == SHAPE
+    assert call(x=None) == NULL
+    assert call(ws=FAKE + 4) == ALIGN              # 4-byte aligned, the 64-bit count needs 8
 
 
 def test_quantize_validation(lib):

@@ -1,6 +1,7 @@
 """GPU parity of delayed scaling (amax history -> window max -> bias -> cast
 with fused amax -> push), step by step against the oracle's history, plus
-checkpoint / resume of the history state."""
+checkpoint / resume of the history state, and the same step in one launch
+(fp8_quantize_delayed) against the call sequence and the oracle."""
 
 import numpy as np
 import pytest
@@ -9,7 +10,7 @@ import torch
 import oracle
 import scaled_quantize_fp8_amd as sq
 from oracle import E4M3
-from workloads import make
+from workloads import f32_to_bf16_bits, make
 
 from gpu_helpers import (DEV, bf16_dev, f32_bits_of, host, need_gpu, oracle_amax_chunked,
                          oracle_quantize_chunked, say)
@@ -147,3 +148,129 @@ def test_delayed_full_size_7b_attn_16_steps():
         say(f"delayed step {t}: bias {rb}, amax {ra:.4g}, saturated {log[-1][2]}")
     # the window lags a growing amax: some step saturates, step 0 never does
     assert log[0][2] == 0 and any(n > 0 for _, _, n in log)
+
+
+def _f32_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+# (name, dtype, shape, transpose, strided view, fmt code, margin): the fused
+# row-wise kernel (vector and element paths), the fused cast-transpose
+# (16-byte aligned bf16) and the three-call form for other transposed inputs
+FUSED_CASES = [
+    ("bf16_rows", "bf16", (256, 512), False, False, 0, 0),
+    ("bf16_transpose", "bf16", (384, 320), True, False, 0, 0),
+    ("bf16_transpose_ragged_e5m2", "bf16", (200, 136), True, False, 1, 1),
+    ("bf16_strided_rows", "bf16", (130, 301), False, True, 0, 0),
+    ("f32_rows_e5m2", "f32", (96, 1000), False, False, 1, 2),
+    ("f32_transpose", "f32", (160, 96), True, False, 0, 0),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_quantize_delayed_matches_three_calls(case):
+    """fp8_quantize_delayed (bias from the window, cast, push in one launch)
+    against fp8_compute_scale_delayed + fp8_quantize_sat + fp8_history_push on
+    a second copy of the history, 20 steps with window 16 (the ring wraps):
+    codes, transposed codes, bias, amax and saturation count bit for bit
+    every step, the same window and state after every step, and the
+    workspace back to zero; the biases and counts also against the oracle's
+    history."""
+    name, dt, shape, transpose, strided, fmt_code, margin = case
+    fmt = oracle.E4M3 if fmt_code == 0 else oracle.E5M2
+    rng = np.random.default_rng(hash(name) % 2**32)
+    ha = torch.empty(H, dtype=torch.float32, device=DEV)
+    sa = torch.empty(2, dtype=torch.int32, device=DEV)
+    sq.fp8_history_init(ha, sa)
+    hb, sb = ha.clone(), sa.clone()
+    ws = sq.amax_scale_workspace(DEV)
+    h = oracle.DelayedScaling(H)
+    for t in range(20):
+        sigma = float(np.exp(rng.uniform(-3, 3)))
+        v = rng.standard_normal(shape) * sigma
+        v[rng.random(shape) < 0.002] *= 60.0                       # outliers that jump past the window
+        if dt == "bf16":
+            bits = f32_to_bf16_bits(v.astype(np.float32))
+            vals = oracle.bf16_bits_to_f64(bits)
+            x = bf16_dev(bits)
+        else:
+            vals = v.astype(np.float32).astype(np.float64)
+            x = _f32_dev(v)
+        if strided:
+            x = x[:, 1:]
+            vals = vals[:, 1:]
+        if t == 0:                                                 # bootstrap both copies and the oracle
+            a0 = sq.fp8_amax(x)
+            sq.fp8_history_push(ha, sa, a0)
+            sq.fp8_history_push(hb, sb, a0)
+            h.push(oracle.amax(vals))
+        q1, qT1, b1, a1, n1 = sq.fp8_quantize_delayed(x, fmt.code, ha, sa, ws, margin, transpose=transpose,
+                                                      want_sat=True)
+        b2, _, _ = sq.fp8_compute_scale_delayed(hb, sb, fmt.code, margin)
+        q2, qT2, a2, n2 = sq.fp8_quantize_sat(x, fmt.code, b2, transpose=transpose, want_amax=True)
+        sq.fp8_history_push(hb, sb, a2)
+        rb = h.bias(fmt, margin)
+        what = f"{name} step {t}"
+        assert int(host(b1)[0]) == int(host(b2)[0]) == rb, what
+        assert f32_bits_of(a1) == f32_bits_of(a2), what
+        assert host(a1)[0] == oracle.amax(vals), what
+        assert int(host(n1)[0]) == int(host(n2)[0]), what
+        assert int(host(n1)[0]) == int(np.count_nonzero(np.abs(np.ldexp(vals, rb)) > fmt.max)), what
+        assert torch.equal(q1, q2), what
+        if transpose:
+            assert torch.equal(qT1, qT2), what
+        assert torch.equal(ha, hb) and torch.equal(sa, sb), what
+        assert not host(ws).any(), what
+        h.push(oracle.amax(vals))
+
+
+def test_quantize_delayed_empty_and_empty_window():
+    """An empty tensor still takes the window's bias and pushes amax 0, as
+    the three calls do; an empty window gives bias 0 (the cast is then
+    current-scaled only after the caller's bootstrap push)."""
+    ws = sq.amax_scale_workspace(DEV)
+    hist = torch.empty(4, dtype=torch.float32, device=DEV)
+    state = torch.empty(2, dtype=torch.int32, device=DEV)
+    sq.fp8_history_init(hist, state)
+    x = bf16_dev(f32_to_bf16_bits(np.full((64, 96), 3.0, dtype=np.float32)))
+    _, _, b, a, _ = sq.fp8_quantize_delayed(x, E4M3.code, hist, state, ws)
+    assert int(host(b)[0]) == 0 and host(a)[0] == 3.0               # empty window: bias 0
+    assert host(state).tolist() == [1, 1] and host(hist)[0] == 3.0
+    empty = torch.zeros((0, 96), dtype=torch.bfloat16, device=DEV)
+    _, _, b, a, n = sq.fp8_quantize_delayed(empty, E4M3.code, hist, state, ws, want_sat=True)
+    assert int(host(b)[0]) == oracle.compute_bias(3.0, E4M3) and host(a)[0] == 0.0 and int(host(n)[0]) == 0
+    assert host(state).tolist() == [2, 2] and host(hist)[1] == 0.0
+    assert not host(ws).any()
+
+
+def test_quantize_delayed_full_size_7b_attn_16_steps():
+    """The delayed-scaling workload at full size (X_t [2048 x 4096], window
+    16), cast with its transposed copy as the linear layer does, in one
+    launch per step: bias, amax, saturation count and every byte of q and qT
+    against the oracle."""
+    hist = torch.empty(H, dtype=torch.float32, device=DEV)
+    state = torch.empty(2, dtype=torch.int32, device=DEV)
+    sq.fp8_history_init(hist, state)
+    ws = sq.amax_scale_workspace(DEV)
+    h = oracle.DelayedScaling(H)
+    for t in range(16):
+        bits = make("c2", "X", step=t)
+        x = bf16_dev(bits)
+        ra = oracle_amax_chunked(bits)
+        if t == 0:
+            sq.fp8_history_push(hist, state, sq.fp8_amax(x))
+            h.push(ra)
+        rb = h.bias(E4M3)
+        q, qT, b, a, n = sq.fp8_quantize_delayed(x, E4M3.code, hist, state, ws, transpose=True, want_sat=True)
+        h.push(ra)
+        assert int(host(b)[0]) == rb and host(a)[0] == ra, t
+        rq = oracle_quantize_chunked(bits, E4M3, rb)
+        gq = host(q)
+        assert np.array_equal(gq, rq), t
+        assert np.array_equal(host(qT), rq.T), t
+        sat = int(np.count_nonzero(np.abs(np.ldexp(oracle.bf16_bits_to_f64(bits), rb)) > E4M3.max))
+        assert int(host(n)[0]) == sat, t
+        say(f"fused delayed step {t}: bias {rb}, saturated {sat}")
+    hist_ref, count, head = h.state()
+    assert np.array_equal(host(hist), np.array(hist_ref, dtype=np.float32))
+    assert host(state).tolist() == [count, head]
