@@ -23,11 +23,12 @@ blocks along their new contiguous axis), dY^T by the backward cast.
 
 Recipes:
     "current"  per-tensor, bias from the tensor's own amax (two passes:
-               amax, then cast);
+               amax and bias in one launch, then the cast);
     "delayed"  per-tensor, bias from the largest amax of the last `history`
-               steps; the cast also reduces the tensor's amax, which is
-               pushed into the history afterwards.  The first step has no
-               history and pushes its own amax first (current scaling);
+               steps; one launch per tensor and step takes the bias from the
+               window, casts, reduces the tensor's amax and pushes it into
+               the history.  The first step has no history and pushes its
+               own amax first (current scaling);
     "mx"       per-block: 1 x 32 blocks along each product's K axis, E8M0
                block scales; `mx_rule` picks the block-exponent rule
                ("fmax": block max at or below the format maximum; "ocp": the
@@ -43,8 +44,8 @@ import math
 
 import torch
 
-from . import (E4M3, E5M2, _rule, amax_scale_workspace, fp8_amax, fp8_amax_scale, fp8_compute_scale_delayed,
-               fp8_history_init, fp8_history_push, fp8_quantize, fp8_quantize_sat, fp8_scaled_gemm, mx_quantize_packed,
+from . import (E4M3, E5M2, _rule, amax_scale_workspace, fp8_amax_scale, fp8_history_init, fp8_history_push,
+               fp8_quantize, fp8_quantize_delayed, fp8_quantize_sat, fp8_scaled_gemm, mx_quantize_packed,
                mx_quantize_rule, mx_quantize_t_packed, mx_quantize_t_rule, mx_scaled_gemm,
                mx_scaled_gemm_packed)
 
@@ -92,14 +93,18 @@ def _per_tensor_cast(x2: torch.Tensor, fmt, recipe: str, margin: int, hist: _His
     elif recipe == "current":
         amax, bias, _, _ = fp8_amax_scale(x2, fmt, ws, margin)       # amax and bias in one launch
         q, qT, _, sat = _cast(x2, fmt, bias, transpose, False, log)
+    elif hist.steps == 0:
+        # delayed, first step: the history bootstraps with this step's own
+        # amax (pushed once), so the step is current-scaled
+        amax, bias, _, _ = fp8_amax_scale(x2, fmt, ws, margin)
+        fp8_history_push(hist.hist, hist.state, amax)
+        q, qT, _, sat = _cast(x2, fmt, bias, transpose, False, log)
+        hist.steps += 1
     else:
-        # delayed: the first step bootstraps the history with its own amax
-        if hist.steps == 0:
-            fp8_history_push(hist.hist, hist.state, fp8_amax(x2))
-        bias, _, _ = fp8_compute_scale_delayed(hist.hist, hist.state, fmt, margin)
-        q, qT, amax, sat = _cast(x2, fmt, bias, transpose, True, log)
-        if hist.steps > 0:
-            fp8_history_push(hist.hist, hist.state, amax)
+        # delayed: bias from the window, cast, push of this step's amax, in
+        # one launch
+        q, qT, bias, amax, sat = fp8_quantize_delayed(x2, fmt, hist.hist, hist.state, ws, margin,
+                                                      transpose=transpose, want_sat=log is not None)
         hist.steps += 1
     if log is not None:
         log.append((name, bias.clone(), None if amax is None else amax.clone(), sat))
@@ -214,10 +219,11 @@ class Fp8Linear(torch.nn.Module):
         torch.nn.init.kaiming_uniform_(self.weight, a=math.sqrt(5))
         self.last_output_amax = None
         self._hx = self._hw = self._hdy = None
-        # current scaling: one reduction workspace for the layer's one-launch
-        # scales (x, w, dy are scaled one after another on the stream); a
-        # buffer, so that it follows the layer to its device
-        if recipe == "current":
+        # current and delayed scaling: one reduction workspace for the
+        # layer's one-launch scales and delayed steps (x, w, dy are cast one
+        # after another on the stream); a buffer, so that it follows the
+        # layer to its device
+        if recipe in ("current", "delayed"):
             self.register_buffer("_ws", amax_scale_workspace(self.weight.device), persistent=False)
         else:
             self._ws = None
