@@ -60,16 +60,16 @@ def cpu_baseline(xb, wb, target_s: float):
     Per element (rows 0..R-1 of X and W, NumPy, one thread): amax, bias, E4M3
     and MX casts, then the reference GEMMs' input preparation (decode and
     block dequantization).  Per GEMM: the oracle's float64 product engine
-    (BLAS over 512-row panels) on a P-row and a 2P-row panel of X against all
-    N rows of W (values tiled from the sample: the cost does not depend on
-    them); the difference is the cost of P more rows, the rest the per-call
-    cost (the transposed copy of W), so each full product is
-    fixed + (M / P) * per_panel.  Both products (per-tensor, MX) use the same
-    engine, so it is timed once and counted twice."""
+    makes one transposed copy of B per call and multiplies row panels of A
+    against it; the copy of all N rows of W is timed once and a panel of
+    _PANEL rows of X (values tiled from the sample: the cost does not depend
+    on them) repeatedly against it, so each full product is
+    copy + (M / _PANEL) * panel.  Both products (per-tensor, MX) use the
+    same engine, so it is timed once and counted twice."""
     import numpy as np
 
     import oracle
-    from oracle.gemm import _panels
+    from oracle.gemm import _PANEL
     try:
         from threadpoolctl import threadpool_info
         threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
@@ -94,21 +94,26 @@ def cpu_baseline(xb, wb, target_s: float):
     oracle.mx_dequantize(mqx, msx, oracle.E4M3)
     oracle.mx_dequantize(mqw, msw, oracle.E4M3)
     t_prep = (time.perf_counter() - t0) / (2 * rows * K)
+    # the product engine of the oracle (oracle.gemm._panels): one transposed
+    # copy of B per call, then row panels of A against it; its two steps are
+    # timed apart (the copy of all 28672 rows of W dwarfs one panel, so the
+    # difference of two calls would be noise)
     wfull = np.tile(aw, (-(-N // rows), 1))[:N]
-    P = 256
+    t0 = time.perf_counter()
+    bt = np.ascontiguousarray(wfull.T)
+    t_copy = time.perf_counter() - t0
+    a = np.tile(ax, (-(-_PANEL // rows), 1))[:_PANEL]
+    reps = 0
+    t0 = time.perf_counter()
     while True:
-        t = {}
-        for p in (P, 2 * P):
-            a = np.tile(ax, (-(-p // rows), 1))[:p]
-            t0 = time.perf_counter()
-            _panels(a, wfull)
-            t[p] = time.perf_counter() - t0
-        if t[P] + t[2 * P] > target_s / 2 or 2 * P >= 4096:
+        _ = a @ bt
+        reps += 1
+        elapsed = time.perf_counter() - t0
+        if elapsed > target_s / 2 or reps >= 64:
             break
-        P *= 2
-    per_panel = max(t[2 * P] - t[P], 1e-9)
-    fixed = max(t[P] - per_panel, 0.0)
-    gemm_time = 2 * (fixed + (M / P) * per_panel)
+    t_panel = elapsed / reps
+    del bt, wfull
+    gemm_time = 2 * (t_copy + (M / _PANEL) * t_panel)
     full_flops = 2 * 2.0 * M * N * K
     full_time = (t_cast + t_prep) * (M + N) * K + gemm_time
     return {
@@ -116,10 +121,11 @@ def cpu_baseline(xb, wb, target_s: float):
         "kind": "oracle",
         "sample": (f"oracle (NumPy float64) on rows 0..{rows - 1} of X and W: amax/bias/E4M3/MX casts "
                    f"{t_cast * 1e9:.1f} ns/element and GEMM input decoding {t_prep * 1e9:.1f} ns/element "
-                   f"(1 thread); its float64 product engine on {P}- and {2 * P}-row panels of X against all "
-                   f"{N} rows of W ({t[P]:.1f} s, {t[2 * P]:.1f} s: "
-                   f"{2.0 * P * N * K / per_panel / 1e9:.0f} GFLOP/s per added panel, BLAS threads={threads}); "
-                   f"extrapolated to the full step (two products): {full_time:.0f} s"),
+                   f"(1 thread); its float64 product engine: the transposed copy of W it makes per call "
+                   f"({t_copy:.1f} s) and {reps} products of a {_PANEL}-row panel of X against it "
+                   f"({t_panel:.2f} s each, {2.0 * _PANEL * N * K / t_panel / 1e9:.0f} GFLOP/s, "
+                   f"BLAS threads={threads}); extrapolated to the full step (two products of "
+                   f"{M // _PANEL} panels each): {full_time:.0f} s"),
     }
 
 
