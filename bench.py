@@ -34,6 +34,16 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 WORKLOAD = "llama2_70b_mlp_16384x28672x8192"
 
 
+def gemm_code_text(src: str) -> str:
+    """The GEMM source without comments and blank space: the key under which
+    profiles/gemm_traffic.json records the counters (an edit of comments
+    alone leaves them valid)."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -601,8 +611,8 @@ def main():
         try:
             with open(tr_path) as f:
                 tr = json.load(f)
-            with open(os.path.join(ROOT, "scaled_quantize_fp8_amd", "csrc", "gemm.hip"), "rb") as f:
-                same = hashlib.sha256(f.read()).hexdigest() == tr.get("gemm_source_sha256")
+            with open(os.path.join(ROOT, "scaled_quantize_fp8_amd", "csrc", "gemm.hip")) as f:
+                same = hashlib.sha256(gemm_code_text(f.read()).encode()).hexdigest() == tr.get("gemm_code_sha256")
             traffic = tr.get(dom) if same else None
         except Exception:
             traffic = None

@@ -13,8 +13,9 @@
 // Two kernels.
 //   * gemm_fwd_kernel: both operands K-contiguous and K % 128 == 0 (the
 //     forward product Y = X W^T and every MX product of that shape): 32x32x64
-//     MFMAs fed from a two-slot LDS pipeline with asynchronous global -> LDS
-//     copies; described where it is defined.
+//     MFMAs fed from a two-slot LDS pipeline (three slots for long per-tensor
+//     products on small grids) with asynchronous global -> LDS copies;
+//     described where it is defined.
 //   * gemm_kernel: every other layout (transposed operands, a K tail) with
 //     the design below.
 //
