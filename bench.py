@@ -469,7 +469,7 @@ def delayed_leg(dev, steps: int = 16):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library has no multi-GPU path; "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
