@@ -2,8 +2,9 @@
 // plain HBM streams with the access pattern and launch shape of the cast and
 // amax kernels but no arithmetic, so that each cast can be reported against
 // what the memory system delivers for its own mix of reads and writes.
-//   read   16-byte non-temporal loads, 8 in flight per lane, 8 iterations per
-//          lane (the amax pass's shape); the loaded words are folded into one
+//   read   16-byte non-temporal loads, 8 in flight per lane, at most one
+//          workgroup per compute unit (the amax pass's shape, grid-stride
+//          over the rest); the loaded words are folded into one
 //          value that is stored only if it equals a sentinel, so the loads
 //          cannot be removed and nothing is written in practice;
 //   r2w1   16 bytes read, 8 bytes written per lane-chunk (bf16 in, one byte
@@ -74,8 +75,14 @@ extern "C" {
 int sfp8_ceiling_read(const void* x, int64_t bytes, uint32_t* sink, hipStream_t s) {
   if (!x || !sink || bytes <= 0 || bytes % 16 || reinterpret_cast<uintptr_t>(x) % 16) return -1;
   const int64_t n16 = bytes / 16;
-  hipLaunchKernelGGL((stream_ceiling_kernel<8, 0>), dim3(blocks_for(n16, (int64_t)kT * 8 * 8)), dim3(kT), 0, s,
-                     static_cast<const v4u*>(x), n16, nullptr, sink);
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || ncu <= 0)
+    ncu = 256;
+  unsigned nb = blocks_for(n16, (int64_t)kT * 8 * 8);
+  if (nb > (unsigned)ncu) nb = (unsigned)ncu;
+  hipLaunchKernelGGL((stream_ceiling_kernel<8, 0>), dim3(nb), dim3(kT), 0, s, static_cast<const v4u*>(x), n16,
+                     nullptr, sink);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

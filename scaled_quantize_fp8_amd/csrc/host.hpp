@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stdint.h>
 
 #include "../../include/scaled_fp8.h"
@@ -40,6 +42,21 @@ inline int launch_status() {
 // Workgroups for a streaming kernel over `units` work items of `per_block`
 // items each, capped so that a grid-stride loop keeps each lane busy with a
 // few iterations (256 CUs x 16 workgroups in flight).
+// Compute units of the current device (the GEMM's small-grid threshold and
+// persistent grid, the read-only passes' grid cap).  Cached per device
+// (concurrent first calls store the same value).
+inline int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 inline unsigned stream_blocks(int64_t units, int64_t per_block) {
   int64_t b = (units + per_block - 1) / per_block;
   if (b < 1) b = 1;
