@@ -355,12 +355,20 @@ static void launch_vec_mode(const StreamArgs& a, bool vec, bool wq, bool am, dim
 // and atomics on one word, which many short workgroups queue on: one
 // workgroup per CU reads the 70B-MLP X at 6.7 TB/s against 5.0 with 1024
 // workgroups of 8 iterations per lane (W: 6.8 against 6.1).
-static void cap_read_grid(unsigned& gx, unsigned& gy) {
-  const unsigned ncu = (unsigned)device_cu_count();
+// Casts that also reduce (fused amax, saturation count, the delayed step)
+// end the same way: at most two workgroups per CU (one was slower: the
+// writes want more memory parallelism; three or four were 5-10% slower).
+// 70B-MLP X / W: cast with fused amax 83 -> 67 / 132 -> 116 us, one-launch
+// delayed step 166 -> 79 / 275 -> 125 us.  Plain casts keep many short
+// workgroups, measured fastest without atomics.
+static void cap_grid(unsigned& gx, unsigned& gy, unsigned per_cu) {
+  const unsigned ncu = per_cu * (unsigned)device_cu_count();
   if (gy > ncu) gy = ncu;
   const unsigned gxmax = ncu / gy > 0 ? ncu / gy : 1;
   if (gx > gxmax) gx = gxmax;
 }
+static void cap_read_grid(unsigned& gx, unsigned& gy) { cap_grid(gx, gy, 1); }
+
 
 void launch_stream_pass(StreamArgs a, int dtype, int fmt, bool write_q, bool amax, hipStream_t stream) {
   const int esz = dtype_size(dtype);
@@ -383,6 +391,7 @@ void launch_stream_pass(StreamArgs a, int dtype, int fmt, bool write_q, bool ama
   // bound the grid for many short rows
   while ((uint64_t)gx * gy > 32768 && gy > 1) gy = (gy + 1) / 2;
   if (!write_q) cap_read_grid(gx, gy);
+  else if (amax || a.sat) cap_grid(gx, gy, 2);
   const dim3 grid(gx, gy);
   if (dtype == FP8_DT_BF16) {
     if (fmt == FP8_E4M3) launch_vec_mode<FP8_DT_BF16, FP8_E4M3>(a, vec, write_q, amax, grid, stream);
@@ -440,6 +449,7 @@ void launch_quantize_delayed(StreamArgs a, int dtype, int fmt, hipStream_t strea
   unsigned gy = (unsigned)(a.rows < 65535 ? a.rows : 65535);
   if (gy < 1) gy = 1;
   while ((uint64_t)gx * gy > 32768 && gy > 1) gy = (gy + 1) / 2;
+  cap_grid(gx, gy, 2);
   if (a.rows * a.cols == 0) gx = gy = 1;
   const dim3 grid(gx, gy);
 #define SFP8_QD(DT, FMT, V)                                                                                  \
@@ -468,6 +478,18 @@ void launch_quantize_delayed(StreamArgs a, int dtype, int fmt, hipStream_t strea
 // bytes go through a padded LDS tile, and each lane then writes 16 bytes of
 // one qT row.
 // ---------------------------------------------------------------------------
+// Workgroups of a cast-transpose launch over ntiles tiles: one per tile, or,
+// when the kernel reduces (amax, saturation count, the delayed step), two per
+// CU walking the tiles.  One per tile, every workgroup ending in atomics on
+// one word, cost the 70B-MLP X 207 us with the amax and 584 us as the
+// delayed step against 103 us for the plain cast.
+static unsigned tile_blocks(int64_t ntiles, bool reduces) {
+  int64_t n = reduces ? 2 * (int64_t)device_cu_count() : ntiles;
+  if (n > ntiles) n = ntiles;
+  if (n > 0x7fffffff) n = 0x7fffffff;
+  return (unsigned)(n < 1 ? 1 : n);
+}
+
 constexpr int kTT = 64;
 
 template <int DT, int FMT, bool AMAX, bool SAT>
@@ -481,44 +503,51 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
   uint32_t nsat = 0;
   constexpr int ESZ = In<DT>::kEsz;
   const int e = *bias;
-  const int64_t r0 = (int64_t)blockIdx.y * kTT;
-  const int64_t c0 = (int64_t)blockIdx.x * kTT;
   const int tr = threadIdx.x / 4;            // tile row 0..63
   const int tc = (threadIdx.x % 4) * 16;     // first tile column of this lane
   uint32_t amax_bits = 0;
-  const int64_t r = r0 + tr;
-  uint32_t packed[4] = {0u, 0u, 0u, 0u};
-  if (r < rows) {
-    const char* xr = reinterpret_cast<const char*>(x) + r * ld * ESZ;
+  // Grid-stride over 64 x 64 tiles, so a reducing launch can be capped at a
+  // few workgroups per CU and pay the end-of-kernel atomics only that often.
+  const int64_t tiles_x = (cols + kTT - 1) / kTT;
+  const int64_t ntiles = tiles_x * ((rows + kTT - 1) / kTT);
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t r0 = (t / tiles_x) * kTT;
+    const int64_t c0 = (t % tiles_x) * kTT;
+    const int64_t r = r0 + tr;
+    uint32_t packed[4] = {0u, 0u, 0u, 0u};
+    if (r < rows) {
+      const char* xr = reinterpret_cast<const char*>(x) + r * ld * ESZ;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int64_t c = c0 + tc + j;
-      uint32_t code = 0;
-      if (c < cols) {
-        float f;
-        const uint32_t bits = load_elem<DT>(xr, c, &f);
-        const uint32_t ab = bits & 0x7fffffffu;
-        if (AMAX) amax_bits = amax_bits > ab ? amax_bits : ab;
-        code = cast_elem<FMT>(bits, e, SAT ? &nsat : nullptr);
-        q[r * ldq + c] = (uint8_t)code;
-      }
-      packed[j / 4] |= code << (8 * (j % 4));
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) tile[tr][tc / 4 + j] = packed[j];
-  __syncthreads();
-  // qT row (c0 + tr) gets tile column tr, tile rows tc .. tc+15
-  const int64_t cT = c0 + tr;
-  if (cT < cols) {
-    uint8_t* dst = qT + cT * ldqT + r0 + tc;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (r0 + tc + j < rows) {
-        const uint32_t w = tile[tc + j][tr / 4];
-        dst[j] = (uint8_t)((w >> (8 * (tr % 4))) & 0xffu);
+      for (int j = 0; j < 16; ++j) {
+        const int64_t c = c0 + tc + j;
+        uint32_t code = 0;
+        if (c < cols) {
+          float f;
+          const uint32_t bits = load_elem<DT>(xr, c, &f);
+          const uint32_t ab = bits & 0x7fffffffu;
+          if (AMAX) amax_bits = amax_bits > ab ? amax_bits : ab;
+          code = cast_elem<FMT>(bits, e, SAT ? &nsat : nullptr);
+          q[r * ldq + c] = (uint8_t)code;
+        }
+        packed[j / 4] |= code << (8 * (j % 4));
       }
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tile[tr][tc / 4 + j] = packed[j];
+    __syncthreads();
+    // qT row (c0 + tr) gets tile column tr, tile rows tc .. tc+15
+    const int64_t cT = c0 + tr;
+    if (cT < cols) {
+      uint8_t* dst = qT + cT * ldqT + r0 + tc;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (r0 + tc + j < rows) {
+          const uint32_t w = tile[tc + j][tr / 4];
+          dst[j] = (uint8_t)((w >> (8 * (tr % 4))) & 0xffu);
+        }
+      }
+    }
+    if (t + gridDim.x < ntiles) __syncthreads();   // the tile is rewritten next pass
   }
   if (AMAX) block_max_to_global(amax_bits, red, amax);
   if (SAT) block_sum_to_global(nsat, red_sat, sat);
@@ -533,6 +562,7 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
 // reaching past the matrix take a per-element path with the same exchange.
 // ---------------------------------------------------------------------------
 constexpr int kCtR = 128, kCtC = 64;
+
 // Elements from which cast_transpose_vec_kernel stores qT through the cache.
 constexpr int64_t kCtCachedMin = 32LL << 20;
 
@@ -571,10 +601,15 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_vec_kernel(
   int e;
   if constexpr (DEL) e = window_bias(del);
   else e = *bias;
-  const int64_t r0 = (int64_t)blockIdx.y * kCtR, c0 = (int64_t)blockIdx.x * kCtC;
+  // one tile per workgroup, or (a grid capped for the reductions) a
+  // grid-stride loop over the tiles, x fastest
+  const int64_t tiles_x = (cols + kCtC - 1) / kCtC;
+  const int64_t ntiles = tiles_x * ((rows + kCtR - 1) / kCtR);
   const int cg = threadIdx.x & 7, rg = threadIdx.x >> 3;
-  const bool interior = r0 + kCtR <= rows && c0 + kCtC <= cols;
   uint32_t amax_bits = 0;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  const int64_t r0 = (tile / tiles_x) * kCtR, c0 = (tile % tiles_x) * kCtC;
+  const bool interior = r0 + kCtR <= rows && c0 + kCtC <= cols;
   uint2 o[4];
   if (interior) {
 #pragma unroll
@@ -643,6 +678,8 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_vec_kernel(
         if (r < rows) qT[cT * ldqT + r] = (uint8_t)(w[b / 4] >> (8 * (b % 4)));
       }
     }
+  }
+  if (tile + gridDim.x < ntiles) __syncthreads();   // T is rewritten by the next tile
   }
   if constexpr (DEL) {
     delayed_finish(amax_bits, nsat, e, red, del);
@@ -956,8 +993,8 @@ static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, i
   if (n == 0) return launch_status();
   const bool am = amax_out != nullptr, sc = sat_out != nullptr;
   if (qT && dtype == FP8_DT_BF16 && aligned(x, 16) && ld % 8 == 0 && aligned(q, 8) && ldq % 8 == 0 &&
-      aligned(qT, 16) && ldqT % 16 == 0 && (rows + kCtR - 1) / kCtR <= 65535) {
-    const dim3 grid((unsigned)((cols + kCtC - 1) / kCtC), (unsigned)((rows + kCtR - 1) / kCtR));
+      aligned(qT, 16) && ldqT % 16 == 0) {
+    const dim3 grid(tile_blocks(((cols + kCtC - 1) / kCtC) * ((rows + kCtR - 1) / kCtR), am || sc));
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const bool nt = n < kCtCachedMin;
 #define SFP8_CTV4(FMT, AM, NT, SC)                                                                              \
@@ -986,8 +1023,7 @@ static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, i
     return launch_status();
   }
   if (qT) {
-    const dim3 grid((unsigned)((cols + kTT - 1) / kTT), (unsigned)((rows + kTT - 1) / kTT));
-    if (grid.y > 65535) return FP8_ERR_SHAPE;
+    const dim3 grid(tile_blocks(((cols + kTT - 1) / kTT) * ((rows + kTT - 1) / kTT), am || sc));
 #define SFP8_CT2(DT, FMT, AM, SC)                                                                                  \
   hipLaunchKernelGGL((cast_transpose_kernel<DT, FMT, AM, SC>), grid, dim3(kThreads), 0, stream, x, rows, cols, ld, \
                      bias, q, ldq, qT, ldqT, amax_out, sat_out)
@@ -1067,8 +1103,8 @@ int fp8_quantize_delayed(const void* x, int dtype, int64_t rows, int64_t cols, i
   d.sat_out = sat;
   if (qT && n > 0) {
     if (dtype == FP8_DT_BF16 && aligned(x, 16) && ld % 8 == 0 && aligned(q, 8) && ldq % 8 == 0 &&
-        aligned(qT, 16) && ldqT % 16 == 0 && (rows + kCtR - 1) / kCtR <= 65535) {
-      const dim3 grid((unsigned)((cols + kCtC - 1) / kCtC), (unsigned)((rows + kCtR - 1) / kCtR));
+        aligned(qT, 16) && ldqT % 16 == 0) {
+      const dim3 grid(tile_blocks(((cols + kCtC - 1) / kCtC) * ((rows + kCtR - 1) / kCtR), true));
       const uint16_t* xb = static_cast<const uint16_t*>(x);
       const bool nt = n < kCtCachedMin;
 #define SFP8_CTD(FMT, NT)                                                                                     \

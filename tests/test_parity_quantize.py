@@ -463,6 +463,34 @@ def test_saturation_count_every_cast_path(path):
         assert int(host(n0)[0]) == _oracle_sat_count(vals, fmt, b - 12)
 
 
+@pytest.mark.parametrize("path", ["transpose_vec", "transpose_generic"])
+def test_cast_transpose_tile_walk(path):
+    """A reducing cast-transpose launches two workgroups per CU that walk the
+    tiles.  A matrix with a few times more tiles than that (ragged in both
+    directions) and the largest magnitude planted in its last tile: q, qT,
+    the fused amax and the saturation count against the oracle."""
+    rng = np.random.default_rng(45)
+    full = (rng.standard_normal((4113, 4112)) * 3).astype(np.float32)
+    if path == "transpose_vec":
+        rs, cs = slice(0, 4112), slice(0, 4104)       # aligned: 33 x 65 tiles of 128 x 64
+    else:
+        rs, cs = slice(1, 4113), slice(3, 4108)       # unaligned view: 65 x 65 tiles of 64 x 64
+    full[rs, cs][-1, -1] = -1000.0
+    fb = f32_to_bf16_bits(full)
+    x = bf16_dev(fb)[rs, cs]
+    vals = oracle.bf16_bits_to_f64(fb[rs, cs])
+    for fmt in FMTS:
+        b = oracle.compute_bias(4.0, fmt)          # clamps |x| > 7, about 2% of the elements
+        say(f"cast-transpose tile walk {path} {fmt.name} {tuple(x.shape)}")
+        q, qT, am, n = sq.fp8_quantize_sat(x, fmt.code, i32_dev(b), transpose=True, want_amax=True)
+        ref = oracle.quantize(vals, fmt, b)
+        assert np.array_equal(host(q), ref)
+        assert np.array_equal(host(qT), ref.T)
+        assert host(am)[0] == 1000.0
+        want = _oracle_sat_count(vals, fmt, b)
+        assert want > 100000 and int(host(n)[0]) == want
+
+
 def _two_step(x, fmt, margin):
     a = sq.fp8_amax(x)
     b, s, si = sq.fp8_compute_scale(a, fmt, margin)
