@@ -471,25 +471,35 @@ void launch_quantize_delayed(StreamArgs a, int dtype, int fmt, hipStream_t strea
 #undef SFP8_QD
 }
 
-// ---------------------------------------------------------------------------
-// Cast-transpose: 64 x 64 tiles; writes q [rows x cols] and qT [cols x rows]
-// (the transposed copy a GEMM contracting over `rows` reads K-contiguous).
-// Each of the 256 lanes casts 16 consecutive elements of one tile row, the
-// bytes go through a padded LDS tile, and each lane then writes 16 bytes of
-// one qT row.
-// ---------------------------------------------------------------------------
 // Workgroups of a cast-transpose launch over ntiles tiles: one per tile, or,
-// when the kernel reduces (amax, saturation count, the delayed step), two per
-// CU walking the tiles.  One per tile, every workgroup ending in atomics on
-// one word, cost the 70B-MLP X 207 us with the amax and 584 us as the
-// delayed step against 103 us for the plain cast.
-static unsigned tile_blocks(int64_t ntiles, bool reduces) {
-  int64_t n = reduces ? 2 * (int64_t)device_cu_count() : ntiles;
-  if (n > ntiles) n = ntiles;
+// when the kernel reduces (amax, saturation count, the delayed step),
+// per_cu per CU (measured best: 2 for the vector kernel's 128 x 64 tiles, 8
+// for the element kernel's 64 x 64 tiles) and at least 4 tiles each,
+// walking the tiles.  Every
+// workgroup ends in atomics on one word (three in the delayed step), which
+// at one workgroup per tile cost the 70B-MLP X [16384 x 8192] 207 us with
+// the amax and 584 us as the delayed step against 103 us for the plain cast.
+static unsigned tile_blocks(int64_t ntiles, bool reduces, int per_cu) {
+  int64_t n = ntiles;
+  if (reduces) {
+    n = (ntiles + 3) / 4;
+    const int64_t cap = (int64_t)per_cu * device_cu_count();
+    if (n > cap) n = cap;
+  }
   if (n > 0x7fffffff) n = 0x7fffffff;
   return (unsigned)(n < 1 ? 1 : n);
 }
 
+// ---------------------------------------------------------------------------
+// Cast-transpose, element form (any input the vector form does not take:
+// fp32, unaligned rows or strides): 64 x 64 tiles; writes q [rows x cols]
+// and qT [cols x rows] (the transposed copy a GEMM contracting over `rows`
+// reads K-contiguous).  Wave w reads tile rows 16w .. 16w+15 one row per
+// load, lane = column, so each load and each q store covers 64 consecutive
+// elements; a lane packs its 16 codes into 4 dwords of a column-major LDS
+// tile, and 4 lanes then write each 64-byte qT row, 16 bytes each (one
+// vector store when qT rows are 16-byte aligned).
+// ---------------------------------------------------------------------------
 constexpr int kTT = 64;
 
 template <int DT, int FMT, bool AMAX, bool SAT>
@@ -497,57 +507,73 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, const int32_t* __restrict__ bias,
     uint8_t* __restrict__ q, int64_t ldq, uint8_t* __restrict__ qT, int64_t ldqT, float* __restrict__ amax,
     unsigned long long* __restrict__ sat) {
-  __shared__ uint32_t tile[kTT][kTT / 4 + 1];     // 64 rows x 64 bytes, padded by one dword
+  static_assert(kThreads == 4 * kWave && kTT == kWave, "4 waves of 16 rows cover a 64 x 64 tile");
+  // tT[16c + (k ^ (c/4 % 16))]: codes of tile column c (one qT row), tile
+  // rows 4k .. 4k+3.  The XOR puts the 64 lanes of a column write and of a
+  // row read on 64 distinct banks.
+  __shared__ uint32_t tT[kTT * kTT / 4];
   __shared__ uint32_t red[kThreads / kWave];
   __shared__ uint32_t red_sat[SAT ? kThreads / kWave : 1];
   uint32_t nsat = 0;
   constexpr int ESZ = In<DT>::kEsz;
   const int e = *bias;
-  const int tr = threadIdx.x / 4;            // tile row 0..63
-  const int tc = (threadIdx.x % 4) * 16;     // first tile column of this lane
+  const int lane = threadIdx.x % kWave;      // load phase: tile column
+  const int w = threadIdx.x / kWave;         // load phase: tile rows 16w .. 16w+15
+  const int tr = threadIdx.x / 4;            // store phase: qT row c0 + tr
+  const int tq = (threadIdx.x % 4) * 16;     // store phase: its bytes tq .. tq+15
+  const bool vec_out = reinterpret_cast<uintptr_t>(qT) % 16 == 0 && ldqT % 16 == 0;
   uint32_t amax_bits = 0;
-  // Grid-stride over 64 x 64 tiles, so a reducing launch can be capped at a
-  // few workgroups per CU and pay the end-of-kernel atomics only that often.
+  // Grid-stride over the tiles, so a reducing launch can be capped at a few
+  // workgroups per CU and pay the end-of-kernel atomics only that often.
   const int64_t tiles_x = (cols + kTT - 1) / kTT;
   const int64_t ntiles = tiles_x * ((rows + kTT - 1) / kTT);
   for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
     const int64_t r0 = (t / tiles_x) * kTT;
     const int64_t c0 = (t % tiles_x) * kTT;
-    const int64_t r = r0 + tr;
+    const int64_t c = c0 + lane;
+    const int64_t rw = r0 + 16 * w;
     uint32_t packed[4] = {0u, 0u, 0u, 0u};
-    if (r < rows) {
-      const char* xr = reinterpret_cast<const char*>(x) + r * ld * ESZ;
+    if (c < cols) {
+      const char* xc = reinterpret_cast<const char*>(x) + (rw * ld + c) * ESZ;
+      uint8_t* qc = q + rw * ldq + c;
+      uint32_t bits[16];                        // all 16 loads ahead of the casts and stores
+      float f;
+      if (rw + 16 <= rows) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) bits[j] = load_elem<DT>(xc + j * ld * ESZ, 0, &f);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) bits[j] = rw + j < rows ? load_elem<DT>(xc + j * ld * ESZ, 0, &f) : 0u;
+      }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int64_t c = c0 + tc + j;
-        uint32_t code = 0;
-        if (c < cols) {
-          float f;
-          const uint32_t bits = load_elem<DT>(xr, c, &f);
-          const uint32_t ab = bits & 0x7fffffffu;
+        if (rw + j < rows) {
+          const uint32_t ab = bits[j] & 0x7fffffffu;
           if (AMAX) amax_bits = amax_bits > ab ? amax_bits : ab;
-          code = cast_elem<FMT>(bits, e, SAT ? &nsat : nullptr);
-          q[r * ldq + c] = (uint8_t)code;
+          const uint32_t code = cast_elem<FMT>(bits[j], e, SAT ? &nsat : nullptr);
+          qc[j * ldq] = (uint8_t)code;
+          packed[j / 4] |= code << (8 * (j % 4));
         }
-        packed[j / 4] |= code << (8 * (j % 4));
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tile[tr][tc / 4 + j] = packed[j];
+    for (int k = 0; k < 4; ++k) tT[16 * lane + ((4 * w + k) ^ ((lane >> 2) & 15))] = packed[k];
     __syncthreads();
-    // qT row (c0 + tr) gets tile column tr, tile rows tc .. tc+15
     const int64_t cT = c0 + tr;
     if (cT < cols) {
-      uint8_t* dst = qT + cT * ldqT + r0 + tc;
+      uint32_t d[4];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (r0 + tc + j < rows) {
-          const uint32_t w = tile[tc + j][tr / 4];
-          dst[j] = (uint8_t)((w >> (8 * (tr % 4))) & 0xffu);
-        }
+      for (int k = 0; k < 4; ++k) d[k] = tT[16 * tr + ((tq / 4 + k) ^ ((tr >> 2) & 15))];
+      uint8_t* dst = qT + cT * ldqT + r0 + tq;
+      if (vec_out && r0 + tq + 16 <= rows) {
+        *reinterpret_cast<uint4*>(dst) = make_uint4(d[0], d[1], d[2], d[3]);
+      } else {
+#pragma unroll
+        for (int b = 0; b < 16; ++b)
+          if (r0 + tq + b < rows) dst[b] = (uint8_t)(d[b / 4] >> (8 * (b % 4)));
       }
     }
-    if (t + gridDim.x < ntiles) __syncthreads();   // the tile is rewritten next pass
+    if (t + gridDim.x < ntiles) __syncthreads();   // tT is rewritten by the next tile
   }
   if (AMAX) block_max_to_global(amax_bits, red, amax);
   if (SAT) block_sum_to_global(nsat, red_sat, sat);
@@ -608,78 +634,88 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_vec_kernel(
   const int cg = threadIdx.x & 7, rg = threadIdx.x >> 3;
   uint32_t amax_bits = 0;
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-  const int64_t r0 = (tile / tiles_x) * kCtR, c0 = (tile % tiles_x) * kCtC;
-  const bool interior = r0 + kCtR <= rows && c0 + kCtC <= cols;
-  uint2 o[4];
-  if (interior) {
+    const int64_t r0 = (tile / tiles_x) * kCtR, c0 = (tile % tiles_x) * kCtC;
+    const bool interior = r0 + kCtR <= rows && c0 + kCtC <= cols;
+    uint2 o[4];
+    if (interior) {
+      // the lane's 4 rows loaded ahead of the tile's stores: all four in
+      // flight at once (a prefetch of the next tile across the LDS phase
+      // measured no faster)
+      uint4 v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t r = r0 + 4 * rg + i;
-      const uint4 v = load_nt(reinterpret_cast<const uint4*>(x + r * ld + c0 + 8 * cg));
-      uint32_t m;
-      o[i] = cast_chunk<FP8_DT_BF16, FMT, SAT>(v, e, &m, true, &nsat);
-      if (AMAX) amax_bits = amax_bits > m ? amax_bits : m;
-      const v2u_t ov = {o[i].x, o[i].y};
-      __builtin_nontemporal_store(ov, reinterpret_cast<v2u_t*>(q + r * ldq + c0 + 8 * cg));
-    }
-  } else {
+      for (int i = 0; i < 4; ++i)
+        v[i] = load_nt(reinterpret_cast<const uint4*>(x + (r0 + 4 * rg + i) * ld + c0 + 8 * cg));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t r = r0 + 4 * rg + i;
-      uint32_t w[2] = {0u, 0u};
-      if (r < rows) {
-        const char* xr = reinterpret_cast<const char*>(x) + r * ld * 2;
+      for (int i = 0; i < 4; ++i) {
+        uint32_t m;
+        o[i] = cast_chunk<FP8_DT_BF16, FMT, SAT>(v[i], e, &m, true, &nsat);
+        if (AMAX) amax_bits = amax_bits > m ? amax_bits : m;
+        const v2u_t ov = {o[i].x, o[i].y};
+        __builtin_nontemporal_store(ov, reinterpret_cast<v2u_t*>(q + (r0 + 4 * rg + i) * ldq + c0 + 8 * cg));
+      }
+    } else {
+      // per element, the loads of a row ahead of its casts and stores
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int64_t c = c0 + 8 * cg + k;
-          if (c < cols) {
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = r0 + 4 * rg + i;
+        uint32_t w[2] = {0u, 0u};
+        if (r < rows) {
+          const char* xr = reinterpret_cast<const char*>(x) + r * ld * 2;
+          uint32_t bits[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
             float f;
-            const uint32_t bits = load_elem<FP8_DT_BF16>(xr, c, &f);
-            const uint32_t ab = bits & 0x7fffffffu;
-            if (AMAX) amax_bits = amax_bits > ab ? amax_bits : ab;
-            const uint32_t code = cast_elem<FMT>(bits, e, SAT ? &nsat : nullptr);
-            q[r * ldq + c] = (uint8_t)code;
-            w[k / 4] |= code << (8 * (k % 4));
+            bits[k] = c0 + 8 * cg + k < cols ? load_elem<FP8_DT_BF16>(xr, c0 + 8 * cg + k, &f) : 0u;
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int64_t c = c0 + 8 * cg + k;
+            if (c < cols) {
+              const uint32_t ab = bits[k] & 0x7fffffffu;
+              if (AMAX) amax_bits = amax_bits > ab ? amax_bits : ab;
+              const uint32_t code = cast_elem<FMT>(bits[k], e, SAT ? &nsat : nullptr);
+              q[r * ldq + c] = (uint8_t)code;
+              w[k / 4] |= code << (8 * (k % 4));
+            }
           }
         }
-      }
-      o[i] = make_uint2(w[0], w[1]);
-    }
-  }
-  uint32_t d[8];
-  {
-    uint32_t t4[4];
-    bytes_transpose4(o[0].x, o[1].x, o[2].x, o[3].x, t4);
-    d[0] = t4[0]; d[1] = t4[1]; d[2] = t4[2]; d[3] = t4[3];
-    bytes_transpose4(o[0].y, o[1].y, o[2].y, o[3].y, t4);
-    d[4] = t4[0]; d[5] = t4[1]; d[6] = t4[2]; d[7] = t4[3];
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) T[8 * cg + k][rg] = d[k];
-  __syncthreads();
-  // qT: each of the tile's 64 rows is one 128-byte line, 8 lanes of 16 bytes
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int idx = threadIdx.x + k * kThreads;
-    const int j = idx >> 3, p = idx & 7;
-    const int64_t cT = c0 + j;
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = T[j][4 * p + i];
-    if (interior) {
-      v4u_t* dst = reinterpret_cast<v4u_t*>(qT + cT * ldqT + r0 + 16 * p);
-      const v4u_t v = {w[0], w[1], w[2], w[3]};
-      if constexpr (NTQT) __builtin_nontemporal_store(v, dst);
-      else dst[0] = v;
-    } else if (cT < cols) {
-#pragma unroll
-      for (int b = 0; b < 16; ++b) {
-        const int64_t r = r0 + 16 * p + b;
-        if (r < rows) qT[cT * ldqT + r] = (uint8_t)(w[b / 4] >> (8 * (b % 4)));
+        o[i] = make_uint2(w[0], w[1]);
       }
     }
-  }
-  if (tile + gridDim.x < ntiles) __syncthreads();   // T is rewritten by the next tile
+    uint32_t d[8];
+    {
+      uint32_t t4[4];
+      bytes_transpose4(o[0].x, o[1].x, o[2].x, o[3].x, t4);
+      d[0] = t4[0]; d[1] = t4[1]; d[2] = t4[2]; d[3] = t4[3];
+      bytes_transpose4(o[0].y, o[1].y, o[2].y, o[3].y, t4);
+      d[4] = t4[0]; d[5] = t4[1]; d[6] = t4[2]; d[7] = t4[3];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) T[8 * cg + k][rg] = d[k];
+    __syncthreads();
+    // qT: each of the tile's 64 rows is one 128-byte line, 8 lanes of 16 bytes
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int idx = threadIdx.x + k * kThreads;
+      const int j = idx >> 3, p = idx & 7;
+      const int64_t cT = c0 + j;
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = T[j][4 * p + i];
+      if (interior) {
+        v4u_t* dst = reinterpret_cast<v4u_t*>(qT + cT * ldqT + r0 + 16 * p);
+        const v4u_t vv = {w[0], w[1], w[2], w[3]};
+        if constexpr (NTQT) __builtin_nontemporal_store(vv, dst);
+        else dst[0] = vv;
+      } else if (cT < cols) {
+#pragma unroll
+        for (int b = 0; b < 16; ++b) {
+          const int64_t r = r0 + 16 * p + b;
+          if (r < rows) qT[cT * ldqT + r] = (uint8_t)(w[b / 4] >> (8 * (b % 4)));
+        }
+      }
+    }
+    if (tile + gridDim.x < ntiles) __syncthreads();   // T is rewritten by the next tile
   }
   if constexpr (DEL) {
     delayed_finish(amax_bits, nsat, e, red, del);
@@ -994,7 +1030,7 @@ static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, i
   const bool am = amax_out != nullptr, sc = sat_out != nullptr;
   if (qT && dtype == FP8_DT_BF16 && aligned(x, 16) && ld % 8 == 0 && aligned(q, 8) && ldq % 8 == 0 &&
       aligned(qT, 16) && ldqT % 16 == 0) {
-    const dim3 grid(tile_blocks(((cols + kCtC - 1) / kCtC) * ((rows + kCtR - 1) / kCtR), am || sc));
+    const dim3 grid(tile_blocks(((cols + kCtC - 1) / kCtC) * ((rows + kCtR - 1) / kCtR), am || sc, 2));
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const bool nt = n < kCtCachedMin;
 #define SFP8_CTV4(FMT, AM, NT, SC)                                                                              \
@@ -1023,7 +1059,7 @@ static int quantize_impl(const void* x, int dtype, int64_t rows, int64_t cols, i
     return launch_status();
   }
   if (qT) {
-    const dim3 grid(tile_blocks(((cols + kTT - 1) / kTT) * ((rows + kTT - 1) / kTT), am || sc));
+    const dim3 grid(tile_blocks(((cols + kTT - 1) / kTT) * ((rows + kTT - 1) / kTT), am || sc, 8));
 #define SFP8_CT2(DT, FMT, AM, SC)                                                                                  \
   hipLaunchKernelGGL((cast_transpose_kernel<DT, FMT, AM, SC>), grid, dim3(kThreads), 0, stream, x, rows, cols, ld, \
                      bias, q, ldq, qT, ldqT, amax_out, sat_out)
@@ -1104,7 +1140,7 @@ int fp8_quantize_delayed(const void* x, int dtype, int64_t rows, int64_t cols, i
   if (qT && n > 0) {
     if (dtype == FP8_DT_BF16 && aligned(x, 16) && ld % 8 == 0 && aligned(q, 8) && ldq % 8 == 0 &&
         aligned(qT, 16) && ldqT % 16 == 0) {
-      const dim3 grid(tile_blocks(((cols + kCtC - 1) / kCtC) * ((rows + kCtR - 1) / kCtR), true));
+      const dim3 grid(tile_blocks(((cols + kCtC - 1) / kCtC) * ((rows + kCtR - 1) / kCtR), true, 2));
       const uint16_t* xb = static_cast<const uint16_t*>(x);
       const bool nt = n < kCtCachedMin;
 #define SFP8_CTD(FMT, NT)                                                                                     \

@@ -465,10 +465,11 @@ def test_saturation_count_every_cast_path(path):
 
 @pytest.mark.parametrize("path", ["transpose_vec", "transpose_generic"])
 def test_cast_transpose_tile_walk(path):
-    """A reducing cast-transpose launches two workgroups per CU that walk the
-    tiles.  A matrix with a few times more tiles than that (ragged in both
-    directions) and the largest magnitude planted in its last tile: q, qT,
-    the fused amax and the saturation count against the oracle."""
+    """A reducing cast-transpose launches a few workgroups per CU, each
+    walking at least four tiles.  A matrix of 2145 (vector kernel) or 4225
+    (element kernel) tiles, ragged in both directions, with the largest
+    magnitude planted in its last tile: q, qT, the fused amax and the
+    saturation count against the oracle."""
     rng = np.random.default_rng(45)
     full = (rng.standard_normal((4113, 4112)) * 3).astype(np.float32)
     if path == "transpose_vec":
