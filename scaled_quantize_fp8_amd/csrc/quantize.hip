@@ -27,6 +27,7 @@ namespace sfp8 {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;         // 16-byte loads in flight per lane (casts)
 constexpr int kUnrollRead = 8;     // same for the read-only amax pass
+constexpr int kUnrollElem = 8;     // element loads in flight per lane (unaligned rows)
 // Unrolled iterations per lane the grid is sized for.  Casts run fastest as
 // many short workgroups (one iteration each); a pass that reduces an amax
 // ends every workgroup with a reduction and one atomic, so it wants fewer,
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
   for (int64_t r = blockIdx.y; r < a.rows; r += gridDim.y) {
     const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ld * ESZ;
     uint8_t* qr = WQ ? a.q + r * a.ldq : nullptr;
-    int64_t e0 = 0;
+    int64_t i0 = tid;            // this lane's first element for the element loop below
     if constexpr (VEC) {
       const int64_t cpr = a.cols / EPC;
       const uint4* x4 = reinterpret_cast<const uint4*>(xr);
@@ -310,9 +311,31 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(StreamArgs a) {
         if (AMAX) amax_bits = amax_bits > m ? amax_bits : m;
         if (WQ) store_codes<DT>(qr, c, o);
       }
-      e0 = cpr * EPC;
+      i0 = cpr * EPC + tid;
+    } else {
+      // unaligned rows: element loads, kUnrollElem in flight per lane.  A
+      // load past the row reads the row's last element instead (no branch
+      // around the loads, which would wait on each one) and is then ignored.
+      for (; i0 < a.cols; i0 += kUnrollElem * stride) {
+        uint32_t bits[kUnrollElem];
+#pragma unroll
+        for (int u = 0; u < kUnrollElem; ++u) {
+          const int64_t i = i0 + u * stride;
+          float f;
+          bits[u] = load_elem<DT>(xr, i < a.cols ? i : a.cols - 1, &f);
+        }
+#pragma unroll
+        for (int u = 0; u < kUnrollElem; ++u) {
+          const int64_t i = i0 + u * stride;
+          if (i < a.cols) {
+            const uint32_t ab = bits[u] & 0x7fffffffu;
+            if (AMAX) amax_bits = amax_bits > ab ? amax_bits : ab;
+            if (WQ) qr[i] = (uint8_t)cast_elem<FMT>(bits[u], e, SAT ? &nsat : nullptr);
+          }
+        }
+      }
     }
-    for (int64_t i = e0 + tid; i < a.cols; i += stride) {   // tail (or all, when !VEC)
+    for (int64_t i = i0; i < a.cols; i += stride) {   // the tail of a vector row
       float f;
       const uint32_t bits = load_elem<DT>(xr, i, &f);
       const uint32_t ab = bits & 0x7fffffffu;
@@ -385,7 +408,7 @@ void launch_stream_pass(StreamArgs a, int dtype, int fmt, bool write_q, bool ama
   const int64_t units = vec ? (a.cols / epc) : a.cols;
   const int unroll = write_q ? kUnroll : kUnrollRead;
   const int iters = !write_q ? kItersRead : (amax ? kItersCastAmax : kItersCast);
-  unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? unroll * iters : iters));
+  unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? unroll : kUnrollElem) * iters);
   unsigned gy = (unsigned)(a.rows < 65535 ? a.rows : 65535);
   if (gy < 1) gy = 1;
   // bound the grid for many short rows
@@ -413,7 +436,7 @@ void launch_amax_scale(StreamArgs a, int dtype, hipStream_t stream) {
   const bool vec = aligned(a.x, 16) && (a.rows == 1 || (a.ld * esz) % 16 == 0);
   const int64_t units = vec ? (a.cols / epc) : a.cols;
   // the amax pass's grid (the reduction state does not depend on it)
-  unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? kUnrollRead * kItersRead : kItersRead));
+  unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? kUnrollRead : kUnrollElem) * kItersRead);
   unsigned gy = (unsigned)(a.rows < 65535 ? a.rows : 65535);
   if (gy < 1) gy = 1;
   while ((uint64_t)gx * gy > 32768 && gy > 1) gy = (gy + 1) / 2;
@@ -445,7 +468,7 @@ void launch_quantize_delayed(StreamArgs a, int dtype, int fmt, hipStream_t strea
   const int64_t units = vec ? (a.cols / epc) : a.cols;
   // the cast-with-amax grid of launch_stream_pass; one workgroup for an
   // empty tensor (it still takes the bias and pushes amax 0)
-  unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? kUnroll * kItersCastAmax : kItersCastAmax));
+  unsigned gx = stream_blocks(units, (int64_t)kThreads * (vec ? kUnroll : kUnrollElem) * kItersCastAmax);
   unsigned gy = (unsigned)(a.rows < 65535 ? a.rows : 65535);
   if (gy < 1) gy = 1;
   while ((uint64_t)gx * gy > 32768 && gy > 1) gy = (gy + 1) / 2;
@@ -536,14 +559,20 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_kernel(
     if (c < cols) {
       const char* xc = reinterpret_cast<const char*>(x) + (rw * ld + c) * ESZ;
       uint8_t* qc = q + rw * ldq + c;
-      uint32_t bits[16];                        // all 16 loads ahead of the casts and stores
+      // all 16 loads ahead of the casts and stores; in the last tile row a
+      // row past the matrix reads its last row instead (no branch around
+      // the loads) and is then ignored
+      uint32_t bits[16];
       float f;
       if (rw + 16 <= rows) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) bits[j] = load_elem<DT>(xc + j * ld * ESZ, 0, &f);
       } else {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) bits[j] = rw + j < rows ? load_elem<DT>(xc + j * ld * ESZ, 0, &f) : 0u;
+        for (int j = 0; j < 16; ++j) {
+          const int64_t dr = rw + j < rows ? j : rows - 1 - rw;
+          bits[j] = load_elem<DT>(xc + dr * ld * ESZ, 0, &f);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -654,29 +683,34 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_vec_kernel(
         __builtin_nontemporal_store(ov, reinterpret_cast<v2u_t*>(q + (r0 + 4 * rg + i) * ldq + c0 + 8 * cg));
       }
     } else {
-      // per element, the loads of a row ahead of its casts and stores
+      // per element, all 32 loads ahead of the casts and stores; an index
+      // past the matrix reads its last row or column instead (no branch
+      // around the loads) and is then ignored
+      uint32_t bits[4][8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t r = r0 + 4 * rg + i;
+        const char* xr = reinterpret_cast<const char*>(x) + (r < rows ? r : rows - 1) * ld * 2;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int64_t c = c0 + 8 * cg + k;
+          float f;
+          bits[i][k] = load_elem<FP8_DT_BF16>(xr, c < cols ? c : cols - 1, &f);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t r = r0 + 4 * rg + i;
         uint32_t w[2] = {0u, 0u};
-        if (r < rows) {
-          const char* xr = reinterpret_cast<const char*>(x) + r * ld * 2;
-          uint32_t bits[8];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            float f;
-            bits[k] = c0 + 8 * cg + k < cols ? load_elem<FP8_DT_BF16>(xr, c0 + 8 * cg + k, &f) : 0u;
-          }
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const int64_t c = c0 + 8 * cg + k;
-            if (c < cols) {
-              const uint32_t ab = bits[k] & 0x7fffffffu;
-              if (AMAX) amax_bits = amax_bits > ab ? amax_bits : ab;
-              const uint32_t code = cast_elem<FMT>(bits[k], e, SAT ? &nsat : nullptr);
-              q[r * ldq + c] = (uint8_t)code;
-              w[k / 4] |= code << (8 * (k % 4));
-            }
+        for (int k = 0; k < 8; ++k) {
+          const int64_t c = c0 + 8 * cg + k;
+          if (r < rows && c < cols) {
+            const uint32_t ab = bits[i][k] & 0x7fffffffu;
+            if (AMAX) amax_bits = amax_bits > ab ? amax_bits : ab;
+            const uint32_t code = cast_elem<FMT>(bits[i][k], e, SAT ? &nsat : nullptr);
+            q[r * ldq + c] = (uint8_t)code;
+            w[k / 4] |= code << (8 * (k % 4));
           }
         }
         o[i] = make_uint2(w[0], w[1]);
@@ -729,7 +763,8 @@ __global__ __launch_bounds__(kThreads) void cast_transpose_vec_kernel(
 // MX cast: 1 x 32 blocks along cols.  Vector kernel: a block is 4 lanes
 // (bf16) or 8 lanes (f32) of 16-byte chunks; the block max is a DPP
 // reduction inside the lane group, the group's first lane stores the E8M0
-// code.  Scalar kernel (unaligned operands): one lane per block.
+// code.  Element kernel (unaligned operands): one element per lane, a block
+// being 32 lanes of a wave.
 // ---------------------------------------------------------------------------
 struct MxArgs {
   const void* x;
@@ -833,28 +868,76 @@ __global__ __launch_bounds__(kThreads) void mx_vec_kernel(MxArgs a) {
   }
 }
 
+// Max across aligned groups of 32 lanes: the group-of-8 DPP steps, the
+// row mirror (16), then a swizzle exchanging lanes 16 apart in each 32.
+__device__ __forceinline__ uint32_t group32_max(uint32_t v) {
+  v = group8_max(v);
+  uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);   // row mirror
+  v = v > o ? v : o;
+  o = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (0x10 << 10) | 0x1f);            // lane ^ 16
+  return v > o ? v : o;
+}
+
+// Element kernel: a wave takes spans of kMxSpan consecutive elements of a
+// row, 64 at a time (one element per lane, so each load and each code store
+// covers 64 consecutive elements: two blocks); the block max is a reduction
+// over the 32 lanes of a block.  The span's 16 E8M0 codes (one packed-layout
+// group, since spans start at multiples of 512 elements) are gathered in
+// every lane and stored by 16 lanes, one byte each.  Not for a packed layout
+// whose rows were collapsed into one long row (a span could cross rows).
+constexpr int kMxElemU = 8;                      // element loads in flight per lane
+constexpr int kMxSpan = kMxElemU * kWave;        // 512 elements, 16 blocks
+
 template <int DT, int FMT, bool OCP>
 __global__ __launch_bounds__(kThreads) void mx_scalar_kernel(MxArgs a) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t nb = a.cols / 32;
+  static_assert(kMxSpan / 32 == kPackBlocks, "a span is one packed-layout group");
+  const int lane = threadIdx.x % kWave;
+  const int half = lane / 32;                    // block 2u + half of the span at step u
+  const int64_t wave = ((int64_t)blockIdx.x * kThreads + threadIdx.x) / kWave;
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / kWave);
+  const int64_t spans = (a.cols + kMxSpan - 1) / kMxSpan;
+  const int64_t kb = a.cols / 32;
   for (int64_t r = blockIdx.y; r < a.rows; r += gridDim.y) {
     const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ld * In<DT>::kEsz;
-    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb; b += stride) {
-      uint32_t m = 0;
-      for (int j = 0; j < 32; ++j) {
+    uint8_t* qr = a.q + r * a.ldq;
+    for (int64_t sp = wave; sp < spans; sp += nwaves) {
+      const int64_t i0 = sp * kMxSpan + lane;
+      // all loads first; an index past the row reads its last element
+      // instead (no branch around the loads).  cols % 32 == 0, so the 32
+      // lanes of a block are past the row together or not at all.
+      uint32_t bits[kMxElemU];
+#pragma unroll
+      for (int u = 0; u < kMxElemU; ++u) {
+        const int64_t i = i0 + u * kWave;
         float f;
-        const uint32_t ab = load_elem<DT>(xr, b * 32 + j, &f) & 0x7fffffffu;
-        m = m > ab ? m : ab;
+        bits[u] = load_elem<DT>(xr, i < a.cols ? i : a.cols - 1, &f);
       }
-      int e;
-      uint32_t code;
-      block_exponent<FMT, OCP>(m, &e, &code);
-      for (int j = 0; j < 32; ++j) {
-        float f;
-        const uint32_t bits = load_elem<DT>(xr, b * 32 + j, &f);
-        a.q[r * a.ldq + b * 32 + j] = (uint8_t)cast_elem<FMT>(bits, e);
+      uint32_t own[2] = {0u, 0u};                // codes of this half's blocks, step u in byte u % 4
+#pragma unroll
+      for (int u = 0; u < kMxElemU; ++u) {
+        const int64_t i = i0 + u * kWave;
+        const uint32_t m = group32_max(bits[u] & 0x7fffffffu);
+        int e;
+        uint32_t code;
+        block_exponent<FMT, OCP>(m, &e, &code);
+        own[u / 4] |= code << (8 * (u % 4));
+        if (i < a.cols) qr[i] = (uint8_t)cast_elem<FMT>(bits[u], e);
       }
-      store_scale(a, r, b, code);
+      // the other half's codes; even blocks come from half 0, odd from half 1
+      const uint32_t oth0 = (uint32_t)__shfl_xor((int)own[0], 32), oth1 = (uint32_t)__shfl_xor((int)own[1], 32);
+      const uint32_t ev0 = half ? oth0 : own[0], ev1 = half ? oth1 : own[1];
+      const uint32_t od0 = half ? own[0] : oth0, od1 = half ? own[1] : oth1;
+      if (lane < kPackBlocks) {
+        const int64_t j = sp * kPackBlocks + lane;       // this lane's block of the row
+        const uint32_t ev = lane < 8 ? ev0 : ev1, od = lane < 8 ? od0 : od1;
+        const uint32_t code = (((lane & 1) ? od : ev) >> (8 * ((lane % 8) / 2))) & 0xffu;
+        if (a.packed) {
+          uint8_t* p = a.scales + ((r / kPackRows) * a.sgroups + sp) * kPackTile + (r % kPackRows) * kPackBlocks;
+          p[lane] = j < kb ? (uint8_t)code : (uint8_t)0x7f;   // 127 pads the row's last group
+        } else if (j < kb) {
+          a.scales[r * a.lds + j] = (uint8_t)code;
+        }
+      }
     }
   }
 }
@@ -862,8 +945,8 @@ __global__ __launch_bounds__(kThreads) void mx_scalar_kernel(MxArgs a) {
 template <int DT, int FMT, bool OCP>
 static void launch_mx(const MxArgs& a, bool vec, hipStream_t s) {
   const int epc = 16 / In<DT>::kEsz;
-  const int64_t units = vec ? a.cols / epc : a.cols / 32;
-  const int64_t per = (int64_t)kThreads * (vec ? kUnroll * kItersCast : kItersCast);
+  const int64_t units = vec ? a.cols / epc : a.cols;
+  const int64_t per = vec ? (int64_t)kThreads * kUnroll * kItersCast : (int64_t)kThreads * kMxElemU;
   // one workgroup per `per` units of a row, rounded down when the matrix has
   // several rows: a second workgroup on a row's short remainder would run
   // only the non-unrolled tail (11008 columns: 1376 chunks, 5.4 per lane
@@ -1227,8 +1310,10 @@ static int mx_cast_rows(const void* x, int dtype, int64_t rows, int64_t cols, in
   // (8192 bf16 columns: 6.0 TB/s per row against 5.7 collapsed), the long
   // row taken otherwise (11008 columns: 4.9 per row).
   const int64_t per_row = (int64_t)kThreads * kUnroll * kItersCast;
+  const bool x_vec = aligned(x, 16) && (rows == 1 || (ld * esz) % 16 == 0) && aligned(q, epc) &&
+                     (rows == 1 || ldq % epc == 0);
   const bool collapse = a.rows > 1 && a.ld == a.cols && a.ldq == a.cols &&
-                        (packed ? (a.cols / epc) % per_row != 0 && rows * (cols / 32) < (1LL << 32)
+                        (packed ? x_vec && (a.cols / epc) % per_row != 0 && rows * (cols / 32) < (1LL << 32)
                                 : a.lds == a.cols / 32);
   if (collapse) {
     a.collapsed = packed;

@@ -187,11 +187,14 @@ def test_mx_cast_bit_exact(fmt, dtype):
     rq, rs = oracle.mx_quantize(vals, fmt)
     assert np.array_equal(host(s), rs)
     assert np.array_equal(host(q), rq)
-    # strided / unaligned views (scalar path) on the same data
-    sub = x[5:, 32:32 + 512]
-    q2, s2 = sq.mx_quantize(sub, fmt.code)
-    rq2, rs2 = oracle.mx_quantize(vals[5:, 32:32 + 512], fmt)
-    assert np.array_equal(host(s2), rs2) and np.array_equal(host(q2), rq2)
+    # a strided view (vector kernel, row by row), a strided view starting at
+    # an odd column (element kernel, row by row) and, for bf16, a contiguous
+    # copy at an odd address (element kernel over one long row)
+    for c0 in (32, 33):
+        sub = x[5:, c0:c0 + 512]
+        q2, s2 = sq.mx_quantize(sub, fmt.code)
+        rq2, rs2 = oracle.mx_quantize(vals[5:, c0:c0 + 512], fmt)
+        assert np.array_equal(host(s2), rs2) and np.array_equal(host(q2), rq2), c0
     if dtype == "bf16":
         odd = torch.empty(bits.size + 1, dtype=torch.bfloat16, device=DEV)[1:].view(bits.shape)
         odd.copy_(x)
@@ -374,11 +377,20 @@ def test_mx_quantize_packed(rows, cols, dtype, fmt, rule):
     assert np.array_equal(host(q), rq)
     assert np.array_equal(host(ps), pack_scales_host(rs))
     if cols >= 64:
-        sub = x[:, 32:]                                      # strided rows
-        q2, ps2 = sq.mx_quantize_packed(sub, fmt.code, rule=rule)
-        rq2, rs2 = oracle.mx_quantize(xv[:, 32:], fmt, rule=rule)
-        assert np.array_equal(host(q2), rq2)
-        assert np.array_equal(host(ps2), pack_scales_host(rs2))
+        for c0 in (32, 1):                                   # strided rows; unaligned (element kernel)
+            sub = x[:, c0:c0 + cols - 32]
+            q2, ps2 = sq.mx_quantize_packed(sub, fmt.code, rule=rule)
+            rq2, rs2 = oracle.mx_quantize(xv[:, c0:c0 + cols - 32], fmt, rule=rule)
+            assert np.array_equal(host(q2), rq2), c0
+            assert np.array_equal(host(ps2), pack_scales_host(rs2)), c0
+    if dtype == "bf16":
+        # contiguous at an odd address: the element kernel, collapsed into one
+        # long row when a row is not a whole number of workgroup iterations
+        odd = torch.empty(rows * cols + 1, dtype=torch.bfloat16, device=DEV)[1:].view(rows, cols)
+        odd.copy_(x)
+        q3, ps3 = sq.mx_quantize_packed(odd, fmt.code, rule=rule)
+        assert np.array_equal(host(q3), rq)
+        assert np.array_equal(host(ps3), pack_scales_host(rs))
 
 
 @pytest.mark.parametrize("rows,cols,dtype,fmt,rule", [
