@@ -993,8 +993,26 @@ __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
   const int64_t r0 = (int64_t)blockIdx.y * kMtR;
   const int64_t c0 = (int64_t)blockIdx.x * kMtC;
   const bool full_cols = c0 + kMtC <= a.cols;
+  constexpr int LPL = kMtR * CPR / kThreads;       // 16-byte chunks per lane
+  if (VEC && full_cols && r0 + kMtR <= a.rows) {
+    // whole tile: a lane's loads all in flight before its LDS writes (a
+    // branch per chunk made the compiler wait on each load)
+    uint4 v[LPL];
 #pragma unroll
-  for (int k = 0; k < kMtR * CPR / kThreads; ++k) {
+    for (int k = 0; k < LPL; ++k) {
+      const int idx = threadIdx.x + k * kThreads;
+      const int64_t r = r0 + idx / CPR;
+      v[k] = load_nt(reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.x) +
+                                                    (r * a.ld + c0 + (idx % CPR) * EPC) * ESZ));
+    }
+#pragma unroll
+    for (int k = 0; k < LPL; ++k) {
+      const int idx = threadIdx.x + k * kThreads;
+      *reinterpret_cast<uint4*>(&tile[idx / CPR][(idx % CPR) * EPC]) = v[k];
+    }
+  } else {
+#pragma unroll
+  for (int k = 0; k < LPL; ++k) {
     const int idx = threadIdx.x + k * kThreads;
     const int tr = idx / CPR, ch = idx % CPR;
     const int64_t r = r0 + tr;
@@ -1016,6 +1034,7 @@ __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
       }
       trow[0] = *reinterpret_cast<const uint4*>(w);
     }
+  }
   }
   __syncthreads();
   const int c = threadIdx.x % kMtC;
