@@ -4,7 +4,8 @@ offsets pass 4 GiB, on every kernel of the path.
 A [49152 x 49152] bf16 tensor (2,415,919,104 elements, 4.8 GB) goes through
 the amax passes, the per-tensor cast with its transposed copy and saturation
 count, the MX casts (row blocks and column blocks, row-major and packed
-scales) and the one-launch delayed step.  A [589824 x 8192] code matrix
+scales) and the one-launch delayed step; a view of it starting one element
+into each row goes through the element kernels.  A [589824 x 8192] code matrix
 (4.8 GB; row 524288 starts at byte 2**32) goes through the per-tensor and
 block-scaled GEMMs.  Inputs are drawn on the device by torch (uniform in
 (-1, 1), with the largest magnitude planted past the 2**31-th element), so
@@ -112,6 +113,31 @@ def test_large_delayed_step(big):
         assert np.array_equal(host(q[r]), oracle.quantize(_row_vals(x, r), E4M3, rb)), r
     for c in COLS:
         assert np.array_equal(host(qT[c]), oracle.quantize(_col_vals(x, c), E4M3, rb)), c
+
+
+def test_large_unaligned_view(big):
+    """The element kernels at the same size: a view starting one element
+    into each row (no 16-byte loads), 49120 columns (a multiple of 32)."""
+    v = big[:, 1:C - 31]
+    cols = [0, 30, PLANT[1] - 1, v.shape[1] - 1]
+    say("large: unaligned view, element amax, cast-transpose and row-wise cast")
+    assert host(sq.fp8_amax(v))[0] == 1000.0
+    bs = oracle.compute_bias(1000.0, E4M3) + 3
+    q, qT, am, n = sq.fp8_quantize_sat(v, E4M3.code, i32_dev(bs), transpose=True, want_amax=True)
+    assert host(am)[0] == 1000.0 and int(host(n)[0]) == 1
+    for r in ROWS:
+        assert np.array_equal(host(q[r]), oracle.quantize(_row_vals(big, r)[1:C - 31], E4M3, bs)), r
+    for c in cols:
+        assert np.array_equal(host(qT[c]), oracle.quantize(_col_vals(big, c + 1), E4M3, bs)), c
+    q2, _, am2, n2 = sq.fp8_quantize_sat(v, E4M3.code, i32_dev(bs), want_amax=True)
+    assert torch.equal(q2, q) and host(am2)[0] == 1000.0 and int(host(n2)[0]) == 1
+    del q, qT, q2
+    torch.cuda.empty_cache()
+    say("large: unaligned view, MX element kernel")
+    mq, ms = sq.mx_quantize(v, E4M3.code)
+    for r in ROWS:
+        rq, rs = oracle.mx_quantize(_row_vals(big, r)[None, 1:C - 31], E4M3)
+        assert np.array_equal(host(mq[r]), rq[0]) and np.array_equal(host(ms[r]), rs[0]), r
 
 
 GM, GN, GK = 589824, 256, 8192            # A: 4.83 GB; row 524288 starts at byte 2**32
