@@ -1012,29 +1012,29 @@ __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
     }
   } else {
 #pragma unroll
-  for (int k = 0; k < LPL; ++k) {
-    const int idx = threadIdx.x + k * kThreads;
-    const int tr = idx / CPR, ch = idx % CPR;
-    const int64_t r = r0 + tr;
-    const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ld * ESZ;
-    uint4* trow = reinterpret_cast<uint4*>(&tile[tr][ch * EPC]);   // one 16-byte chunk of the row
-    if (VEC && full_cols && r < a.rows) {
-      trow[0] = load_nt(reinterpret_cast<const uint4*>(xr + (c0 + ch * EPC) * ESZ));
-    } else {
-      TT w[EPC];
+    for (int k = 0; k < LPL; ++k) {
+      const int idx = threadIdx.x + k * kThreads;
+      const int tr = idx / CPR, ch = idx % CPR;
+      const int64_t r = r0 + tr;
+      const char* xr = reinterpret_cast<const char*>(a.x) + r * a.ld * ESZ;
+      uint4* trow = reinterpret_cast<uint4*>(&tile[tr][ch * EPC]);   // one 16-byte chunk of the row
+      if (VEC && full_cols && r < a.rows) {
+        trow[0] = load_nt(reinterpret_cast<const uint4*>(xr + (c0 + ch * EPC) * ESZ));
+      } else {
+        // element loads; an index past the matrix reads its last row or
+        // column instead (no branch around the loads) and stores 0
+        const char* xc = reinterpret_cast<const char*>(a.x) + (r < a.rows ? r : a.rows - 1) * a.ld * ESZ;
+        TT w[EPC];
 #pragma unroll
-      for (int j = 0; j < EPC; ++j) {
-        const int64_t c = c0 + ch * EPC + j;
-        w[j] = 0;
-        if (r < a.rows && c < a.cols) {
+        for (int j = 0; j < EPC; ++j) {
+          const int64_t c = c0 + ch * EPC + j;
           float f;
-          const uint32_t bits = load_elem<DT>(xr, c, &f);
-          w[j] = (TT)(DT == FP8_DT_BF16 ? bits >> 16 : bits);
+          const uint32_t bits = load_elem<DT>(xc, c < a.cols ? c : a.cols - 1, &f);
+          w[j] = r < a.rows && c < a.cols ? (TT)(DT == FP8_DT_BF16 ? bits >> 16 : bits) : (TT)0;
         }
+        trow[0] = *reinterpret_cast<const uint4*>(w);
       }
-      trow[0] = *reinterpret_cast<const uint4*>(w);
     }
-  }
   }
   __syncthreads();
   const int c = threadIdx.x % kMtC;

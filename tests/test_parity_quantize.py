@@ -232,6 +232,15 @@ def test_mx_cast_transposed_bit_exact(fmt, dtype):
     sq.mx_quantize_t(big[:, :100], fmt.code, qT=qbig[:, :96], scalesT=sbig[:, :3])
     assert np.array_equal(host(qbig[:, :96]), rq) and np.array_equal(host(sbig[:, :3]), rs)
     assert np.all(host(qbig[:, 96:]) == 0xA5) and np.all(host(sbig[:, 3:]) == 0x5A)
+    # a view starting one element into each row (element loads), 288 rows:
+    # two whole 128-row tiles and a partial one
+    tall = torch.zeros((320, 129), dtype=x.dtype, device=DEV)
+    tall[:96, 1:101] = x
+    tall[96:192, 1:101] = x
+    tall[192:288, 1:101] = x
+    rq3, rs3 = oracle.mx_quantize(np.ascontiguousarray(np.concatenate([vals, vals, vals])[:288].T), fmt)
+    q3, s3 = sq.mx_quantize_t(tall[:288, 1:101], fmt.code)
+    assert np.array_equal(host(q3), rq3) and np.array_equal(host(s3), rs3)
 
 
 def test_mx_cast_transposed_full_size_sampled():
