@@ -186,7 +186,8 @@ def gemm_configs(dev, reps: int = 10):
     Llama-2-7B attention projection of the delayed-scaling workload (per
     tensor, 2048 x 4096 x 4096: 128 output tiles for 256 compute units) and
     the 13B-MLP up-projection of the MXFP8 workload (8192 x 13824 x 5120 on
-    packed scales)."""
+    packed scales).  The median of 3 rounds; for the per-tensor product also
+    hipBLASLt on the same codes, alternated with ours, as context."""
     import torch
     import scaled_quantize_fp8_amd as sq
     out = {}
@@ -205,17 +206,33 @@ def gemm_configs(dev, reps: int = 10):
             qx, _, _ = sq.fp8_quantize(x, sq.E4M3, bx)
             qw, _, _ = sq.fp8_quantize(w, sq.E4M3, bw)
             fn = lambda: sq.fp8_scaled_gemm(qx, sq.E4M3, bx, qw, sq.E4M3, bw, out=y)
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        fns = [("ours", fn)]
+        if not mx:
+            # context only: hipBLASLt (torch._scaled_mm) on the same codes,
+            # alternated with ours so that both see the same clock
+            f8 = torch.float8_e4m3fn
+            sa = torch.exp2(-bx.float()).reshape(())
+            sb = torch.exp2(-bw.float()).reshape(())
+            fns.append(("hipblaslt", lambda: torch._scaled_mm(qx.view(f8), qw.view(f8).t(), scale_a=sa,
+                                                               scale_b=sb, out_dtype=torch.bfloat16)))
+        times = {k: [] for k, _ in fns}
+        for _ in range(3):
+            for k, f in fns:
+                f()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    f()
+                e1.record()
+                torch.cuda.synchronize()
+                times[k].append(e0.elapsed_time(e1) / reps)
+        ms = sorted(times["ours"])[1]
         tf = 2.0 * M * N * K / ms / 1e9
         out[name] = {"ms": round(ms, 4), "TFLOPs": round(tf, 1), "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+        if "hipblaslt" in times:
+            msb = sorted(times["hipblaslt"])[1]
+            out[name]["hipblaslt_TFLOPs_context"] = round(2.0 * M * N * K / msb / 1e9, 1)
         del x, w, y, qx, qw
     torch.cuda.empty_cache()
     return out
