@@ -7,6 +7,7 @@ codes, and invariants of round-to-nearest-even.
 """
 
 import json
+import math
 import os
 
 import numpy as np
@@ -231,3 +232,30 @@ def test_bf16_ulp_between_codes():
     lo = np.where(i + 1 > table.size - 1, i - 1, i)
     want = table[hi] - table[lo]
     assert np.array_equal(oracle.bf16_ulp(v), want)
+
+
+def test_f32_bits_to_f64_closed_form():
+    """float32 bit patterns against the IEEE binary32 definition written out:
+    (-1)^s 2^(e-127) (1 + m/2^23) for normal codes, (-1)^s 2^-126 m/2^23 for
+    subnormals, infinities and NaN for e = 255; spot values plus 4096 random
+    patterns."""
+    def ieee(u):
+        s, e, m = u >> 31, (u >> 23) & 0xFF, u & 0x7FFFFF
+        sign = -1.0 if s else 1.0
+        if e == 255:
+            return sign * math.inf if m == 0 else math.nan
+        if e == 0:
+            return sign * math.ldexp(m, -149)
+        return sign * math.ldexp(0x800000 + m, e - 150)
+    spots = {0x3F800000: 1.0, 0xC0000000: -2.0, 0x00000001: 2.0 ** -149, 0x00800000: 2.0 ** -126,
+             0x7F7FFFFF: (2 - 2.0 ** -23) * 2.0 ** 127, 0x80000000: -0.0, 0x7F800000: math.inf}
+    got = oracle.f32_bits_to_f64(np.array(list(spots), dtype=np.uint32))
+    for g, (u, want) in zip(got, spots.items()):
+        assert g == want and math.copysign(1.0, g) == math.copysign(1.0, want), hex(u)
+    assert np.isnan(oracle.f32_bits_to_f64(np.array([0x7FC00000, 0xFF800001], dtype=np.uint32))).all()
+    rng = np.random.default_rng(7)
+    u = rng.integers(0, 2 ** 32, size=4096, dtype=np.uint64).astype(np.uint32)
+    got = oracle.f32_bits_to_f64(u)
+    for g, x in zip(got, u.tolist()):
+        w = ieee(x)
+        assert (math.isnan(g) and math.isnan(w)) or (g == w and math.copysign(1.0, g) == math.copysign(1.0, w)), hex(x)
