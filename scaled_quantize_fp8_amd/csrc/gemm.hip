@@ -11,13 +11,17 @@
 // Answered": per-block scaling, each block with its own factor.
 //
 // Two kernels.
-//   * gemm_fwd_kernel: both operands K-contiguous and K % 128 == 0 (the
-//     forward product Y = X W^T and every MX product of that shape): 32x32x64
+//   * gemm_fwd_kernel: K % 128 == 0, both operands K-contiguous (the
+//     forward product Y = X W^T and every MX product of that shape) or, in
+//     the per-tensor product, either operand MN-major ([K x M] / [K x N]
+//     storage, the backward products dX = dY W and dW = dY^T X): 32x32x64
 //     MFMAs fed from a two-slot LDS pipeline (three slots for long per-tensor
-//     products on small grids) with asynchronous global -> LDS copies;
-//     described where it is defined.
-//   * gemm_kernel: every other layout (transposed operands, a K tail) with
-//     the design below.
+//     products on small grids) with asynchronous global -> LDS copies; an
+//     MN-major operand is copied as K rows and its fragments are read with
+//     the LDS transpose read ds_read_b64_tr_b8.  Described where it is
+//     defined.
+//   * gemm_kernel: every other case (a K tail, an MN-major op(A) on a grid of
+//     fewer 256 x 256 tiles than compute units) with the design below.
 //
 // gemm_kernel's CDNA4 mapping.
 //   * Macro tile 256 (M) x 256 (N) x 128 (K bytes), 256 lanes = 4 waves in a
@@ -562,6 +566,33 @@ __device__ __forceinline__ v8i frag_at(const uint8_t* lds, uint32_t base_lo, uin
   return f;
 }
 
+// The same operand from an MN-major stage (K rows of 256 bytes, MN
+// contiguous, the 16-byte chunk c of K row k stored at chunk c ^ tswz(k),
+// tswz(k) = (k & 7) | ((k >> 4) & 1) << 3), by four LDS transpose reads.
+// ds_read_b64_tr_b8 works on groups of 16 lanes: lane j of a group gives
+// the address of 8 bytes, row j / 2 and half j % 2 of an 8 x 16-byte block,
+// and receives column j of the block, its 8 rows.  Lane l (group q = l / 16,
+// j = l % 16, g = l / 32) takes 8 K rows at 16 g + {0, 8, 32, 40} + 64 h of
+// MN column 16 (q & 1) + j of the fragment: the 8-byte pieces of its
+// operand in K order.  Its rows all have tswz = (j >> 1) | g << 3, so
+// `base` (per lane and fragment) plus an immediate (slot, sub-step, piece)
+// addresses every read.
+template <int OFF>
+__device__ __forceinline__ v8i frag_tr(const uint8_t* lds, uint32_t base) {
+  typedef int v2i_t __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) v2i_t* lds_v2i;
+  const v2i_t p0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(lds + base + OFF));
+  const v2i_t p1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(lds + base + OFF + 8 * 256));
+  const v2i_t p2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(lds + base + OFF + 32 * 256));
+  const v2i_t p3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(lds + base + OFF + 40 * 256));
+  v8i f;
+  f[0] = p0.x; f[1] = p0.y; f[2] = p1.x; f[3] = p1.y;
+  f[4] = p2.x; f[5] = p2.y; f[6] = p3.x; f[7] = p3.y;
+  return f;
+}
+
+template <int N> using IC = std::integral_constant<int, N>;
+
 // Workgroup -> tile mapping of virtual block id vb (32-bit): XCD-aware remap,
 // then groups of kGroupM tile-rows (the mapping tile_coords gives blockIdx).
 __device__ __forceinline__ void tile_coords_vb(int vb, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -586,7 +617,7 @@ struct TileSrd {
   v4i a, b, sa, sb;
 };
 
-template <int FA, int FB, bool MX, int BMX, int NSLOT>
+template <int FA, int FB, bool MX, int BMX, int NSLOT, bool TA = false, bool TB = false>
 __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // BMX: tile rows (256, or 128 for grids with fewer 256 x 256 tiles than
   // compute units).  A 256-row tile puts the 4 waves in 2 x 2, each 128 x
@@ -607,6 +638,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // K = 8192 +17%; below K = 4096 two slots were 2-4% faster.
   constexpr int NS = NSLOT;
   static_assert(NS == 2 || (NS == 3 && BMX == 128 && !MX), "slot count");
+  // TA / TB: op(A) / op(B) stored MN-major ([K x M] / [K x N], the
+  // transposed layouts of the per-tensor product); their stages hold K rows
+  // of the tile's 256 MN bytes, read by LDS transposes (frag_tr)
+  static_assert(!(TA || TB) || !MX, "MN-major operands: per-tensor products");
+  static_assert(!TA || BMX == 256, "MN-major op(A): 256-row tiles");
   constexpr int kSlotA = NS == 3 ? BMX * BK : kTileBytes;   // op(A) bytes per slot
   constexpr int kSlotB = kTileBytes;                        // op(B) bytes per slot
   constexpr bool PF = NS == 2;                              // L2 prefetch of op(B)
@@ -653,8 +689,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
       tile_coords_vb(vb, tiles_m, tiles_n, tm, tn);
       const int64_t m0 = (int64_t)tm * BMX, n0 = (int64_t)tn * BN;
       const int64_t ra = g.M - m0 < BMX ? g.M - m0 : BMX, rb = g.N - n0 < BN ? g.N - n0 : BN;
-      T.a = make_srd(g.A + m0 * g.lda, (ra - 1) * g.lda + g.K);
-      T.b = make_srd(g.B + n0 * g.ldb, (rb - 1) * g.ldb + g.K);
+      // MN-major: the panel is K rows from column m0 / n0; a ragged tile's
+      // columns past the matrix end the last row's range (whole chunks:
+      // M, N % 16 == 0) and elsewhere read bytes that only reach C rows or
+      // columns past the matrix
+      T.a = TA ? make_srd(g.A + m0, (g.K - 1) * g.lda + ra) : make_srd(g.A + m0 * g.lda, (ra - 1) * g.lda + g.K);
+      T.b = TB ? make_srd(g.B + n0, (g.K - 1) * g.ldb + rb) : make_srd(g.B + n0 * g.ldb, (rb - 1) * g.ldb + g.K);
       if constexpr (MX) {
         if (g.scales_packed) {
           // one 256-row tile of the packed layout: sgroups x 4 KiB, rows past
@@ -687,13 +727,19 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // offset rides in soffset.  Offsets do not depend on the tile: a row past
   // the matrix has offset >= ra * ld >= (ra - 1) * ld + K, the panel's size.
   const int cl = (lane & 7) ^ (lane >> 3);          // ^ (blk & 1) = ^ (i & 1) below
+  // MN-major: block b of the stage is K rows 4b .. 4b+3 (256 bytes each);
+  // lane L lands at row 4b + L/16, stored chunk L%16, so it fetches logical
+  // chunk (L%16) ^ tswz(row); the stage's K offset (k0 rows) rides in
+  // soffset as k0 * ld.
   uint32_t offa[8], offb[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = (wave * 8 + i) * 8 + (lane >> 3);
     const int rowa_c = (wave * NA + (i % NA)) * 8 + (lane >> 3);
-    offa[i] = (uint32_t)(rowa_c * g.lda + 16 * (cl ^ (i & 1)));
-    offb[i] = (uint32_t)(row * g.ldb + 16 * (cl ^ (i & 1)));
+    const int krow = (wave * 8 + i) * 4 + (lane >> 4);
+    const int kc = (lane & 15) ^ ((krow & 7) | (((krow >> 4) & 1) << 3));
+    offa[i] = TA ? (uint32_t)(krow * g.lda + 16 * kc) : (uint32_t)(rowa_c * g.lda + 16 * (cl ^ (i & 1)));
+    offb[i] = TB ? (uint32_t)(krow * g.ldb + 16 * kc) : (uint32_t)(row * g.ldb + 16 * (cl ^ (i & 1)));
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
   // MX scales: lane L of wave w copies 16 bytes (the codes of 4 stages) of
@@ -709,7 +755,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // landing in pf_sink; the other workgroups issue the same load through a
   // size-0 descriptor.  Measured: +5% per-tensor, +7% MX (prefetching from
   // every workgroup, or both operands 2 stages ahead, was slower).
-  const uint32_t pfb = (uint32_t)((wave * 64 + lane) * g.ldb);
+  // (MN-major op(B): the stage's 128 K rows of 256 bytes are 256 lines, one
+  // per lane, and the K offset rides in soffset as k0 * ldb)
+  const uint32_t pfb = TB ? (uint32_t)(((wave * 64 + lane) >> 1) * g.ldb + 128 * (lane & 1))
+                          : (uint32_t)((wave * 64 + lane) * g.ldb);
   const uint32_t pf_lds = __builtin_amdgcn_readfirstlane(lds_offset(pf_sink));
   uint32_t offsa = 0, offsb = 0, ldss = 0;
   if constexpr (MX) {
@@ -748,10 +797,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     v4i srd = isb ? cur.b : cur.a;
     if constexpr (PERSIST) srd = nx ? (isb ? nxt.b : nxt.a) : srd;
     srd[2] = live ? srd[2] : 0;
+    const bool mn = isb ? TB : TA;
+    const uint32_t so = mn ? k0 * (uint32_t)(isb ? g.ldb : g.lda) : k0;
     if (t == 0 || t == NA)
-      dma_b128_so<5>(uniform_srd(srd), __builtin_amdgcn_readfirstlane(la), off, __builtin_amdgcn_readfirstlane(k0));
+      dma_b128_so<5>(uniform_srd(srd), __builtin_amdgcn_readfirstlane(la), off, __builtin_amdgcn_readfirstlane(so));
     else
-      dma_b128_so<1>(uniform_srd(srd), __builtin_amdgcn_readfirstlane(la), off, __builtin_amdgcn_readfirstlane(k0));
+      dma_b128_so<1>(uniform_srd(srd), __builtin_amdgcn_readfirstlane(la), off, __builtin_amdgcn_readfirstlane(so));
   };
   // prefetch of op(B) stage s (descriptor choice as for the copies)
   auto prefetch_b = [&](int s, bool owner) {
@@ -762,7 +813,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     v4i srd = cur.b;
     if constexpr (PERSIST) srd = nx ? nxt.b : srd;
     srd[2] = live ? srd[2] : 0;
-    dma_b32_so<5>(uniform_srd(srd), pf_lds, pfb, __builtin_amdgcn_readfirstlane(k0));
+    dma_b32_so<5>(uniform_srd(srd), pf_lds, pfb, __builtin_amdgcn_readfirstlane(TB ? k0 * (uint32_t)g.ldb : k0));
   };
   // Scale group G of the current tile, 0 <= G <= ngroups (G == ngroups: the
   // next tile's group 0, whose copy starts at block 0).
@@ -820,6 +871,27 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   const uint32_t a1lo = rowa + (((4 + gq) ^ s7) << 4), a1hi = rowa + (((6 + gq) ^ s7) << 4);
   const uint32_t b0lo = rowb + (((0 + gq) ^ s7) << 4), b0hi = rowb + (((2 + gq) ^ s7) << 4);
   const uint32_t b1lo = rowb + (((4 + gq) ^ s7) << 4), b1hi = rowb + (((6 + gq) ^ s7) << 4);
+  // MN-major operands: per-lane base of fragment j (frag_tr), slot 0, sub-step 0
+  const int tq = lane >> 4, tj = lane & 15;
+  const int tsw = (tj >> 1) | (gq << 3);
+  uint32_t abase[4], bbase[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t kr = (uint32_t)((16 * gq + (tj >> 1)) * 256 + 8 * (tj & 1));
+    abase[j] = kr + (uint32_t)(((((wm * 128 + 32 * j) >> 4) + (tq & 1)) ^ tsw) << 4);
+    bbase[j] = kRegB + kr + (uint32_t)(((((wn * WN + 32 * j) >> 4) + (tq & 1)) ^ tsw) << 4);
+  }
+  // fragment j of sub-step H at slot offset OFF, in either layout
+  auto frA = [&](auto off_c, auto h_c, auto j_c) -> v8i {
+    constexpr int OFF = decltype(off_c)::value, H = decltype(h_c)::value, J = decltype(j_c)::value;
+    if constexpr (TA) return frag_tr<OFF + H * 64 * 256>(smem, abase[J]);
+    else return frag_at<OFF + J * kFrag>(smem, H ? a1lo : a0lo, H ? a1hi : a0hi);
+  };
+  auto frB = [&](auto off_c, auto h_c, auto j_c) -> v8i {
+    constexpr int OFF = decltype(off_c)::value, H = decltype(h_c)::value, J = decltype(j_c)::value;
+    if constexpr (TB) return frag_tr<OFF + H * 64 * 256>(smem, bbase[J]);
+    else return frag_at<OFF + J * kFrag>(smem, H ? b1lo : b0lo, H ? b1hi : b0hi);
+  };
 
   // prologue (first tile only; later tiles are prefetched by the previous
   // tile's last two stages): stages 0 and 1 in flight, stage 0 published,
@@ -841,16 +913,17 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // and each wait leaves the next stage's LPS copies in flight.
   prefetch_b(7, pf_owner);
   if constexpr (NS == 3) wait_vm<2 * LPS>();
-  else wait_vm<LPS + 1>();
+  else if constexpr (PF) wait_vm<LPS + 1>();
+  else wait_vm<LPS>();                               // no prefetch (MN-major op(B)): stage 1's copies
   __syncthreads();
   v8i x0[4], w0[4], x1[4], w1[4];
   int sc[2][8] = {};                                 // scale registers of stages 0-1 and 2-3 of the group
   int sc_next[8] = {};                               // the next group's stages 2-3, read with its 0-1
-  x0[0] = frag_at<0 * kFrag>(smem, a0lo, a0hi); x0[1] = frag_at<1 * kFrag>(smem, a0lo, a0hi);
-  x0[2] = frag_at<2 * kFrag>(smem, a0lo, a0hi); x0[3] = frag_at<3 * kFrag>(smem, a0lo, a0hi);
-  w0[0] = frag_at<0 * kFrag>(smem, b0lo, b0hi); w0[1] = frag_at<1 * kFrag>(smem, b0lo, b0hi);
+  x0[0] = frA(IC<0>{}, IC<0>{}, IC<0>{}); x0[1] = frA(IC<0>{}, IC<0>{}, IC<1>{});
+  x0[2] = frA(IC<0>{}, IC<0>{}, IC<2>{}); x0[3] = frA(IC<0>{}, IC<0>{}, IC<3>{});
+  w0[0] = frB(IC<0>{}, IC<0>{}, IC<0>{}); w0[1] = frB(IC<0>{}, IC<0>{}, IC<1>{});
   if constexpr (NI == 4) {
-    w0[2] = frag_at<2 * kFrag>(smem, b0lo, b0hi); w0[3] = frag_at<3 * kFrag>(smem, b0lo, b0hi);
+    w0[2] = frB(IC<0>{}, IC<0>{}, IC<2>{}); w0[3] = frB(IC<0>{}, IC<0>{}, IC<3>{});
   }
   read_group(0, sc[0], sc[1], 0, 4);
 
@@ -871,14 +944,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     for (int t = 0; t < NT; ++t) {
       const int i = t >> 2, j = t & 3;
       switch (t) {
-        case 0: x1[0] = frag_at<SLOT * kSlotA + 0 * kFrag>(smem, a1lo, a1hi); break;
-        case 1: x1[1] = frag_at<SLOT * kSlotA + 1 * kFrag>(smem, a1lo, a1hi); break;
-        case 2: x1[2] = frag_at<SLOT * kSlotA + 2 * kFrag>(smem, a1lo, a1hi); break;
-        case 3: x1[3] = frag_at<SLOT * kSlotA + 3 * kFrag>(smem, a1lo, a1hi); break;
-        case 4: w1[0] = frag_at<SLOT * kSlotB + 0 * kFrag>(smem, b1lo, b1hi); break;
-        case 5: w1[1] = frag_at<SLOT * kSlotB + 1 * kFrag>(smem, b1lo, b1hi); break;
-        case 6: if constexpr (NI == 4) w1[2] = frag_at<SLOT * kSlotB + 2 * kFrag>(smem, b1lo, b1hi); break;
-        case 7: if constexpr (NI == 4) w1[3] = frag_at<SLOT * kSlotB + 3 * kFrag>(smem, b1lo, b1hi); break;
+        case 0: x1[0] = frA(IC<SLOT * kSlotA>{}, IC<1>{}, IC<0>{}); break;
+        case 1: x1[1] = frA(IC<SLOT * kSlotA>{}, IC<1>{}, IC<1>{}); break;
+        case 2: x1[2] = frA(IC<SLOT * kSlotA>{}, IC<1>{}, IC<2>{}); break;
+        case 3: x1[3] = frA(IC<SLOT * kSlotA>{}, IC<1>{}, IC<3>{}); break;
+        case 4: w1[0] = frB(IC<SLOT * kSlotB>{}, IC<1>{}, IC<0>{}); break;
+        case 5: w1[1] = frB(IC<SLOT * kSlotB>{}, IC<1>{}, IC<1>{}); break;
+        case 6: if constexpr (NI == 4) w1[2] = frB(IC<SLOT * kSlotB>{}, IC<1>{}, IC<2>{}); break;
+        case 7: if constexpr (NI == 4) w1[3] = frB(IC<SLOT * kSlotB>{}, IC<1>{}, IC<3>{}); break;
         default: break;
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -889,7 +962,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (NS == 3) wait_vm<LPS>();            // all but stage kt+2's copies
-    else wait_vm<1>();                                // all but the prefetch, issued last
+    else if constexpr (PF) wait_vm<1>();              // all but the prefetch, issued last
+    else wait_vm<0>();                                // no prefetch: every copy
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -904,14 +978,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
         if constexpr (MX && POS == 2)
           if (t >= T0 && t < T0 + 4) read_group((kt >> 2) + 1, sc[0], sc_next, t - T0, t - T0 + 1);
         switch (t) {
-          case 0: x0[0] = frag_at<NSL * kSlotA + 0 * kFrag>(smem, a0lo, a0hi); break;
-          case 1: x0[1] = frag_at<NSL * kSlotA + 1 * kFrag>(smem, a0lo, a0hi); break;
-          case 2: x0[2] = frag_at<NSL * kSlotA + 2 * kFrag>(smem, a0lo, a0hi); break;
-          case 3: x0[3] = frag_at<NSL * kSlotA + 3 * kFrag>(smem, a0lo, a0hi); break;
-          case 4: w0[0] = frag_at<NSL * kSlotB + 0 * kFrag>(smem, b0lo, b0hi); break;
-          case 5: w0[1] = frag_at<NSL * kSlotB + 1 * kFrag>(smem, b0lo, b0hi); break;
-          case 6: if constexpr (NI == 4) w0[2] = frag_at<NSL * kSlotB + 2 * kFrag>(smem, b0lo, b0hi); break;
-          case 7: if constexpr (NI == 4) w0[3] = frag_at<NSL * kSlotB + 3 * kFrag>(smem, b0lo, b0hi); break;
+          case 0: x0[0] = frA(IC<NSL * kSlotA>{}, IC<0>{}, IC<0>{}); break;
+          case 1: x0[1] = frA(IC<NSL * kSlotA>{}, IC<0>{}, IC<1>{}); break;
+          case 2: x0[2] = frA(IC<NSL * kSlotA>{}, IC<0>{}, IC<2>{}); break;
+          case 3: x0[3] = frA(IC<NSL * kSlotA>{}, IC<0>{}, IC<3>{}); break;
+          case 4: w0[0] = frB(IC<NSL * kSlotB>{}, IC<0>{}, IC<0>{}); break;
+          case 5: w0[1] = frB(IC<NSL * kSlotB>{}, IC<0>{}, IC<1>{}); break;
+          case 6: if constexpr (NI == 4) w0[2] = frB(IC<NSL * kSlotB>{}, IC<0>{}, IC<2>{}); break;
+          case 7: if constexpr (NI == 4) w0[3] = frB(IC<NSL * kSlotB>{}, IC<0>{}, IC<3>{}); break;
           default: break;
         }
       }
@@ -1153,24 +1227,33 @@ static void launch_gemm(const GemmArgs& g, hipStream_t s) {
   // (whole groups; packed scales are padded to whole groups); one tile
   // per workgroup (or, with kFwdPersistent, per-tensor products walk tiles
   // with one workgroup per compute unit)
-  if (!TA && !TB && g.K > 0 && (g.K % 128) == 0 && (!MX || g.scales_dma)) {
-    const int64_t ncu = device_cu_count();
+  // MN-major operands (TA / TB, per-tensor) take the forward kernel with
+  // LDS transpose reads when K % 128 == 0; MN-major op(A) only with 256-row
+  // tiles, so a grid of fewer 256 x 256 tiles than compute units keeps the
+  // generic kernel for it
+  const int64_t ncu = device_cu_count();
+  const bool fwd = g.K > 0 && (g.K % 128) == 0 && (!MX || g.scales_dma) && (!TA || tiles >= ncu);
+  if (fwd) {
     if (tiles < ncu) {
       // fewer 256 x 256 tiles than compute units: 128 x 256 tiles
       const int64_t t128 = ((g.M + 127) / 128) * ((g.N + BN - 1) / BN);
       // three LDS slots for long per-tensor products (see gemm_fwd_kernel)
-      if constexpr (!MX) {
+      if constexpr (!MX && !TA) {
         if (g.K >= 4096) {
-          hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 3>), dim3((unsigned)t128), dim3(kGemmThreads), 0, s, g);
+          hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 3, false, TB>), dim3((unsigned)t128),
+                             dim3(kGemmThreads), 0, s, g);
           return;
         }
       }
-      hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 2>), dim3((unsigned)t128), dim3(kGemmThreads), 0, s, g);
+      if constexpr (!TA)
+        hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 2, false, TB>), dim3((unsigned)t128),
+                           dim3(kGemmThreads), 0, s, g);
       return;
     }
     const int64_t cus = (MX || !kFwdPersistent) ? tiles : ncu;
     const int64_t grid = tiles < cus ? tiles : cus;
-    hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 256, 2>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s, g);
+    hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 256, 2, TA, TB>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s,
+                       g);
   } else {
     hipLaunchKernelGGL((gemm_kernel<FA, FB, MX, TA, TB>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, g);
   }

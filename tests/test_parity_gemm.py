@@ -188,6 +188,31 @@ def test_gemm_transposed_operands(ta, tb):
     _check_amax(C, am)
 
 
+@pytest.mark.parametrize("M,N,K", [(4112, 4112, 512), (272, 528, 1024), (272, 528, 4096)],
+                         ids=["289tiles_K512", "small_K1024", "small_K4096"])
+@pytest.mark.parametrize("ta,tb", [(False, True), (True, False), (True, True)], ids=["NT", "TN", "TT"])
+def test_gemm_mn_major_operands_forward_kernel(ta, tb, M, N, K):
+    """MN-major storage ([K x M] / [K x N]) with K % 128 == 0 takes the
+    forward kernel, whose stages hold K rows of the operand and whose
+    fragments come from LDS transpose reads: ragged M and N tiles, a grid of
+    289 256 x 256 tiles, and small grids (128 x 256 tiles; two and three LDS
+    slots; MN-major op(A) keeps the generic kernel there).  Every output
+    against the oracle, and bit for bit equal to the same product from
+    K-major copies of the operands."""
+    rng = np.random.default_rng(26)
+    qa, ba = _operand(rng, (M, K), 1e-4, E5M2)
+    qb, bb = _operand(rng, (N, K), 0.02, E4M3)
+    say(f"gemm MN-major ta={ta} tb={tb} {M}x{N}x{K}")
+    C, am = _run_pt(qa, E5M2, ba, qb, E4M3, bb, ta, tb, torch.bfloat16)
+    C0, am0 = _run_pt(qa, E5M2, ba, qb, E4M3, bb, False, False, torch.bfloat16)
+    assert torch.equal(C.view(torch.int16), C0.view(torch.int16)) and f32_bits_of(am) == f32_bits_of(am0)
+    ref = oracle.scaled_gemm_ref(qa, E5M2, ba, qb, E4M3, bb)
+    s = oracle.abs_product_sum(qa, E5M2, ba, qb, E4M3, bb)
+    gt = mfma_operands_pt(qa, E5M2, ba, qb, E4M3, bb)
+    assert_gemm_close(host_f64(C), ref, s, True, f"MN-major {ta}{tb}", gt)
+    _check_amax(C, am)
+
+
 def test_gemm_degenerate_shapes():
     rng = np.random.default_rng(23)
     qa, ba = _operand(rng, (64, 32), 1.0, E4M3)
