@@ -312,10 +312,13 @@ def vs_hipblaslt(x, w, rounds: int = 3, reps: int = 5):
 
 def backward_extras(dev, reps: int = 5):
     """The 7B-MLP down-projection backward (dY [4096 x 11008], W [11008 x
-    4096], X [4096 x 4096]) as the linear layer runs it: transposed casts,
-    then dX = dY W and dW = dY^T X as K-contiguous (TN) products; per-tensor
-    (E5M2 gradient x E4M3) and MX.  Synthetic N(0, s) inputs drawn on the
-    device; timed outside the headline step."""
+    4096], X [4096 x 4096]) as the linear layer runs it: per tensor (E5M2
+    gradient x E4M3), the cast of dY and the products dX = dY W and
+    dW = dY^T X on the stored codes (MN-major operands), and for comparison
+    the transposed-copy scheme (casts writing dY^T, W^T, X^T, then TN
+    products); MX: transposed MX casts, then TN products on packed scales.
+    Synthetic N(0, s) inputs drawn on the device; timed outside the headline
+    step."""
     import torch
     import scaled_quantize_fp8_amd as sq
     T, H, F = 4096, 4096, 11008
@@ -330,11 +333,23 @@ def backward_extras(dev, reps: int = 5):
     qx, qxT = torch.empty(T, H, dtype=torch.uint8, device=dev), torch.empty(H, T, dtype=torch.uint8, device=dev)
     dx = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
     dw = torch.empty(F, H, dtype=torch.bfloat16, device=dev)
-    pt = [("cast_t_dY", lambda: sq.fp8_quantize(dy, sq.E5M2, bdy, q=qdy, qT=qdyT), 4 * T * F),
-          ("cast_t_W", lambda: sq.fp8_quantize(w, sq.E4M3, bw, q=qw, qT=qwT), 4 * F * H),
-          ("cast_t_X", lambda: sq.fp8_quantize(x, sq.E4M3, bx, q=qx, qT=qxT), 4 * T * H),
-          ("gemm_dX", lambda: sq.fp8_scaled_gemm(qdy, sq.E5M2, bdy, qwT, sq.E4M3, bw, out=dx), None),
-          ("gemm_dW", lambda: sq.fp8_scaled_gemm(qdyT, sq.E5M2, bdy, qxT, sq.E4M3, bx, out=dw), None)]
+    # per tensor, as Fp8Linear runs it: the backward products read the
+    # stored codes MN-major (dX = dY W with W [F x H] as op(B); dW = dY^T X
+    # with dY [T x F] and X [T x H]), so only dY is cast, without a
+    # transposed copy (W and X come from the forward casts)
+    sq.fp8_quantize(w, sq.E4M3, bw, q=qw)
+    sq.fp8_quantize(x, sq.E4M3, bx, q=qx)
+    pt = [("cast_dY", lambda: sq.fp8_quantize(dy, sq.E5M2, bdy, q=qdy), 3 * T * F),
+          ("gemm_dX_NN", lambda: sq.fp8_scaled_gemm(qdy, sq.E5M2, bdy, qw, sq.E4M3, bw, trans_b=True, out=dx), None),
+          ("gemm_dW_TT", lambda: sq.fp8_scaled_gemm(qdy, sq.E5M2, bdy, qx, sq.E4M3, bx, trans_a=True, trans_b=True,
+                                                     out=dw), None)]
+    # the transposed-copy scheme: casts of dY, W and X that also write the
+    # transposed copies, then K-contiguous (TN) products
+    ptt = [("cast_t_dY", lambda: sq.fp8_quantize(dy, sq.E5M2, bdy, q=qdy, qT=qdyT), 4 * T * F),
+           ("cast_t_W", lambda: sq.fp8_quantize(w, sq.E4M3, bw, q=qw, qT=qwT), 4 * F * H),
+           ("cast_t_X", lambda: sq.fp8_quantize(x, sq.E4M3, bx, q=qx, qT=qxT), 4 * T * H),
+           ("gemm_dX", lambda: sq.fp8_scaled_gemm(qdy, sq.E5M2, bdy, qwT, sq.E4M3, bw, out=dx), None),
+           ("gemm_dW", lambda: sq.fp8_scaled_gemm(qdyT, sq.E5M2, bdy, qxT, sq.E4M3, bx, out=dw), None)]
     # MX: every cast writes its E8M0 codes in the packed layout the products
     # read (as Fp8Linear does when K % 128 == 0 and K >= 512)
     u8 = dict(dtype=torch.uint8, device=dev)
@@ -350,7 +365,7 @@ def backward_extras(dev, reps: int = 5):
           ("mx_gemm_dW", lambda: sq.mx_scaled_gemm_packed(mqT, sq.E5M2, msT, mxT, sq.E4M3, msxT, out=dw), None)]
     flops = 2.0 * T * H * F
     out = {"shapes": "dY [4096 x 11008] E5M2, W [11008 x 4096], X [4096 x 4096] E4M3; bf16 out"}
-    for tag, ops in (("per_tensor", pt), ("mx", mx)):
+    for tag, ops in (("per_tensor", pt), ("per_tensor_transposed_copies", ptt), ("mx", mx)):
         total = 0.0
         res = {}
         for name, fn, byts in ops:

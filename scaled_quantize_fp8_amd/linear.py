@@ -10,16 +10,21 @@ Answered": the scale may come from the amaxes of past iterations (delayed
 scaling) or from each block of the tensor (per-block, MX).
 
 Every step runs in the HIP library; this module only routes tensors between
-entry points.  The three products all read K-contiguous operands (the fast
-TN GEMM):
+entry points.  The products:
 
     forward   Y  = X W^T      A = X   [T x in],   B = W   [out x in]
-    backward  dX = dY W       A = dY  [T x out],  B = W^T [in x out]
-              dW = dY^T X     A = dY^T [out x T], B = X^T [in x T]
+    backward  dX = dY W       op(A) = dY [T x out],  op(B) = W^T [in x out]
+              dW = dY^T X     op(A) = dY^T [out x T], op(B) = X^T [in x T]
 
-W^T and X^T are the transposed copies written by the forward casts (the
-per-tensor cast writes both layouts in one pass; MX casts W^T and X^T with
-blocks along their new contiguous axis), dY^T by the backward cast.
+Per-tensor recipes pass the backward products the codes as they are stored:
+W and X from the forward casts and dY as op(B) / op(A) stored MN-major
+(`trans_a` / `trans_b`), which the forward GEMM kernel reads with LDS
+transposes as fast as K-contiguous operands, so no transposed copy is cast.
+It needs the product's K % 128 == 0 (and, for dW's MN-major op(A), at least
+as many 256 x 256 output tiles as compute units); where a product does not
+qualify, the casts also write the transposed copy (one pass) and that
+product reads K-contiguous operands.  The MX recipe casts W^T, X^T and dY^T
+with blocks along their new contiguous axis, the products' K.
 
 Recipes:
     "current"  per-tensor, bias from the tensor's own amax (two passes:
@@ -50,6 +55,23 @@ from . import (E4M3, E5M2, _rule, amax_scale_workspace, fp8_amax_scale, fp8_hist
                mx_scaled_gemm_packed)
 
 RECIPES = ("current", "delayed", "mx", "constant")
+
+
+def _cu_count(device) -> int:
+    device = torch.device(device)
+    if device.type != "cuda":
+        return 1 << 30           # no GPU tensor: the library calls refuse it anyway
+    return torch.cuda.get_device_properties(device).multi_processor_count
+
+
+def _mn_major_ok(m: int, n: int, k: int, lda_k: int, ldb_k: int, trans_a: bool, device) -> bool:
+    """Whether a per-tensor product with MN-major operands runs on the fast
+    kernel: K % 128 == 0, an MN-major operand spans < 2 GiB (K x its leading
+    dimension), and an MN-major op(A) needs at least one 256 x 256 tile per
+    compute unit."""
+    if k % 128 or k == 0 or lda_k >= (1 << 31) - 4096 or ldb_k >= (1 << 31) - 4096:
+        return False
+    return not trans_a or ((m + 255) // 256) * ((n + 255) // 256) >= _cu_count(device)
 
 
 def _packable(m: int, n: int, k: int) -> bool:
@@ -141,12 +163,18 @@ class Fp8LinearFunction(torch.autograd.Function):
                 qxT, sxT = (mx_quantize_t_packed if ctx.pk_dw else mx_quantize_t_rule)(x2, E4M3, rule)
                 ctx.save_for_backward(qwT, swT, qxT, sxT)
         else:
-            bx, qx, qxT = _per_tensor_cast(x2, E4M3, recipe, layer.margin, layer._hx, True, layer._bias,
-                                           layer._log, "x", layer._ws)
-            bw, qw, qwT = _per_tensor_cast(w, E4M3, recipe, layer.margin, layer._hw, True, layer._bias,
-                                           layer._log, "w", layer._ws)
+            # backward products on the stored codes where the fast kernel
+            # takes them MN-major: dX = dY W with W [out x in] as op(B)
+            # (K = out), dW = dY^T X with dY [T x out] and X [T x in] (K = T)
+            T, N, D = x2.shape[0], w.shape[0], w.shape[1]
+            ctx.mn_dx = _mn_major_ok(T, D, N, 0, N * D, False, x.device)
+            ctx.mn_dw = _mn_major_ok(N, D, T, T * N, T * D, True, x.device)
+            bx, qx, qxT = _per_tensor_cast(x2, E4M3, recipe, layer.margin, layer._hx, not ctx.mn_dw,
+                                           layer._bias, layer._log, "x", layer._ws)
+            bw, qw, qwT = _per_tensor_cast(w, E4M3, recipe, layer.margin, layer._hw, not ctx.mn_dx,
+                                           layer._bias, layer._log, "w", layer._ws)
             y, amax = fp8_scaled_gemm(qx, E4M3, bx, qw, E4M3, bw, out_dtype=x.dtype, want_amax=True)
-            ctx.save_for_backward(qwT, bw, qxT, bx)
+            ctx.save_for_backward(qw if ctx.mn_dx else qwT, bw, qx if ctx.mn_dw else qxT, bx)
         layer.last_output_amax = amax
         ctx.layer = layer
         ctx.lead = lead
@@ -179,13 +207,18 @@ class Fp8LinearFunction(torch.autograd.Function):
                     qdyT, sdyT = mx_quantize_t_rule(dy2, E5M2, layer.mx_rule)
                     dw, _ = mx_scaled_gemm(qdyT, E5M2, sdyT, qxT, E4M3, sxT, out_dtype=ctx.dtype)
         else:
-            qwT, bw, qxT, bx = ctx.saved_tensors
+            qw_, bw, qx_, bx = ctx.saved_tensors           # W, X codes (MN-major use) or W^T, X^T
             bdy, qdy, qdyT = _per_tensor_cast(dy2, E5M2, layer.recipe, layer.margin, layer._hdy,
-                                              ctx.needs_input_grad[1], layer._bias, layer._log, "dy", layer._ws)
+                                              ctx.needs_input_grad[1] and not ctx.mn_dw, layer._bias,
+                                              layer._log, "dy", layer._ws)
             if ctx.needs_input_grad[0]:
-                dx, _ = fp8_scaled_gemm(qdy, E5M2, bdy, qwT, E4M3, bw, out_dtype=ctx.dtype)
+                dx, _ = fp8_scaled_gemm(qdy, E5M2, bdy, qw_, E4M3, bw, trans_b=ctx.mn_dx, out_dtype=ctx.dtype)
             if ctx.needs_input_grad[1]:
-                dw, _ = fp8_scaled_gemm(qdyT, E5M2, bdy, qxT, E4M3, bx, out_dtype=ctx.dtype)
+                if ctx.mn_dw:
+                    dw, _ = fp8_scaled_gemm(qdy, E5M2, bdy, qx_, E4M3, bx, trans_a=True, trans_b=True,
+                                            out_dtype=ctx.dtype)
+                else:
+                    dw, _ = fp8_scaled_gemm(qdyT, E5M2, bdy, qx_, E4M3, bx, out_dtype=ctx.dtype)
         if dx is not None:
             dx = dx.reshape(*ctx.lead, dx.shape[-1])
         return dx, dw, None

@@ -176,6 +176,58 @@ def test_linear_scale_log_16_delayed_steps():
 
 
 @pytest.mark.gpu
+@pytest.mark.parametrize("recipe", ["current", "delayed"])
+def test_linear_backward_on_stored_codes(recipe):
+    """A layer large enough that both backward products read the stored
+    codes MN-major (dX = dY W with W [out x in] as op(B); dW = dY^T X with
+    dY [T x out] and X [T x in], 272 output tiles), so no cast writes a
+    transposed copy: Y, dX and dW on sampled rows and columns (two per
+    256-wide tile, so every output tile) against the oracle's products, two
+    steps for the delayed recipe."""
+    from scaled_quantize_fp8_amd.linear import _mn_major_ok
+    need_gpu()
+    t, i, o = 2048, 4352, 4096
+    assert _mn_major_ok(t, i, o, 0, o * i, False, DEV) and _mn_major_ok(o, i, t, t * o, t * i, True, DEV)
+    layer = Fp8Linear(i, o, recipe=recipe, device=DEV)
+    rng = np.random.default_rng(61)
+
+    def rows(n):
+        return np.unique(np.concatenate([np.minimum(np.arange(0, n, 256)[:, None] + rng.integers(0, 256, (1, 2)),
+                                                    n - 1).ravel(), [0, n - 1]]))
+    hs = [oracle.DelayedScaling(16) for _ in range(3)]
+    for step in range(2 if recipe == "delayed" else 1):
+        x, w, dy = _tensors(step=step, shape=(t, i, o))
+        with torch.no_grad():
+            layer.weight.copy_(_dev(w))
+        layer.weight.grad = None
+        say(f"fp8 linear {recipe} step {step}, backward on stored codes, {t} x {i} -> {o}")
+        y, dx, dw, _ = _run(layer, x, dy)
+        if recipe == "current":
+            bx, bw, bdy = (oracle.compute_bias(oracle.amax(x), E4M3), oracle.compute_bias(oracle.amax(w), E4M3),
+                           oracle.compute_bias(oracle.amax(dy), E5M2))
+        else:
+            # step 0 pushes its own amax first; later steps take the window's bias, then push
+            biases = []
+            for h, v, fmt in zip(hs, (x, w, dy), (E4M3, E4M3, E5M2)):
+                if step == 0:
+                    h.push(oracle.amax(v))
+                biases.append(h.bias(fmt))
+                if step > 0:
+                    h.push(oracle.amax(v))
+            bx, bw, bdy = biases
+        qx, qw, qdy = oracle.quantize(x, E4M3, bx), oracle.quantize(w, E4M3, bw), oracle.quantize(dy, E5M2, bdy)
+        rt, ri, ro = rows(t), rows(i), rows(o)
+        for what, got, a, fa, ba, b, fb, bb in (
+                ("y", y[np.ix_(rt, ro)], qx[rt], E4M3, bx, qw[ro], E4M3, bw),
+                ("dx", dx[np.ix_(rt, ri)], qdy[rt], E5M2, bdy, np.ascontiguousarray(qw.T[ri]), E4M3, bw),
+                ("dw", dw[np.ix_(ro, ri)], np.ascontiguousarray(qdy.T[ro]), E5M2, bdy,
+                 np.ascontiguousarray(qx.T[ri]), E4M3, bx)):
+            ref = oracle.scaled_gemm_ref(a, fa, ba, b, fb, bb)
+            s = oracle.abs_product_sum(a, fa, ba, b, fb, bb)
+            _check(f"{recipe} step {step} {what}", got, ref, s, mfma_operands_pt(a, fa, ba, b, fb, bb))
+
+
+@pytest.mark.gpu
 def test_linear_batched_input_shape():
     need_gpu()
     layer = Fp8Linear(IN, OUT, device=DEV)
