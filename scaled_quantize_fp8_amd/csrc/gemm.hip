@@ -20,8 +20,8 @@
 //     MN-major operand is copied as K rows and its fragments are read with
 //     the LDS transpose read ds_read_b64_tr_b8.  Described where it is
 //     defined.
-//   * gemm_kernel: every other case (a K tail, an MN-major op(A) on a grid of
-//     fewer 256 x 256 tiles than compute units) with the design below.
+//   * gemm_kernel: every other case (a K tail, K % 128 != 0; MX on
+//     row-major scales with K % 512 != 0) with the design below.
 //
 // gemm_kernel's CDNA4 mapping.
 //   * Macro tile 256 (M) x 256 (N) x 128 (K bytes), 256 lanes = 4 waves in a
@@ -566,25 +566,27 @@ __device__ __forceinline__ v8i frag_at(const uint8_t* lds, uint32_t base_lo, uin
   return f;
 }
 
-// The same operand from an MN-major stage (K rows of 256 bytes, MN
-// contiguous, the 16-byte chunk c of K row k stored at chunk c ^ tswz(k),
-// tswz(k) = (k & 7) | ((k >> 4) & 1) << 3), by four LDS transpose reads.
+// The same operand from an MN-major stage (K rows of RS = 256 or 128 bytes,
+// MN contiguous, the 16-byte chunk c of K row k stored at chunk c ^ tswz(k):
+// (k & 7) | ((k >> 4) & 1) << 3 for 256-byte rows, ((k >> 1) & 3) << 1 for
+// 128-byte rows), by four LDS transpose reads.
 // ds_read_b64_tr_b8 works on groups of 16 lanes: lane j of a group gives
 // the address of 8 bytes, row j / 2 and half j % 2 of an 8 x 16-byte block,
 // and receives column j of the block, its 8 rows.  Lane l (group q = l / 16,
 // j = l % 16, g = l / 32) takes 8 K rows at 16 g + {0, 8, 32, 40} + 64 h of
 // MN column 16 (q & 1) + j of the fragment: the 8-byte pieces of its
-// operand in K order.  Its rows all have tswz = (j >> 1) | g << 3, so
-// `base` (per lane and fragment) plus an immediate (slot, sub-step, piece)
-// addresses every read.
-template <int OFF>
+// operand in K order.  Its rows all have one tswz ((j >> 1) | g << 3 for
+// 256-byte rows, ((j >> 2) & 3) << 1 for 128-byte rows), so `base` (per lane
+// and fragment) plus an immediate (slot, sub-step, piece) addresses every
+// read.
+template <int OFF, int RS>
 __device__ __forceinline__ v8i frag_tr(const uint8_t* lds, uint32_t base) {
   typedef int v2i_t __attribute__((ext_vector_type(2)));
   typedef __attribute__((address_space(3))) v2i_t* lds_v2i;
   const v2i_t p0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(lds + base + OFF));
-  const v2i_t p1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(lds + base + OFF + 8 * 256));
-  const v2i_t p2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(lds + base + OFF + 32 * 256));
-  const v2i_t p3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(lds + base + OFF + 40 * 256));
+  const v2i_t p1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(lds + base + OFF + 8 * RS));
+  const v2i_t p2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(lds + base + OFF + 32 * RS));
+  const v2i_t p3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(lds + base + OFF + 40 * RS));
   v8i f;
   f[0] = p0.x; f[1] = p0.y; f[2] = p1.x; f[3] = p1.y;
   f[4] = p2.x; f[5] = p2.y; f[6] = p3.x; f[7] = p3.y;
@@ -642,7 +644,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // transposed layouts of the per-tensor product); their stages hold K rows
   // of the tile's 256 MN bytes, read by LDS transposes (frag_tr)
   static_assert(!(TA || TB) || !MX, "MN-major operands: per-tensor products");
-  static_assert(!TA || BMX == 256, "MN-major op(A): 256-row tiles");
+
   constexpr int kSlotA = NS == 3 ? BMX * BK : kTileBytes;   // op(A) bytes per slot
   constexpr int kSlotB = kTileBytes;                        // op(B) bytes per slot
   constexpr bool PF = NS == 2;                              // L2 prefetch of op(B)
@@ -738,7 +740,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     const int rowa_c = (wave * NA + (i % NA)) * 8 + (lane >> 3);
     const int krow = (wave * 8 + i) * 4 + (lane >> 4);
     const int kc = (lane & 15) ^ ((krow & 7) | (((krow >> 4) & 1) << 3));
-    offa[i] = TA ? (uint32_t)(krow * g.lda + 16 * kc) : (uint32_t)(rowa_c * g.lda + 16 * (cl ^ (i & 1)));
+    // op(A) of a 128-row tile: K rows of 128 bytes, block b = rows 8b .. 8b+7
+    const int krow_a = BMX == 256 ? krow : (wave * NA + (i % NA)) * 8 + (lane >> 3);
+    const int kc_a = BMX == 256 ? kc : (lane & 7) ^ (((krow_a >> 1) & 3) << 1);
+    offa[i] = TA ? (uint32_t)(krow_a * g.lda + 16 * kc_a) : (uint32_t)(rowa_c * g.lda + 16 * (cl ^ (i & 1)));
     offb[i] = TB ? (uint32_t)(krow * g.ldb + 16 * kc) : (uint32_t)(row * g.ldb + 16 * (cl ^ (i & 1)));
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
@@ -874,22 +879,24 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // MN-major operands: per-lane base of fragment j (frag_tr), slot 0, sub-step 0
   const int tq = lane >> 4, tj = lane & 15;
   const int tsw = (tj >> 1) | (gq << 3);
+  const int tsw_a = BMX == 256 ? tsw : ((tj >> 2) & 3) << 1;     // op(A) rows of BMX bytes
   uint32_t abase[4], bbase[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint32_t kr = (uint32_t)((16 * gq + (tj >> 1)) * 256 + 8 * (tj & 1));
-    abase[j] = kr + (uint32_t)(((((wm * 128 + 32 * j) >> 4) + (tq & 1)) ^ tsw) << 4);
+    const uint32_t kr_a = (uint32_t)((16 * gq + (tj >> 1)) * BMX + 8 * (tj & 1));
+    abase[j] = kr_a + (uint32_t)(((((wm * 128 + 32 * j) >> 4) + (tq & 1)) ^ tsw_a) << 4);
     bbase[j] = kRegB + kr + (uint32_t)(((((wn * WN + 32 * j) >> 4) + (tq & 1)) ^ tsw) << 4);
   }
   // fragment j of sub-step H at slot offset OFF, in either layout
   auto frA = [&](auto off_c, auto h_c, auto j_c) -> v8i {
     constexpr int OFF = decltype(off_c)::value, H = decltype(h_c)::value, J = decltype(j_c)::value;
-    if constexpr (TA) return frag_tr<OFF + H * 64 * 256>(smem, abase[J]);
+    if constexpr (TA) return frag_tr<OFF + H * 64 * BMX, BMX>(smem, abase[J]);
     else return frag_at<OFF + J * kFrag>(smem, H ? a1lo : a0lo, H ? a1hi : a0hi);
   };
   auto frB = [&](auto off_c, auto h_c, auto j_c) -> v8i {
     constexpr int OFF = decltype(off_c)::value, H = decltype(h_c)::value, J = decltype(j_c)::value;
-    if constexpr (TB) return frag_tr<OFF + H * 64 * 256>(smem, bbase[J]);
+    if constexpr (TB) return frag_tr<OFF + H * 64 * 256, 256>(smem, bbase[J]);
     else return frag_at<OFF + J * kFrag>(smem, H ? b1lo : b0lo, H ? b1hi : b0hi);
   };
 
@@ -1228,26 +1235,23 @@ static void launch_gemm(const GemmArgs& g, hipStream_t s) {
   // per workgroup (or, with kFwdPersistent, per-tensor products walk tiles
   // with one workgroup per compute unit)
   // MN-major operands (TA / TB, per-tensor) take the forward kernel with
-  // LDS transpose reads when K % 128 == 0; MN-major op(A) only with 256-row
-  // tiles, so a grid of fewer 256 x 256 tiles than compute units keeps the
-  // generic kernel for it
+  // LDS transpose reads when K % 128 == 0
   const int64_t ncu = device_cu_count();
-  const bool fwd = g.K > 0 && (g.K % 128) == 0 && (!MX || g.scales_dma) && (!TA || tiles >= ncu);
+  const bool fwd = g.K > 0 && (g.K % 128) == 0 && (!MX || g.scales_dma);
   if (fwd) {
     if (tiles < ncu) {
       // fewer 256 x 256 tiles than compute units: 128 x 256 tiles
       const int64_t t128 = ((g.M + 127) / 128) * ((g.N + BN - 1) / BN);
       // three LDS slots for long per-tensor products (see gemm_fwd_kernel)
-      if constexpr (!MX && !TA) {
+      if constexpr (!MX) {
         if (g.K >= 4096) {
-          hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 3, false, TB>), dim3((unsigned)t128),
+          hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 3, TA, TB>), dim3((unsigned)t128),
                              dim3(kGemmThreads), 0, s, g);
           return;
         }
       }
-      if constexpr (!TA)
-        hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 2, false, TB>), dim3((unsigned)t128),
-                           dim3(kGemmThreads), 0, s, g);
+      hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 2, TA, TB>), dim3((unsigned)t128), dim3(kGemmThreads),
+                         0, s, g);
       return;
     }
     const int64_t cus = (MX || !kFwdPersistent) ? tiles : ncu;

@@ -20,10 +20,9 @@ Per-tensor recipes pass the backward products the codes as they are stored:
 W and X from the forward casts and dY as op(B) / op(A) stored MN-major
 (`trans_a` / `trans_b`), which the forward GEMM kernel reads with LDS
 transposes as fast as K-contiguous operands, so no transposed copy is cast.
-It needs the product's K % 128 == 0 (and, for dW's MN-major op(A), at least
-as many 256 x 256 output tiles as compute units); where a product does not
-qualify, the casts also write the transposed copy (one pass) and that
-product reads K-contiguous operands.  The MX recipe casts W^T, X^T and dY^T
+It needs the product's K % 128 == 0; where a product does not qualify, the
+casts also write the transposed copy (one pass) and that product reads
+K-contiguous operands.  The MX recipe casts W^T, X^T and dY^T
 with blocks along their new contiguous axis, the products' K.
 
 Recipes:
@@ -57,21 +56,11 @@ from . import (E4M3, E5M2, _rule, amax_scale_workspace, fp8_amax_scale, fp8_hist
 RECIPES = ("current", "delayed", "mx", "constant")
 
 
-def _cu_count(device) -> int:
-    device = torch.device(device)
-    if device.type != "cuda":
-        return 1 << 30           # no GPU tensor: the library calls refuse it anyway
-    return torch.cuda.get_device_properties(device).multi_processor_count
-
-
-def _mn_major_ok(m: int, n: int, k: int, lda_k: int, ldb_k: int, trans_a: bool, device) -> bool:
+def _mn_major_ok(k: int, lda_k: int, ldb_k: int) -> bool:
     """Whether a per-tensor product with MN-major operands runs on the fast
-    kernel: K % 128 == 0, an MN-major operand spans < 2 GiB (K x its leading
-    dimension), and an MN-major op(A) needs at least one 256 x 256 tile per
-    compute unit."""
-    if k % 128 or k == 0 or lda_k >= (1 << 31) - 4096 or ldb_k >= (1 << 31) - 4096:
-        return False
-    return not trans_a or ((m + 255) // 256) * ((n + 255) // 256) >= _cu_count(device)
+    kernel: K % 128 == 0 and each MN-major operand spans < 2 GiB (K x its
+    leading dimension)."""
+    return k > 0 and k % 128 == 0 and lda_k < (1 << 31) - 4096 and ldb_k < (1 << 31) - 4096
 
 
 def _packable(m: int, n: int, k: int) -> bool:
@@ -167,8 +156,8 @@ class Fp8LinearFunction(torch.autograd.Function):
             # takes them MN-major: dX = dY W with W [out x in] as op(B)
             # (K = out), dW = dY^T X with dY [T x out] and X [T x in] (K = T)
             T, N, D = x2.shape[0], w.shape[0], w.shape[1]
-            ctx.mn_dx = _mn_major_ok(T, D, N, 0, N * D, False, x.device)
-            ctx.mn_dw = _mn_major_ok(N, D, T, T * N, T * D, True, x.device)
+            ctx.mn_dx = _mn_major_ok(N, 0, N * D)
+            ctx.mn_dw = _mn_major_ok(T, T * N, T * D)
             bx, qx, qxT = _per_tensor_cast(x2, E4M3, recipe, layer.margin, layer._hx, not ctx.mn_dw,
                                            layer._bias, layer._log, "x", layer._ws)
             bw, qw, qwT = _per_tensor_cast(w, E4M3, recipe, layer.margin, layer._hw, not ctx.mn_dx,

@@ -195,10 +195,10 @@ def test_gemm_mn_major_operands_forward_kernel(ta, tb, M, N, K):
     """MN-major storage ([K x M] / [K x N]) with K % 128 == 0 takes the
     forward kernel, whose stages hold K rows of the operand and whose
     fragments come from LDS transpose reads: ragged M and N tiles, a grid of
-    289 256 x 256 tiles, and small grids (128 x 256 tiles; two and three LDS
-    slots; MN-major op(A) keeps the generic kernel there).  Every output
-    against the oracle, and bit for bit equal to the same product from
-    K-major copies of the operands."""
+    289 256 x 256 tiles, and small grids (128 x 256 tiles, op(A) stages of
+    128-byte K rows; two and three LDS slots).  Every output against the
+    oracle, and bit for bit equal to the same product from K-contiguous
+    copies of the operands."""
     rng = np.random.default_rng(26)
     qa, ba = _operand(rng, (M, K), 1e-4, E5M2)
     qb, bb = _operand(rng, (N, K), 0.02, E4M3)
