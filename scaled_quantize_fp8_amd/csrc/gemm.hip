@@ -641,8 +641,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   constexpr int NS = NSLOT;
   static_assert(NS == 2 || (NS == 3 && BMX == 128 && !MX), "slot count");
   // TA / TB: op(A) / op(B) stored MN-major ([K x M] / [K x N], the
-  // transposed layouts of the per-tensor product); their stages hold K rows
-  // of the tile's 256 MN bytes, read by LDS transposes (frag_tr)
+  // transposed layouts of the per-tensor product); their stages hold the
+  // stage's 128 K rows of the tile's MN bytes (256, or BMX for op(A)), read
+  // by LDS transposes (frag_tr)
   static_assert(!(TA || TB) || !MX, "MN-major operands: per-tensor products");
 
   constexpr int kSlotA = NS == 3 ? BMX * BK : kTileBytes;   // op(A) bytes per slot
@@ -729,8 +730,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // offset rides in soffset.  Offsets do not depend on the tile: a row past
   // the matrix has offset >= ra * ld >= (ra - 1) * ld + K, the panel's size.
   const int cl = (lane & 7) ^ (lane >> 3);          // ^ (blk & 1) = ^ (i & 1) below
-  // MN-major: block b of the stage is K rows 4b .. 4b+3 (256 bytes each);
-  // lane L lands at row 4b + L/16, stored chunk L%16, so it fetches logical
+  // MN-major: block b of the stage is K rows 4b .. 4b+3 (256 bytes each;
+  // 8b .. 8b+7 of 128 bytes for op(A) of a 128-row tile); lane L lands at
+  // row 4b + L/16, stored chunk L%16 (8b + L/8, L%8), so it fetches logical
   // chunk (L%16) ^ tswz(row); the stage's K offset (k0 rows) rides in
   // soffset as k0 * ld.
   uint32_t offa[8], offb[8];
