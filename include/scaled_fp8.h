@@ -345,7 +345,9 @@ int fp8_scaled_gemm(int64_t M, int64_t N, int64_t K,
  * and B_scales [N x K/32] E8M0 codes (as written by mx_quantize), fp32
  * accumulation, C [M x N] bf16 or fp32, optional fused out_amax as above.
  * Requirements: K % 32 == 0; A, B 16-byte aligned with lda, ldb multiples of
- * 16.  Scales may have any alignment (4-byte aligned rows read faster).
+ * 16.  Scales may have any alignment; with 4-byte aligned scale rows,
+ * K % 128 == 0 and K >= 512 the product runs the faster kernel (the bytes
+ * after a scale row's K/32 codes are never read).
  */
 int mx_scaled_gemm(int64_t M, int64_t N, int64_t K,
                    const uint8_t* A, int fmt_a, int64_t lda,

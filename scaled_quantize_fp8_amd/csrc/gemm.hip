@@ -20,8 +20,9 @@
 //     MN-major operand is copied as K rows and its fragments are read with
 //     the LDS transpose read ds_read_b64_tr_b8.  Described where it is
 //     defined.
-//   * gemm_kernel: every other case (a K tail, K % 128 != 0; MX on
-//     row-major scales with K % 512 != 0) with the design below.
+//   * gemm_kernel: every other case (a K tail, K % 128 != 0; MX with
+//     K < 512, or on row-major scale rows that are not 4-byte aligned) with
+//     the design below.
 //
 // gemm_kernel's CDNA4 mapping.
 //   * Macro tile 256 (M) x 256 (N) x 128 (K bytes), 256 lanes = 4 waves in a
@@ -496,6 +497,14 @@ template <int N> __device__ __forceinline__ void wait_vm() {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
+// The four dwords of v with the first s (uniform, 0..3) dropped: dword d of
+// the result is dword d + s of v where d + s < 4; the rest repeat dwords of v.
+__device__ __forceinline__ uint4 drop_dwords(uint4 v, int s) {
+  const bool h = (s & 2) != 0, o = (s & 1) != 0;
+  const uint32_t u0 = h ? v.z : v.x, u1 = h ? v.w : v.y;
+  return make_uint4(o ? u1 : u0, o ? v.z : u1, o ? v.w : v.z, v.w);
+}
+
 // 32x32x64 MFMA with E8M0 scales picked by byte (op_sel) from packed registers.
 template <int FA_, int FB_>
 __device__ __forceinline__ v16f mfma32(v8i a, v8i b, v16f c, int sa, int oa, int sb, int ob) {
@@ -619,13 +628,17 @@ struct TileSrd {
   v4i a, b, sa, sb;
 };
 
-template <int FA, int FB, bool MX, int BMX, int NSLOT, bool TA = false, bool TB = false>
+template <int FA, int FB, bool MX, int BMX, int NSLOT, bool TA = false, bool TB = false, bool PG = false>
 __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // BMX: tile rows (256, or 128 for grids with fewer 256 x 256 tiles than
   // compute units).  A 256-row tile puts the 4 waves in 2 x 2, each 128 x
   // 128 of C; a 128-row tile in 1 x 4, each 128 x 64 (4 op(A) and 2 op(B)
   // fragments, 8 MFMAs per sub-step, 12 copies per stage).
   static_assert(BMX == 256 || BMX == 128, "tile rows");
+  // PG: MX on row-major scales with a partial last group of scale codes
+  // (K % 512 != 0); its own instantiation, so that the others carry none of
+  // the selects that group needs (they cost packed products 2-5%).
+  static_assert(!PG || MX, "partial scale groups are MX only");
   constexpr int NI = BMX == 256 ? 4 : 2;            // op(B) fragments per wave
   constexpr int WN = NI * 32;                       // C columns per wave
   constexpr int NA = BMX / 32;                      // op(A) copies per stage per wave
@@ -685,6 +698,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   const int nkU = (nk + U - 1) / U * U;             // stages run per tile (zero stages past nk)
   const int ngroups = nkU / 4;                      // MX scale copies per tile
   const bool pk = MX && g.scales_packed;            // tiled scale layout (uniform)
+  // Row-major scales with nk % 4 != 0: the last group holds nk % 4 real
+  // stages.  Its copy is moved back to end at the row's end (codes
+  // nkb - 16 .. nkb - 1, inside the row since K >= 512), so stage p of the
+  // group sits at dword p + gsh(G) of the 16 bytes; the group's stages past
+  // nk run on zero operands with whatever codes the other dwords hold.
+  auto gsh = [&](int G) {
+    const int s = 4 * G + 4 - nk;
+    return (!PG || G >= ngroups || s < 0) ? 0 : s;
+  };
 
   auto make_tile = [&](int vb, TileSrd& T) {
     if (vb < tiles && (PERSIST || vb == (int)blockIdx.x)) {
@@ -751,8 +773,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(smem));
   // MX scales: lane L of wave w copies 16 bytes (the codes of 4 stages) of
   // tile row 64 w + L of each operand.  Group G covers stages 4G .. 4G+3:
-  // bytes 16 G .. 16 G + 15 of a row-major scale row (K % 512 == 0 there,
-  // so every group is whole) or the 4 KiB block G of the packed layout
+  // bytes 16 G .. 16 G + 15 of a row-major scale row (a partial last group
+  // from 4 gsh(G) bytes earlier) or the 4 KiB block G of the packed layout
   // (padded with code 127 past the last block).
   // L2 prefetch of op(B) (the weight panel): every stage of a tile touches a
   // new K slice of it, and all XCDs walk the same panels in step, so its
@@ -829,7 +851,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
       const bool nx = G >= ngroups;
       // packed: group G is the 4 KiB block G of the tile (whole lines);
       // row-major: bytes 16 G .. 16 G + 15 of each row
-      const uint32_t so = (uint32_t)(nx ? 0 : (pk ? G * kPackTile : 16 * G));
+      uint32_t so = (uint32_t)(nx ? 0 : (pk ? G * kPackTile : 16 * G));
+      if constexpr (PG) so -= (uint32_t)(4 * gsh(G));
       const uint32_t la = ldss + (uint32_t)((((gbase + G) & 1) * 2 * BM + wave * 64) * 16);
       v4i sa = cur.sa, sb = cur.sb;
       if constexpr (PERSIST) {
@@ -852,16 +875,23 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // v_perm packs bytes g, 2 + g of dwords (0, 1) into the register of stages
   // 0 and 1 and of dwords (2, 3) into that of stages 2 and 3: stage p,
   // sub-step h takes byte 2 (p & 1) + h (op_sel) of register p >> 1.  Rows
-  // 16 bytes apart read as one contiguous span: no bank conflicts.
+  // 16 bytes apart read as one contiguous span: no bank conflicts.  A
+  // partial last group (PG) first drops its gsh(G) leading dwords (uniform
+  // selects; the identity on whole groups).
   const uint32_t psel = (lane >> 5) ? 0x07050301u : 0x06040200u;
   auto read_group = [&](int G, int (&lo)[8], int (&hi)[8], int j0, int j1) {
     if constexpr (MX) {
       const int gs = (gbase + G) & 1;
+      const int sh = gsh(G);
 #pragma unroll
       for (int j = j0; j < j1; ++j) {
-        const uint4 da = *reinterpret_cast<const uint4*>(&s_scale[((gs * 2) * BM + wm * 128 + j * 32 + (lane & 31)) * 4]);
-        const uint4 db = *reinterpret_cast<const uint4*>(
+        uint4 da = *reinterpret_cast<const uint4*>(&s_scale[((gs * 2) * BM + wm * 128 + j * 32 + (lane & 31)) * 4]);
+        uint4 db = *reinterpret_cast<const uint4*>(
             &s_scale[((gs * 2 + 1) * BM + wn * WN + (j % NI) * 32 + (lane & 31)) * 4]);
+        if constexpr (PG) {
+          da = drop_dwords(da, sh);
+          db = drop_dwords(db, sh);
+        }
         lo[j] = (int)__builtin_amdgcn_perm(da.y, da.x, psel);
         hi[j] = (int)__builtin_amdgcn_perm(da.w, da.z, psel);
         lo[4 + j] = (int)__builtin_amdgcn_perm(db.y, db.x, psel);
@@ -1228,18 +1258,26 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   if (g.out_amax) block_max_to_global(amax_bits, red, g.out_amax);
 }
 
-template <int FA, int FB, bool MX, bool TA, bool TB>
+template <int FA, int FB, bool MX, bool TA, bool TB, bool PG = false>
 static void launch_gemm(const GemmArgs& g, hipStream_t s) {
   const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   // the forward kernel copies MX scales 16 codes (4 stages) per row at a
-  // time: row-major scale rows must be 4-byte aligned with K % 512 == 0
-  // (whole groups; packed scales are padded to whole groups); one tile
+  // time: row-major scale rows must be 4-byte aligned with K >= 512 (a
+  // partial last group is copied from 16 codes before the row's end;
+  // packed scales are padded to whole groups); one tile
   // per workgroup (or, with kFwdPersistent, per-tensor products walk tiles
   // with one workgroup per compute unit)
   // MN-major operands (TA / TB, per-tensor) take the forward kernel with
   // LDS transpose reads when K % 128 == 0
   const int64_t ncu = device_cu_count();
   const bool fwd = g.K > 0 && (g.K % 128) == 0 && (!MX || g.scales_dma);
+  if constexpr (MX && !PG) {
+    // row-major scales whose last group of 4 stages is partial
+    if (fwd && !g.scales_packed && (g.K % 512) != 0) {
+      launch_gemm<FA, FB, MX, TA, TB, true>(g, s);
+      return;
+    }
+  }
   if (fwd) {
     if (tiles < ncu) {
       // fewer 256 x 256 tiles than compute units: 128 x 256 tiles
@@ -1247,18 +1285,18 @@ static void launch_gemm(const GemmArgs& g, hipStream_t s) {
       // three LDS slots for long per-tensor products (see gemm_fwd_kernel)
       if constexpr (!MX) {
         if (g.K >= 4096) {
-          hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 3, TA, TB>), dim3((unsigned)t128),
+          hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 3, TA, TB, PG>), dim3((unsigned)t128),
                              dim3(kGemmThreads), 0, s, g);
           return;
         }
       }
-      hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 2, TA, TB>), dim3((unsigned)t128), dim3(kGemmThreads),
+      hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 2, TA, TB, PG>), dim3((unsigned)t128), dim3(kGemmThreads),
                          0, s, g);
       return;
     }
     const int64_t cus = (MX || !kFwdPersistent) ? tiles : ncu;
     const int64_t grid = tiles < cus ? tiles : cus;
-    hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 256, 2, TA, TB>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s,
+    hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 256, 2, TA, TB, PG>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s,
                        g);
   } else {
     hipLaunchKernelGGL((gemm_kernel<FA, FB, MX, TA, TB>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, g);
@@ -1397,7 +1435,7 @@ int mx_scaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* A, int fmt_a,
   g.sa = A_scales; g.lds_a = lds_a; g.sb = B_scales; g.lds_b = lds_b;
   g.sa_dword = aligned(A_scales, 4) && (lds_a % 4) == 0;
   g.sb_dword = aligned(B_scales, 4) && (lds_b % 4) == 0;
-  g.scales_dma = g.sa_dword && g.sb_dword && (K % 512) == 0 && lds_a < (1LL << 23) && lds_b < (1LL << 23);
+  g.scales_dma = g.sa_dword && g.sb_dword && K >= 512 && lds_a < (1LL << 23) && lds_b < (1LL << 23);
   g.scales_packed = 0; g.sgroups = 0;
   g.C = C; g.ldc = ldc; g.out_amax = out_amax;
   g.out_f32 = out_dtype == FP8_DT_F32;

@@ -297,11 +297,11 @@ def test_mx_gemm_ragged(fa, fb, out_dtype):
                          ids=["e4e4", "e5e4", "e4e5", "e5e5"])
 def test_mx_gemm_k_multiple_of_128(fa, fb, K):
     """K a multiple of 128 (stage counts 3, 5, 8, 9) with ragged M = 300,
-    N = 260: on row-major scales K = 1024 runs the 32x32x64 kernel (whole
-    4-stage scale groups) and the others the 16x16x128 kernel; scales passed
-    twice:
-    packed rows (K/32 bytes each, dword-aligned) and rows padded to an odd
-    stride (K/32 + 1 bytes), which the kernel must read byte by byte."""
+    N = 260, scales passed twice: packed rows (K/32 bytes each,
+    dword-aligned: the 32x32x64 kernel from K = 512 on, a partial last
+    4-stage scale group at K = 640 and 1152; K = 384 runs the 16x16x128
+    kernel) and rows padded to an odd stride (K/32 + 1 bytes), which only
+    the 16x16x128 kernel takes, reading them byte by byte."""
     xb = make("c4", "X", shape=(300, K))
     wb = make("c4", "W", shape=(260, K))
     qa, sa = oracle.mx_quantize(oracle.bf16_bits_to_f64(xb), fa)
@@ -365,6 +365,45 @@ def test_mx_gemm_packed_scales(fa, fb, M, N, K):
         assert f32_bits_of(amp) == f32_bits_of(amr)
         assert_gemm_close(host_f64(Cp), ref, s, dt == torch.bfloat16, f"mx packed {M}x{N}x{K}", gt)
         _check_amax(Cp, amp)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 260, 640), (300, 260, 768), (300, 260, 896), (4352, 4096, 896)],
+                         ids=["300x260x640", "300x260x768", "300x260x896", "4352x4096x896"])
+def test_mx_gemm_row_major_partial_scale_group(M, N, K):
+    """Row-major scales with K % 512 != 0 on the 32x32x64 kernel: the last
+    4-stage group of scale codes holds 1, 2 or 3 stages (K = 640, 768, 896)
+    and is copied from 16 codes before each row's end.  Each scale row is
+    followed by 4 bytes of NaN codes (0xFF) that the kernel must not read.
+    The product equals the packed-scale product bit for bit and the oracle
+    within tolerance; 128-row tiles (4 tiles) and 256-row tiles (272 tiles,
+    every output of two rows and columns per tile checked)."""
+    xb = make("c4", "X", shape=(M, K))
+    wb = make("c4", "W", shape=(N, K))
+    qa, sa = oracle.mx_quantize(oracle.bf16_bits_to_f64(xb), E4M3)
+    qb, sb = oracle.mx_quantize(oracle.bf16_bits_to_f64(wb), E4M3)
+    nb = K // 32
+    psa = np.full((M, nb + 4), 0xFF, dtype=np.uint8)
+    psb = np.full((N, nb + 4), 0xFF, dtype=np.uint8)
+    psa[:, :nb], psb[:, :nb] = sa, sb
+    A, B = u8_dev(qa), u8_dev(qb)
+    SA, SB = u8_dev(psa)[:, :nb], u8_dev(psb)[:, :nb]
+    say(f"mx gemm row-major partial scale group {M}x{N}x{K}")
+    Cr, amr = sq.mx_scaled_gemm(A, E4M3.code, SA, B, E4M3.code, SB, want_amax=True)
+    Cp, amp = sq.mx_scaled_gemm_packed(A, E4M3.code, sq.mx_pack_scales(SA), B, E4M3.code, sq.mx_pack_scales(SB),
+                                       want_amax=True)
+    torch.cuda.synchronize()
+    assert torch.equal(Cr.view(torch.int16), Cp.view(torch.int16)) and f32_bits_of(amr) == f32_bits_of(amp)
+    _check_amax(Cr, amr)
+    if M * N <= 300 * 260:
+        rs, cs = np.arange(M), np.arange(N)
+    else:
+        rng = np.random.default_rng(K)
+        rs, cs = _tile_rows(rng, M), _tile_rows(rng, N)
+    got = host_f64(Cr[torch.from_numpy(rs).to(DEV)][:, torch.from_numpy(cs).to(DEV)])
+    a, b, ssa, ssb = qa[rs], qb[cs], sa[rs], sb[cs]
+    assert_gemm_close(got, oracle.mx_gemm_ref(a, ssa, E4M3, b, ssb, E4M3),
+                      oracle.mx_abs_product_sum(a, ssa, E4M3, b, ssb, E4M3), True, f"mx rm {M}x{N}x{K}",
+                      mfma_operands_mx(a, ssa, E4M3, b, ssb, E4M3))
 
 
 def test_mx_gemm_extreme_block_scales():
