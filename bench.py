@@ -383,7 +383,42 @@ def backward_extras(dev, reps: int = 5):
         res["backward_TFLOPs"] = round(2 * flops / total / 1e9, 1)
         res["ms"] = round(total, 4)
         out[tag] = res
+    # what the memory system delivers for the transposed MX casts' own access
+    # pattern (tile and store kind as the kernel picks them, no arithmetic)
+    ceil = {k: transposed_ceiling(dev, t, reps) for k, t in (("dY", dy), ("W", w), ("X", x))}
+    out["mx"]["t2w1_ceiling_GBps"] = ceil
+    for k, v in ceil.items():
+        out["mx"][f"mx_cast_t_{k}_frac_of_ceiling"] = round(out["mx"][f"mx_cast_t_{k}_GBps"] / v, 4)
     return out
+
+
+def transposed_ceiling(dev, x, reps: int = 5) -> float:
+    """GB/s of libsfp8_ceiling.so's t2w1 stream over bf16 x: 2 bytes read
+    and 1 written per element at the transposed position, in the tiles the
+    transposed MX cast uses for this size (128 x 128 with cached stores from
+    64M elements, else 128 x 64 with non-temporal stores)."""
+    import ctypes
+    import torch
+    from scaled_quantize_fp8_amd.build import CEILING_LIB
+    lib = ctypes.CDLL(CEILING_LIB)
+    fn = lib.sfp8_ceiling_t2w1
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                   ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    R, C = x.shape
+    wide = R * C >= (64 << 20)
+    qT = torch.empty(C, R, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    args = (x.data_ptr(), R, C, x.stride(0), qT.data_ptr(), R, 128 if wide else 64, 0 if wide else 1, stream)
+    assert fn(*args) == 0
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn(*args)
+    e1.record()
+    torch.cuda.synchronize()
+    return round(3 * R * C / (e0.elapsed_time(e1) / reps) / 1e6, 1)
 
 
 def hbm_ceilings(dev, xs, ws, qxs, qws, reps: int = 5):

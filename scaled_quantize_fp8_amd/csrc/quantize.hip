@@ -966,18 +966,20 @@ static void launch_mx(const MxArgs& a, bool vec, hipStream_t s) {
 // Transposed MX cast: blocks of 32 consecutive ROWS of one column, written as
 // qT [cols x rows] with scalesT [cols x rows/32], i.e. the MX cast of x^T
 // (for a GEMM that contracts over `rows`, such as a weight gradient whose K
-// is the token axis).  128 x 64 tiles: the workgroup stages the tile in LDS
+// is the token axis).  128 x 64 tiles (128 x 128 for large bf16 inputs: the
+// longer row pieces read faster): the workgroup stages the tile in LDS
 // (consecutive lanes load consecutive 16-byte chunks of a row), then lane
-// (c, b) owns the whole 32-row block b of tile column c: it reduces the
+// (c, b) owns the whole 32-row block b of tile column c (two columns per
+// lane on wide tiles): it reduces the
 // block's maximum, casts its 32 elements and puts them, as 32 contiguous
 // bytes of qT row c, back into LDS, from where the workgroup writes each of
-// its 64 qT rows as one full 128-byte line.
+// its qT rows as one full 128-byte line.
 // ---------------------------------------------------------------------------
-constexpr int kMtR = 128, kMtC = 64;
+constexpr int kMtR = 128, kMtC = 64, kMtCWide = 128;
 // Elements from which mx_transpose_kernel stores qT through the cache.
 constexpr int64_t kMxtCachedMin = 64LL << 20;
 
-template <int DT, int FMT, bool VEC, bool OCP>
+template <int DT, int FMT, bool VEC, bool OCP, int TC = kMtC>
 __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
   // The tile is staged in the input's own width (bf16 as 16-bit words, rows
   // of 72: 144 bytes; fp32 rows of 68 dwords): 16-byte aligned rows for the
@@ -986,13 +988,14 @@ __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
   // so twice as many workgroups fit on a compute unit.
   using TT = std::conditional_t<DT == FP8_DT_BF16, uint16_t, uint32_t>;
   constexpr int PAD = DT == FP8_DT_BF16 ? 8 : 4;
-  __shared__ __attribute__((aligned(16))) TT tile[kMtR][kMtC + PAD];
+  static_assert(TC == 64 || TC == 128, "tile columns");
+  __shared__ __attribute__((aligned(16))) TT tile[kMtR][TC + PAD];
   constexpr int ESZ = In<DT>::kEsz;
   constexpr int EPC = In<DT>::kEpc;                // elements per 16-byte chunk
-  constexpr int CPR = kMtC / EPC;                  // chunks per tile row
+  constexpr int CPR = TC / EPC;                    // chunks per tile row
   const int64_t r0 = (int64_t)blockIdx.y * kMtR;
-  const int64_t c0 = (int64_t)blockIdx.x * kMtC;
-  const bool full_cols = c0 + kMtC <= a.cols;
+  const int64_t c0 = (int64_t)blockIdx.x * TC;
+  const bool full_cols = c0 + TC <= a.cols;
   constexpr int LPL = kMtR * CPR / kThreads;       // 16-byte chunks per lane
   if (VEC && full_cols && r0 + kMtR <= a.rows) {
     // whole tile: a lane's loads all in flight before its LDS writes (a
@@ -1037,39 +1040,46 @@ __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
     }
   }
   __syncthreads();
-  const int c = threadIdx.x % kMtC;
-  const int blk = threadIdx.x / kMtC;              // 0..3 (the wave): tile rows 32 blk .. 32 blk + 31
-  const int64_t col = c0 + c;                      // qT row
+  // lane (c, blk), c = lane + 64 h for each of the TC / 64 column halves h,
+  // blk = the wave: tile rows 32 blk .. 32 blk + 31 of column c
+  constexpr int NH = TC / 64;
+  const int blk = threadIdx.x / 64;
   const int64_t rr = r0 + 32 * blk;                // first qT column of this block
-  const bool live = col < a.cols && rr < a.rows;   // rows % 32 == 0: a block exists whole or not at all
-  uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (live) {
-    uint32_t v[32];
-    uint32_t bm = 0;
+  uint32_t w[NH][8];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      v[i] = DT == FP8_DT_BF16 ? (uint32_t)tile[32 * blk + i][c] << 16 : (uint32_t)tile[32 * blk + i][c];
-      const uint32_t ab = v[i] & 0x7fffffffu;
-      bm = bm > ab ? bm : ab;
+  for (int h = 0; h < NH; ++h) {
+    const int c = threadIdx.x % 64 + 64 * h;
+    const int64_t col = c0 + c;                    // qT row
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[h][k] = 0;
+    if (col < a.cols && rr < a.rows) {             // rows % 32 == 0: a block exists whole or not at all
+      uint32_t v[32];
+      uint32_t bm = 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        v[i] = DT == FP8_DT_BF16 ? (uint32_t)tile[32 * blk + i][c] << 16 : (uint32_t)tile[32 * blk + i][c];
+        const uint32_t ab = v[i] & 0x7fffffffu;
+        bm = bm > ab ? bm : ab;
+      }
+      int e;
+      uint32_t code;
+      block_exponent<FMT, OCP>(bm, &e, &code);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        w[h][k] = cvt4<FMT>(__builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k]), e),
+                            __builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k + 1]), e),
+                            __builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k + 2]), e),
+                            __builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k + 3]), e));
+      if (__builtin_expect(bm > 0x7f800000u, 0)) {  // a NaN in the block: patch its codes
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+          if ((v[i] & 0x7fffffffu) > 0x7f800000u)
+            w[h][i / 4] = (w[h][i / 4] & ~(0xffu << (8 * (i % 4)))) | (nan_code_f32(v[i]) << (8 * (i % 4)));
+      }
+      store_scale(a, col, rr / 32, code);          // qT row col, block rr / 32
     }
-    int e;
-    uint32_t code;
-    block_exponent<FMT, OCP>(bm, &e, &code);
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      w[k] = cvt4<FMT>(__builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k]), e),
-                       __builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k + 1]), e),
-                       __builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k + 2]), e),
-                       __builtin_amdgcn_ldexpf(__uint_as_float(v[4 * k + 3]), e));
-    if (__builtin_expect(bm > 0x7f800000u, 0)) {    // a NaN in the block: patch its codes
-#pragma unroll
-      for (int i = 0; i < 32; ++i)
-        if ((v[i] & 0x7fffffffu) > 0x7f800000u)
-          w[i / 4] = (w[i / 4] & ~(0xffu << (8 * (i % 4)))) | (nan_code_f32(v[i]) << (8 * (i % 4)));
-    }
-    store_scale(a, col, rr / 32, code);            // qT row col, block rr / 32
   }
-  // The codes go out through LDS: the tile's kMtC qT rows of kMtR bytes
+  // The codes go out through LDS: the tile's TC qT rows of kMtR bytes
   // (row stride kMtR + 16: the 16-byte writes of 16 lanes hit 64 distinct
   // banks) are written back as whole 128-byte lines, 8 lanes per line, where
   // each lane had written 32 bytes into each of 64 rows.  Non-temporal
@@ -1077,15 +1087,19 @@ __global__ __launch_bounds__(kThreads) void mx_transpose_kernel(MxArgs a) {
   // choice, a.nt): measured on the 7B-MLP tensors (16.7M and 45M elements)
   // and the 70B-MLP X (134M).
   constexpr int OS = kMtR + 16;
-  static_assert(kMtC * OS <= (int)sizeof(tile), "output staging fits in the tile");
+  static_assert(TC * OS <= (int)sizeof(tile), "output staging fits in the tile");
   uint8_t* ost = reinterpret_cast<uint8_t*>(&tile[0][0]);
   __syncthreads();                                 // every column has been read
-  *reinterpret_cast<uint4*>(ost + c * OS + 32 * blk) = make_uint4(w[0], w[1], w[2], w[3]);
-  *reinterpret_cast<uint4*>(ost + c * OS + 32 * blk + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const int c = threadIdx.x % 64 + 64 * h;
+    *reinterpret_cast<uint4*>(ost + c * OS + 32 * blk) = make_uint4(w[h][0], w[h][1], w[h][2], w[h][3]);
+    *reinterpret_cast<uint4*>(ost + c * OS + 32 * blk + 16) = make_uint4(w[h][4], w[h][5], w[h][6], w[h][7]);
+  }
   __syncthreads();
   constexpr int CH = kMtR / 16;                    // 16-byte chunks per qT row of the tile
 #pragma unroll
-  for (int k = 0; k < kMtC * CH / kThreads; ++k) {
+  for (int k = 0; k < TC * CH / kThreads; ++k) {
     const int idx = threadIdx.x + k * kThreads;
     const int orow = idx / CH, ch = idx % CH;
     const int64_t ocol = c0 + orow, orr = r0 + 16 * ch;
@@ -1418,16 +1432,24 @@ static int mx_cast_t(const void* x, int dtype, int64_t rows, int64_t cols, int64
     hipLaunchKernelGGL(fill_u8_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, stream, scalesT, n16,
                        0x7f7f7f7fu);
   }
-  const dim3 grid((unsigned)((cols + kMtC - 1) / kMtC), (unsigned)gy);
   // 16-byte loads when every row start is 16-byte aligned
   const bool vec = aligned(x, 16) && (ld * dtype_size(dtype)) % 16 == 0;
+  // bf16 with 16-byte loads from kMxtCachedMin elements: tiles of 128 x 128
+  // (70B-MLP X and W +6-13%; the 7B-MLP tensors gained on X, lost 4% on dY;
+  // fp32 at 128 x 64 takes the same LDS; element loads ran 10-20% slower)
+  const bool wide = dtype == FP8_DT_BF16 && vec && rows * cols >= kMxtCachedMin;
+  const int tc = wide ? kMtCWide : kMtC;
+  const dim3 grid((unsigned)((cols + tc - 1) / tc), (unsigned)gy);
 #define SFP8_MXT(DT, FMT)                                                                              \
   do {                                                                                                 \
+    constexpr int TW = DT == FP8_DT_BF16 ? kMtCWide : kMtC;                                            \
     if (rule == MX_RULE_OCP) {                                                                         \
-      if (vec) hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, true, true>), grid, dim3(kThreads), 0, stream, a); \
+      if (wide) hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, true, true, TW>), grid, dim3(kThreads), 0, stream, a); \
+      else if (vec) hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, true, true>), grid, dim3(kThreads), 0, stream, a); \
       else hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, false, true>), grid, dim3(kThreads), 0, stream, a);   \
     } else {                                                                                           \
-      if (vec) hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, true, false>), grid, dim3(kThreads), 0, stream, a); \
+      if (wide) hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, true, false, TW>), grid, dim3(kThreads), 0, stream, a); \
+      else if (vec) hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, true, false>), grid, dim3(kThreads), 0, stream, a); \
       else hipLaunchKernelGGL((mx_transpose_kernel<DT, FMT, false, false>), grid, dim3(kThreads), 0, stream, a);   \
     }                                                                                                  \
   } while (0)

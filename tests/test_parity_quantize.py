@@ -258,6 +258,27 @@ def test_mx_cast_transposed_full_size_sampled():
     assert np.array_equal(host(qT[idx]), rq)
 
 
+def test_mx_cast_transposed_wide_tiles_ragged():
+    """A bf16 tensor above 64M elements takes 128 x 128 tiles: [8192 x 8328]
+    (the last tile column holds 8 columns) against the oracle on two columns
+    of every tile and every column of the partial tile; the packed-scale
+    variant writes the same codes and mx_pack_scales of the same scales."""
+    bits = make("c5", "X", shape=(8192, 8328))
+    x = bf16_dev(bits)
+    say("mx transposed cast, wide tiles, 8192 x 8328")
+    qT, sT = sq.mx_quantize_t(x, E4M3.code)
+    rng = np.random.default_rng(12)
+    t = np.arange(0, 8328, 128)
+    cols = np.unique(np.concatenate([t + rng.integers(0, np.minimum(128, 8328 - t)) for _ in range(2)] +
+                                    [np.arange(8320, 8328), [0, 127, 128]]))
+    rq, rs = oracle.mx_quantize(oracle.bf16_bits_to_f64(np.ascontiguousarray(bits[:, cols].T)), E4M3)
+    idx = torch.from_numpy(cols).to(DEV)
+    assert np.array_equal(host(sT[idx]), rs)
+    assert np.array_equal(host(qT[idx]), rq)
+    pq, ps = sq.mx_quantize_t_packed(x, E4M3.code)
+    assert torch.equal(pq, qT) and torch.equal(ps, sq.mx_pack_scales(sT))
+
+
 def _every_bf16_as_block_max(seed=21):
     """[2048 x 1024] bf16 bits: block i (1 x 32) holds bf16 pattern i and 31
     elements of smaller or equal magnitude field (the pattern's field minus
