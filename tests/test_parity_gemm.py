@@ -367,20 +367,24 @@ def test_mx_gemm_packed_scales(fa, fb, M, N, K):
         _check_amax(Cp, amp)
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 260, 640), (300, 260, 768), (300, 260, 896), (4352, 4096, 896)],
-                         ids=["300x260x640", "300x260x768", "300x260x896", "4352x4096x896"])
-def test_mx_gemm_row_major_partial_scale_group(M, N, K):
+@pytest.mark.parametrize("M,N,K,fa,fb", [(300, 260, 640, E4M3, E4M3), (300, 260, 768, E4M3, E4M3),
+                                         (300, 260, 896, E4M3, E4M3), (4352, 4096, 896, E4M3, E4M3),
+                                         (300, 260, 1152, E5M2, E4M3), (1, 33, 2176, E4M3, E5M2)],
+                         ids=["300x260x640", "300x260x768", "300x260x896", "4352x4096x896", "300x260x1152_e5e4",
+                              "1x33x2176_e4e5"])
+def test_mx_gemm_row_major_partial_scale_group(M, N, K, fa, fb):
     """Row-major scales with K % 512 != 0 on the 32x32x64 kernel: the last
     4-stage group of scale codes holds 1, 2 or 3 stages (K = 640, 768, 896)
     and is copied from 16 codes before each row's end.  Each scale row is
     followed by 4 bytes of NaN codes (0xFF) that the kernel must not read.
     The product equals the packed-scale product bit for bit and the oracle
     within tolerance; 128-row tiles (4 tiles) and 256-row tiles (272 tiles,
-    every output of two rows and columns per tile checked)."""
+    every output of two rows and columns per tile checked); also E5M2
+    operands and a single-row product."""
     xb = make("c4", "X", shape=(M, K))
     wb = make("c4", "W", shape=(N, K))
-    qa, sa = oracle.mx_quantize(oracle.bf16_bits_to_f64(xb), E4M3)
-    qb, sb = oracle.mx_quantize(oracle.bf16_bits_to_f64(wb), E4M3)
+    qa, sa = oracle.mx_quantize(oracle.bf16_bits_to_f64(xb), fa)
+    qb, sb = oracle.mx_quantize(oracle.bf16_bits_to_f64(wb), fb)
     nb = K // 32
     psa = np.full((M, nb + 4), 0xFF, dtype=np.uint8)
     psb = np.full((N, nb + 4), 0xFF, dtype=np.uint8)
@@ -388,8 +392,8 @@ def test_mx_gemm_row_major_partial_scale_group(M, N, K):
     A, B = u8_dev(qa), u8_dev(qb)
     SA, SB = u8_dev(psa)[:, :nb], u8_dev(psb)[:, :nb]
     say(f"mx gemm row-major partial scale group {M}x{N}x{K}")
-    Cr, amr = sq.mx_scaled_gemm(A, E4M3.code, SA, B, E4M3.code, SB, want_amax=True)
-    Cp, amp = sq.mx_scaled_gemm_packed(A, E4M3.code, sq.mx_pack_scales(SA), B, E4M3.code, sq.mx_pack_scales(SB),
+    Cr, amr = sq.mx_scaled_gemm(A, fa.code, SA, B, fb.code, SB, want_amax=True)
+    Cp, amp = sq.mx_scaled_gemm_packed(A, fa.code, sq.mx_pack_scales(SA), B, fb.code, sq.mx_pack_scales(SB),
                                        want_amax=True)
     torch.cuda.synchronize()
     assert torch.equal(Cr.view(torch.int16), Cp.view(torch.int16)) and f32_bits_of(amr) == f32_bits_of(amp)
@@ -401,9 +405,9 @@ def test_mx_gemm_row_major_partial_scale_group(M, N, K):
         rs, cs = _tile_rows(rng, M), _tile_rows(rng, N)
     got = host_f64(Cr[torch.from_numpy(rs).to(DEV)][:, torch.from_numpy(cs).to(DEV)])
     a, b, ssa, ssb = qa[rs], qb[cs], sa[rs], sb[cs]
-    assert_gemm_close(got, oracle.mx_gemm_ref(a, ssa, E4M3, b, ssb, E4M3),
-                      oracle.mx_abs_product_sum(a, ssa, E4M3, b, ssb, E4M3), True, f"mx rm {M}x{N}x{K}",
-                      mfma_operands_mx(a, ssa, E4M3, b, ssb, E4M3))
+    assert_gemm_close(got, oracle.mx_gemm_ref(a, ssa, fa, b, ssb, fb),
+                      oracle.mx_abs_product_sum(a, ssa, fa, b, ssb, fb), True, f"mx rm {M}x{N}x{K}",
+                      mfma_operands_mx(a, ssa, fa, b, ssb, fb))
 
 
 def test_mx_gemm_extreme_block_scales():
