@@ -11,18 +11,18 @@
 // Answered": per-block scaling, each block with its own factor.
 //
 // Two kernels.
-//   * gemm_fwd_kernel: K % 128 == 0, both operands K-contiguous (the
-//     forward product Y = X W^T and every MX product of that shape) or, in
-//     the per-tensor product, either operand MN-major ([K x M] / [K x N]
-//     storage, the backward products dX = dY W and dW = dY^T X): 32x32x64
-//     MFMAs fed from a two-slot LDS pipeline (three slots for long per-tensor
-//     products on small grids) with asynchronous global -> LDS copies; an
-//     MN-major operand is copied as K rows and its fragments are read with
-//     the LDS transpose read ds_read_b64_tr_b8.  Described where it is
-//     defined.
-//   * gemm_kernel: every other case (a K tail, K % 128 != 0; MX with
-//     K < 512, or on row-major scale rows that are not 4-byte aligned) with
-//     the design below.
+//   * gemm_fwd_kernel: every per-tensor product (both operands
+//     K-contiguous, the forward product Y = X W^T, or either one MN-major,
+//     [K x M] / [K x N] storage, the backward products dX = dY W and
+//     dW = dY^T X; any K, a last partial K stage included) and every MX
+//     product with K % 128 == 0 and K >= 512: 32x32x64 MFMAs fed from a
+//     two-slot LDS pipeline (three slots for long per-tensor products on
+//     small grids) with asynchronous global -> LDS copies; an MN-major
+//     operand is copied as K rows and its fragments are read with the LDS
+//     transpose read ds_read_b64_tr_b8.  Described where it is defined.
+//   * gemm_kernel: every other case (MX with K % 128 != 0 or K < 512, or on
+//     row-major scale rows that are not 4-byte aligned; K = 0) with the
+//     design below.
 //
 // gemm_kernel's CDNA4 mapping.
 //   * Macro tile 256 (M) x 256 (N) x 128 (K bytes), 256 lanes = 4 waves in a
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmArgs g) {
 
 
 // ===========================================================================
-// Forward-layout kernel (both operands K-contiguous, K % 128 == 0).
+// Forward kernel (32x32x64 MFMAs from LDS-DMA stages; K-contiguous or MN-major operands).
 // ===========================================================================
 // Global -> LDS copies are issued as inline assembly
 // (buffer_load_dwordx4 ... lds): for the compiler's own LDS-DMA builtin, its
@@ -628,17 +628,18 @@ struct TileSrd {
   v4i a, b, sa, sb;
 };
 
-template <int FA, int FB, bool MX, int BMX, int NSLOT, bool TA = false, bool TB = false, bool PG = false>
+template <int FA, int FB, bool MX, int BMX, int NSLOT, bool TA = false, bool TB = false, bool TL = false>
 __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // BMX: tile rows (256, or 128 for grids with fewer 256 x 256 tiles than
   // compute units).  A 256-row tile puts the 4 waves in 2 x 2, each 128 x
   // 128 of C; a 128-row tile in 1 x 4, each 128 x 64 (4 op(A) and 2 op(B)
   // fragments, 8 MFMAs per sub-step, 12 copies per stage).
   static_assert(BMX == 256 || BMX == 128, "tile rows");
-  // PG: MX on row-major scales with a partial last group of scale codes
-  // (K % 512 != 0); its own instantiation, so that the others carry none of
-  // the selects that group needs (they cost packed products 2-5%).
-  static_assert(!PG || MX, "partial scale groups are MX only");
+  // TL (tail): the last K stage or scale group is partial.  MX on row-major
+  // scales: the last group of scale codes (K % 512 != 0); per-tensor:
+  // K % 128 != 0, the last stage's K-contiguous copies read zeros past K.
+  // Its own instantiation, so that the others carry none of its selects
+  // (in every instantiation they had cost packed MX products 2-5%).
   constexpr int NI = BMX == 256 ? 4 : 2;            // op(B) fragments per wave
   constexpr int WN = NI * 32;                       // C columns per wave
   constexpr int NA = BMX / 32;                      // op(A) copies per stage per wave
@@ -693,7 +694,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   const int tiles_n = (int)((g.N + BN - 1) / BN);
   const int tiles = tiles_m * tiles_n;
   const int P = gridDim.x;                          // persistent: tiles vb, vb + P, ...
-  const int nk = (int)(g.K / BK);                   // K % 128 == 0, nk < 2^24
+  // stages (K % 128 == 0 unless TL), nk < 2^24
+  const int nk = (int)(TL ? (g.K + BK - 1) / BK : g.K / BK);
   const int nkb = 4 * nk;                           // 32-wide K blocks
   const int nkU = (nk + U - 1) / U * U;             // stages run per tile (zero stages past nk)
   const int ngroups = nkU / 4;                      // MX scale copies per tile
@@ -705,7 +707,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // nk run on zero operands with whatever codes the other dwords hold.
   auto gsh = [&](int G) {
     const int s = 4 * G + 4 - nk;
-    return (!PG || G >= ngroups || s < 0) ? 0 : s;
+    return (!(TL && MX) || G >= ngroups || s < 0) ? 0 : s;
   };
 
   auto make_tile = [&](int vb, TileSrd& T) {
@@ -752,6 +754,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // offset rides in soffset.  Offsets do not depend on the tile: a row past
   // the matrix has offset >= ra * ld >= (ra - 1) * ld + K, the panel's size.
   const int cl = (lane & 7) ^ (lane >> 3);          // ^ (blk & 1) = ^ (i & 1) below
+  // Per-tensor K tail: in the last stage a K-contiguous copy whose chunk
+  // (cl ^ (i & 1)) starts at or past K % 128 gets an offset out of range
+  // and reads zeros (it would read the next row's bytes).  An MN-major
+  // operand's K rows past K are past its descriptor already: the range
+  // check counts soffset, where the stage's K offset rides (measured with
+  // an in-bounds probe: voffset + soffset >= num_records reads zero).
+  const int krem = (int)(g.K % BK);
+  const bool tail_e = TL && !MX && krem > 0 && 16 * cl >= krem;
+  const bool tail_o = TL && !MX && krem > 0 && 16 * (cl ^ 1) >= krem;
   // MN-major: block b of the stage is K rows 4b .. 4b+3 (256 bytes each;
   // 8b .. 8b+7 of 128 bytes for op(A) of a 128-row tile); lane L lands at
   // row 4b + L/16, stored chunk L%16 (8b + L/8, L%8), so it fetches logical
@@ -820,7 +831,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     const uint32_t k0 = (uint32_t)((nx ? s - nkU : s) * BK);
     const bool isb = t >= NA;
     const int i = isb ? t - NA : t;
-    const uint32_t off = isb ? offb[i] : offa[i];
+    uint32_t off = isb ? offb[i] : offa[i];
+    if constexpr (TL && !MX) {
+      if (!(isb ? TB : TA)) off = (!nx && s == nk - 1 && ((i & 1) ? tail_o : tail_e)) ? kOOB : off;
+    }
     const uint32_t la = lds0 + (uint32_t)(isb ? kRegB + (wave * 8 + i) * 1024 + slot * kSlotB
                                               : (wave * NA + i) * 1024 + slot * kSlotA);
     v4i srd = isb ? cur.b : cur.a;
@@ -852,7 +866,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
       // packed: group G is the 4 KiB block G of the tile (whole lines);
       // row-major: bytes 16 G .. 16 G + 15 of each row
       uint32_t so = (uint32_t)(nx ? 0 : (pk ? G * kPackTile : 16 * G));
-      if constexpr (PG) so -= (uint32_t)(4 * gsh(G));
+      if constexpr (TL) so -= (uint32_t)(4 * gsh(G));
       const uint32_t la = ldss + (uint32_t)((((gbase + G) & 1) * 2 * BM + wave * 64) * 16);
       v4i sa = cur.sa, sb = cur.sb;
       if constexpr (PERSIST) {
@@ -876,7 +890,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // 0 and 1 and of dwords (2, 3) into that of stages 2 and 3: stage p,
   // sub-step h takes byte 2 (p & 1) + h (op_sel) of register p >> 1.  Rows
   // 16 bytes apart read as one contiguous span: no bank conflicts.  A
-  // partial last group (PG) first drops its gsh(G) leading dwords (uniform
+  // partial last group (TL) first drops its gsh(G) leading dwords (uniform
   // selects; the identity on whole groups).
   const uint32_t psel = (lane >> 5) ? 0x07050301u : 0x06040200u;
   auto read_group = [&](int G, int (&lo)[8], int (&hi)[8], int j0, int j1) {
@@ -888,7 +902,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
         uint4 da = *reinterpret_cast<const uint4*>(&s_scale[((gs * 2) * BM + wm * 128 + j * 32 + (lane & 31)) * 4]);
         uint4 db = *reinterpret_cast<const uint4*>(
             &s_scale[((gs * 2 + 1) * BM + wn * WN + (j % NI) * 32 + (lane & 31)) * 4]);
-        if constexpr (PG) {
+        if constexpr (TL) {
           da = drop_dwords(da, sh);
           db = drop_dwords(db, sh);
         }
@@ -1258,7 +1272,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   if (g.out_amax) block_max_to_global(amax_bits, red, g.out_amax);
 }
 
-template <int FA, int FB, bool MX, bool TA, bool TB, bool PG = false>
+template <int FA, int FB, bool MX, bool TA, bool TB, bool TL = false>
 static void launch_gemm(const GemmArgs& g, hipStream_t s) {
   const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   // the forward kernel copies MX scales 16 codes (4 stages) per row at a
@@ -1268,16 +1282,19 @@ static void launch_gemm(const GemmArgs& g, hipStream_t s) {
   // per workgroup (or, with kFwdPersistent, per-tensor products walk tiles
   // with one workgroup per compute unit)
   // MN-major operands (TA / TB, per-tensor) take the forward kernel with
-  // LDS transpose reads when K % 128 == 0
+  // LDS transpose reads; per-tensor K tails (K % 128 != 0) take it too
   const int64_t ncu = device_cu_count();
-  const bool fwd = g.K > 0 && (g.K % 128) == 0 && (!MX || g.scales_dma);
-  if constexpr (MX && !PG) {
-    // row-major scales whose last group of 4 stages is partial
-    if (fwd && !g.scales_packed && (g.K % 512) != 0) {
+  if constexpr (!TL) {
+    // the last K stage (per-tensor) or group of 4 stages' scale codes
+    // (MX, row-major scales) is partial: the TL instantiation
+    const bool tail = MX ? (g.K > 0 && (g.K % 128) == 0 && g.scales_dma && !g.scales_packed && (g.K % 512) != 0)
+                         : (g.K > 0 && (g.K % 128) != 0);
+    if (tail) {
       launch_gemm<FA, FB, MX, TA, TB, true>(g, s);
       return;
     }
   }
+  const bool fwd = g.K > 0 && (TL || (g.K % 128) == 0) && (!MX || g.scales_dma);
   if (fwd) {
     if (tiles < ncu) {
       // fewer 256 x 256 tiles than compute units: 128 x 256 tiles
@@ -1285,18 +1302,18 @@ static void launch_gemm(const GemmArgs& g, hipStream_t s) {
       // three LDS slots for long per-tensor products (see gemm_fwd_kernel)
       if constexpr (!MX) {
         if (g.K >= 4096) {
-          hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 3, TA, TB, PG>), dim3((unsigned)t128),
+          hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 3, TA, TB, TL>), dim3((unsigned)t128),
                              dim3(kGemmThreads), 0, s, g);
           return;
         }
       }
-      hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 2, TA, TB, PG>), dim3((unsigned)t128), dim3(kGemmThreads),
+      hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 128, 2, TA, TB, TL>), dim3((unsigned)t128), dim3(kGemmThreads),
                          0, s, g);
       return;
     }
     const int64_t cus = (MX || !kFwdPersistent) ? tiles : ncu;
     const int64_t grid = tiles < cus ? tiles : cus;
-    hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 256, 2, TA, TB, PG>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s,
+    hipLaunchKernelGGL((gemm_fwd_kernel<FA, FB, MX, 256, 2, TA, TB, TL>), dim3((unsigned)grid), dim3(kGemmThreads), 0, s,
                        g);
   } else {
     hipLaunchKernelGGL((gemm_kernel<FA, FB, MX, TA, TB>), dim3((unsigned)tiles), dim3(kGemmThreads), 0, s, g);

@@ -20,8 +20,8 @@ Per-tensor recipes pass the backward products the codes as they are stored:
 W and X from the forward casts and dY as op(B) / op(A) stored MN-major
 (`trans_a` / `trans_b`), which the forward GEMM kernel reads with LDS
 transposes as fast as K-contiguous operands, so no transposed copy is cast.
-It needs the product's K % 128 == 0; where a product does not qualify, the
-casts also write the transposed copy (one pass) and that product reads
+Only an MN-major operand of 2 GiB or more does not qualify; then the casts
+also write the transposed copy (one pass) and that product reads
 K-contiguous operands.  The MX recipe casts W^T, X^T and dY^T
 with blocks along their new contiguous axis, the products' K.
 
@@ -57,10 +57,10 @@ RECIPES = ("current", "delayed", "mx", "constant")
 
 
 def _mn_major_ok(k: int, lda_k: int, ldb_k: int) -> bool:
-    """Whether a per-tensor product with MN-major operands runs on the fast
-    kernel: K % 128 == 0 and each MN-major operand spans < 2 GiB (K x its
-    leading dimension)."""
-    return k > 0 and k % 128 == 0 and lda_k < (1 << 31) - 4096 and ldb_k < (1 << 31) - 4096
+    """Whether a per-tensor product can read its operands MN-major: K % 16
+    == 0 (any K tail runs on the fast kernel) and each MN-major operand
+    spans < 2 GiB (K x its leading dimension)."""
+    return k > 0 and k % 16 == 0 and lda_k < (1 << 31) - 4096 and ldb_k < (1 << 31) - 4096
 
 
 def _packable(m: int, n: int, k: int) -> bool:
@@ -219,8 +219,8 @@ class Fp8Linear(torch.nn.Module):
     for every tensor); the layer has no additive bias.
 
     in_features, out_features and the token count must be multiples of 32
-    (the MX block; the per-tensor path needs 16, and multiples of 128 take the
-    fastest GEMM).  `last_output_amax` holds max |y| of the latest forward,
+    (the MX block; the per-tensor products would take any multiple of 16).
+    `last_output_amax` holds max |y| of the latest forward,
     reduced in the GEMM's epilogue, for a next layer's scale."""
 
     def __init__(self, in_features: int, out_features: int, recipe: str = "current",

@@ -71,6 +71,28 @@ def test_linear_current_scaling_matches_oracle():
 
 
 @pytest.mark.gpu
+def test_linear_backward_k_tails_on_stored_codes():
+    """T = 288 tokens and 416 outputs: the backward products' K (T for dW,
+    out for dX) are not multiples of 128, and they still read the stored
+    codes MN-major (K tails on the fast kernel); Y, dX and dW against the
+    oracle."""
+    from scaled_quantize_fp8_amd.linear import _mn_major_ok
+    need_gpu()
+    t, i, o = 288, 512, 416
+    assert _mn_major_ok(o, 0, o * i) and _mn_major_ok(t, t * o, t * i)
+    x, w, dy = _tensors(shape=(t, i, o))
+    layer = Fp8Linear(i, o, recipe="current", device=DEV)
+    with torch.no_grad():
+        layer.weight.copy_(_dev(w))
+    say("fp8 linear, current scaling, K tails in the backward")
+    y, dx, dw, amax = _run(layer, x, dy)
+    bx, bw = oracle.compute_bias(oracle.amax(x), E4M3), oracle.compute_bias(oracle.amax(w), E4M3)
+    bdy = oracle.compute_bias(oracle.amax(dy), E5M2)
+    _check_pt(y, dx, dw, x, w, dy, bx, bw, bdy)
+    assert host(amax)[0] == np.max(np.abs(y))
+
+
+@pytest.mark.gpu
 def test_linear_delayed_scaling_three_steps():
     """Activations whose scale jumps (x1, x16, x1/8): the layer's biases follow
     the oracle's delayed-scaling history (step 0 current, later steps the

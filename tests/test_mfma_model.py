@@ -5,8 +5,9 @@ bug).
 CPU: the model's values on hand-worked product lists.  GPU: the same lists
 placed in single rows of A and B and multiplied by the library's own GEMM
 entry points, on every kernel path the library has (32x32x64 instructions
-with 128- and 256-row tiles, 16x16x128 instructions for a transposed operand,
-the block-scaled forms of both, packed and row-major scales), E4M3 x E4M3 and
+with 128- and 256-row tiles, an MN-major operand read by LDS transposes and
+a K tail; the block-scaled form with packed and row-major scales; 16x16x128
+instructions for a block-scaled product with K % 128 != 0), E4M3 x E4M3 and
 E5M2 x E4M3, fp32 output: every diagonal output must equal the model exactly
 (each case's sums are exact in float32), every other output must agree with
 the model to float32 accumulation and the untouched rows must stay zero."""
@@ -122,7 +123,8 @@ PATHS = [
     # (id, kind, M, K)
     ("pt_32x32x64_tile128", "pt", 32, 128),
     ("pt_32x32x64_tile256", "pt", 4096, 128),
-    ("pt_16x16x128_transposed_b", "pt_tb", 32, 128),
+    ("pt_32x32x64_mn_major_b", "pt_tb", 32, 128),
+    ("pt_32x32x64_k_tail", "pt", 32, 144),
     ("mx_32x32x64", "mx", 32, 512),
     ("mx_32x32x64_packed", "mx_packed", 32, 512),
     ("mx_16x16x128_k96", "mx", 32, 96),

@@ -213,6 +213,42 @@ def test_gemm_mn_major_operands_forward_kernel(ta, tb, M, N, K):
     _check_amax(C, am)
 
 
+@pytest.mark.parametrize("M,N,K", [(4112, 4112, 528), (272, 528, 1104), (272, 528, 4208), (48, 80, 16)],
+                         ids=["289tiles_K528", "small_K1104", "small_K4208", "one_partial_stage_K16"])
+@pytest.mark.parametrize("ta,tb", [(False, False), (False, True), (True, False), (True, True)],
+                         ids=["TN", "NT", "TN_a", "TT"])
+def test_gemm_k_tail_forward_kernel(ta, tb, M, N, K):
+    """K % 128 != 0 on the forward kernel: the last stage holds K % 128 =
+    16, 80 or 112 bytes (or is the only stage, K = 16), and its copies read
+    zeros past K (K-contiguous chunks and MN-major K rows alike), on a grid
+    of 289 256 x 256 tiles and on small grids (128 x 256 tiles, two and
+    three LDS slots).  Every output against the oracle; bit for bit equal to
+    the same product with both operands padded by zero bytes to a multiple
+    of 128 in K (which runs without the tail) and across operand layouts."""
+    rng = np.random.default_rng(27 + K)
+    qa, ba = _operand(rng, (M, K), 1e-4, E5M2)
+    qb, bb = _operand(rng, (N, K), 0.02, E4M3)
+    say(f"gemm K tail ta={ta} tb={tb} {M}x{N}x{K}")
+    C, am = _run_pt(qa, E5M2, ba, qb, E4M3, bb, ta, tb, torch.bfloat16)
+    kp = (K + 127) // 128 * 128
+    pa = np.zeros((M, kp), dtype=np.uint8)
+    pb = np.zeros((N, kp), dtype=np.uint8)
+    pa[:, :K], pb[:, :K] = qa, qb
+    C0, am0 = _run_pt(pa, E5M2, ba, pb, E4M3, bb, False, False, torch.bfloat16)
+    assert torch.equal(C.view(torch.int16), C0.view(torch.int16)) and f32_bits_of(am) == f32_bits_of(am0)
+    if M * N <= 272 * 528:
+        rs, cs = np.arange(M), np.arange(N)
+    else:
+        rng2 = np.random.default_rng(K)
+        rs, cs = _tile_rows(rng2, M), _tile_rows(rng2, N)
+    got = host_f64(C[torch.from_numpy(rs).to(DEV)][:, torch.from_numpy(cs).to(DEV)])
+    a, b = qa[rs], qb[cs]
+    assert_gemm_close(got, oracle.scaled_gemm_ref(a, E5M2, ba, b, E4M3, bb),
+                      oracle.abs_product_sum(a, E5M2, ba, b, E4M3, bb), True, f"K tail {ta}{tb} {M}x{N}x{K}",
+                      mfma_operands_pt(a, E5M2, ba, b, E4M3, bb))
+    _check_amax(C, am)
+
+
 def test_gemm_degenerate_shapes():
     rng = np.random.default_rng(23)
     qa, ba = _operand(rng, (64, 32), 1.0, E4M3)
