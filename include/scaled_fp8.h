@@ -414,10 +414,11 @@ int mx_quantize_t_packed(const void* x, int dtype, int64_t rows, int64_t cols, i
  * mx_scaled_gemm_packed — mx_scaled_gemm with both scale operands in the
  * packed layout (A_packed from mx_pack_scales of A's [M x K/32] codes or from
  * mx_quantize_packed / mx_quantize_t_packed, B_packed likewise for B's
- * [N x K/32] codes).  Same result, bit for bit, as
- * mx_scaled_gemm on the row-major codes.  Requirements: those of
- * mx_scaled_gemm, plus K % 128 == 0 and K >= 512 (else FP8_ERR_UNSUPPORTED:
- * use mx_scaled_gemm) and 16-byte aligned packed buffers (FP8_ERR_ALIGN).
+ * [N x K/32] codes).  Same result as mx_scaled_gemm on the row-major codes,
+ * bit for bit where that call runs the same kernel (4-byte aligned scale
+ * rows, K % 128 == 0, K >= 512); this call runs it for every K.
+ * Requirements: those of mx_scaled_gemm, plus K > 0 (else
+ * FP8_ERR_UNSUPPORTED) and 16-byte aligned packed buffers (FP8_ERR_ALIGN).
  */
 int mx_scaled_gemm_packed(int64_t M, int64_t N, int64_t K,
                           const uint8_t* A, int fmt_a, int64_t lda, const uint8_t* A_packed,

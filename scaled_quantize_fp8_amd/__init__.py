@@ -567,7 +567,8 @@ def mx_scaled_gemm_packed(A: torch.Tensor, fmt_a, A_packed: torch.Tensor, B: tor
                           amax_out: torch.Tensor | None = None):
     """mx_scaled_gemm with both scale operands in the packed layout
     (mx_pack_scales of A's [M x K/32] and B's [N x K/32] codes); needs
-    K % 128 == 0 and K >= 512.  Returns (C, amax of C or None)."""
+    K > 0 (K % 32 == 0 as for mx_scaled_gemm).  Returns (C, amax of C or
+    None)."""
     _u8(A, "A")
     _u8(B, "B")
     _u8(A_packed, "A_packed")

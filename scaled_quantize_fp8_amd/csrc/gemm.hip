@@ -15,14 +15,15 @@
 //     K-contiguous, the forward product Y = X W^T, or either one MN-major,
 //     [K x M] / [K x N] storage, the backward products dX = dY W and
 //     dW = dY^T X; any K, a last partial K stage included) and every MX
-//     product with K % 128 == 0 and K >= 512: 32x32x64 MFMAs fed from a
+//     product on packed scales, or on row-major scales with K % 128 == 0
+//     and K >= 512: 32x32x64 MFMAs fed from a
 //     two-slot LDS pipeline (three slots for long per-tensor products on
 //     small grids) with asynchronous global -> LDS copies; an MN-major
 //     operand is copied as K rows and its fragments are read with the LDS
 //     transpose read ds_read_b64_tr_b8.  Described where it is defined.
-//   * gemm_kernel: every other case (MX with K % 128 != 0 or K < 512, or on
-//     row-major scale rows that are not 4-byte aligned; K = 0) with the
-//     design below.
+//   * gemm_kernel: every other case (MX on row-major scales with
+//     K % 128 != 0, K < 512 or rows that are not 4-byte aligned; K = 0)
+//     with the design below.
 //
 // gemm_kernel's CDNA4 mapping.
 //   * Macro tile 256 (M) x 256 (N) x 128 (K bytes), 256 lanes = 4 waves in a
@@ -91,7 +92,7 @@ struct GemmArgs {
   int row16;                 // C and every row start 16-byte aligned (full-line bf16 stores)
   int sa_dword;            // scale rows 4-byte aligned: one dword per stage
   int sb_dword;
-  int scales_dma;          // both scale matrices dword-aligned rows, K % 128 == 0, K >= 512
+  int scales_dma;          // forward kernel's scale copies: packed, or dword-aligned rows with K >= 512
   int scales_packed;       // sa / sb in the tiled layout of mx_pack_scales (forward kernel only)
   int64_t sgroups;         // packed layout: 16-block groups per row, ceil(K / 512)
 };
@@ -636,8 +637,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // fragments, 8 MFMAs per sub-step, 12 copies per stage).
   static_assert(BMX == 256 || BMX == 128, "tile rows");
   // TL (tail): the last K stage or scale group is partial.  MX on row-major
-  // scales: the last group of scale codes (K % 512 != 0); per-tensor:
-  // K % 128 != 0, the last stage's K-contiguous copies read zeros past K.
+  // scales: the last group of scale codes (K % 512 != 0, K % 128 == 0);
+  // per-tensor, and MX on packed scales: K % 128 != 0, the last stage's
+  // K-contiguous copies read zeros past K.
   // Its own instantiation, so that the others carry none of its selects
   // (in every instantiation they had cost packed MX products 2-5%).
   constexpr int NI = BMX == 256 ? 4 : 2;            // op(B) fragments per wave
@@ -707,7 +709,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // nk run on zero operands with whatever codes the other dwords hold.
   auto gsh = [&](int G) {
     const int s = 4 * G + 4 - nk;
-    return (!(TL && MX) || G >= ngroups || s < 0) ? 0 : s;
+    return (!(TL && MX) || pk || G >= ngroups || s < 0) ? 0 : s;
   };
 
   auto make_tile = [&](int vb, TileSrd& T) {
@@ -754,15 +756,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // offset rides in soffset.  Offsets do not depend on the tile: a row past
   // the matrix has offset >= ra * ld >= (ra - 1) * ld + K, the panel's size.
   const int cl = (lane & 7) ^ (lane >> 3);          // ^ (blk & 1) = ^ (i & 1) below
-  // Per-tensor K tail: in the last stage a K-contiguous copy whose chunk
+  // K tail (per-tensor K % 128 != 0; MX on packed scales, whose padding
+  // codes are 127, K % 128 != 0): in the last stage a K-contiguous copy whose chunk
   // (cl ^ (i & 1)) starts at or past K % 128 gets an offset out of range
   // and reads zeros (it would read the next row's bytes).  An MN-major
   // operand's K rows past K are past its descriptor already: the range
   // check counts soffset, where the stage's K offset rides (measured with
   // an in-bounds probe: voffset + soffset >= num_records reads zero).
   const int krem = (int)(g.K % BK);
-  const bool tail_e = TL && !MX && krem > 0 && 16 * cl >= krem;
-  const bool tail_o = TL && !MX && krem > 0 && 16 * (cl ^ 1) >= krem;
+  const bool tail_e = TL && krem > 0 && 16 * cl >= krem;
+  const bool tail_o = TL && krem > 0 && 16 * (cl ^ 1) >= krem;
   // MN-major: block b of the stage is K rows 4b .. 4b+3 (256 bytes each;
   // 8b .. 8b+7 of 128 bytes for op(A) of a 128-row tile); lane L lands at
   // row 4b + L/16, stored chunk L%16 (8b + L/8, L%8), so it fetches logical
@@ -832,7 +835,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
     const bool isb = t >= NA;
     const int i = isb ? t - NA : t;
     uint32_t off = isb ? offb[i] : offa[i];
-    if constexpr (TL && !MX) {
+    if constexpr (TL) {
       if (!(isb ? TB : TA)) off = (!nx && s == nk - 1 && ((i & 1) ? tail_o : tail_e)) ? kOOB : off;
     }
     const uint32_t la = lds0 + (uint32_t)(isb ? kRegB + (wave * 8 + i) * 1024 + slot * kSlotB
@@ -1285,9 +1288,11 @@ static void launch_gemm(const GemmArgs& g, hipStream_t s) {
   // LDS transpose reads; per-tensor K tails (K % 128 != 0) take it too
   const int64_t ncu = device_cu_count();
   if constexpr (!TL) {
-    // the last K stage (per-tensor) or group of 4 stages' scale codes
-    // (MX, row-major scales) is partial: the TL instantiation
-    const bool tail = MX ? (g.K > 0 && (g.K % 128) == 0 && g.scales_dma && !g.scales_packed && (g.K % 512) != 0)
+    // the last K stage (per-tensor, MX on packed scales) or group of 4
+    // stages' scale codes (MX on row-major scales) is partial: the TL
+    // instantiation
+    const bool tail = MX ? (g.K > 0 && g.scales_dma &&
+                            (g.scales_packed ? (g.K % 128) != 0 : (g.K % 128) == 0 && (g.K % 512) != 0))
                          : (g.K > 0 && (g.K % 128) != 0);
     if (tail) {
       launch_gemm<FA, FB, MX, TA, TB, true>(g, s);
@@ -1496,7 +1501,7 @@ int mx_scaled_gemm_packed(int64_t M, int64_t N, int64_t K, const uint8_t* A, int
   if (check_matrix(M, N, ldc) || check_matrix(M, K, lda) || check_matrix(N, K, ldb)) return FP8_ERR_SHAPE;
   if (M > 0 && N > 0 && !C) return FP8_ERR_NULL;
   if (M > 0 && N > 0) {
-    if ((K % 128) != 0 || K < 512) return FP8_ERR_UNSUPPORTED;
+    if (K == 0) return FP8_ERR_UNSUPPORTED;
     if (!A || !B || !A_packed || !B_packed) return FP8_ERR_NULL;
     if (!aligned(A_packed, 16) || !aligned(B_packed, 16)) return FP8_ERR_ALIGN;
     int st = check_operand(A, lda, false, K);

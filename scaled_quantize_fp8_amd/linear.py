@@ -65,9 +65,10 @@ def _mn_major_ok(k: int, lda_k: int, ldb_k: int) -> bool:
 
 def _packable(m: int, n: int, k: int) -> bool:
     """Whether an MX product of these sizes runs on packed scales: the casts
-    then write the layout the GEMM copies whole cache lines of (same result,
-    bit for bit)."""
-    return k % 128 == 0 and k >= 512 and m > 0 and n > 0
+    then write the layout the GEMM copies whole cache lines of (the fast
+    kernel for every K; same result, bit for bit, as row-major scales where
+    both run it)."""
+    return k > 0 and k % 32 == 0 and m > 0 and n > 0
 
 
 class _History:

@@ -228,8 +228,7 @@ void gemms() {
                int64_t ldb, const uint8_t* pb, void* C, int64_t ldc) {
     return mx_scaled_gemm_packed(M, N, K, A, 0, lda, pa, B, 0, ldb, pb, C, 0, ldc, nullptr, S);
   };
-  expect("packed gemm K % 128", p(64, 64, 544, U16, 544, U16, U16, 544, U16, A16, 64), FP8_ERR_UNSUPPORTED);
-  expect("packed gemm K < 512", p(64, 64, 256, U16, 256, U16, U16, 256, U16, A16, 64), FP8_ERR_UNSUPPORTED);
+  expect("packed gemm K == 0", p(64, 64, 0, U16, 16, U16, U16, 16, U16, A16, 64), FP8_ERR_UNSUPPORTED);
   expect("packed gemm unaligned scales", p(64, 64, 512, U16, 512, U1, U16, 512, U16, A16, 64), FP8_ERR_ALIGN);
   expect("packed gemm null scales", p(64, 64, 512, U16, 512, nullptr, U16, 512, U16, A16, 64), FP8_ERR_NULL);
   expect("packed gemm null C", p(64, 64, 512, U16, 512, U16, U16, 512, U16, nullptr, 64), FP8_ERR_NULL);

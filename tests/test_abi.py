@@ -244,8 +244,7 @@ def test_packed_scales_size_and_validation(lib):
     assert t(FAKE, 0, 64, 16, 16, 0, 7, FAKE, 64, FAKE, S) == FORMAT
     g = lib.mx_scaled_gemm_packed
     # M, N, K, A, fa, lda, Ap, B, fb, ldb, Bp, C, dt, ldc, amax, s
-    assert g(64, 64, 256, FAKE, 0, 256, FAKE, FAKE, 0, 256, FAKE, FAKE, 0, 64, None, S) == UNSUP
-    assert g(64, 64, 576, FAKE, 0, 576, FAKE, FAKE, 0, 576, FAKE, FAKE, 0, 64, None, S) == UNSUP
+    assert g(64, 64, 0, FAKE, 0, 16, FAKE, FAKE, 0, 16, FAKE, FAKE, 0, 64, None, S) == UNSUP
     assert g(64, 64, 48, FAKE, 0, 48, FAKE, FAKE, 0, 48, FAKE, FAKE, 0, 64, None, S) == SHAPE
     assert g(64, 64, 512, FAKE, 0, 512, None, FAKE, 0, 512, FAKE, FAKE, 0, 64, None, S) == NULL
     assert g(64, 64, 512, FAKE, 0, 512, FAKE, FAKE, 0, 512, FAKE + 4, FAKE, 0, 64, None, S) == ALIGN

@@ -446,6 +446,43 @@ def test_mx_gemm_row_major_partial_scale_group(M, N, K, fa, fb):
                       mfma_operands_mx(a, ssa, fa, b, ssb, fb))
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 260, 672), (300, 260, 416), (130, 1030, 96), (4352, 4096, 736)],
+                         ids=["300x260x672", "300x260x416", "130x1030x96", "4352x4096x736"])
+def test_mx_gemm_packed_k_tail(M, N, K):
+    """Packed scales with K % 128 != 0 (and K < 512) on the 32x32x64 kernel:
+    the last stage holds 1 or 3 blocks of 32 (or is the only stage, K = 96),
+    its copies read zeros past K and its missing blocks take the layout's
+    padding code 127.  Bit for bit equal to the same product with both
+    operands padded by zero bytes to a multiple of 128 in K (the same packed
+    scales: the padding blocks are 127 either way), and the oracle within
+    tolerance (every output, or two rows and columns per tile)."""
+    xb = make("c4", "X", shape=(M, K))
+    wb = make("c4", "W", shape=(N, K))
+    qa, sa = oracle.mx_quantize(oracle.bf16_bits_to_f64(xb), E4M3)
+    qb, sb = oracle.mx_quantize(oracle.bf16_bits_to_f64(wb), E4M3)
+    PA, PB = sq.mx_pack_scales(u8_dev(sa)), sq.mx_pack_scales(u8_dev(sb))
+    say(f"mx gemm packed K tail {M}x{N}x{K}")
+    C, am = sq.mx_scaled_gemm_packed(u8_dev(qa), E4M3.code, PA, u8_dev(qb), E4M3.code, PB, want_amax=True)
+    kp = (K + 127) // 128 * 128
+    pa = np.zeros((M, kp), dtype=np.uint8)
+    pb = np.zeros((N, kp), dtype=np.uint8)
+    pa[:, :K], pb[:, :K] = qa, qb
+    C0, am0 = sq.mx_scaled_gemm_packed(u8_dev(pa), E4M3.code, PA, u8_dev(pb), E4M3.code, PB, want_amax=True)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), C0.view(torch.int16)) and f32_bits_of(am) == f32_bits_of(am0)
+    _check_amax(C, am)
+    if M * N <= 300 * 260:
+        rs, cs = np.arange(M), np.arange(N)
+    else:
+        rng = np.random.default_rng(K)
+        rs, cs = _tile_rows(rng, M), _tile_rows(rng, N)
+    got = host_f64(C[torch.from_numpy(rs).to(DEV)][:, torch.from_numpy(cs).to(DEV)])
+    a, b, ssa, ssb = qa[rs], qb[cs], sa[rs], sb[cs]
+    assert_gemm_close(got, oracle.mx_gemm_ref(a, ssa, E4M3, b, ssb, E4M3),
+                      oracle.mx_abs_product_sum(a, ssa, E4M3, b, ssb, E4M3), True, f"mx packed tail {M}x{N}x{K}",
+                      mfma_operands_mx(a, ssa, E4M3, b, ssb, E4M3))
+
+
 def test_mx_gemm_extreme_block_scales():
     """Per-block codes spread over a wide range (2^-40 .. 2^40 per block), so a
     wrong block <-> scale pairing cannot hide inside the tolerance."""
