@@ -345,9 +345,9 @@ int fp8_scaled_gemm(int64_t M, int64_t N, int64_t K,
  * and B_scales [N x K/32] E8M0 codes (as written by mx_quantize), fp32
  * accumulation, C [M x N] bf16 or fp32, optional fused out_amax as above.
  * Requirements: K % 32 == 0; A, B 16-byte aligned with lda, ldb multiples of
- * 16.  Scales may have any alignment; with 4-byte aligned scale rows,
- * K % 128 == 0 and K >= 512 the product runs the faster kernel (the bytes
- * after a scale row's K/32 codes are never read).
+ * 16.  Scales may have any alignment; with 4-byte aligned scale rows and
+ * K >= 512 the product runs the faster kernel (the bytes after a scale
+ * row's K/32 codes are never read).
  */
 int mx_scaled_gemm(int64_t M, int64_t N, int64_t K,
                    const uint8_t* A, int fmt_a, int64_t lda,
@@ -416,7 +416,7 @@ int mx_quantize_t_packed(const void* x, int dtype, int64_t rows, int64_t cols, i
  * mx_quantize_packed / mx_quantize_t_packed, B_packed likewise for B's
  * [N x K/32] codes).  Same result as mx_scaled_gemm on the row-major codes,
  * bit for bit where that call runs the same kernel (4-byte aligned scale
- * rows, K % 128 == 0, K >= 512); this call runs it for every K.
+ * rows, K >= 512); this call runs it for every K.
  * Requirements: those of mx_scaled_gemm, plus K > 0 (else
  * FP8_ERR_UNSUPPORTED) and 16-byte aligned packed buffers (FP8_ERR_ALIGN).
  */

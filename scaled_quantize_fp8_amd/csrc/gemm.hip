@@ -15,15 +15,14 @@
 //     K-contiguous, the forward product Y = X W^T, or either one MN-major,
 //     [K x M] / [K x N] storage, the backward products dX = dY W and
 //     dW = dY^T X; any K, a last partial K stage included) and every MX
-//     product on packed scales, or on row-major scales with K % 128 == 0
-//     and K >= 512: 32x32x64 MFMAs fed from a
+//     product on packed scales, or on 4-byte aligned row-major scale rows
+//     with K >= 512: 32x32x64 MFMAs fed from a
 //     two-slot LDS pipeline (three slots for long per-tensor products on
 //     small grids) with asynchronous global -> LDS copies; an MN-major
 //     operand is copied as K rows and its fragments are read with the LDS
 //     transpose read ds_read_b64_tr_b8.  Described where it is defined.
-//   * gemm_kernel: every other case (MX on row-major scales with
-//     K % 128 != 0, K < 512 or rows that are not 4-byte aligned; K = 0)
-//     with the design below.
+//   * gemm_kernel: every other case (MX on row-major scales with K < 512 or
+//     rows that are not 4-byte aligned; K = 0) with the design below.
 //
 // gemm_kernel's CDNA4 mapping.
 //   * Macro tile 256 (M) x 256 (N) x 128 (K bytes), 256 lanes = 4 waves in a
@@ -498,12 +497,16 @@ template <int N> __device__ __forceinline__ void wait_vm() {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// The four dwords of v with the first s (uniform, 0..3) dropped: dword d of
-// the result is dword d + s of v where d + s < 4; the rest repeat dwords of v.
-__device__ __forceinline__ uint4 drop_dwords(uint4 v, int s) {
-  const bool h = (s & 2) != 0, o = (s & 1) != 0;
+// The 16 bytes of v with the first s (uniform, 0..15) dropped: byte j of the
+// result is byte j + s of v where j + s < 16; the rest repeat bytes of v.
+__device__ __forceinline__ uint4 drop_bytes(uint4 v, int s) {
+  const int q = s >> 2, b = s & 3;
+  const bool h = (q & 2) != 0, o = (q & 1) != 0;
   const uint32_t u0 = h ? v.z : v.x, u1 = h ? v.w : v.y;
-  return make_uint4(o ? u1 : u0, o ? v.z : u1, o ? v.w : v.z, v.w);
+  const uint4 d = make_uint4(o ? u1 : u0, o ? v.z : u1, o ? v.w : v.z, v.w);   // dwords dropped
+  // then bytes: dword k takes bytes b .. 3 of d[k] and 0 .. b - 1 of d[k + 1]
+  return make_uint4(__builtin_amdgcn_alignbyte(d.y, d.x, b), __builtin_amdgcn_alignbyte(d.z, d.y, b),
+                    __builtin_amdgcn_alignbyte(d.w, d.z, b), __builtin_amdgcn_alignbyte(d.w, d.w, b));
 }
 
 // 32x32x64 MFMA with E8M0 scales picked by byte (op_sel) from packed registers.
@@ -636,10 +639,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // 128 of C; a 128-row tile in 1 x 4, each 128 x 64 (4 op(A) and 2 op(B)
   // fragments, 8 MFMAs per sub-step, 12 copies per stage).
   static_assert(BMX == 256 || BMX == 128, "tile rows");
-  // TL (tail): the last K stage or scale group is partial.  MX on row-major
-  // scales: the last group of scale codes (K % 512 != 0, K % 128 == 0);
-  // per-tensor, and MX on packed scales: K % 128 != 0, the last stage's
-  // K-contiguous copies read zeros past K.
+  // TL (tail): the last K stage or scale group is partial.  K % 128 != 0:
+  // the last stage's K-contiguous copies read zeros past K; MX on row-major
+  // scales with K % 512 != 0: the last group of scale codes is copied from
+  // 16 codes before the row's end and shifted into place.
   // Its own instantiation, so that the others carry none of its selects
   // (in every instantiation they had cost packed MX products 2-5%).
   constexpr int NI = BMX == 256 ? 4 : 2;            // op(B) fragments per wave
@@ -698,17 +701,17 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   const int P = gridDim.x;                          // persistent: tiles vb, vb + P, ...
   // stages (K % 128 == 0 unless TL), nk < 2^24
   const int nk = (int)(TL ? (g.K + BK - 1) / BK : g.K / BK);
-  const int nkb = 4 * nk;                           // 32-wide K blocks
   const int nkU = (nk + U - 1) / U * U;             // stages run per tile (zero stages past nk)
   const int ngroups = nkU / 4;                      // MX scale copies per tile
   const bool pk = MX && g.scales_packed;            // tiled scale layout (uniform)
-  // Row-major scales with nk % 4 != 0: the last group holds nk % 4 real
-  // stages.  Its copy is moved back to end at the row's end (codes
-  // nkb - 16 .. nkb - 1, inside the row since K >= 512), so stage p of the
-  // group sits at dword p + gsh(G) of the 16 bytes; the group's stages past
-  // nk run on zero operands with whatever codes the other dwords hold.
-  auto gsh = [&](int G) {
-    const int s = 4 * G + 4 - nk;
+  // Row-major scales with K % 512 != 0: the last group holds fewer than 16
+  // real codes (K / 32 of a row in all).  Its copy is moved back to end at
+  // the row's end (codes K/32 - 16 .. K/32 - 1, inside the row since
+  // K >= 512), so code c of the group sits at byte c + gsb(G) of the 16;
+  // blocks past K (zero operands) take whatever codes the other bytes hold.
+  const int kbr = (int)(g.K / 32);                  // real 32-wide K blocks of a row
+  auto gsb = [&](int G) {
+    const int s = 16 * (G + 1) - kbr;
     return (!(TL && MX) || pk || G >= ngroups || s < 0) ? 0 : s;
   };
 
@@ -735,8 +738,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
           T.sa = make_srd(g.sa + (int64_t)(tm / (256 / BMX)) * tb + ah, tb - ah);
           T.sb = make_srd(g.sb + (int64_t)tn * tb, tb);
         } else {
-          T.sa = make_srd(g.sa + m0 * g.lds_a, (ra - 1) * g.lds_a + nkb);
-          T.sb = make_srd(g.sb + n0 * g.lds_b, (rb - 1) * g.lds_b + nkb);
+          const int kb = TL ? kbr : 4 * nk;         // (the same when K % 128 == 0)
+          T.sa = make_srd(g.sa + m0 * g.lds_a, (ra - 1) * g.lds_a + kb);
+          T.sb = make_srd(g.sb + n0 * g.lds_b, (rb - 1) * g.lds_b + kb);
         }
       } else {
         T.sa = T.a;
@@ -756,8 +760,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // offset rides in soffset.  Offsets do not depend on the tile: a row past
   // the matrix has offset >= ra * ld >= (ra - 1) * ld + K, the panel's size.
   const int cl = (lane & 7) ^ (lane >> 3);          // ^ (blk & 1) = ^ (i & 1) below
-  // K tail (per-tensor K % 128 != 0; MX on packed scales, whose padding
-  // codes are 127, K % 128 != 0): in the last stage a K-contiguous copy whose chunk
+  // K tail (K % 128 != 0; the missing blocks' scale codes are the packed
+  // layout's padding, 127, or other codes of the row): in the last stage a
+  // K-contiguous copy whose chunk
   // (cl ^ (i & 1)) starts at or past K % 128 gets an offset out of range
   // and reads zeros (it would read the next row's bytes).  An MN-major
   // operand's K rows past K are past its descriptor already: the range
@@ -788,7 +793,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // MX scales: lane L of wave w copies 16 bytes (the codes of 4 stages) of
   // tile row 64 w + L of each operand.  Group G covers stages 4G .. 4G+3:
   // bytes 16 G .. 16 G + 15 of a row-major scale row (a partial last group
-  // from 4 gsh(G) bytes earlier) or the 4 KiB block G of the packed layout
+  // from gsb(G) bytes earlier) or the 4 KiB block G of the packed layout
   // (padded with code 127 past the last block).
   // L2 prefetch of op(B) (the weight panel): every stage of a tile touches a
   // new K slice of it, and all XCDs walk the same panels in step, so its
@@ -869,7 +874,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
       // packed: group G is the 4 KiB block G of the tile (whole lines);
       // row-major: bytes 16 G .. 16 G + 15 of each row
       uint32_t so = (uint32_t)(nx ? 0 : (pk ? G * kPackTile : 16 * G));
-      if constexpr (TL) so -= (uint32_t)(4 * gsh(G));
+      if constexpr (TL) so -= (uint32_t)gsb(G);
       const uint32_t la = ldss + (uint32_t)((((gbase + G) & 1) * 2 * BM + wave * 64) * 16);
       v4i sa = cur.sa, sb = cur.sb;
       if constexpr (PERSIST) {
@@ -893,21 +898,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_fwd_kernel(GemmArgs g) {
   // 0 and 1 and of dwords (2, 3) into that of stages 2 and 3: stage p,
   // sub-step h takes byte 2 (p & 1) + h (op_sel) of register p >> 1.  Rows
   // 16 bytes apart read as one contiguous span: no bank conflicts.  A
-  // partial last group (TL) first drops its gsh(G) leading dwords (uniform
+  // partial last group (TL) first drops its gsb(G) leading bytes (uniform
   // selects; the identity on whole groups).
   const uint32_t psel = (lane >> 5) ? 0x07050301u : 0x06040200u;
   auto read_group = [&](int G, int (&lo)[8], int (&hi)[8], int j0, int j1) {
     if constexpr (MX) {
       const int gs = (gbase + G) & 1;
-      const int sh = gsh(G);
+      const int sh = gsb(G);
 #pragma unroll
       for (int j = j0; j < j1; ++j) {
         uint4 da = *reinterpret_cast<const uint4*>(&s_scale[((gs * 2) * BM + wm * 128 + j * 32 + (lane & 31)) * 4]);
         uint4 db = *reinterpret_cast<const uint4*>(
             &s_scale[((gs * 2 + 1) * BM + wn * WN + (j % NI) * 32 + (lane & 31)) * 4]);
         if constexpr (TL) {
-          da = drop_dwords(da, sh);
-          db = drop_dwords(db, sh);
+          da = drop_bytes(da, sh);
+          db = drop_bytes(db, sh);
         }
         lo[j] = (int)__builtin_amdgcn_perm(da.y, da.x, psel);
         hi[j] = (int)__builtin_amdgcn_perm(da.w, da.z, psel);
@@ -1285,14 +1290,12 @@ static void launch_gemm(const GemmArgs& g, hipStream_t s) {
   // per workgroup (or, with kFwdPersistent, per-tensor products walk tiles
   // with one workgroup per compute unit)
   // MN-major operands (TA / TB, per-tensor) take the forward kernel with
-  // LDS transpose reads; per-tensor K tails (K % 128 != 0) take it too
+  // LDS transpose reads; K tails (K % 128 != 0) take it too
   const int64_t ncu = device_cu_count();
   if constexpr (!TL) {
-    // the last K stage (per-tensor, MX on packed scales) or group of 4
-    // stages' scale codes (MX on row-major scales) is partial: the TL
-    // instantiation
-    const bool tail = MX ? (g.K > 0 && g.scales_dma &&
-                            (g.scales_packed ? (g.K % 128) != 0 : (g.K % 128) == 0 && (g.K % 512) != 0))
+    // the last K stage or group of 4 stages' row-major scale codes is
+    // partial: the TL instantiation
+    const bool tail = MX ? (g.K > 0 && g.scales_dma && (g.scales_packed ? (g.K % 128) != 0 : (g.K % 512) != 0))
                          : (g.K > 0 && (g.K % 128) != 0);
     if (tail) {
       launch_gemm<FA, FB, MX, TA, TB, true>(g, s);

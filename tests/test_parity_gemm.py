@@ -405,14 +405,20 @@ def test_mx_gemm_packed_scales(fa, fb, M, N, K):
 
 @pytest.mark.parametrize("M,N,K,fa,fb", [(300, 260, 640, E4M3, E4M3), (300, 260, 768, E4M3, E4M3),
                                          (300, 260, 896, E4M3, E4M3), (4352, 4096, 896, E4M3, E4M3),
-                                         (300, 260, 1152, E5M2, E4M3), (1, 33, 2176, E4M3, E5M2)],
+                                         (300, 260, 1152, E5M2, E4M3), (1, 33, 2176, E4M3, E5M2),
+                                         (300, 260, 544, E4M3, E4M3), (300, 260, 608, E5M2, E4M3),
+                                         (4352, 4096, 992, E4M3, E4M3), (1, 33, 2080, E4M3, E5M2)],
                          ids=["300x260x640", "300x260x768", "300x260x896", "4352x4096x896", "300x260x1152_e5e4",
-                              "1x33x2176_e4e5"])
+                              "1x33x2176_e4e5", "300x260x544", "300x260x608_e5e4", "4352x4096x992",
+                              "1x33x2080_e4e5"])
 def test_mx_gemm_row_major_partial_scale_group(M, N, K, fa, fb):
     """Row-major scales with K % 512 != 0 on the 32x32x64 kernel: the last
-    4-stage group of scale codes holds 1, 2 or 3 stages (K = 640, 768, 896)
-    and is copied from 16 codes before each row's end.  Each scale row is
-    followed by 4 bytes of NaN codes (0xFF) that the kernel must not read.
+    group of 16 scale codes holds 1, 2 or 3 whole stages (K = 640, 768, 896)
+    or ends inside a stage (K % 128 != 0: 544, 608, 992, 2080, the last
+    stage's copies reading zeros past K), and is copied from 16 codes
+    before each row's end.  Each scale row is
+    followed by NaN codes (0xFF) up to a dword-aligned stride and 4 more,
+    which the kernel must not read.
     The product equals the packed-scale product bit for bit and the oracle
     within tolerance; 128-row tiles (4 tiles) and 256-row tiles (272 tiles,
     every output of two rows and columns per tile checked); also E5M2
@@ -422,8 +428,9 @@ def test_mx_gemm_row_major_partial_scale_group(M, N, K, fa, fb):
     qa, sa = oracle.mx_quantize(oracle.bf16_bits_to_f64(xb), fa)
     qb, sb = oracle.mx_quantize(oracle.bf16_bits_to_f64(wb), fb)
     nb = K // 32
-    psa = np.full((M, nb + 4), 0xFF, dtype=np.uint8)
-    psb = np.full((N, nb + 4), 0xFF, dtype=np.uint8)
+    ldp = (nb + 3) // 4 * 4 + 4                      # dword-aligned rows, at least 4 bytes of NaN codes after
+    psa = np.full((M, ldp), 0xFF, dtype=np.uint8)
+    psb = np.full((N, ldp), 0xFF, dtype=np.uint8)
     psa[:, :nb], psb[:, :nb] = sa, sb
     A, B = u8_dev(qa), u8_dev(qb)
     SA, SB = u8_dev(psa)[:, :nb], u8_dev(psb)[:, :nb]
