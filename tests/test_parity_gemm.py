@@ -453,6 +453,30 @@ def test_mx_gemm_row_major_partial_scale_group(M, N, K, fa, fb):
                       mfma_operands_mx(a, ssa, fa, b, ssb, fb))
 
 
+@pytest.mark.parametrize("K", [544, 1120], ids=["K544", "K1120"])
+def test_mx_gemm_tight_row_major_scales_k_tail(K):
+    """Row-major scales in tight rows of K/32 codes with K % 128 != 0 (rows
+    not 4-byte aligned: the 16x16x128 kernel) and the same codes packed (the
+    32x32x64 kernel with a K tail): both against the oracle, every output of
+    a ragged 300 x 260 product, bf16 and fp32 out."""
+    xb = make("c4", "X", shape=(300, K))
+    wb = make("c4", "W", shape=(260, K))
+    qa, sa = oracle.mx_quantize(oracle.bf16_bits_to_f64(xb), E4M3)
+    qb, sb = oracle.mx_quantize(oracle.bf16_bits_to_f64(wb), E4M3)
+    ref = oracle.mx_gemm_ref(qa, sa, E4M3, qb, sb, E4M3)
+    s_ = oracle.mx_abs_product_sum(qa, sa, E4M3, qb, sb, E4M3)
+    gt = mfma_operands_mx(qa, sa, E4M3, qb, sb, E4M3)
+    A, B, SA, SB = u8_dev(qa), u8_dev(qb), u8_dev(sa), u8_dev(sb)
+    for dt in (torch.bfloat16, torch.float32):
+        say(f"mx gemm tight row-major scales K={K} {dt}")
+        Cr, amr = sq.mx_scaled_gemm(A, E4M3.code, SA, B, E4M3.code, SB, out_dtype=dt, want_amax=True)
+        Cp, amp = sq.mx_scaled_gemm_packed(A, E4M3.code, sq.mx_pack_scales(SA), B, E4M3.code,
+                                           sq.mx_pack_scales(SB), out_dtype=dt, want_amax=True)
+        for what, C, am in (("row-major", Cr, amr), ("packed", Cp, amp)):
+            assert_gemm_close(host_f64(C), ref, s_, dt == torch.bfloat16, f"mx tight {what} K={K}", gt)
+            _check_amax(C, am)
+
+
 @pytest.mark.parametrize("M,N,K", [(300, 260, 672), (300, 260, 416), (130, 1030, 96), (4352, 4096, 736)],
                          ids=["300x260x672", "300x260x416", "130x1030x96", "4352x4096x736"])
 def test_mx_gemm_packed_k_tail(M, N, K):
